@@ -1,0 +1,152 @@
+"""Decode attention over the decoded grouped + residual cache (oracle; test infrastructure only).
+
+synthetic.wiki "Keys are harder than values", last bullet: attention scores combine the grouped key part and the
+residual key part. Decoding reaches exactly (up to rounding order) plain softmax attention over the decoded cache,
+so this module writes that definition out in float64:
+
+    K_hat[t, c] = code_K[t, c] * s_K[c, t // 32] + z_K[c, t // 32]      (t < n_quant)
+    V_hat[t, c] = code_V[t, c] * s_V[t, c // 32] + z_V[t, c // 32]      (t < n_quant)
+    K_hat[t], V_hat[t] = the float16 residual tokens, widened              (n_quant <= t < N)
+    score_t = sigma * sum_c q_c K_hat[t, c],  out = sum_t softmax(score)_t V_hat[t]
+
+Readings taken where the pages are silent: sigma = 1/sqrt(head_dim) unless the caller gives another scale; query
+head hq uses KV head hq // G with G = Hq / Hkv (consecutive query heads share a KV head); the output is float64
+here and float32 in the library.
+
+Long caches are processed in token chunks (two passes: the global maximum first, then the exponential sums), so
+a million-token slice never materializes in float64 all at once.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import quant
+from .cache import SliceCache
+
+CHUNK = 65536
+
+
+def decoded_range(cache: SliceCache, t0: int, t1: int):
+    """Decoded keys and values of tokens ``[t0, t1)`` of every slice, float64 ``[S, t1 - t0, D]``."""
+    g = cache.group
+    kq, ks, kz, vq, vs, vz = cache.quantized()
+    nq = cache.n_quant
+    S, D = cache.slices, cache.head_dim
+    K = np.empty((S, t1 - t0, D), np.float64)
+    V = np.empty((S, t1 - t0, D), np.float64)
+    a, b = t0, min(t1, nq)
+    if b > a:
+        # expand to whole key groups so the per-channel scale of each token is indexed by t // 32
+        ga, gb = a // g, (b + g - 1) // g
+        kh = quant.dequantize_keys(kq[:, ga * g:gb * g], ks[:, ga:gb], kz[:, ga:gb], g)
+        K[:, :b - a] = kh[:, a - ga * g:b - ga * g]
+        V[:, :b - a] = quant.dequantize_values(vq[:, a:b], vs[:, a:b], vz[:, a:b], g)
+    a2 = max(t0, nq)
+    if t1 > a2:
+        K[:, a2 - t0:] = cache.k_res[:, a2 - nq:t1 - nq].astype(np.float64)
+        V[:, a2 - t0:] = cache.v_res[:, a2 - nq:t1 - nq].astype(np.float64)
+    return K, V
+
+
+def _q_for_slices(q: np.ndarray, batch: int, kv_heads: int) -> np.ndarray:
+    """float16 [B, Hq, D] -> float64 [S = B*Hkv, G, D] (query heads grouped by the KV head they use)."""
+    B, Hq, D = q.shape
+    G = Hq // kv_heads
+    return q.astype(np.float64).reshape(B, kv_heads, G, D).reshape(B * kv_heads, G, D)
+
+
+def decode_attention(cache: SliceCache, q: np.ndarray, batch: int, kv_heads: int, sm_scale: float | None = None,
+                     chunk: int = CHUNK) -> np.ndarray:
+    """Attention output float64 ``[B, Hq, D]`` of query ``q`` (float16 ``[B, Hq, D]``) over the whole cache.
+
+    Slice index of (b, hkv) is ``b * kv_heads + hkv``.
+    """
+    B, Hq, D = q.shape
+    if cache.slices != batch * kv_heads or Hq % kv_heads:
+        raise ValueError("cache slices must be batch * kv_heads and Hq a multiple of kv_heads")
+    if cache.n_tokens == 0:
+        raise ValueError("attention over an empty cache is undefined")
+    sigma = 1.0 / np.sqrt(D) if sm_scale is None or sm_scale <= 0 else float(sm_scale)
+    qs = _q_for_slices(q, batch, kv_heads)                       # [S, G, D]
+    N = cache.n_tokens
+    S, G = qs.shape[0], qs.shape[1]
+    # pass 1: global maximum of the scores
+    m = np.full((S, G), -np.inf)
+    for t0 in range(0, N, chunk):
+        K, _ = decoded_range(cache, t0, min(N, t0 + chunk))
+        sc = sigma * np.einsum("sgd,std->sgt", qs, K)
+        m = np.maximum(m, sc.max(axis=-1))
+    # pass 2: exponential sums and the weighted sum of values
+    l = np.zeros((S, G))
+    acc = np.zeros((S, G, D))
+    for t0 in range(0, N, chunk):
+        K, V = decoded_range(cache, t0, min(N, t0 + chunk))
+        sc = sigma * np.einsum("sgd,std->sgt", qs, K)
+        p = np.exp(sc - m[..., None])
+        l += p.sum(axis=-1)
+        acc += np.einsum("sgt,std->sgd", p, V)
+    out = acc / l[..., None]
+    return out.reshape(batch, kv_heads, G, D).reshape(batch, Hq, D)
+
+
+def refolded_scores(cache: SliceCache, q: np.ndarray, batch: int, kv_heads: int, sm_scale: float | None = None):
+    """Scores over the quantized part computed with scales and zero-points folded into the query.
+
+    score_t = sigma * (sum_c (q_c * s_K[c, j]) * code_K[t, c] + sum_c q_c * z_K[c, j]),  j = t // 32.
+    This is the algebra a fused kernel uses instead of decoding the keys; float64 ``[S, G, n_quant]``.
+    """
+    D = q.shape[-1]
+    sigma = 1.0 / np.sqrt(D) if sm_scale is None or sm_scale <= 0 else float(sm_scale)
+    qs = _q_for_slices(q, batch, kv_heads)
+    kq, ks, kz, _, _, _ = cache.quantized()
+    nt = kq.shape[1] // cache.group
+    codes = kq.astype(np.float64).reshape(cache.slices, nt, cache.group, D)
+    qt = qs[:, :, None, :] * ks.astype(np.float64)[:, None, :, :]          # [S, G, tiles, D]
+    beta = np.einsum("sgd,sjd->sgj", qs, kz.astype(np.float64))            # [S, G, tiles]
+    sc = np.einsum("sgjd,sjtd->sgjt", qt, codes) + beta[..., None]
+    return sigma * sc.reshape(cache.slices, qs.shape[1], nt * cache.group)
+
+
+def refolded_values(cache: SliceCache, p: np.ndarray) -> np.ndarray:
+    """sum_t p_t V_hat[t] over the quantized part with value scales folded into p.
+
+    sum_t (p_t * s_V[t, g]) * code_V[t, c] + sum_t p_t * z_V[t, g],  g = c // 32.  ``p``: ``[S, G, n_quant]``.
+    """
+    _, _, _, vq, vs, vz = cache.quantized()
+    S, nq, D = vq.shape
+    gsz = cache.group
+    ng = D // gsz
+    codes = vq.astype(np.float64).reshape(S, nq, ng, gsz)
+    pt = p[..., None] * vs.astype(np.float64)[:, None, :, :]               # [S, G, nq, ng]
+    main = np.einsum("sgtk,stkc->sgkc", pt, codes)
+    zterm = np.einsum("sgt,stk->sgk", p, vz.astype(np.float64))
+    return (main + zterm[..., None]).reshape(S, p.shape[1], D)
+
+
+def split_partials(cache: SliceCache, q: np.ndarray, batch: int, kv_heads: int, bounds, sm_scale=None):
+    """Per-split (m, l, o) over token ranges ``bounds`` = [(t0, t1), ...]; empty ranges give (-inf, 0, 0).
+
+    m is the maximum score of the range, l = sum exp(score - m), o = sum exp(score - m) V_hat (unnormalized).
+    """
+    D = q.shape[-1]
+    sigma = 1.0 / np.sqrt(D) if sm_scale is None or sm_scale <= 0 else float(sm_scale)
+    qs = _q_for_slices(q, batch, kv_heads)
+    S, G = qs.shape[:2]
+    ms, ls, os_ = [], [], []
+    for t0, t1 in bounds:
+        if t1 <= t0:
+            ms.append(np.full((S, G), -np.inf)); ls.append(np.zeros((S, G))); os_.append(np.zeros((S, G, D)))
+            continue
+        K, V = decoded_range(cache, t0, t1)
+        sc = sigma * np.einsum("sgd,std->sgt", qs, K)
+        m = sc.max(axis=-1)
+        p = np.exp(sc - m[..., None])
+        ms.append(m); ls.append(p.sum(-1)); os_.append(np.einsum("sgt,std->sgd", p, V))
+    return np.stack(ms), np.stack(ls), np.stack(os_)
+
+
+def merge_partials(m: np.ndarray, l: np.ndarray, o: np.ndarray) -> np.ndarray:
+    """Second pass: out = sum_s e^(m_s - M) o_s / sum_s e^(m_s - M) l_s with M = max_s m_s; -inf splits drop out."""
+    M = m.max(axis=0)
+    w = np.where(np.isneginf(m), 0.0, np.exp(m - M))
+    return (w[..., None] * o).sum(0) / (w * l).sum(0)[..., None]
