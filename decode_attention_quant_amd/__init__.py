@@ -1,0 +1,185 @@
+"""Python binding of the 2-bit KV-cache library (``libkvq.so``, C ABI in ``include/kvq.h``).
+
+Argument marshalling only: every step of quantization, window management and attention runs in the library's HIP
+kernels. PyTorch provides device memory and the current HIP stream. The library must be built
+(``python -m decode_attention_quant_amd.build`` or ``__graft_entry__.build()``); importing this package without it
+raises, there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch  # loaded first so the library binds to the HIP runtime torch already uses
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+
+OK = 0
+E_NULL, E_SHAPE, E_BITS, E_ALIGN, E_CAPACITY, E_WORKSPACE, E_EMPTY, E_LAUNCH, E_STATE = range(-1, -10, -1)
+HEAD_DIM = 128
+GROUP = 32
+TILE_TOKENS = 32
+RECORD_BYTES = 3072
+
+
+class KvqShape(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("q_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("bits", ctypes.c_int32), ("group", ctypes.c_int32),
+                ("residual_cap", ctypes.c_int32), ("reserved", ctypes.c_int32), ("max_tokens", ctypes.c_int64)]
+
+
+class KvqCache(ctypes.Structure):
+    _fields_ = [("tiles", ctypes.c_void_p), ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
+                ("n_quant", ctypes.c_int64), ("n_resid", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m decode_attention_quant_amd.build`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, I64, I32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
+    SP, CP = ctypes.POINTER(KvqShape), ctypes.POINTER(KvqCache)
+    sigs = {
+        "kv_quant_keys_per_channel": (ctypes.c_int, [SP, P, I64, I64, I64, I64, I64, P, P]),
+        "kv_quant_values_per_token": (ctypes.c_int, [SP, P, I64, I64, I64, I64, I64, P, P]),
+        "kv_append_and_flush": (ctypes.c_int, [SP, CP, P, P, I64, I64, I64, I64, P]),
+        "kv_decode_attention_splits": (I32, [SP, CP]),
+        "kv_decode_attention_workspace_bytes": (ctypes.c_size_t, [SP, CP]),
+        "kv_decode_attention": (ctypes.c_int, [SP, CP, P, F, P, P, ctypes.c_size_t, P]),
+        "kvq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+EXPORTS = ("kv_quant_keys_per_channel", "kv_quant_values_per_token", "kv_append_and_flush",
+           "kv_decode_attention_splits", "kv_decode_attention_workspace_bytes", "kv_decode_attention",
+           "kvq_status_string")
+
+
+def library():
+    """The loaded ``ctypes.CDLL`` (for tests that call the C ABI directly)."""
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.kvq_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != OK:
+        raise KvqError(fn, status)
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _f16_4d(t: torch.Tensor, name: str):
+    if t.dtype != torch.float16 or not t.is_cuda or t.dim() != 4 or t.shape[-1] != HEAD_DIM or t.stride(-1) != 1:
+        raise ValueError(f"{name} must be a CUDA float16 tensor [B, H, T, 128] with unit channel stride")
+    return ctypes.c_void_p(t.data_ptr()), t.stride(0), t.stride(1), t.stride(2)
+
+
+@dataclass
+class Shape:
+    batch: int
+    kv_heads: int
+    q_heads: int
+    max_tokens: int
+    residual_cap: int = 128
+    bits: int = 2
+    head_dim: int = HEAD_DIM
+    group: int = GROUP
+
+    def c(self) -> KvqShape:
+        return KvqShape(self.batch, self.kv_heads, self.q_heads, self.head_dim, self.bits, self.group,
+                        self.residual_cap, 0, self.max_tokens)
+
+
+class KVCache:
+    """Device buffers of one cache (allocated through torch) and the C struct that describes them."""
+
+    def __init__(self, shape: Shape, device="cuda"):
+        self.shape = shape
+        self._cshape = shape.c()
+        tiles = shape.max_tokens // TILE_TOKENS
+        self.tiles = torch.zeros((shape.batch, shape.kv_heads, tiles, RECORD_BYTES), dtype=torch.uint8, device=device)
+        self.k_res = torch.zeros((shape.batch, shape.kv_heads, shape.residual_cap, HEAD_DIM), dtype=torch.float16,
+                                 device=device)
+        self.v_res = torch.zeros_like(self.k_res)
+        self.c = KvqCache(self.tiles.data_ptr(), self.k_res.data_ptr(), self.v_res.data_ptr(), 0, 0, 0)
+
+    @property
+    def n_quant(self) -> int:
+        return int(self.c.n_quant)
+
+    @property
+    def n_resid(self) -> int:
+        return int(self.c.n_resid)
+
+    @property
+    def n_tokens(self) -> int:
+        return self.n_quant + self.n_resid
+
+
+def kv_quant_keys_per_channel(shape: Shape, k: torch.Tensor, tile0: int, tiles: torch.Tensor, stream=None):
+    p, sb, sh, st = _f16_4d(k, "k")
+    cs = shape.c()
+    _check("kv_quant_keys_per_channel", _lib.kv_quant_keys_per_channel(
+        ctypes.byref(cs), p, sb, sh, st, k.shape[2], tile0, ctypes.c_void_p(tiles.data_ptr()), _stream(stream)))
+
+
+def kv_quant_values_per_token(shape: Shape, v: torch.Tensor, tile0: int, tiles: torch.Tensor, stream=None):
+    p, sb, sh, st = _f16_4d(v, "v")
+    cs = shape.c()
+    _check("kv_quant_values_per_token", _lib.kv_quant_values_per_token(
+        ctypes.byref(cs), p, sb, sh, st, v.shape[2], tile0, ctypes.c_void_p(tiles.data_ptr()), _stream(stream)))
+
+
+def kv_append_and_flush(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
+    pk, sb, sh, st = _f16_4d(k_new, "k_new")
+    pv, sb2, sh2, st2 = _f16_4d(v_new, "v_new")
+    if (sb, sh, st) != (sb2, sh2, st2) or k_new.shape != v_new.shape:
+        raise ValueError("k_new and v_new must have the same shape and strides")
+    _check("kv_append_and_flush", _lib.kv_append_and_flush(
+        ctypes.byref(cache._cshape), ctypes.byref(cache.c), pk, pv, sb, sh, st, k_new.shape[2], _stream(stream)))
+
+
+def kv_decode_attention_splits(cache: KVCache) -> int:
+    return int(_lib.kv_decode_attention_splits(ctypes.byref(cache._cshape), ctypes.byref(cache.c)))
+
+
+def kv_decode_attention_workspace_bytes(cache: KVCache) -> int:
+    return int(_lib.kv_decode_attention_workspace_bytes(ctypes.byref(cache._cshape), ctypes.byref(cache.c)))
+
+
+def kv_decode_attention(cache: KVCache, q: torch.Tensor, out: torch.Tensor | None = None, sm_scale: float = 0.0,
+                        workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    s = cache.shape
+    if q.dtype != torch.float16 or not q.is_cuda or tuple(q.shape) != (s.batch, s.q_heads, HEAD_DIM) \
+            or not q.is_contiguous():
+        raise ValueError("q must be a contiguous CUDA float16 tensor [B, Hq, 128]")
+    if out is None:
+        out = torch.empty((s.batch, s.q_heads, HEAD_DIM), dtype=torch.float32, device=q.device)
+    need = kv_decode_attention_workspace_bytes(cache)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _check("kv_decode_attention", _lib.kv_decode_attention(
+        ctypes.byref(cache._cshape), ctypes.byref(cache.c), ctypes.c_void_p(q.data_ptr()), float(sm_scale),
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out

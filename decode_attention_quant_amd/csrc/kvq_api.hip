@@ -1,0 +1,226 @@
+// C-ABI entry points declared in include/kvq.h: host-side validation, the residual-window state machine and the
+// split-K sizing; every step of the computation runs in the kernels of kvq_kernels.hip.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kvq.h"
+#include "kvq_kernels.h"
+
+namespace {
+
+constexpr int64_t kTargetWaves = 8192;   // about eight wavefronts per SIMD on 256 CUs x 4 SIMDs
+constexpr int64_t kMinTilesPerSplit = 4;
+constexpr int64_t kMaxSplits = 1024;
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_shape(const kvq_shape *s) {
+    if (!s) return KVQ_E_NULL;
+    if (s->bits != 2) return KVQ_E_BITS;
+    if (s->batch <= 0 || s->kv_heads <= 0 || s->q_heads <= 0 || s->head_dim != KVQ_HEAD_DIM ||
+        s->group != KVQ_GROUP || s->q_heads % s->kv_heads != 0 || s->residual_cap <= 0 ||
+        s->residual_cap % KVQ_TILE_TOKENS != 0 || s->reserved != 0 || s->max_tokens <= 0 ||
+        s->max_tokens % KVQ_TILE_TOKENS != 0 || s->batch > 65535 || s->kv_heads > 65535)
+        return KVQ_E_SHAPE;
+    return KVQ_OK;
+}
+
+int check_cache(const kvq_shape *s, const kvq_cache *c) {
+    if (!c) return KVQ_E_NULL;
+    if (!c->tiles || !c->k_res || !c->v_res) return KVQ_E_NULL;
+    if (!aligned16(c->tiles) || !aligned16(c->k_res) || !aligned16(c->v_res)) return KVQ_E_ALIGN;
+    if (c->reserved != 0 || c->n_quant < 0 || c->n_quant % KVQ_TILE_TOKENS != 0 || c->n_quant > s->max_tokens ||
+        c->n_resid < 0 || c->n_resid > s->residual_cap)
+        return KVQ_E_STATE;
+    return KVQ_OK;
+}
+
+int check_src(const void *p, int64_t sb, int64_t sh, int64_t st) {
+    if (!p) return KVQ_E_NULL;
+    if (!aligned16(p) || sb % 8 != 0 || sh % 8 != 0 || st % 8 != 0) return KVQ_E_ALIGN;
+    if (sb < 0 || sh < 0 || st < 0) return KVQ_E_ALIGN;
+    return KVQ_OK;
+}
+
+int launched(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_E_LAUNCH; }
+
+kvq::TokSrc single_src(const void *p, int64_t sb, int64_t sh, int64_t st) {
+    kvq::TokSrc s;
+    s.a = static_cast<const _Float16 *>(p);
+    s.a_sb = sb; s.a_sh = sh; s.a_st = st;
+    s.n_a = INT64_MAX;
+    s.b = s.a; s.b_sb = sb; s.b_sh = sh; s.b_st = st;
+    return s;
+}
+
+int quant_common(const kvq_shape *shape, const void *x, int64_t sb, int64_t sh, int64_t st, int64_t n_tokens,
+                 int64_t tile0, void *tiles, bool keys, void *stream) {
+    int e = check_shape(shape);
+    if (e) return e;
+    if (!tiles) return KVQ_E_NULL;
+    if ((e = check_src(x, sb, sh, st))) return e;
+    if (!aligned16(tiles)) return KVQ_E_ALIGN;
+    if (n_tokens <= 0 || n_tokens % KVQ_TILE_TOKENS != 0 || tile0 < 0) return KVQ_E_SHAPE;
+    const int64_t max_tiles = shape->max_tokens / KVQ_TILE_TOKENS;
+    if (tile0 + n_tokens / KVQ_TILE_TOKENS > max_tiles) return KVQ_E_CAPACITY;
+    const kvq::TokSrc src = single_src(x, sb, sh, st);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t *t = static_cast<uint8_t *>(tiles);
+    const int64_t nt = n_tokens / KVQ_TILE_TOKENS;
+    return launched(keys ? kvq::launch_quant_keys(src, 0, nt, shape->batch, shape->kv_heads, t, max_tiles, tile0, s)
+                         : kvq::launch_quant_values(src, 0, nt, shape->batch, shape->kv_heads, t, max_tiles, tile0, s));
+}
+
+struct SplitPlan {
+    int64_t n_vt;       // 32-token tiles to visit (quantized + residual)
+    int32_t splits;
+    int32_t tiles_per_split;
+    int32_t chunks;
+};
+
+SplitPlan plan(const kvq_shape *s, const kvq_cache *c) {
+    SplitPlan p;
+    p.n_vt = c->n_quant / KVQ_TILE_TOKENS + (c->n_resid + KVQ_TILE_TOKENS - 1) / KVQ_TILE_TOKENS;
+    const int G = s->q_heads / s->kv_heads;
+    p.chunks = (G + 3) / 4;
+    const int64_t units = (int64_t)s->batch * s->kv_heads * p.chunks;
+    int64_t S = (kTargetWaves + units - 1) / units;
+    const int64_t by_len = (p.n_vt + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
+    if (S > by_len) S = by_len;
+    if (S > kMaxSplits) S = kMaxSplits;
+    if (S < 1) S = 1;
+    int64_t tps = (p.n_vt + S - 1) / S;
+    if (tps < 1) tps = 1;
+    S = (p.n_vt + tps - 1) / tps;
+    if (S < 1) S = 1;
+    p.splits = (int32_t)S;
+    p.tiles_per_split = (int32_t)tps;
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kvq_status_string(int status) {
+    switch (status) {
+        case KVQ_OK: return "ok";
+        case KVQ_E_NULL: return "null pointer";
+        case KVQ_E_SHAPE: return "unsupported shape or size";
+        case KVQ_E_BITS: return "unsupported bit width";
+        case KVQ_E_ALIGN: return "misaligned pointer or stride";
+        case KVQ_E_CAPACITY: return "cache capacity exceeded";
+        case KVQ_E_WORKSPACE: return "workspace missing or too small";
+        case KVQ_E_EMPTY: return "attention over an empty cache";
+        case KVQ_E_LAUNCH: return "HIP launch error";
+        case KVQ_E_STATE: return "inconsistent cache state";
+        default: return "unknown status";
+    }
+}
+
+int kv_quant_keys_per_channel(const kvq_shape *shape, const void *k, int64_t stride_b, int64_t stride_h,
+                              int64_t stride_t, int64_t n_tokens, int64_t tile0, void *tiles, void *stream) {
+    return quant_common(shape, k, stride_b, stride_h, stride_t, n_tokens, tile0, tiles, true, stream);
+}
+
+int kv_quant_values_per_token(const kvq_shape *shape, const void *v, int64_t stride_b, int64_t stride_h,
+                              int64_t stride_t, int64_t n_tokens, int64_t tile0, void *tiles, void *stream) {
+    return quant_common(shape, v, stride_b, stride_h, stride_t, n_tokens, tile0, tiles, false, stream);
+}
+
+int kv_append_and_flush(const kvq_shape *shape, kvq_cache *cache, const void *k_new, const void *v_new,
+                        int64_t stride_b, int64_t stride_h, int64_t stride_t, int64_t n_tokens, void *stream) {
+    int e = check_shape(shape);
+    if (e) return e;
+    if ((e = check_cache(shape, cache))) return e;
+    if ((e = check_src(k_new, stride_b, stride_h, stride_t))) return e;
+    if ((e = check_src(v_new, stride_b, stride_h, stride_t))) return e;
+    if (n_tokens <= 0) return KVQ_E_SHAPE;
+    const int64_t R = shape->residual_cap;
+    const int64_t nr0 = cache->n_resid;
+    const int64_t flushed = R * ((nr0 + n_tokens - 1) / R);
+    if (cache->n_quant + flushed > shape->max_tokens) return KVQ_E_CAPACITY;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int B = shape->batch, H = shape->kv_heads;
+    const int64_t max_tiles = shape->max_tokens / KVQ_TILE_TOKENS;
+    _Float16 *kres = static_cast<_Float16 *>(cache->k_res);
+    _Float16 *vres = static_cast<_Float16 *>(cache->v_res);
+    const kvq::TokSrc knew = single_src(k_new, stride_b, stride_h, stride_t);
+    const kvq::TokSrc vnew = single_src(v_new, stride_b, stride_h, stride_t);
+    int64_t copy_from, dst0;
+    if (flushed > 0) {
+        // the flushed tokens: the whole window, then the first flushed - nr0 new tokens
+        kvq::TokSrc ksrc = knew, vsrc = vnew;
+        ksrc.a = kres; vsrc.a = vres;
+        ksrc.a_sb = vsrc.a_sb = (int64_t)H * R * KVQ_HEAD_DIM;
+        ksrc.a_sh = vsrc.a_sh = R * KVQ_HEAD_DIM;
+        ksrc.a_st = vsrc.a_st = KVQ_HEAD_DIM;
+        ksrc.n_a = vsrc.n_a = nr0;
+        uint8_t *tiles = static_cast<uint8_t *>(cache->tiles);
+        const int64_t tile0 = cache->n_quant / KVQ_TILE_TOKENS, nt = flushed / KVQ_TILE_TOKENS;
+        if ((e = launched(kvq::launch_quant_keys(ksrc, 0, nt, B, H, tiles, max_tiles, tile0, s)))) return e;
+        if ((e = launched(kvq::launch_quant_values(vsrc, 0, nt, B, H, tiles, max_tiles, tile0, s)))) return e;
+        copy_from = flushed - nr0;
+        dst0 = 0;
+    } else {
+        copy_from = 0;
+        dst0 = nr0;
+    }
+    const int64_t n_copy = n_tokens - copy_from;
+    if ((e = launched(kvq::launch_copy_rows(knew, copy_from, n_copy, B, H, kres, (int)R, (int)dst0, s)))) return e;
+    if ((e = launched(kvq::launch_copy_rows(vnew, copy_from, n_copy, B, H, vres, (int)R, (int)dst0, s)))) return e;
+    cache->n_quant += flushed;
+    cache->n_resid = (int32_t)(dst0 + n_copy);
+    return KVQ_OK;
+}
+
+int32_t kv_decode_attention_splits(const kvq_shape *shape, const kvq_cache *cache) {
+    if (check_shape(shape) || check_cache(shape, cache)) return 0;
+    const SplitPlan p = plan(shape, cache);
+    return p.n_vt > 0 ? p.splits : 0;
+}
+
+size_t kv_decode_attention_workspace_bytes(const kvq_shape *shape, const kvq_cache *cache) {
+    const int32_t S = kv_decode_attention_splits(shape, cache);
+    if (S <= 0) return 0;
+    return (size_t)shape->batch * shape->q_heads * S * (KVQ_HEAD_DIM + 2) * sizeof(float);
+}
+
+int kv_decode_attention(const kvq_shape *shape, const kvq_cache *cache, const void *q, float sm_scale, float *out,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    int e = check_shape(shape);
+    if (e) return e;
+    if ((e = check_cache(shape, cache))) return e;
+    if (!q || !out) return KVQ_E_NULL;
+    if (!aligned16(q) || !aligned16(out)) return KVQ_E_ALIGN;
+    const SplitPlan p = plan(shape, cache);
+    if (p.n_vt == 0) return KVQ_E_EMPTY;
+    const size_t need = (size_t)shape->batch * shape->q_heads * p.splits * (KVQ_HEAD_DIM + 2) * sizeof(float);
+    if (!workspace || workspace_bytes < need) return KVQ_E_WORKSPACE;
+    if (!aligned16(workspace)) return KVQ_E_ALIGN;
+    if (!(sm_scale > 0.0f)) sm_scale = 1.0f / sqrtf((float)KVQ_HEAD_DIM);
+
+    kvq::DecodeArgs a;
+    a.tiles = static_cast<const uint8_t *>(cache->tiles);
+    a.k_res = static_cast<const _Float16 *>(cache->k_res);
+    a.v_res = static_cast<const _Float16 *>(cache->v_res);
+    a.q = static_cast<const _Float16 *>(q);
+    a.part_o = static_cast<float *>(workspace);
+    a.part_ml = a.part_o + (size_t)shape->batch * shape->q_heads * p.splits * KVQ_HEAD_DIM;
+    a.out = out;
+    a.max_tiles = shape->max_tokens / KVQ_TILE_TOKENS;
+    a.n_qtiles = (int)(cache->n_quant / KVQ_TILE_TOKENS);
+    a.n_resid = cache->n_resid;
+    a.res_cap = shape->residual_cap;
+    a.batch = shape->batch;
+    a.kv_heads = shape->kv_heads;
+    a.q_heads = shape->q_heads;
+    a.chunks = p.chunks;
+    a.tiles_per_split = p.tiles_per_split;
+    a.sm_log2 = sm_scale * 1.4426950408889634f;
+    return launched(kvq::launch_decode(a, p.splits, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Internal interface between the C-ABI entry points (kvq_api.hip) and the HIP kernels (kvq_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvq {
+
+// Tokens 0 .. n_a - 1 come from `a`, tokens n_a .. from `b` (element strides; the channel stride is 1). Lets one
+// kernel read a flush block that starts in the residual window and continues in the new tokens.
+struct TokSrc {
+    const _Float16 *a;
+    int64_t a_sb, a_sh, a_st;
+    int64_t n_a;
+    const _Float16 *b;
+    int64_t b_sb, b_sh, b_st;
+};
+
+struct DecodeArgs {
+    const uint8_t *tiles;
+    const _Float16 *k_res;
+    const _Float16 *v_res;
+    const _Float16 *q;
+    float *part_o;   // [B][Hq][splits][128]
+    float *part_ml;  // [B][Hq][splits][2]: maximum (log2 domain) and exponent sum
+    float *out;      // [B][Hq][128]
+    int64_t max_tiles;
+    int n_qtiles;
+    int n_resid;
+    int res_cap;
+    int batch;
+    int kv_heads;
+    int q_heads;
+    int chunks;           // ceil(G / 4): query heads are processed four per wavefront
+    int tiles_per_split;  // 32-token tiles (quantized, then residual) per split
+    float sm_log2;        // softmax scale * log2(e)
+};
+
+hipError_t launch_quant_keys(const TokSrc &src, int64_t t_begin, int64_t n_tiles, int batch, int kv_heads,
+                             uint8_t *tiles, int64_t max_tiles, int64_t tile0, hipStream_t st);
+hipError_t launch_quant_values(const TokSrc &src, int64_t t_begin, int64_t n_tiles, int batch, int kv_heads,
+                               uint8_t *tiles, int64_t max_tiles, int64_t tile0, hipStream_t st);
+hipError_t launch_copy_rows(const TokSrc &src, int64_t t_begin, int64_t n, int batch, int kv_heads, _Float16 *res,
+                            int res_cap, int dst0, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs &a, int splits, hipStream_t st);
+
+}  // namespace kvq

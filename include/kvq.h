@@ -1,0 +1,181 @@
+/*
+ * kvq.h — C ABI of a 2-bit KV-cache library for AMD MI355X (gfx950): KIVI-style asymmetric quantization of keys
+ * per channel and values per token, a full-precision window of the newest tokens, and decode attention computed
+ * straight from the packed codes plus that window.
+ *
+ * Sources (the pages this library follows):
+ *  - KIVI page, fdeinterviews.com "KIVI: A Tuning-Free Asymmetric 2bit Quantization for KV Cache": keys grouped per
+ *    channel (a group is 32 tokens of one channel), values per token, the newest tokens (up to R = 128) kept in full
+ *    precision and quantized in blocks when the window fills; 2 bits per element.
+ *  - synthetic.wiki "KV cache quantization", section "Keys are harder than values": per-channel keys, per-token
+ *    values, and a key cache split into a grouped part and a residual part that are combined when computing
+ *    attention scores.
+ *
+ * Conventions for every call:
+ *  - All pointers named as device pointers refer to memory on the current HIP device; host pointers are named so.
+ *    The caller owns every buffer. The library never allocates or frees memory and holds no global state; calls are
+ *    re-entrant. Work is enqueued on the caller's HIP stream (`stream` is a hipStream_t; NULL = the null stream);
+ *    no call synchronizes. Calls that touch one cache must be issued on one stream, in order.
+ *  - Return value: 0 on success (work enqueued; device faults, if any, surface at the caller's next
+ *    synchronization). A negative KVQ_E_* code means the arguments were rejected on the host and NOTHING was
+ *    launched or modified (host-side cache fields included), except KVQ_E_LAUNCH, which reports a launch failure
+ *    returned by the HIP runtime after host validation succeeded.
+ *  - Inputs must be finite; non-finite keys or values give unspecified codes.
+ *  - Element type "fp16" is IEEE binary16; "fp32" is IEEE binary32.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define KVQ_API __attribute__((visibility("default")))
+#else
+#define KVQ_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define KVQ_OK 0
+#define KVQ_E_NULL (-1)      /* a required pointer is NULL */
+#define KVQ_E_SHAPE (-2)     /* head_dim != 128, group != 32, q_heads % kv_heads != 0, R not a positive multiple
+                                of 32, non-positive sizes, or a token count/offset that is not a multiple of 32 */
+#define KVQ_E_BITS (-3)      /* bits != 2 */
+#define KVQ_E_ALIGN (-4)     /* a device pointer is not 16-byte aligned, or a token/head/batch stride is not a
+                                multiple of 8 elements (rows must be 16-byte aligned; the channel stride is 1) */
+#define KVQ_E_CAPACITY (-5)  /* the quantized part would exceed max_tokens, or a tile range exceeds it */
+#define KVQ_E_WORKSPACE (-6) /* workspace NULL or smaller than kv_decode_attention_workspace_bytes() */
+#define KVQ_E_EMPTY (-7)     /* attention over a cache that holds no token */
+#define KVQ_E_LAUNCH (-8)    /* the HIP runtime reported an error when launching */
+#define KVQ_E_STATE (-9)     /* cache host fields inconsistent: n_quant not a multiple of 32 or outside
+                                [0, max_tokens], n_resid outside [0, R] */
+
+/* Fixed sizes of the 2-bit layout. */
+#define KVQ_HEAD_DIM 128
+#define KVQ_GROUP 32
+#define KVQ_TILE_TOKENS 32
+#define KVQ_RECORD_BYTES 3072
+
+/*
+ * Shape of one cache (one attention layer).
+ *   batch, kv_heads, q_heads: B, Hkv, Hq (Hq a multiple of Hkv; query head hq uses KV head hq / (Hq / Hkv), i.e.
+ *   consecutive query heads share a KV head — the usual grouped-query layout);
+ *   head_dim: must be 128; bits: must be 2; group: must be 32 (tokens per key group, channels per value group);
+ *   residual_cap: R, the number of newest tokens kept in fp16 (a positive multiple of 32; 128 on the pages);
+ *   max_tokens: capacity of the quantized part in tokens (a positive multiple of 32).
+ */
+typedef struct kvq_shape {
+    int32_t batch;
+    int32_t kv_heads;
+    int32_t q_heads;
+    int32_t head_dim;
+    int32_t bits;
+    int32_t group;
+    int32_t residual_cap;
+    int32_t reserved; /* must be 0 */
+    int64_t max_tokens;
+} kvq_shape;
+
+/*
+ * One cache: caller-owned device buffers plus two host integers.
+ *   tiles: device, uint8 [B][Hkv][max_tokens / 32][3072]: the quantized part. Tile j of slice (b, h) holds tokens
+ *     32 j .. 32 j + 31 as one 3072-byte record:
+ *       bytes    0..1023  key codes,   256 little-endian uint32 words (16 two-bit codes each)
+ *       bytes 1024..2047  value codes, 256 uint32 words
+ *       bytes 2048..2303  key scale s_K[c] (fp16, c = 0..127; one per channel of the tile)
+ *       bytes 2304..2559  key zero  z_K[c] (fp16)
+ *       bytes 2560..2815  value scale s_V[g][t] (fp16 at index 32 g + t; g = channel group 0..3, t = token 0..31)
+ *       bytes 2816..3071  value zero  z_V[g][t] (fp16)
+ *     Key code of token t, channel c: word 4 (t%16 + 16 ((c%32)/8)) + 2 (t/16) + (c/32)/2,
+ *       bit 4 (c%8) + 2 ((c/32)%2).
+ *     Value code of channel c, token t: with (kc, e) = (t/4, t%4) for t < 16 and ((t-16)/4, 4 + (t-16)%4) otherwise,
+ *       word 4 (c%16 + 16 kc) + (c/16)/2, bit 4 e + 2 ((c/16)%2).
+ *     Decoding: x = code * s + z.
+ *   k_res, v_res: device, fp16 [B][Hkv][R][128]: the residual window; rows 0 .. n_resid-1 hold tokens
+ *     n_quant .. n_quant + n_resid - 1 exactly as appended.
+ *   n_quant (host): tokens in the quantized part (a multiple of 32). n_resid (host): tokens in the window (0..R).
+ */
+typedef struct kvq_cache {
+    void *tiles;
+    void *k_res;
+    void *v_res;
+    int64_t n_quant;
+    int32_t n_resid;
+    int32_t reserved; /* must be 0 */
+} kvq_cache;
+
+/*
+ * Per-channel key quantization (KIVI page, paragraph on the cache contents: each key group is 32 tokens of one
+ * channel; asymmetric min/max form).
+ *   k: device fp16, element (b, h, t, c) at k[b*stride_b + h*stride_h + t*stride_t + c], t in [0, n_tokens).
+ *   n_tokens: a positive multiple of 32. tile0: first destination tile index (tokens 32*tile0 ...).
+ *   tiles: device, the tile array of a cache of this shape; for tiles tile0 .. tile0 + n_tokens/32 - 1 of every
+ *     slice, the key codes and key scale/zero fields are written; the value fields are left untouched.
+ * Per group (32 tokens of one channel), with x the fp16 inputs and L = 3:
+ *   r = RN32(max - min); s = RN16(RN32(r / L)); if (L + 1/2) * s < r then s = next binary16 above s;
+ *   z = min (a zero minimum stored as +0); code = 0 if s == 0, else
+ *   clamp(round_half_even(RN32(RN32(x - z) / s)), 0, L); RN32/RN16 = round to nearest even into binary32/binary16,
+ *   division correctly rounded.
+ * Errors: KVQ_E_NULL, KVQ_E_SHAPE, KVQ_E_BITS, KVQ_E_ALIGN, KVQ_E_CAPACITY (tile range beyond max_tokens/32),
+ *   KVQ_E_LAUNCH.
+ */
+KVQ_API int kv_quant_keys_per_channel(const kvq_shape *shape, const void *k, int64_t stride_b, int64_t stride_h,
+                              int64_t stride_t, int64_t n_tokens, int64_t tile0, void *tiles, void *stream);
+
+/*
+ * Per-token value quantization (KIVI page and synthetic.wiki "Keys are harder than values": values grouped per
+ * token; 32 channels per group, four groups per token). Same quantizer and arguments as
+ * kv_quant_keys_per_channel; writes the value codes and value scale/zero fields of the tiles only.
+ */
+KVQ_API int kv_quant_values_per_token(const kvq_shape *shape, const void *v, int64_t stride_b, int64_t stride_h,
+                              int64_t stride_t, int64_t n_tokens, int64_t tile0, void *tiles, void *stream);
+
+/*
+ * Append n_tokens new tokens to every slice and manage the residual window (KIVI page, paragraph on the
+ * recent-token window). The result equals n_tokens single appends, each of which first flushes a full window
+ * (quantizing its R tokens into R/32 tiles, keys per channel and values per token) and then stores the token:
+ *   F = R * floor((n_resid + n_tokens - 1) / R) tokens are flushed: the first F of (window, new tokens);
+ *   the remaining tokens become the window.
+ *   k_new, v_new: device fp16 with the same stride convention as kv_quant_keys_per_channel; n_tokens >= 1.
+ *   cache: host struct; on success cache->n_quant and cache->n_resid are updated at enqueue time.
+ * Errors: KVQ_E_NULL, KVQ_E_SHAPE, KVQ_E_BITS, KVQ_E_ALIGN, KVQ_E_STATE, KVQ_E_CAPACITY (n_quant + F > max_tokens),
+ *   KVQ_E_LAUNCH.
+ */
+KVQ_API int kv_append_and_flush(const kvq_shape *shape, kvq_cache *cache, const void *k_new, const void *v_new,
+                        int64_t stride_b, int64_t stride_h, int64_t stride_t, int64_t n_tokens, void *stream);
+
+/*
+ * Number of token splits kv_decode_attention uses for the cache's current length (split-K along tokens; each
+ * split covers a contiguous range of 32-token tiles, the residual window being the last tiles), and the workspace
+ * it needs: batch * q_heads * splits * (128 + 2) * 4 bytes. Return 0 when the arguments are invalid.
+ */
+KVQ_API int32_t kv_decode_attention_splits(const kvq_shape *shape, const kvq_cache *cache);
+KVQ_API size_t kv_decode_attention_workspace_bytes(const kvq_shape *shape, const kvq_cache *cache);
+
+/*
+ * Decode attention of one query per (batch row, query head) over the whole cache: grouped part and residual
+ * window (synthetic.wiki "Keys are harder than values", last bullet). For query head hq of batch row b, with
+ * KV head h = hq / (Hq / Hkv) and decoded keys/values K, V (codes * scale + zero; window tokens as stored):
+ *   out[b][hq][c] = sum_t softmax_t(sm_scale * q . K[t]) V[t][c].
+ *   q: device fp16 [B][Hq][128], contiguous. sm_scale: softmax scale; a value <= 0 selects 1/sqrt(128).
+ *   out: device fp32 [B][Hq][128], contiguous.
+ *   workspace: device, >= kv_decode_attention_workspace_bytes(shape, cache) bytes, 16-byte aligned (split
+ *     partials: maximum, exponent sum and unnormalized output per split, merged by a second kernel).
+ * Errors: KVQ_E_NULL, KVQ_E_SHAPE, KVQ_E_BITS, KVQ_E_ALIGN, KVQ_E_STATE, KVQ_E_EMPTY, KVQ_E_WORKSPACE,
+ *   KVQ_E_LAUNCH.
+ */
+KVQ_API int kv_decode_attention(const kvq_shape *shape, const kvq_cache *cache, const void *q, float sm_scale, float *out,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Human-readable name of a status code (static string, never NULL). */
+KVQ_API const char *kvq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

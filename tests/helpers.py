@@ -1,0 +1,51 @@
+"""Test-side glue: oracle expectations for GPU results (imports the oracle; test infrastructure only)."""
+from __future__ import annotations
+
+import numpy as np
+
+import kvsynth
+from oracle import attention as oa
+from oracle import cache as oc
+from oracle import layout
+
+
+def oracle_records(cache: oc.SliceCache) -> np.ndarray:
+    """Tile records [S, n_quant / 32, 3072] of the oracle's quantized part, packed by the oracle."""
+    kq, ks, kz, vq, vs, vz = cache.quantized()
+    S, nq, D = kq.shape
+    nt = nq // 32
+    return layout.pack_tiles(kq.reshape(S, nt, 32, D), ks, kz, vq.reshape(S, nt, 32, D),
+                             vs.reshape(S, nt, 32, 4), vz.reshape(S, nt, 32, 4))
+
+
+def records_from_device(tiles, n_tiles: int, slices=None) -> np.ndarray:
+    """GPU tile array [B, H, max_tiles, 3072] -> numpy [S, n_tiles, 3072] (optionally only slice indices)."""
+    B, H = tiles.shape[:2]
+    t = tiles[:, :, :n_tiles].reshape(B * H, n_tiles, 3072)
+    if slices is not None:
+        t = t[list(slices)]
+    return t.cpu().numpy()
+
+
+def first_mismatch(a: np.ndarray, b: np.ndarray) -> str:
+    """Describe the first differing byte of two record arrays (slice, tile, field, byte)."""
+    idx = np.argwhere(a != b)
+    if len(idx) == 0:
+        return "identical"
+    s, t, off = idx[0][0], idx[0][1], idx[0][-1]
+    field = ["k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"][
+        0 if off < 1024 else 1 if off < 2048 else 2 + (off - 2048) // 256]
+    return f"{len(idx)} bytes differ; first at slice {s} tile {t} byte {off} ({field}): gpu {a[tuple(idx[0])]} oracle {b[tuple(idx[0])]}"
+
+
+def oracle_out(cache: oc.SliceCache, q: np.ndarray, batch: int, kv_heads: int, sm_scale=None) -> np.ndarray:
+    return oa.decode_attention(cache, q, batch, kv_heads, sm_scale)
+
+
+def workload_tokens(w: kvsynth.Workload, tensor_id: int, t0: int, t1: int, b=None, h=None, threads=None):
+    """Synthetic K (tensor_id 0, with the workload's outlier channels) or V (1) for tokens [t0, t1)."""
+    n_out, factor = (w.k_outliers, w.k_factor) if tensor_id == kvsynth.K_ID else (0, 1.0)
+    if b is not None:
+        return kvsynth.slice_tokens(w.seed, tensor_id, b, h, t0, t1, w.head_dim, n_out, factor)
+    return kvsynth.kv_tensor(w.seed, tensor_id, w.batch, w.kv_heads, t0, t1, w.head_dim, n_out, factor,
+                             threads=threads)

@@ -1,0 +1,153 @@
+"""The C-ABI library loads, exports every entry point ``include/kvq.h`` declares, and rejects bad arguments on the
+host with the documented status codes before anything reaches the GPU (no compute call is made here; every
+call below fails validation, so no pointer is dereferenced and nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+LIB = os.path.join(ROOT, "decode_attention_quant_amd", "libkvq.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libkvq.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    return re.findall(r"KVQ_API\s+[\w\s\*]+?\b(\w+)\s*\(", src)
+
+
+def test_header_declares_the_four_operations_and_helpers():
+    names = set(declared_functions())
+    assert {"kv_quant_keys_per_channel", "kv_quant_values_per_token", "kv_append_and_flush",
+            "kv_decode_attention"} <= names
+    assert {"kv_decode_attention_workspace_bytes", "kv_decode_attention_splits", "kvq_status_string"} <= names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(LIB)
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_only_declared_symbols_are_exported():
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert exported == set(declared_functions())
+
+
+@pytest.fixture(scope="module")
+def kvq():
+    import decode_attention_quant_amd as m
+    return m
+
+
+def _shape(kvq, **kw):
+    d = dict(batch=2, kv_heads=2, q_heads=4, head_dim=128, bits=2, group=32, residual_cap=128, reserved=0,
+             max_tokens=1024)
+    d.update(kw)
+    return kvq.KvqShape(**d)
+
+
+FAKE = 0x7f0000000000     # 16-byte aligned, never dereferenced: every call below fails validation first
+
+
+def _cache(kvq, n_quant=0, n_resid=0, tiles=FAKE, k_res=FAKE + 4096, v_res=FAKE + 8192):
+    return kvq.KvqCache(tiles, k_res, v_res, n_quant, n_resid, 0)
+
+
+def test_status_strings(kvq):
+    for code in range(0, -10, -1):
+        assert kvq.status_string(code) and kvq.status_string(code) != "unknown status"
+    assert kvq.status_string(-77) == "unknown status"
+
+
+def test_shape_validation(kvq):
+    lib = kvq.library()
+    cases = [
+        (dict(bits=4), kvq.E_BITS), (dict(head_dim=64), kvq.E_SHAPE), (dict(group=16), kvq.E_SHAPE),
+        (dict(q_heads=3), kvq.E_SHAPE), (dict(residual_cap=100), kvq.E_SHAPE), (dict(residual_cap=0), kvq.E_SHAPE),
+        (dict(max_tokens=1000), kvq.E_SHAPE), (dict(batch=0), kvq.E_SHAPE), (dict(reserved=1), kvq.E_SHAPE),
+    ]
+    for kw, code in cases:
+        s = _shape(kvq, **kw)
+        assert lib.kv_quant_keys_per_channel(ctypes.byref(s), FAKE, 0, 0, 128, 32, 0, FAKE, None) == code, kw
+        c = _cache(kvq)
+        assert lib.kv_append_and_flush(ctypes.byref(s), ctypes.byref(c), FAKE, FAKE, 0, 0, 128, 1, None) == code
+        assert lib.kv_decode_attention(ctypes.byref(s), ctypes.byref(c), FAKE, 0.0, FAKE, FAKE, 1 << 30,
+                                       None) == code
+    assert lib.kv_quant_keys_per_channel(None, FAKE, 0, 0, 128, 32, 0, FAKE, None) == kvq.E_NULL
+
+
+def test_quant_argument_validation(kvq):
+    lib = kvq.library()
+    s = _shape(kvq)
+    q = lambda *a: lib.kv_quant_keys_per_channel(ctypes.byref(s), *a, None)
+    v = lambda *a: lib.kv_quant_values_per_token(ctypes.byref(s), *a, None)
+    for fn in (q, v):
+        assert fn(None, 0, 0, 128, 32, 0, FAKE) == kvq.E_NULL
+        assert fn(FAKE, 0, 0, 128, 32, 0, None) == kvq.E_NULL
+        assert fn(FAKE + 2, 0, 0, 128, 32, 0, FAKE) == kvq.E_ALIGN
+        assert fn(FAKE, 0, 0, 100, 32, 0, FAKE) == kvq.E_ALIGN
+        assert fn(FAKE, 0, 0, 128, 32, 0, FAKE + 8) == kvq.E_ALIGN
+        assert fn(FAKE, 0, 0, 128, 31, 0, FAKE) == kvq.E_SHAPE
+        assert fn(FAKE, 0, 0, 128, 0, 0, FAKE) == kvq.E_SHAPE
+        assert fn(FAKE, 0, 0, 128, 32, -1, FAKE) == kvq.E_SHAPE
+        assert fn(FAKE, 0, 0, 128, 1024, 1, FAKE) == kvq.E_CAPACITY     # tiles 1..32 of 32
+        assert fn(FAKE, 0, 0, 128, 64, 31, FAKE) == kvq.E_CAPACITY
+
+
+def test_append_validation_and_capacity(kvq):
+    lib = kvq.library()
+    s = _shape(kvq)
+    ap = lambda c, *a: lib.kv_append_and_flush(ctypes.byref(s), ctypes.byref(c), *a, None)
+    c = _cache(kvq, tiles=0)
+    assert ap(c, FAKE, FAKE, 0, 0, 128, 1) == kvq.E_NULL
+    c = _cache(kvq)
+    assert ap(c, None, FAKE, 0, 0, 128, 1) == kvq.E_NULL
+    assert ap(c, FAKE, FAKE, 0, 0, 128, 0) == kvq.E_SHAPE
+    assert ap(c, FAKE, FAKE + 4, 0, 0, 128, 1) == kvq.E_ALIGN
+    for nq, nr in [(16, 0), (-32, 0), (1056, 0), (0, 129), (0, -1)]:
+        c = _cache(kvq, nq, nr)
+        assert ap(c, FAKE, FAKE, 0, 0, 128, 1) == kvq.E_STATE, (nq, nr)
+    # 1024 quantized tokens of capacity: 1024 + 128 appended tokens flush 1024 -> fits; one more token does not
+    c = _cache(kvq, 1024, 128)
+    assert ap(c, FAKE, FAKE, 0, 0, 128, 1) == kvq.E_CAPACITY
+    c = _cache(kvq, 0, 0)
+    assert ap(c, FAKE, FAKE, 0, 0, 128, 1024 + 129) == kvq.E_CAPACITY
+    assert (c.n_quant, c.n_resid) == (0, 0)          # nothing modified on error
+
+
+def test_decode_validation(kvq):
+    lib = kvq.library()
+    s = _shape(kvq)
+    dec = lambda c, q, out, ws, nbytes: lib.kv_decode_attention(ctypes.byref(s), ctypes.byref(c), q, 0.0, out, ws,
+                                                                nbytes, None)
+    empty = _cache(kvq)
+    assert dec(empty, FAKE, FAKE, FAKE, 1 << 30) == kvq.E_EMPTY
+    c = _cache(kvq, 512, 5)
+    assert dec(c, None, FAKE, FAKE, 1 << 30) == kvq.E_NULL
+    assert dec(c, FAKE + 2, FAKE, FAKE, 1 << 30) == kvq.E_ALIGN
+    need = lib.kv_decode_attention_workspace_bytes(ctypes.byref(s), ctypes.byref(c))
+    S = lib.kv_decode_attention_splits(ctypes.byref(s), ctypes.byref(c))
+    assert need == 2 * 4 * S * 130 * 4 and S >= 1
+    assert dec(c, FAKE, FAKE, FAKE, need - 1) == kvq.E_WORKSPACE
+    assert dec(c, FAKE, FAKE, None, need) == kvq.E_WORKSPACE
+    assert lib.kv_decode_attention_splits(ctypes.byref(s), ctypes.byref(empty)) == 0
+    assert lib.kv_decode_attention_workspace_bytes(ctypes.byref(s), ctypes.byref(empty)) == 0
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,n_q,n_r,min_splits", [
+    (64, 32, 8, 32640, 128, 8), (1, 32, 32, 1048448, 128, 64), (8, 32, 32, 3968, 128, 8), (1, 1, 1, 896, 128, 1)])
+def test_split_plan_covers_every_tile(kvq, B, Hq, Hkv, n_q, n_r, min_splits):
+    lib = kvq.library()
+    s = _shape(kvq, batch=B, q_heads=Hq, kv_heads=Hkv, max_tokens=n_q + 1024)
+    c = _cache(kvq, n_q, n_r)
+    S = lib.kv_decode_attention_splits(ctypes.byref(s), ctypes.byref(c))
+    n_vt = n_q // 32 + (n_r + 31) // 32
+    assert min_splits <= S <= n_vt
+    tps = -(-n_vt // S)
+    assert (S - 1) * tps < n_vt <= S * tps       # no empty split, every tile covered
