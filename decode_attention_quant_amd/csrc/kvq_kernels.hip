@@ -179,22 +179,37 @@ __device__ __forceinline__ float pow2(int k) { return __builtin_bit_cast(float, 
 
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
-// value of lane (l ^ 16 row pair) / (l ^ 32 half) combined: all four 16-lane rows end up with the reduction
-__device__ __forceinline__ float row_max4(float v) {
-    uint32_t u = __builtin_bit_cast(uint32_t, v);
-    auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    v = fmaxf(__builtin_bit_cast(float, p[0]), __builtin_bit_cast(float, p[1]));
-    u = __builtin_bit_cast(uint32_t, v);
-    auto q = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return fmaxf(__builtin_bit_cast(float, q[0]), __builtin_bit_cast(float, q[1]));
+// Cross-row reductions over the four 16-lane rows of a wavefront with the gfx950 row swaps. Two compiler traps
+// are avoided here: the second operand goes through an empty asm statement (a swap whose operands the compiler
+// can prove equal is folded into the identity), and the result pair is copied into named integers before use
+// (reading element 1 of the pair through a bit cast was lowered as element 0).
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+    asm volatile("" : "+v"(v));
+    return v;
 }
-__device__ __forceinline__ float row_sum4(float v) {
-    uint32_t u = __builtin_bit_cast(uint32_t, v);
-    auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    v = __builtin_bit_cast(float, p[0]) + __builtin_bit_cast(float, p[1]);
-    u = __builtin_bit_cast(uint32_t, v);
-    auto q = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    return __builtin_bit_cast(float, q[0]) + __builtin_bit_cast(float, q[1]);
+__device__ __forceinline__ void swap16(uint32_t u, uint32_t &a, uint32_t &b) {
+    auto p = __builtin_amdgcn_permlane16_swap(u, opaque(u), false, false);   // rows (0,1) and (2,3)
+    a = p[0];
+    b = p[1];
+}
+__device__ __forceinline__ void swap32(uint32_t u, uint32_t &a, uint32_t &b) {
+    auto p = __builtin_amdgcn_permlane32_swap(u, opaque(u), false, false);   // halves (0,1) and (2,3)
+    a = p[0];
+    b = p[1];
+}
+__device__ __forceinline__ float rows_max(float v) {
+    uint32_t a, b;
+    swap16(__builtin_bit_cast(uint32_t, v), a, b);
+    v = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+    swap32(__builtin_bit_cast(uint32_t, v), a, b);
+    return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+    uint32_t a, b;
+    swap16(__builtin_bit_cast(uint32_t, v), a, b);
+    v = __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
+    swap32(__builtin_bit_cast(uint32_t, v), a, b);
+    return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
 // One wavefront per (split, batch row, KV head, chunk of up to 4 query heads of that KV head).
@@ -234,7 +249,7 @@ __global__ __launch_bounds__(64) void decode_pass1_kernel(DecodeArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, fabsf((float)qv[ks][e]));
     }
-    qmax = row_max4(qmax);
+    qmax = rows_max(qmax);
     // q' = q * 2^-E with 2^E > max |q|: |q'| < 1 keeps q' * s_K within binary16 range for any fp16 scale
     int E = 0;   // qmax is a float16 value widened, hence a normal binary32 number: read its exponent field
     if (qmax > 0.0f) E = (int)((__builtin_bit_cast(uint32_t, qmax) >> 23) & 0xffu) - 127 + 1;
@@ -307,7 +322,7 @@ __global__ __launch_bounds__(64) void decode_pass1_kernel(DecodeArgs a) {
         float mx = x[0];
 #pragma unroll
         for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-        mx = row_max4(mx);
+        mx = rows_max(mx);
         const float mnew = fmaxf(m, mx);
         if (__any(mnew > m)) {
             const float alpha = __builtin_amdgcn_exp2f(m - mnew);
@@ -384,7 +399,7 @@ __global__ __launch_bounds__(64) void decode_pass1_kernel(DecodeArgs a) {
         float mx = x[0];
 #pragma unroll
         for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-        mx = row_max4(mx);
+        mx = rows_max(mx);
         const float mnew = fmaxf(m, mx);
         if (__any(mnew > m)) {
             const float alpha = __builtin_amdgcn_exp2f(m - mnew);
@@ -422,8 +437,8 @@ __global__ __launch_bounds__(64) void decode_pass1_kernel(DecodeArgs a) {
     }
 
     // ------------------------------------------------------------------ partials of this split
-    lsum = row_sum4(lsum);
-    gam = row_sum4(gam);
+    lsum = rows_sum(lsum);
+    gam = rows_sum(gam);
     float gr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) gr[r] = __shfl(gam, 4 * kc + r);
