@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Decode-step benchmark of the 2-bit KV cache on one MI355X.
+
+One step = one token appended to every sequence (window append, with the 128-token flush into packed 2-bit tiles
+when the window is full) followed by decode attention of one query per (sequence, query head) over the whole
+cache. The cache is built from seeded synthetic keys/values/queries (kvsynth) and is resident in HBM before the
+timed region starts. The default workload is the GQA decode at 32K context (batch 64, 32 query heads sharing
+8 KV heads); the prefill is sized so the first timed step attends over exactly 32768 tokens, and the default
+128 timed steps contain exactly one flush (the steady-state mix).
+
+Printed (one JSON line on stdout): KV tokens/s over the timed steps (value), the decode-attention call's achieved
+algorithmic HBM bandwidth against the 8 TB/s peak (roofline), and the CPU oracle timed on a sample of the same
+workload (cpu_baseline). Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+METRIC = "2-bit KV decode attention: KV tokens/s and achieved HBM GB/s (% of peak)"
+PEAK_GBS = 8000.0          # MI355X HBM3E
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_pass1_traffic_llama3_8b_gqa_32k.json")
+KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_quant_amd", "csrc", "kvq_kernels.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(batch, kv_heads, q_heads, n_quant, n_resid, head_dim=128):
+    """Bytes one decode-attention call must move: per quantized token and KV head 96 B (32 B key codes, 32 B value
+    codes, 16 B key scale/zero, 16 B value scale/zero), per window token 512 B of fp16 K and V, the fp16 query
+    and the fp32 output."""
+    return (batch * kv_heads * (n_quant * 96 + n_resid * 2 * head_dim * 2)
+            + batch * q_heads * head_dim * 2 + batch * q_heads * head_dim * 4)
+
+
+def lengths_after(n_quant, n_resid, appended, R):
+    """Cache lengths after `appended` single-token appends (lazy flush of a full window)."""
+    for _ in range(appended):
+        if n_resid == R:
+            n_quant, n_resid = n_quant + R, 0
+        n_resid += 1
+    return n_quant, n_resid
+
+
+def traffic_per_launch():
+    """HBM bytes per decode pass-1 launch from the committed counter summary, if the kernel source still matches."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        with open(KERNEL_SOURCE, "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()
+        if rec.get("kernel_source_sha256") == sha:
+            return rec.get("traffic_bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+def cpu_baseline(w, queries_step1, n_slices, context):
+    """The oracle (as it stands) on a sample of slices of the same workload: decode attention of the first timed
+    step's queries over `context` tokens. Returns the rate in the metric's unit (KV tokens/s, where one batch row
+    of all heads over N tokens counts N)."""
+    import numpy as np
+
+    import kvsynth
+    from oracle import attention as oa
+    from oracle import cache as oc
+    try:
+        from threadpoolctl import threadpool_info
+        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
+                           or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        blas_threads = 1
+    G = w.q_heads // w.kv_heads
+    step = max(1, (w.batch * w.kv_heads) // n_slices)
+    slices = [(i // w.kv_heads, i % w.kv_heads) for i in range(0, w.batch * w.kv_heads, step)][:n_slices]
+    k = np.stack([kvsynth.slice_tokens(w.seed, kvsynth.K_ID, b, h, 0, context, w.head_dim, w.k_outliers,
+                                       w.k_factor) for b, h in slices])
+    v = np.stack([kvsynth.slice_tokens(w.seed, kvsynth.V_ID, b, h, 0, context, w.head_dim) for b, h in slices])
+    c = oc.SliceCache(len(slices), residual_cap=w.residual)
+    oc.append_block(c, k, v)
+    q = np.stack([queries_step1[b, h * G:(h + 1) * G] for b, h in slices])       # [S, G, D]
+    t = time.perf_counter()
+    oa.decode_attention(c, q, len(slices), 1)
+    dt = time.perf_counter() - t
+    kv_tokens = len(slices) / w.kv_heads * context
+    return {"value": kv_tokens / dt, "unit": "KV tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "sample": f"{len(slices)} of {w.batch * w.kv_heads} (batch row, KV head) slices of {w.name} at "
+                      f"{context} tokens: float64 decode attention (dequantize + softmax) of the first timed "
+                      f"step's queries, {dt:.2f} s; quantization not timed",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="llama3_8b_gqa_32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-slices", type=int, default=12)
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (every (batch row, KV head) slice "
+              "is independent; sharding is described in the design notes). Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import decode_attention_quant_amd as kvq
+    import kvsynth
+    from kvsynth import device as kdev
+
+    w = kvsynth.WORKLOADS[args.workload]
+    W, K, R = args.warmup, args.steps, w.residual
+    P = w.context - W - 1                      # first timed step attends over exactly w.context tokens
+    total = P + W + K
+    shape = kvq.Shape(w.batch, w.kv_heads, w.q_heads, residual_cap=R, max_tokens=((total + 31) // 32) * 32)
+    cache = kvq.KVCache(shape)
+    t0 = time.time()
+    Kd = kdev.kv_to_device(w, kvsynth.K_ID, 0, total)
+    Vd = kdev.kv_to_device(w, kvsynth.V_ID, 0, total)
+    Q = kdev.queries_to_device(w, range(1, W + K + 1))
+    log(f"[bench] {w.name}: generated and uploaded {total} tokens x {w.batch * w.kv_heads} slices "
+        f"in {time.time() - t0:.1f}s")
+    kvq.kv_append_and_flush(cache, Kd[:, :, :P], Vd[:, :, :P])
+    torch.cuda.synchronize()
+    log(f"[bench] prefill {P} tokens: n_quant={cache.n_quant} n_resid={cache.n_resid}")
+
+    # workspace for the largest split count any step will use (host-side length simulation only)
+    ws_bytes = 16
+    nq, nr = cache.n_quant, cache.n_resid
+    for i in range(W + K):
+        nq, nr = lengths_after(nq, nr, 1, R)
+        probe = kvq.KvqCache(cache.c.tiles, cache.c.k_res, cache.c.v_res, nq, nr, 0)
+        ws_bytes = max(ws_bytes, int(kvq.library().kv_decode_attention_workspace_bytes(
+            kvq.ctypes.byref(cache._cshape), kvq.ctypes.byref(probe))))
+    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    out = torch.empty((w.batch, w.q_heads, 128), dtype=torch.float32, device="cuda")
+
+    def step(i):
+        t = P + i
+        kvq.kv_append_and_flush(cache, Kd[:, :, t:t + 1], Vd[:, :, t:t + 1])
+
+    for i in range(W):
+        step(i)
+        kvq.kv_decode_attention(cache, Q[i], out=out, workspace=workspace)
+    torch.cuda.synchronize()
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * K + 2)]
+    call_bytes, kv_tokens, contexts = [], 0, []
+    ev[0].record()
+    for j in range(K):
+        i = W + j
+        ev[3 * j + 1].record()
+        step(i)
+        ev[3 * j + 2].record()
+        kvq.kv_decode_attention(cache, Q[i], out=out, workspace=workspace)
+        ev[3 * j + 3].record()
+        n = cache.n_tokens
+        contexts.append(n)
+        kv_tokens += w.batch * n
+        call_bytes.append(algorithmic_bytes(w.batch, w.kv_heads, w.q_heads, cache.n_quant, cache.n_resid))
+    ev[3 * K + 1].record()
+    torch.cuda.synchronize()
+    total_ms = ev[0].elapsed_time(ev[3 * K + 1])
+    decode_ms = [ev[3 * j + 2].elapsed_time(ev[3 * j + 3]) for j in range(K)]
+    append_ms = [ev[3 * j + 1].elapsed_time(ev[3 * j + 2]) for j in range(K)]
+    value = kv_tokens / (total_ms * 1e-3)
+    achieved = sum(call_bytes) / (sum(decode_ms) * 1e-3) / 1e9
+    splits = kvq.kv_decode_attention_splits(cache)
+    log(f"[bench] {K} steps in {total_ms:.3f} ms; decode call avg {1e3 * sum(decode_ms) / K:.1f} us "
+        f"({achieved:.0f} GB/s); append avg {1e3 * sum(append_ms) / K:.1f} us, max {1e3 * max(append_ms):.1f} us; "
+        f"splits={splits}")
+
+    res = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "KV tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": total_ms / K,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+                   "context_first_timed_step": contexts[0], "context_last_timed_step": contexts[-1],
+                   "bits": w.bits, "group": w.group, "residual": R, "head_dim": w.head_dim},
+        "hbm_gb_s": achieved,
+        "pct_of_peak": 100.0 * achieved / PEAK_GBS,
+        "decode_call_us": 1e3 * sum(decode_ms) / K,
+        "append_us_avg": 1e3 * sum(append_ms) / K,
+        "append_us_max": 1e3 * max(append_ms),
+        "splits": splits,
+        "dtype_detail": "2-bit codes expanded to fp16 MFMA operands (scales folded as fp16 hi+lo), fp32 accumulation",
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / PEAK_GBS, "traffic": traffic_per_launch(),
+                     "kernel": "decode_pass1_kernel + decode_pass2_kernel (one kv_decode_attention call)",
+                     "bytes_per_call": sum(call_bytes) / K},
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the CPU oracle on {args.cpu_slices} slices")
+        res["cpu_baseline"] = cpu_baseline(w, Q[W].cpu().numpy(), args.cpu_slices, contexts[0])
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -74,17 +74,17 @@ def decode_attention(cache: SliceCache, q: np.ndarray, batch: int, kv_heads: int
     m = np.full((S, G), -np.inf)
     for t0 in range(0, N, chunk):
         K, _ = decoded_range(cache, t0, min(N, t0 + chunk))
-        sc = sigma * np.einsum("sgd,std->sgt", qs, K)
+        sc = sigma * np.matmul(qs, np.swapaxes(K, 1, 2))
         m = np.maximum(m, sc.max(axis=-1))
     # pass 2: exponential sums and the weighted sum of values
     l = np.zeros((S, G))
     acc = np.zeros((S, G, D))
     for t0 in range(0, N, chunk):
         K, V = decoded_range(cache, t0, min(N, t0 + chunk))
-        sc = sigma * np.einsum("sgd,std->sgt", qs, K)
+        sc = sigma * np.matmul(qs, np.swapaxes(K, 1, 2))
         p = np.exp(sc - m[..., None])
         l += p.sum(axis=-1)
-        acc += np.einsum("sgt,std->sgd", p, V)
+        acc += np.matmul(p, V)
     out = acc / l[..., None]
     return out.reshape(batch, kv_heads, G, D).reshape(batch, Hq, D)
 
@@ -138,10 +138,10 @@ def split_partials(cache: SliceCache, q: np.ndarray, batch: int, kv_heads: int, 
             ms.append(np.full((S, G), -np.inf)); ls.append(np.zeros((S, G))); os_.append(np.zeros((S, G, D)))
             continue
         K, V = decoded_range(cache, t0, t1)
-        sc = sigma * np.einsum("sgd,std->sgt", qs, K)
+        sc = sigma * np.matmul(qs, np.swapaxes(K, 1, 2))
         m = sc.max(axis=-1)
         p = np.exp(sc - m[..., None])
-        ms.append(m); ls.append(p.sum(-1)); os_.append(np.einsum("sgt,std->sgd", p, V))
+        ms.append(m); ls.append(p.sum(-1)); os_.append(np.matmul(p, V))
     return np.stack(ms), np.stack(ls), np.stack(os_)
 
 
