@@ -223,9 +223,21 @@ __device__ __forceinline__ float rows_sum(float v) {
 // (head n / 4, group n % 4): P~[n][t] = p[t] * s_V[g][t] (fp16 high + low), contracted against the value codes of
 // all 128 channels (8 N-blocks of 16); for channel block j only row group g = j / 2 is kept. The value zero-point
 // term sum_t p[t] z_V[g][t] is accumulated on the VALU and added at the end.
-__global__ __launch_bounds__(64) void decode_pass1_kernel(DecodeArgs a) {
-    __shared__ __align__(16) uint32_t sz_lds[2][256];
-    __shared__ __align__(16) _Float16 vres_lds[32 * 128];
+//
+// Per-wavefront LDS: the tile's 1 KB of scales/zeros and the 2 KB folded query (high and low parts, computed once
+// per (head, channel) rather than once per replicated column). Both are written for tile v + 1 at the end of
+// iteration v, after every read of tile v has been issued (a wavefront's LDS operations complete in order), so
+// the next iteration starts with its operands in place. The fp16 window tiles reuse the same 8 KB.
+constexpr int LDS_SZ = 0;            // 256 x uint32: s_K[128], z_K[128], s_V[4][32], z_V[4][32] (fp16)
+constexpr int LDS_QT = 1024;         // fp16 [2 (high, low)][4 heads][128 channels]
+constexpr int LDS_BYTES = 8192;      // also the fp16 window tile [32][128]
+
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void decode_pass1_kernel(DecodeArgs a) {
+    __shared__ __align__(16) unsigned char smem[LDS_BYTES];
+    uint32_t *sz_lds = reinterpret_cast<uint32_t *>(smem + LDS_SZ);
+    const _Float16 *szh = reinterpret_cast<const _Float16 *>(smem + LDS_SZ);
+    _Float16 *qt_lds = reinterpret_cast<_Float16 *>(smem + LDS_QT);
+    _Float16 *vres_lds = reinterpret_cast<_Float16 *>(smem);
 
     const int l = threadIdx.x;
     const int n = l & 15, kc = l >> 4, hl = n >> 2, g = n & 3;
@@ -239,7 +251,8 @@ __global__ __launch_bounds__(64) void decode_pass1_kernel(DecodeArgs a) {
     const int h0 = hkv * G + 4 * chunk;
     const bool col_valid = hl < gc;
 
-    // ---- query: lane (n, kc) holds head h0 + n/4, channels 32 ks + 8 kc + e (e = 0..7) for ks = 0..3
+    // ---- query, two layouts. MFMA B layout (column n, channels 32 ks + 8 kc + e): used for the zero-point term and
+    // the window tiles. Folding layout (head kc, channels 8 n .. 8 n + 7): one (head, channel) per lane slot.
     const _Float16 *qp = a.q + ((int64_t)b * a.q_heads + h0 + (col_valid ? hl : 0)) * D;
     h8 qv[4];
     float qmax = 0.0f;
@@ -258,6 +271,20 @@ __global__ __launch_bounds__(64) void decode_pass1_kernel(DecodeArgs a) {
     for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int e = 0; e < 8; ++e) qv[ks][e] = col_valid ? (_Float16)((float)qv[ks][e] * qsc) : (_Float16)0.0f;
+    // folding layout: lane (n, kc) holds head kc of the chunk (if valid), channels 8n .. 8n+7; its own scale 2^-E_kc
+    h8 qf = {};
+    {
+        const bool fv = kc < gc;
+        const _Float16 *qfp = a.q + ((int64_t)b * a.q_heads + h0 + (fv ? kc : 0)) * D + 8 * n;
+        const h8 raw = *reinterpret_cast<const h8 *>(qfp);
+        // after rows_max, lane 4 kc (column 4 kc, head kc) holds the maximum of head kc
+        const float qm_head = __shfl(qmax, 4 * kc);
+        int Eh = 0;
+        if (qm_head > 0.0f) Eh = (int)((__builtin_bit_cast(uint32_t, qm_head) >> 23) & 0xffu) - 127 + 1;
+        const float sch = pow2(-Eh);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[e] = fv ? (_Float16)((float)raw[e] * sch) : (_Float16)0.0f;
+    }
     const float C = a.sm_log2 * pow2(E);   // score (in q' units) -> log2 domain
 
     float m = -__builtin_inff();
@@ -272,6 +299,18 @@ __global__ __launch_bounds__(64) void decode_pass1_kernel(DecodeArgs a) {
     const int qend = min(v1, a.n_qtiles);
     const uint8_t *base = a.tiles + ((int64_t)b * a.kv_heads + hkv) * a.max_tiles * (int64_t)REC;
 
+    // stage a tile's scales/zeros and its folded query (high, low) into LDS
+    auto stage = [&](const uint4 &sw) {
+        reinterpret_cast<uint4 *>(sz_lds)[l] = sw;
+        __syncthreads();
+        const h8 sk = *reinterpret_cast<const h8 *>(szh + 8 * n);
+        const h8 hi = qf * sk;
+        const h8 lo = __builtin_elementwise_fma(qf, sk, -hi);
+        *reinterpret_cast<h8 *>(qt_lds + 128 * kc + 8 * n) = hi;
+        *reinterpret_cast<h8 *>(qt_lds + 512 + 128 * kc + 8 * n) = lo;
+        __syncthreads();
+    };
+
     // ------------------------------------------------------------------ quantized tiles
     uint4 kw, vw, sw;
     if (v0 < qend) {
@@ -279,35 +318,32 @@ __global__ __launch_bounds__(64) void decode_pass1_kernel(DecodeArgs a) {
         kw = reinterpret_cast<const uint4 *>(rec)[l];
         vw = reinterpret_cast<const uint4 *>(rec + 1024)[l];
         sw = reinterpret_cast<const uint4 *>(rec + 2048)[l];
+        stage(sw);
     }
     for (int v = v0; v < qend; ++v) {
-        const int buf = v & 1;
-        reinterpret_cast<uint4 *>(sz_lds[buf])[l] = sw;
         const uint32_t kwa[4] = {kw.x, kw.y, kw.z, kw.w};
         const uint32_t vwa[4] = {vw.x, vw.y, vw.z, vw.w};
-        if (v + 1 < qend) {    // prefetch the next tile
+        const bool more = v + 1 < qend;
+        if (more) {    // prefetch the next tile
             const uint8_t *rec = base + (int64_t)(v + 1) * REC;
             kw = reinterpret_cast<const uint4 *>(rec)[l];
             vw = reinterpret_cast<const uint4 *>(rec + 1024)[l];
             sw = reinterpret_cast<const uint4 *>(rec + 2048)[l];
         }
-        __syncthreads();
-        const _Float16 *szh = reinterpret_cast<const _Float16 *>(sz_lds[buf]);
 
         // zero-point term: acc0[t][n] = sum_c z_K[c] q'[c][n] (the same for every token row)
         f4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f};
-        h8 sk[4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const h8 zk = *reinterpret_cast<const h8 *>(szh + 128 + 32 * ks + 8 * kc);
-            sk[ks] = *reinterpret_cast<const h8 *>(szh + 32 * ks + 8 * kc);
             acc0 = mfma(zk, qv[ks], acc0);
         }
         f4 acc1 = acc0;
+        const _Float16 *qth = qt_lds + 128 * hl + 8 * kc;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const h8 hi = qv[ks] * sk[ks];
-            const h8 lo = __builtin_elementwise_fma(qv[ks], sk[ks], -hi);
+            const h8 hi = *reinterpret_cast<const h8 *>(qth + 32 * ks);
+            const h8 lo = *reinterpret_cast<const h8 *>(qth + 512 + 32 * ks);
             const h8 a0 = expand8(nibbles(kwa[ks >> 1], ks & 1));
             const h8 a1 = expand8(nibbles(kwa[2 + (ks >> 1)], ks & 1));
             acc0 = mfma(a0, hi, acc0);
@@ -315,14 +351,11 @@ __global__ __launch_bounds__(64) void decode_pass1_kernel(DecodeArgs a) {
             acc0 = mfma(a0, lo, acc0);
             acc1 = mfma(a1, lo, acc1);
         }
-        // acc0[r]: token 4 kc + r; acc1[r]: token 16 + 4 kc + r; column n
-        float x[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) { x[r] = acc0[r] * C; x[4 + r] = acc1[r] * C; }
-        float mx = x[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-        mx = rows_max(mx);
+        // acc0[r]: token 4 kc + r; acc1[r]: token 16 + 4 kc + r; column n. C > 0, so the maximum is taken on the
+        // raw accumulators and scaled once.
+        float mx = fmaxf(fmaxf(fmaxf(acc0[0], acc0[1]), fmaxf(acc0[2], acc0[3])),
+                         fmaxf(fmaxf(acc1[0], acc1[1]), fmaxf(acc1[2], acc1[3])));
+        mx = rows_max(mx) * C;
         const float mnew = fmaxf(m, mx);
         if (__any(mnew > m)) {
             const float alpha = __builtin_amdgcn_exp2f(m - mnew);
@@ -339,7 +372,11 @@ __global__ __launch_bounds__(64) void decode_pass1_kernel(DecodeArgs a) {
         }
         float p[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { p[i] = __builtin_amdgcn_exp2f(x[i] - m); lsum += p[i]; }
+        for (int r = 0; r < 4; ++r) {
+            p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc0[r], C, -m));
+            p[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc1[r], C, -m));
+        }
+        lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
 
         // value scales/zeros of tokens 4kc..4kc+3 and 16+4kc..16+4kc+3, channel group g
         const h4 sv0 = *reinterpret_cast<const h4 *>(szh + 256 + 32 * g + 4 * kc);
@@ -355,7 +392,8 @@ __global__ __launch_bounds__(64) void decode_pass1_kernel(DecodeArgs a) {
             phi[4 + i] = (_Float16)t1;
             plo[i] = (_Float16)(t0 - (float)phi[i]);
             plo[4 + i] = (_Float16)(t1 - (float)phi[4 + i]);
-            gam += p[i] * (float)zv0[i] + p[4 + i] * (float)zv1[i];
+            gam = __builtin_fmaf(p[i], (float)zv0[i], gam);
+            gam = __builtin_fmaf(p[4 + i], (float)zv1[i], gam);
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -363,6 +401,7 @@ __global__ __launch_bounds__(64) void decode_pass1_kernel(DecodeArgs a) {
             o[j] = mfma(phi, bv, o[j]);
             o[j] = mfma(plo, bv, o[j]);
         }
+        if (more) stage(sw);   // every LDS read of this tile has been issued: overwrite with the next tile
     }
 
     // ------------------------------------------------------------------ residual (fp16) tiles
