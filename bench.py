@@ -107,6 +107,8 @@ def main(argv=None):
     ap.add_argument("--workload", default="llama3_8b_gqa_32k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-slices", type=int, default=12)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (5 times), the reference for HBM byte counters")
     args = ap.parse_args(argv)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -116,6 +118,17 @@ def main(argv=None):
         return 2
 
     import torch
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 5}}))
+        return 0
 
     import decode_attention_quant_amd as kvq
     import kvsynth
