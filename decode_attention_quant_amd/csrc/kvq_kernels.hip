@@ -212,31 +212,73 @@ __device__ __forceinline__ float rows_sum(float v) {
     return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
-// One wavefront per (split, batch row, KV head, chunk of up to 4 query heads of that KV head).
+// Sum over the 16 lanes of each row with DPP lane permutations (every lane of the row ends with the same value:
+// each step adds a lane and its mirror, an exchange that gives both the same rounded sum).
+template <int CTRL>
+__device__ __forceinline__ float dpp_xadd(float v) {
+    const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
+    return v + __builtin_bit_cast(float, s);
+}
+constexpr int DPP_QUAD_1032 = 0xB1;      // quad_perm [1, 0, 3, 2]: lane pairs (0,1), (2,3)
+constexpr int DPP_QUAD_2301 = 0x4E;      // quad_perm [2, 3, 0, 1]
+constexpr int DPP_ROW_HALF_MIRROR = 0x141;
+constexpr int DPP_ROW_MIRROR = 0x140;
+__device__ __forceinline__ float row16_sum(float v) {
+    v = dpp_xadd<DPP_QUAD_1032>(v);
+    v = dpp_xadd<DPP_QUAD_2301>(v);
+    v = dpp_xadd<DPP_ROW_HALF_MIRROR>(v);
+    return dpp_xadd<DPP_ROW_MIRROR>(v);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_xmax(float v) {
+    const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
+    return fmaxf(v, __builtin_bit_cast(float, s));
+}
+__device__ __forceinline__ float row16_max(float v) {
+    v = dpp_xmax<DPP_QUAD_1032>(v);
+    v = dpp_xmax<DPP_QUAD_2301>(v);
+    v = dpp_xmax<DPP_ROW_HALF_MIRROR>(v);
+    return dpp_xmax<DPP_ROW_MIRROR>(v);
+}
+
+// One wavefront per (split, batch row, KV head, chunk of up to 4 query heads of that KV head); lane l = n + 16 kc.
 //
-// Lane l = n + 16 kc (n = 0..15, kc = 0..3). Scores are computed transposed, S^T[t][n] = sum_c code[t][c] q~[c][n],
-// with 16x16x32 fp16 MFMAs: the A operand is a 16-token block of key codes (exact small integers), the B operand
-// holds the query with the tile's key scales folded in (q~ = q' * s_K, split into an fp16 high part and an fp16
-// low part that are contracted one after the other), and a leading contraction with A = z_K (rows broadcast) and
-// B = q' adds the zero-point term sum_c q' z_K. Column n carries query head n / 4 of the chunk, replicated over
-// the four value channel groups g = n % 4, so that lane n's probabilities are exactly the PV A-operand row
-// (head n / 4, group n % 4): P~[n][t] = p[t] * s_V[g][t] (fp16 high + low), contracted against the value codes of
-// all 128 channels (8 N-blocks of 16); for channel block j only row group g = j / 2 is kept. The value zero-point
-// term sum_t p[t] z_V[g][t] is accumulated on the VALU and added at the end.
+// Scores. The query with the tile's key scales folded in, q~[h][c] = q'[h][c] s_K[c], is split into an fp16 high
+// part and an fp16 low part (q' = q 2^-E_h with |q'| < 1, so both stay in range for any fp16 scale). One
+// 16x16x32 fp16 MFMA per (16-token block, 32-channel block) takes A = q~ with row m = 4 h + r carrying the high
+// part of head h for even r and the low part for odd r, and B = the key codes (exact small integers, expanded
+// from the packed 2-bit words with the gfx950 fp4 converter), column = token. Output lane (t, kc) then holds head
+// kc's high-part and low-part sums for token t in its first two accumulator registers: one add gives the score,
+// and each lane owns the scores of exactly one (head, token) pair per block, two per tile. The accumulator starts
+// at beta[h] - mr[h] in the high-part row, where beta[h] = sum_c q'[h][c] z_K[c] is the tile's zero-point term
+// (computed once per tile on the VALU: packed fp16 dot products, fp32 sums) and mr[h] the running maximum, so the
+// sum is already relative to the maximum.
 //
-// Per-wavefront LDS: the tile's 1 KB of scales/zeros and the 2 KB folded query (high and low parts, computed once
-// per (head, channel) rather than once per replicated column). Both are written for tile v + 1 at the end of
-// iteration v, after every read of tile v has been issued (a wavefront's LDS operations complete in order), so
-// the next iteration starts with its operands in place. The fp16 window tiles reuse the same 8 KB.
+// Softmax. Lagged maximum: p = 2^(C_h (score - mr)) is taken directly unless some score exceeds mr (or on the
+// first tile); only then the tile maximum is reduced over the row, mr raised and the accumulators rescaled.
+//
+// PV. The probabilities go through 512 B of LDS to the A layout of the PV contraction: row n = (head n / 4,
+// value group g = n % 4) carries p~ = p s_V[g][t] as fp16 high and low parts (mixed-precision fmas, one rounding
+// each), contracted in turn against the value codes of the 8 channel blocks of 16; for channel block j only row
+// group g = j / 2 is kept. The value zero-point term sum_t p z_V[g][t] is accumulated on the VALU.
+//
+// Per-wavefront LDS: the tile's scales/zeros (1 KB), the folded query (2 KB) and beta, all written for tile v + 1
+// at the end of iteration v after every read of tile v has been issued (a wavefront's LDS operations complete in
+// order); the probability exchange (512 B); the fp16 window value tile (8 KB, reusing the first region).
 constexpr int LDS_SZ = 0;            // 256 x uint32: s_K[128], z_K[128], s_V[4][32], z_V[4][32] (fp16)
 constexpr int LDS_QT = 1024;         // fp16 [2 (high, low)][4 heads][128 channels]
-constexpr int LDS_BYTES = 8192;      // also the fp16 window tile [32][128]
+constexpr int LDS_BETA = 3072;       // fp32 [4 heads]
+constexpr int LDS_P = 8192;          // fp32 [4 heads][16][2]: p of tokens i and 16 + i
+constexpr int LDS_BYTES = 8704;      // [0, 8192) also holds the fp16 window value tile [32][128]
 
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void decode_pass1_kernel(DecodeArgs a) {
     __shared__ __align__(16) unsigned char smem[LDS_BYTES];
     uint32_t *sz_lds = reinterpret_cast<uint32_t *>(smem + LDS_SZ);
     const _Float16 *szh = reinterpret_cast<const _Float16 *>(smem + LDS_SZ);
     _Float16 *qt_lds = reinterpret_cast<_Float16 *>(smem + LDS_QT);
+    float *beta_lds = reinterpret_cast<float *>(smem + LDS_BETA);
+    float *p_lds = reinterpret_cast<float *>(smem + LDS_P);
     _Float16 *vres_lds = reinterpret_cast<_Float16 *>(smem);
 
     const int l = threadIdx.x;
@@ -249,46 +291,32 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     const int G = a.q_heads / a.kv_heads;
     const int gc = min(4, G - 4 * chunk);
     const int h0 = hkv * G + 4 * chunk;
-    const bool col_valid = hl < gc;
 
-    // ---- query, two layouts. MFMA B layout (column n, channels 32 ks + 8 kc + e): used for the zero-point term and
-    // the window tiles. Folding layout (head kc, channels 8 n .. 8 n + 7): one (head, channel) per lane slot.
-    const _Float16 *qp = a.q + ((int64_t)b * a.q_heads + h0 + (col_valid ? hl : 0)) * D;
-    h8 qv[4];
-    float qmax = 0.0f;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        qv[ks] = *reinterpret_cast<const h8 *>(qp + 32 * ks + 8 * kc);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, fabsf((float)qv[ks][e]));
-    }
-    qmax = rows_max(qmax);
-    // q' = q * 2^-E with 2^E > max |q|: |q'| < 1 keeps q' * s_K within binary16 range for any fp16 scale
-    int E = 0;   // qmax is a float16 value widened, hence a normal binary32 number: read its exponent field
-    if (qmax > 0.0f) E = (int)((__builtin_bit_cast(uint32_t, qmax) >> 23) & 0xffu) - 127 + 1;
-    const float qsc = pow2(-E);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qv[ks][e] = col_valid ? (_Float16)((float)qv[ks][e] * qsc) : (_Float16)0.0f;
-    // folding layout: lane (n, kc) holds head kc of the chunk (if valid), channels 8n .. 8n+7; its own scale 2^-E_kc
+    // ---- query: lane (n, kc) holds head kc of the chunk (if valid), channels 8n .. 8n+7, scaled by 2^-E with
+    // 2^E > max |q| of that head (qmax is a float16 value widened, hence a normal binary32 number: its exponent
+    // field gives E). C turns a raw score of head kc (in q' units) into the log2 domain.
     h8 qf = {};
+    float C;
     {
-        const bool fv = kc < gc;
-        const _Float16 *qfp = a.q + ((int64_t)b * a.q_heads + h0 + (fv ? kc : 0)) * D + 8 * n;
-        const h8 raw = *reinterpret_cast<const h8 *>(qfp);
-        // after rows_max, lane 4 kc (column 4 kc, head kc) holds the maximum of head kc
-        const float qm_head = __shfl(qmax, 4 * kc);
-        int Eh = 0;
-        if (qm_head > 0.0f) Eh = (int)((__builtin_bit_cast(uint32_t, qm_head) >> 23) & 0xffu) - 127 + 1;
-        const float sch = pow2(-Eh);
+        const bool hv = kc < gc;
+        const h8 raw = *reinterpret_cast<const h8 *>(a.q + ((int64_t)b * a.q_heads + h0 + (hv ? kc : 0)) * D + 8 * n);
+        float qmax = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qf[e] = fv ? (_Float16)((float)raw[e] * sch) : (_Float16)0.0f;
+        for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, fabsf((float)raw[e]));
+        qmax = row16_max(qmax);
+        int E = 0;
+        if (qmax > 0.0f) E = (int)((__builtin_bit_cast(uint32_t, qmax) >> 23) & 0xffu) - 127 + 1;
+        const float qsc = pow2(-E);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[e] = hv ? (_Float16)((float)raw[e] * qsc) : (_Float16)0.0f;
+        C = a.sm_log2 * pow2(E);
     }
-    const float C = a.sm_log2 * pow2(E);   // score (in q' units) -> log2 domain
 
-    float m = -__builtin_inff();
-    float lsum = 0.0f, gam = 0.0f;
+    // softmax state of head kc (lanes of row kc agree): running maximum mr of the raw scores, valid once `seen`
+    float mr = 0.0f, lsum = 0.0f;
+    bool seen = false;
+    // PV state: o[j] rows (head kc, group r), column n = channel n + 16 j; gam: lane (n, kc) for (head hl, group g)
+    float gam = 0.0f;
     f4 o[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = f4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -299,19 +327,59 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     const int qend = min(v1, a.n_qtiles);
     const uint8_t *base = a.tiles + ((int64_t)b * a.kv_heads + hkv) * a.max_tiles * (int64_t)REC;
 
-    // stage a tile's scales/zeros and its folded query (high, low) into LDS
+    // s0, s1: raw score minus mr of head kc for tokens n and 16 + n of the tile (-inf for absent tokens).
+    // Raises mr to the tile maximum where it is exceeded (every head on the first tile) and rescales.
+    auto rescale = [&](float &s0, float &s1) {
+        float d = row16_max(fmaxf(s0, s1));
+        if (seen) d = fmaxf(d, 0.0f);
+        const float alpha = seen ? __builtin_amdgcn_exp2f(-d * C) : 1.0f;
+        mr += d;
+        s0 -= d;
+        s1 -= d;
+        lsum *= alpha;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[j][r] *= alpha;
+        gam *= __shfl(alpha, 16 * hl);
+        seen = true;
+    };
+    // p of tokens n and 16 + n to LDS; returns, for the PV A layout of lane (n, kc), p of tokens 4kc + i (p[i]) and
+    // 16 + 4kc + i (p[4 + i]) of head hl
+    auto exchange = [&](float p0, float p1, float p[8]) {
+        reinterpret_cast<float2 *>(p_lds)[16 * kc + n] = float2{p0, p1};
+        __syncthreads();
+        const f4 pa = reinterpret_cast<const f4 *>(p_lds)[(16 * hl + 4 * kc) / 2];
+        const f4 pb = reinterpret_cast<const f4 *>(p_lds)[(16 * hl + 4 * kc) / 2 + 1];
+        p[0] = pa[0]; p[4] = pa[1]; p[1] = pa[2]; p[5] = pa[3];
+        p[2] = pb[0]; p[6] = pb[1]; p[3] = pb[2]; p[7] = pb[3];
+    };
+
+    // stage a tile's scales/zeros, its folded query (high, low) and beta into LDS
     auto stage = [&](const uint4 &sw) {
         reinterpret_cast<uint4 *>(sz_lds)[l] = sw;
         __syncthreads();
         const h8 sk = *reinterpret_cast<const h8 *>(szh + 8 * n);
+        const h8 zk = *reinterpret_cast<const h8 *>(szh + 128 + 8 * n);
         const h8 hi = qf * sk;
         const h8 lo = __builtin_elementwise_fma(qf, sk, -hi);
         *reinterpret_cast<h8 *>(qt_lds + 128 * kc + 8 * n) = hi;
         *reinterpret_cast<h8 *>(qt_lds + 512 + 128 * kc + 8 * n) = lo;
+        float bp = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2)
+            bp = __builtin_amdgcn_fdot2(h2{zk[e], zk[e + 1]}, h2{qf[e], qf[e + 1]}, bp, false);
+        bp = row16_sum(bp);    // beta of head kc, in every lane of row kc
+        if (n == 0) beta_lds[kc] = bp;
         __syncthreads();
     };
 
     // ------------------------------------------------------------------ quantized tiles
+    // Each code word is reloaded for the next tile right after its last use in this one (scales: at the top of the
+    // iteration, key codes after the score contraction, value codes after PV), so no register holds two tiles. On
+    // the last tile the index is clamped: the reload hits the just-read record in cache.
+    const float zero_f = __builtin_bit_cast(float, opaque(0u));   // keeps fma(p, s, 0) a mixed-precision fma
+    const _Float16 *qta = qt_lds + 512 * (n & 1) + 128 * hl + 8 * kc;   // A operand row n: head hl, part n % 2
     uint4 kw, vw, sw;
     if (v0 < qend) {
         const uint8_t *rec = base + (int64_t)v0 * REC;
@@ -321,64 +389,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
         stage(sw);
     }
     for (int v = v0; v < qend; ++v) {
-        const uint32_t kwa[4] = {kw.x, kw.y, kw.z, kw.w};
-        const uint32_t vwa[4] = {vw.x, vw.y, vw.z, vw.w};
         const bool more = v + 1 < qend;
-        if (more) {    // prefetch the next tile
-            const uint8_t *rec = base + (int64_t)(v + 1) * REC;
-            kw = reinterpret_cast<const uint4 *>(rec)[l];
-            vw = reinterpret_cast<const uint4 *>(rec + 1024)[l];
-            sw = reinterpret_cast<const uint4 *>(rec + 2048)[l];
-        }
+        const uint8_t *next = base + (int64_t)(more ? v + 1 : v) * REC;
+        sw = reinterpret_cast<const uint4 *>(next + 2048)[l];
 
-        // zero-point term: acc0[t][n] = sum_c z_K[c] q'[c][n] (the same for every token row)
-        f4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f};
+        const f4 ci = {beta_lds[kc] - mr, 0.0f, 0.0f, 0.0f};
+        f4 acc0 = ci, acc1 = ci;    // tokens n (acc0) and 16 + n (acc1); rows (head kc, part r)
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const h8 zk = *reinterpret_cast<const h8 *>(szh + 128 + 32 * ks + 8 * kc);
-            acc0 = mfma(zk, qv[ks], acc0);
+            const h8 bq = *reinterpret_cast<const h8 *>(qta + 32 * ks);
+            acc0 = mfma(bq, expand8(nibbles(kw[ks >> 1], ks & 1)), acc0);
+            acc1 = mfma(bq, expand8(nibbles(kw[2 + (ks >> 1)], ks & 1)), acc1);
         }
-        f4 acc1 = acc0;
-        const _Float16 *qth = qt_lds + 128 * hl + 8 * kc;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const h8 hi = *reinterpret_cast<const h8 *>(qth + 32 * ks);
-            const h8 lo = *reinterpret_cast<const h8 *>(qth + 512 + 32 * ks);
-            const h8 a0 = expand8(nibbles(kwa[ks >> 1], ks & 1));
-            const h8 a1 = expand8(nibbles(kwa[2 + (ks >> 1)], ks & 1));
-            acc0 = mfma(a0, hi, acc0);
-            acc1 = mfma(a1, hi, acc1);
-            acc0 = mfma(a0, lo, acc0);
-            acc1 = mfma(a1, lo, acc1);
-        }
-        // acc0[r]: token 4 kc + r; acc1[r]: token 16 + 4 kc + r; column n. C > 0, so the maximum is taken on the
-        // raw accumulators and scaled once.
-        float mx = fmaxf(fmaxf(fmaxf(acc0[0], acc0[1]), fmaxf(acc0[2], acc0[3])),
-                         fmaxf(fmaxf(acc1[0], acc1[1]), fmaxf(acc1[2], acc1[3])));
-        mx = rows_max(mx) * C;
-        const float mnew = fmaxf(m, mx);
-        if (__any(mnew > m)) {
-            const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-            lsum *= alpha;
-            gam *= alpha;
-            float ar[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * kc + r);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) o[j][r] *= ar[r];
-            m = mnew;
-        }
+        kw = reinterpret_cast<const uint4 *>(next)[l];
+        float s0 = acc0[0] + acc0[1], s1 = acc1[0] + acc1[1];
+        if (!seen || __any(fmaxf(s0, s1) > 0.0f)) rescale(s0, s1);
+        const float p0 = __builtin_amdgcn_exp2f(s0 * C), p1 = __builtin_amdgcn_exp2f(s1 * C);
+        lsum += p0 + p1;
         float p[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            p[r] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc0[r], C, -m));
-            p[4 + r] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc1[r], C, -m));
-        }
-        lsum += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
+        exchange(p0, p1, p);
 
-        // value scales/zeros of tokens 4kc..4kc+3 and 16+4kc..16+4kc+3, channel group g
+        // p~ = p * s_V of group g, fp16 high part and the fp16 rounding of the remainder; value zero points
         const h4 sv0 = *reinterpret_cast<const h4 *>(szh + 256 + 32 * g + 4 * kc);
         const h4 sv1 = *reinterpret_cast<const h4 *>(szh + 256 + 32 * g + 16 + 4 * kc);
         const h4 zv0 = *reinterpret_cast<const h4 *>(szh + 384 + 32 * g + 4 * kc);
@@ -386,98 +417,89 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
         h8 phi, plo;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float t0 = p[i] * (float)sv0[i];
-            const float t1 = p[4 + i] * (float)sv1[i];
-            phi[i] = (_Float16)t0;
-            phi[4 + i] = (_Float16)t1;
-            plo[i] = (_Float16)(t0 - (float)phi[i]);
-            plo[4 + i] = (_Float16)(t1 - (float)phi[4 + i]);
+            phi[i] = (_Float16)__builtin_fmaf(p[i], (float)sv0[i], zero_f);
+            phi[4 + i] = (_Float16)__builtin_fmaf(p[4 + i], (float)sv1[i], zero_f);
+            plo[i] = (_Float16)__builtin_fmaf(p[i], (float)sv0[i], -(float)phi[i]);
+            plo[4 + i] = (_Float16)__builtin_fmaf(p[4 + i], (float)sv1[i], -(float)phi[4 + i]);
             gam = __builtin_fmaf(p[i], (float)zv0[i], gam);
             gam = __builtin_fmaf(p[4 + i], (float)zv1[i], gam);
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const h8 bv = expand8(nibbles(vwa[j >> 1], j & 1));
+            const h8 bv = expand8(nibbles(vw[j >> 1], j & 1));
             o[j] = mfma(phi, bv, o[j]);
             o[j] = mfma(plo, bv, o[j]);
         }
+        vw = reinterpret_cast<const uint4 *>(next + 1024)[l];
         if (more) stage(sw);   // every LDS read of this tile has been issued: overwrite with the next tile
     }
 
     // ------------------------------------------------------------------ residual (fp16) tiles
-    const _Float16 *kres = a.k_res + ((int64_t)b * a.kv_heads + hkv) * a.res_cap * D;
-    const _Float16 *vres = a.v_res + ((int64_t)b * a.kv_heads + hkv) * a.res_cap * D;
-    for (int v = max(v0, a.n_qtiles); v < v1; ++v) {
-        const int r0 = (v - a.n_qtiles) * 32;
-        const int nv = min(32, a.n_resid - r0);
+    // The same contraction with A = q' (high part) and 0 (low part), B = the fp16 key rows; p~ = p (no scales).
+    const int w0 = max(v0, a.n_qtiles);
+    if (w0 < v1) {
+        h8 qw[4];
         __syncthreads();
-        // stage the value rows (zeros beyond the valid ones) for the transposed PV operand
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int idx = l + 64 * i;        // 16-byte chunk: token idx / 16, channels 8 (idx % 16) ..
-            const int tok = idx >> 4;
-            uint4 val = {0u, 0u, 0u, 0u};
-            if (tok < nv) val = reinterpret_cast<const uint4 *>(vres + (int64_t)(r0 + tok) * D)[idx & 15];
-            reinterpret_cast<uint4 *>(vres_lds)[idx] = val;
-        }
-        f4 acc0 = {0.0f, 0.0f, 0.0f, 0.0f}, acc1 = acc0;
-        const int t0 = min(n, nv - 1), t1 = min(16 + n, nv - 1);
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const h8 k0 = *reinterpret_cast<const h8 *>(kres + (int64_t)(r0 + t0) * D + 32 * ks + 8 * kc);
-            const h8 k1 = *reinterpret_cast<const h8 *>(kres + (int64_t)(r0 + t1) * D + 32 * ks + 8 * kc);
-            acc0 = mfma(k0, qv[ks], acc0);
-            acc1 = mfma(k1, qv[ks], acc1);
-        }
-        float x[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            x[r] = (4 * kc + r < nv) ? acc0[r] * C : -__builtin_inff();
-            x[4 + r] = (16 + 4 * kc + r < nv) ? acc1[r] * C : -__builtin_inff();
-        }
-        float mx = x[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) mx = fmaxf(mx, x[i]);
-        mx = rows_max(mx);
-        const float mnew = fmaxf(m, mx);
-        if (__any(mnew > m)) {
-            const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-            lsum *= alpha;
-            gam *= alpha;
-            float ar[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * kc + r);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) o[j][r] *= ar[r];
-            m = mnew;
-        }
-        h8 phi, plo;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float p = __builtin_amdgcn_exp2f(x[i] - m);
-            lsum += p;
-            phi[i] = (_Float16)p;
-            plo[i] = (_Float16)(p - (float)phi[i]);
-        }
+        *reinterpret_cast<h8 *>(qt_lds + 128 * kc + 8 * n) = qf;
+        *reinterpret_cast<h8 *>(qt_lds + 512 + 128 * kc + 8 * n) = h8{};
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            h8 bv;
+        for (int ks = 0; ks < 4; ++ks) qw[ks] = *reinterpret_cast<const h8 *>(qta + 32 * ks);
+        const _Float16 *kres = a.k_res + ((int64_t)b * a.kv_heads + hkv) * a.res_cap * D;
+        const _Float16 *vres = a.v_res + ((int64_t)b * a.kv_heads + hkv) * a.res_cap * D;
+        for (int v = w0; v < v1; ++v) {
+            const int r0 = (v - a.n_qtiles) * 32;
+            const int nv = min(32, a.n_resid - r0);
+            __syncthreads();
+            // stage the value rows (zeros beyond the valid ones) for the transposed PV operand
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int tok = (e < 4) ? (4 * kc + e) : (16 + 4 * kc + e - 4);
-                bv[e] = vres_lds[tok * 128 + n + 16 * j];
+            for (int i = 0; i < 8; ++i) {
+                const int idx = l + 64 * i;        // 16-byte chunk: token idx / 16, channels 8 (idx % 16) ..
+                const int tok = idx >> 4;
+                uint4 val = {0u, 0u, 0u, 0u};
+                if (tok < nv) val = reinterpret_cast<const uint4 *>(vres + (int64_t)(r0 + tok) * D)[idx & 15];
+                reinterpret_cast<uint4 *>(vres_lds)[idx] = val;
             }
-            o[j] = mfma(phi, bv, o[j]);
-            o[j] = mfma(plo, bv, o[j]);
+            const f4 ci = {-mr, 0.0f, 0.0f, 0.0f};
+            f4 acc0 = ci, acc1 = ci;
+            const int t0 = min(n, nv - 1), t1 = min(16 + n, nv - 1);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const h8 k0 = *reinterpret_cast<const h8 *>(kres + (int64_t)(r0 + t0) * D + 32 * ks + 8 * kc);
+                const h8 k1 = *reinterpret_cast<const h8 *>(kres + (int64_t)(r0 + t1) * D + 32 * ks + 8 * kc);
+                acc0 = mfma(qw[ks], k0, acc0);
+                acc1 = mfma(qw[ks], k1, acc1);
+            }
+            float s0 = (n < nv) ? acc0[0] + acc0[1] : -__builtin_inff();
+            float s1 = (16 + n < nv) ? acc1[0] + acc1[1] : -__builtin_inff();
+            if (!seen || __any(fmaxf(s0, s1) > 0.0f)) rescale(s0, s1);
+            const float p0 = __builtin_amdgcn_exp2f(s0 * C), p1 = __builtin_amdgcn_exp2f(s1 * C);
+            lsum += p0 + p1;
+            float p[8];
+            exchange(p0, p1, p);
+            h8 phi, plo;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                phi[i] = (_Float16)p[i];
+                plo[i] = (_Float16)(p[i] - (float)phi[i]);
+            }
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                h8 bv;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int tok = (e < 4) ? (4 * kc + e) : (16 + 4 * kc + e - 4);
+                    bv[e] = vres_lds[tok * 128 + n + 16 * j];
+                }
+                o[j] = mfma(phi, bv, o[j]);
+                o[j] = mfma(plo, bv, o[j]);
+            }
         }
     }
 
     // ------------------------------------------------------------------ partials of this split
-    lsum = rows_sum(lsum);
-    gam = rows_sum(gam);
+    lsum = row16_sum(lsum);    // head kc
+    gam = rows_sum(gam);       // (head hl, group g)
     float gr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) gr[r] = __shfl(gam, 4 * kc + r);
@@ -487,12 +509,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
         float *po = a.part_o + (((int64_t)b * a.q_heads + hq) * S + split) * D;
 #pragma unroll
         for (int j = 0; j < 8; ++j) po[n + 16 * j] = o[j][j >> 1] + gr[j >> 1];
-    }
-    if (kc == 0 && g == 0 && col_valid) {
-        const int hq = h0 + hl;
-        float *pm = a.part_ml + (((int64_t)b * a.q_heads + hq) * S + split) * 2;
-        pm[0] = m;
-        pm[1] = lsum;
+        if (n == 0) {
+            float *pm = a.part_ml + (((int64_t)b * a.q_heads + hq) * S + split) * 2;
+            pm[0] = seen ? mr * C : -__builtin_inff();
+            pm[1] = lsum;
+        }
     }
 }
 
