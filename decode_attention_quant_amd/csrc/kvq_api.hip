@@ -9,7 +9,9 @@
 
 namespace {
 
-constexpr int64_t kTargetWaves = 8192;   // about eight wavefronts per SIMD on 256 CUs x 4 SIMDs
+// One wavefront per resident slot: the decode kernel holds four wavefronts per SIMD (its register budget), so
+// 256 CUs x 4 SIMDs x 4 = 4096 wavefronts run as a single round with no tail of partly filled rounds.
+constexpr int64_t kTargetWaves = 4096;
 constexpr int64_t kMinTilesPerSplit = 4;
 constexpr int64_t kMaxSplits = 1024;
 

@@ -179,6 +179,17 @@ __device__ __forceinline__ float pow2(int k) { return __builtin_bit_cast(float, 
 
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
+// x = (pa * s.lo, pb * s.hi) for an fp32 pair (pa, pb) and a packed fp16 pair s: hi = RN16(x), lo = RN16(x - hi),
+// each element one mixed-precision fma with a single rounding, written straight into the packed halves
+__device__ __forceinline__ void split_pair(float pa, float pb, uint32_t s, uint32_t &hi, uint32_t &lo) {
+    asm("v_fma_mixlo_f16 %0, %2, %4, 0 op_sel_hi:[0,1,0]\n\t"
+        "v_fma_mixhi_f16 %0, %3, %4, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]\n\t"
+        "v_fma_mixlo_f16 %1, %2, %4, -%0 op_sel_hi:[0,1,1]\n\t"
+        "v_fma_mixhi_f16 %1, %3, %4, -%0 op_sel:[0,1,1] op_sel_hi:[0,1,1]"
+        : "=&v"(hi), "=&v"(lo)
+        : "v"(pa), "v"(pb), "v"(s));
+}
+
 // Cross-row reductions over the four 16-lane rows of a wavefront with the gfx950 row swaps. Two compiler traps
 // are avoided here: the second operand goes through an empty asm statement (a swap whose operands the compiler
 // can prove equal is folded into the identity), and the result pair is copied into named integers before use
@@ -284,7 +295,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     const int l = threadIdx.x;
     const int n = l & 15, kc = l >> 4, hl = n >> 2, g = n & 3;
     const int unit = blockIdx.x;
-    const int split = blockIdx.y;
+    const int split = gridDim.y - 1 - blockIdx.y;   // the split holding the fp16 window tiles is dispatched first
     const int chunk = unit % a.chunks;
     const int hkv = (unit / a.chunks) % a.kv_heads;
     const int b = unit / (a.chunks * a.kv_heads);
@@ -378,7 +389,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     // Each code word is reloaded for the next tile right after its last use in this one (scales: at the top of the
     // iteration, key codes after the score contraction, value codes after PV), so no register holds two tiles. On
     // the last tile the index is clamped: the reload hits the just-read record in cache.
-    const float zero_f = __builtin_bit_cast(float, opaque(0u));   // keeps fma(p, s, 0) a mixed-precision fma
     const _Float16 *qta = qt_lds + 512 * (n & 1) + 128 * hl + 8 * kc;   // A operand row n: head hl, part n % 2
     uint4 kw, vw, sw;
     if (v0 < qend) {
@@ -389,8 +399,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
         stage(sw);
     }
     for (int v = v0; v < qend; ++v) {
-        const bool more = v + 1 < qend;
-        const uint8_t *next = base + (int64_t)(more ? v + 1 : v) * REC;
+        const uint8_t *next = base + (int64_t)min(v + 1, qend - 1) * REC;
         sw = reinterpret_cast<const uint4 *>(next + 2048)[l];
 
         const f4 ci = {beta_lds[kc] - mr, 0.0f, 0.0f, 0.0f};
@@ -414,13 +423,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
         const h4 sv1 = *reinterpret_cast<const h4 *>(szh + 256 + 32 * g + 16 + 4 * kc);
         const h4 zv0 = *reinterpret_cast<const h4 *>(szh + 384 + 32 * g + 4 * kc);
         const h4 zv1 = *reinterpret_cast<const h4 *>(szh + 384 + 32 * g + 16 + 4 * kc);
-        h8 phi, plo;
+        const uint2 sa = __builtin_bit_cast(uint2, sv0), sb = __builtin_bit_cast(uint2, sv1);
+        uint4 uh, ul;
+        split_pair(p[0], p[1], sa.x, uh.x, ul.x);
+        split_pair(p[2], p[3], sa.y, uh.y, ul.y);
+        split_pair(p[4], p[5], sb.x, uh.z, ul.z);
+        split_pair(p[6], p[7], sb.y, uh.w, ul.w);
+        const h8 phi = __builtin_bit_cast(h8, uh), plo = __builtin_bit_cast(h8, ul);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            phi[i] = (_Float16)__builtin_fmaf(p[i], (float)sv0[i], zero_f);
-            phi[4 + i] = (_Float16)__builtin_fmaf(p[4 + i], (float)sv1[i], zero_f);
-            plo[i] = (_Float16)__builtin_fmaf(p[i], (float)sv0[i], -(float)phi[i]);
-            plo[4 + i] = (_Float16)__builtin_fmaf(p[4 + i], (float)sv1[i], -(float)phi[4 + i]);
             gam = __builtin_fmaf(p[i], (float)zv0[i], gam);
             gam = __builtin_fmaf(p[4 + i], (float)zv1[i], gam);
         }
@@ -431,7 +442,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
             o[j] = mfma(plo, bv, o[j]);
         }
         vw = reinterpret_cast<const uint4 *>(next + 1024)[l];
-        if (more) stage(sw);   // every LDS read of this tile has been issued: overwrite with the next tile
+        // every LDS read of this tile has been issued: overwrite with the next tile (after the last tile, with
+        // that tile again; unconditional, so no load sits on only one path of the loop)
+        stage(sw);
     }
 
     // ------------------------------------------------------------------ residual (fp16) tiles
