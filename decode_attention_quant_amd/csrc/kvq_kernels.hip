@@ -280,6 +280,7 @@ __device__ __forceinline__ float row16_max(float v) {
 constexpr int LDS_SZ = 0;            // 256 x uint32: s_K[128], z_K[128], s_V[4][32], z_V[4][32] (fp16)
 constexpr int LDS_QT = 1024;         // fp16 [2 (high, low)][4 heads][128 channels]
 constexpr int LDS_BETA = 3072;       // fp32 [4 heads]
+constexpr int LDS_ZERO = 3088;       // 256 zero bytes: A-operand rows 4 h + 2, 4 h + 3 of the score contraction
 constexpr int LDS_P = 8192;          // fp32 [4 heads][16][2]: p of tokens i and 16 + i
 constexpr int LDS_BYTES = 8704;      // [0, 8192) also holds the fp16 window value tile [32][128]
 
@@ -389,7 +390,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     // Each code word is reloaded for the next tile right after its last use in this one (scales: at the top of the
     // iteration, key codes after the score contraction, value codes after PV), so no register holds two tiles. On
     // the last tile the index is clamped: the reload hits the just-read record in cache.
-    const _Float16 *qta = qt_lds + 512 * (n & 1) + 128 * hl + 8 * kc;   // A operand row n: head hl, part n % 2
+    // A operand row n = 4 h + r: head h, high part (r = 0), low part (r = 1), zeros (r = 2, 3: unused outputs)
+    const _Float16 *qta = (n & 2) ? reinterpret_cast<const _Float16 *>(smem + LDS_ZERO) + 8 * kc
+                                  : qt_lds + 512 * (n & 1) + 128 * hl + 8 * kc;
+    reinterpret_cast<uint32_t *>(smem + LDS_ZERO)[l] = 0u;
     uint4 kw, vw, sw;
     if (v0 < qend) {
         const uint8_t *rec = base + (int64_t)v0 * REC;
