@@ -103,6 +103,38 @@ def cpu_baseline(w, queries, n_slices, context):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def fp16_comparator(kvq, w, Kd, Vd, q, context, call_us_2bit, calls):
+    """The same decode-attention call over an all-fp16 cache of the same context: a window as large as the context,
+    so nothing is quantized (same library, same kernel, fp16 tiles only). Timed with HIP events over `calls` calls
+    after 3 warm-ups; the cache is built from the same synthetic K/V."""
+    import torch
+    cap = ((context + 31) // 32) * 32
+    shape = kvq.Shape(w.batch, w.kv_heads, w.q_heads, residual_cap=cap, max_tokens=cap)
+    c16 = kvq.KVCache(shape)
+    kvq.kv_append_and_flush(c16, Kd[:, :, :context], Vd[:, :, :context])
+    out = torch.empty((w.batch, w.q_heads, 128), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(16, kvq.kv_decode_attention_workspace_bytes(c16)), dtype=torch.uint8, device="cuda")
+    for _ in range(3):
+        kvq.kv_decode_attention(c16, q, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(calls + 1)]
+    ev[0].record()
+    for i in range(calls):
+        kvq.kv_decode_attention(c16, q, out=out, workspace=ws)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(calls)]
+    us = 1e3 * sum(ms) / calls
+    nbytes = w.batch * w.kv_heads * context * 512 + w.batch * w.q_heads * 128 * 6
+    del c16, ws
+    torch.cuda.empty_cache()
+    log(f"[bench] fp16 comparator: {context} fp16 tokens, {us:.1f} us per call, {nbytes / us / 1e3:.0f} GB/s")
+    return {"context": context, "decode_call_us": us, "bytes_per_call": nbytes, "hbm_gb_s": nbytes / us / 1e3,
+            "pct_of_peak": 100.0 * nbytes / us / 1e3 / PEAK_GBS, "kv_tokens_per_s": w.batch * context / (us * 1e-6),
+            "speedup_2bit_over_fp16": us / call_us_2bit,
+            "note": "same library and kernel over a window as large as the context (no quantized tiles)"}
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +144,8 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-slices", type=int, default=24)
     ap.add_argument("--cpu-queries", type=int, default=12)
+    ap.add_argument("--no-fp16-comparator", action="store_true")
+    ap.add_argument("--fp16-calls", type=int, default=20)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (5 times), the reference for HBM byte counters")
     args = ap.parse_args(argv)
@@ -197,6 +231,8 @@ def main(argv=None):
     value = kv_tokens / (total_ms * 1e-3)
     achieved = sum(call_bytes) / (sum(decode_ms) * 1e-3) / 1e9
     splits = kvq.kv_decode_attention_splits(cache)
+    dsorted = sorted(decode_ms)
+    pct = lambda f: 1e3 * dsorted[min(K - 1, int(f * (K - 1) + 0.5))]
     log(f"[bench] {K} steps in {total_ms:.3f} ms; decode call avg {1e3 * sum(decode_ms) / K:.1f} us "
         f"({achieved:.0f} GB/s); append avg {1e3 * sum(append_ms) / K:.1f} us, max {1e3 * max(append_ms):.1f} us; "
         f"splits={splits}")
@@ -223,12 +259,16 @@ def main(argv=None):
         "append_us_avg": 1e3 * sum(append_ms) / K,
         "append_us_max": 1e3 * max(append_ms),
         "splits": splits,
+        "decode_call_us_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
         "dtype_detail": "2-bit codes expanded to fp16 MFMA operands (scales folded as fp16 hi+lo), fp32 accumulation",
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / PEAK_GBS, "traffic": traffic_per_launch(),
                      "kernel": "decode_pass1_kernel + decode_pass2_kernel (one kv_decode_attention call)",
                      "bytes_per_call": sum(call_bytes) / K},
     }
+    if not args.no_fp16_comparator:
+        res["fp16_comparator"] = fp16_comparator(kvq, w, Kd, Vd, Q[W], contexts[0], res["decode_call_us"],
+                                                 args.fp16_calls)
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle on {args.cpu_slices} slices x {args.cpu_queries} queries")
         qs = [Q[W + j].cpu().numpy() for j in range(min(args.cpu_queries, K))]

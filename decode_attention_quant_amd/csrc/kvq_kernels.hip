@@ -223,6 +223,31 @@ __device__ __forceinline__ float rows_sum(float v) {
     return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
 }
 
+// LDS-DMA load: 16 bytes per lane from `src` into LDS at lds_base + 16 * lane (lds_base goes through M0, which
+// the statement saves and restores). Issued from inline asm so that the compiler's wait insertion, which cannot tell
+// the destination from the other LDS buffers, does not drain the vector-memory counter before every LDS access; the
+// destination's readers wait explicitly (wait_vmcnt), and loads complete in order, so these extra loads can only
+// make the compiler's own counted waits stricter.
+__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+}
+// gfx950 LDS transpose read of 16-bit elements: within each 16-lane row, lane i receives element i % 4 of the 8-byte
+// chunks read by lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 (in that order)
+typedef short s4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ h4 read_tr16(const _Float16 *lds) {
+    return __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4 *)lds));
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
+
 // Sum over the 16 lanes of each row with DPP lane permutations (every lane of the row ends with the same value:
 // each step adds a lane and its mirror, an exchange that gives both the same rounded sum).
 template <int CTRL>
@@ -452,7 +477,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     }
 
     // ------------------------------------------------------------------ residual (fp16) tiles
-    // The same contraction with A = q' (high part) and 0 (low part), B = the fp16 key rows; p~ = p (no scales).
+    // The same contraction with A = q' (high part; low part and rows 2, 3 zero) and B = the fp16 key rows, loaded
+    // straight into registers at the top of each iteration. The value rows of a tile are copied into LDS by LDS-DMA
+    // loads (issued for the next tile once PV has read the current one) and reach the PV B layout through transpose
+    // reads; p~ = p (no scales). Window tiles (at most four per split in the normal case) and all-fp16 caches (the
+    // fp16 comparator, bandwidth-bound: 16 KB per tile and wavefront) share this loop.
     const int w0 = max(v0, a.n_qtiles);
     if (w0 < v1) {
         h8 qw[4];
@@ -462,30 +491,46 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
         __syncthreads();
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) qw[ks] = *reinterpret_cast<const h8 *>(qta + 32 * ks);
+        wait_lgkmcnt0();    // the query rows are in registers: the LDS below may be overwritten
         const _Float16 *kres = a.k_res + ((int64_t)b * a.kv_heads + hkv) * a.res_cap * D;
         const _Float16 *vres = a.v_res + ((int64_t)b * a.kv_heads + hkv) * a.res_cap * D;
+        const uint32_t vt_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)smem;
+        // 32 value rows of tile v (8 KB, contiguous in the window; rows past the window's length are read from
+        // the buffer's capacity, which is a multiple of 32 rows, and zeroed in LDS before use)
+        auto v_dma = [&](int v) {
+            const unsigned char *src =
+                reinterpret_cast<const unsigned char *>(vres + (int64_t)(v - a.n_qtiles) * 32 * D) + 16 * l;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) lds_dma16(src + 1024 * i, vt_base + 1024 * i);
+        };
+        // key rows of tokens n and 16 + n (clamped to the window's length), channels 32 ks + 8 kc ..
+        auto k_load = [&](int v, h8 kr[8]) {
+            const int r0 = (v - a.n_qtiles) * 32;
+            const int nv = min(32, a.n_resid - r0);
+            const _Float16 *k0 = kres + (int64_t)(r0 + min(n, nv - 1)) * D + 8 * kc;
+            const _Float16 *k1 = kres + (int64_t)(r0 + min(16 + n, nv - 1)) * D + 8 * kc;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                kr[ks] = *reinterpret_cast<const h8 *>(k0 + 32 * ks);
+                kr[4 + ks] = *reinterpret_cast<const h8 *>(k1 + 32 * ks);
+            }
+        };
+        // transpose-read addressing: lane (n, kc) reads token 4 TQ + n / 4, channels 16 j + 4 (n % 4) .. + 3 and
+        // receives tokens 4 TQ .. 4 TQ + 3 of channel 16 j + n; TQ = kc (tokens 4 kc ..) and 4 + kc (16 + 4 kc ..)
+        const _Float16 *vt0 = vres_lds + (4 * kc + (n >> 2)) * 128 + 4 * (n & 3);
+        const _Float16 *vt1 = vt0 + 16 * 128;
+        v_dma(w0);
         for (int v = w0; v < v1; ++v) {
             const int r0 = (v - a.n_qtiles) * 32;
             const int nv = min(32, a.n_resid - r0);
-            __syncthreads();
-            // stage the value rows (zeros beyond the valid ones) for the transposed PV operand
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int idx = l + 64 * i;        // 16-byte chunk: token idx / 16, channels 8 (idx % 16) ..
-                const int tok = idx >> 4;
-                uint4 val = {0u, 0u, 0u, 0u};
-                if (tok < nv) val = reinterpret_cast<const uint4 *>(vres + (int64_t)(r0 + tok) * D)[idx & 15];
-                reinterpret_cast<uint4 *>(vres_lds)[idx] = val;
-            }
+            h8 kr[8];
+            k_load(v, kr);
             const f4 ci = {-mr, 0.0f, 0.0f, 0.0f};
             f4 acc0 = ci, acc1 = ci;
-            const int t0 = min(n, nv - 1), t1 = min(16 + n, nv - 1);
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const h8 k0 = *reinterpret_cast<const h8 *>(kres + (int64_t)(r0 + t0) * D + 32 * ks + 8 * kc);
-                const h8 k1 = *reinterpret_cast<const h8 *>(kres + (int64_t)(r0 + t1) * D + 32 * ks + 8 * kc);
-                acc0 = mfma(qw[ks], k0, acc0);
-                acc1 = mfma(qw[ks], k1, acc1);
+                acc0 = mfma(qw[ks], kr[ks], acc0);
+                acc1 = mfma(qw[ks], kr[4 + ks], acc1);
             }
             float s0 = (n < nv) ? acc0[0] + acc0[1] : -__builtin_inff();
             float s1 = (16 + n < nv) ? acc1[0] + acc1[1] : -__builtin_inff();
@@ -500,18 +545,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
                 phi[i] = (_Float16)p[i];
                 plo[i] = (_Float16)(p[i] - (float)phi[i]);
             }
+            wait_vmcnt<0>();    // this tile's value rows have landed
+            if (nv < 32) {      // zero the rows past the window's length (their p is 0, their contents arbitrary)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int idx = l + 64 * i;   // 16-byte chunk: row idx / 16
+                    if ((idx >> 4) >= nv) reinterpret_cast<uint4 *>(vres_lds)[idx] = uint4{0u, 0u, 0u, 0u};
+                }
+                wait_lgkmcnt0();
+            }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                h8 bv;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int tok = (e < 4) ? (4 * kc + e) : (16 + 4 * kc + e - 4);
-                    bv[e] = vres_lds[tok * 128 + n + 16 * j];
-                }
+                const h4 lo4 = read_tr16(vt0 + 16 * j);
+                const h4 hi4 = read_tr16(vt1 + 16 * j);
+                const h8 bv = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
                 o[j] = mfma(phi, bv, o[j]);
                 o[j] = mfma(plo, bv, o[j]);
             }
+            wait_lgkmcnt0();    // PV has read the value rows: the next tile may overwrite them
+            if (v + 1 < v1) v_dma(v + 1);
         }
+        wait_vmcnt<0>();
     }
 
     // ------------------------------------------------------------------ partials of this split

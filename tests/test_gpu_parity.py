@@ -211,3 +211,64 @@ def test_decode_is_deterministic(kvq):
     b = kvq.kv_decode_attention(cache, q)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+FP16_CASES = [
+    # (B, Hq, Hkv, N, window capacity, note)
+    (1, 1, 1, 1, 64, "one token"),
+    (2, 8, 2, 1000, 1024, "GQA G=4, ragged last tile"),
+    (1, 4, 4, 4096, 4096, "MHA, window full"),
+    (2, 16, 2, 2500, 2560, "G=8, two head chunks"),
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,cap,note", FP16_CASES)
+def test_decode_all_fp16_cache(kvq, B, Hq, Hkv, N, cap, note):
+    """A window as large as the context: nothing is quantized and the call is plain fp16 attention (the comparator
+    the 2-bit cache is measured against)."""
+    say(f"[decode-fp16] B={B} Hq={Hq} Hkv={Hkv} N={N} cap={cap} ({note})")
+    rng = np.random.default_rng(N + 31 * Hq)
+    k = _family(rng, "normal_outliers", (B, Hkv, N, 128))
+    v = rng.standard_normal((B, Hkv, N, 128)).astype(np.float16)
+    q = rng.standard_normal((B, Hq, 128)).astype(np.float16)
+    shape = kvq.Shape(B, Hkv, Hq, residual_cap=cap, max_tokens=cap)
+    cache = kvq.KVCache(shape)
+    kvq.kv_append_and_flush(cache, _dev(k), _dev(v))
+    assert (cache.n_quant, cache.n_resid) == (0, N)
+    out = kvq.kv_decode_attention(cache, _dev(q))
+    torch.cuda.synchronize()
+    ref = oc.SliceCache(B * Hkv, residual_cap=cap)
+    oc.append_block(ref, k.reshape(B * Hkv, N, 128), v.reshape(B * Hkv, N, 128))
+    assert (ref.n_quant, ref.n_resid) == (0, N)
+    want = helpers.oracle_out(ref, q, B, Hkv)
+    got = out.cpu().numpy().astype(np.float64)
+    err = np.abs(got - want)
+    say(f"    splits={kvq.kv_decode_attention_splits(cache)} max_abs={err.max():.3e}")
+    assert np.all(np.isfinite(got))
+    assert err.max() <= ATOL
+
+
+@pytest.mark.parametrize("N", [1000, 1101])
+def test_window_rows_past_length_are_ignored(kvq, N):
+    """Window rows past the cache's length hold arbitrary bytes (here NaN): the ragged last window tile must mask
+    them in the scores and in P V."""
+    say(f"[decode-window-nan] N={N}")
+    rng = np.random.default_rng(N)
+    B, Hq, Hkv = 2, 8, 2
+    k = _family(rng, "normal_outliers", (B, Hkv, N, 128))
+    v = rng.standard_normal((B, Hkv, N, 128)).astype(np.float16)
+    q = rng.standard_normal((B, Hq, 128)).astype(np.float16)
+    cache = kvq.KVCache(kvq.Shape(B, Hkv, Hq, max_tokens=1280))
+    cache.k_res.fill_(float("nan"))
+    cache.v_res.fill_(float("nan"))
+    kvq.kv_append_and_flush(cache, _dev(k), _dev(v))
+    assert cache.n_resid % 32 != 0
+    out = kvq.kv_decode_attention(cache, _dev(q))
+    torch.cuda.synchronize()
+    ref = oc.SliceCache(B * Hkv)
+    oc.append_block(ref, k.reshape(B * Hkv, N, 128), v.reshape(B * Hkv, N, 128))
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - helpers.oracle_out(ref, q, B, Hkv))
+    say(f"    n_resid={cache.n_resid} max_abs={err.max():.3e}")
+    assert err.max() <= ATOL
