@@ -278,6 +278,11 @@ __device__ __forceinline__ float row16_max(float v) {
     return dpp_xmax<DPP_ROW_MIRROR>(v);
 }
 
+// Cross-lane exchange through LDS inside one wavefront (every workgroup of the decode kernel is a single
+// wavefront). LDS operations are performed in one order per CU and complete in a wavefront's execution order, so a
+// read issued after a write sees it without draining the LDS counter first; only the compiler must not reorder them.
+__device__ __forceinline__ void wave_lds_order() { asm volatile("" : : : "memory"); }
+
 // One wavefront per (split, batch row, KV head, chunk of up to 4 query heads of that KV head); lane l = n + 16 kc.
 //
 // Scores. The query with the tile's key scales folded in, q~[h][c] = q'[h][c] s_K[c], is split into an fp16 high
@@ -385,7 +390,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     // 16 + 4kc + i (p[4 + i]) of head hl
     auto exchange = [&](float p0, float p1, float p[8]) {
         reinterpret_cast<float2 *>(p_lds)[16 * kc + n] = float2{p0, p1};
-        __syncthreads();
+        wave_lds_order();
         const f4 pa = reinterpret_cast<const f4 *>(p_lds)[(16 * hl + 4 * kc) / 2];
         const f4 pb = reinterpret_cast<const f4 *>(p_lds)[(16 * hl + 4 * kc) / 2 + 1];
         p[0] = pa[0]; p[4] = pa[1]; p[1] = pa[2]; p[5] = pa[3];
@@ -395,7 +400,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     // stage a tile's scales/zeros, its folded query (high, low) and beta into LDS
     auto stage = [&](const uint4 &sw) {
         reinterpret_cast<uint4 *>(sz_lds)[l] = sw;
-        __syncthreads();
+        wave_lds_order();
         const h8 sk = *reinterpret_cast<const h8 *>(szh + 8 * n);
         const h8 zk = *reinterpret_cast<const h8 *>(szh + 128 + 8 * n);
         const h8 hi = qf * sk;
@@ -408,7 +413,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
             bp = __builtin_amdgcn_fdot2(h2{zk[e], zk[e + 1]}, h2{qf[e], qf[e + 1]}, bp, false);
         bp = row16_sum(bp);    // beta of head kc, in every lane of row kc
         if (n == 0) beta_lds[kc] = bp;
-        __syncthreads();
+        wave_lds_order();
     };
 
     // ------------------------------------------------------------------ quantized tiles
