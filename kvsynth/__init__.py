@@ -111,6 +111,8 @@ class Workload:
     head_dim: int = 128
     group: int = 32
     residual: int = 128
+    sink: bool = False              # token 0's keys kept in fp16 (KVQuant variant)
+    rope_base: float | None = None  # keys cached before the rotary embedding, rotated at decode time
     notes: str = ""
     extra: dict = field(default_factory=dict)
 
@@ -128,4 +130,9 @@ WORKLOADS = {
     # One sequence of 1,048,576 tokens, 32 heads.
     "long_1m": Workload("long_1m", 1, 32, 32, 1048576, 1048575, 1, 1004, 4, 20.0,
                         notes="B1 H32 D128 N1048576, K outliers 4 ch x20"),
+    # KVQuant-style variant: 4-bit codes, keys cached before RoPE (base 10000), token 0's keys in fp16.
+    "kvquant_4bit_16k": Workload("kvquant_4bit_16k", 16, 32, 32, 16384, 16383, 1, 1005, 4, 20.0, bits=4,
+                                 sink=True, rope_base=10000.0,
+                                 notes="B16 H32 D128 N16384, 4-bit, pre-RoPE keys (base 10000), fp16 sink token 0, "
+                                       "K outliers 4 ch x20 (values plain N(0,1))"),
 }

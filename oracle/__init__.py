@@ -1,4 +1,4 @@
-"""CPU oracle for KIVI-style 2-bit KV-cache quantization and decode attention.
+"""CPU oracle for KIVI-style 2-bit (and KVQuant-style 4-bit) KV-cache quantization and decode attention.
 
 TEST INFRASTRUCTURE ONLY. Only the tests, the package smoke check and the benchmark's CPU-baseline leg may import
 this package. The product path (the HIP library and its Python binding) never imports, calls or links it, and the
@@ -20,5 +20,12 @@ Modules:
 - ``quant``: the asymmetric min/max group quantizer and its decoder.
 - ``layout``: the packed 3072-byte tile record the library stores, packed and unpacked independently here.
 - ``cache``: the grouped + residual cache state machine (append one token at a time, flush a full window).
-- ``attention``: attention over the decoded cache, chunked, plus the algebraic refold and split-K merge.
+- ``attention``: attention over the decoded cache, chunked, plus the algebraic refold and split-K merge; with the
+  KVQuant variant's sink token and rotary embedding of pre-RoPE keys.
+- ``layout4``: the 5120-byte 4-bit tile record and the per-slice sink record of the KVQuant variant.
+- ``rope``: the rotary embedding (adjacent channel pairs, theta_i = base ** (-2 i / D), absolute positions).
+
+KVQuant page (fdeinterviews.com, "KVQuant: Towards 10 Million Context Length LLM Inference with KV Cache
+Quantization"): keys quantized before RoPE and rotated after dequantization; the first token's keys kept in full
+precision; 4-bit codes.
 """

@@ -13,6 +13,10 @@ Readings taken where the pages are silent: sigma = 1/sqrt(head_dim) unless the c
 head hq uses KV head hq // G with G = Hq / Hkv (consecutive query heads share a KV head); the output is float64
 here and float32 in the library.
 
+KVQuant variant: with a sink, token 0 is the sink (its float16 key, its value decoded from per-token codes); with
+``rope_base`` set the cached keys are pre-RoPE and every decoded key is rotated by its absolute position before the
+dot product (see ``rope``): score_t = sigma * sum_c q_c (R(t) K_hat[t])_c.
+
 Long caches are processed in token chunks (two passes: the global maximum first, then the exponential sums), so
 a million-token slice never materializes in float64 all at once.
 """
@@ -20,31 +24,42 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import quant
+from . import quant, rope
 from .cache import SliceCache
 
 CHUNK = 65536
 
 
 def decoded_range(cache: SliceCache, t0: int, t1: int):
-    """Decoded keys and values of tokens ``[t0, t1)`` of every slice, float64 ``[S, t1 - t0, D]``."""
+    """Decoded keys and values of tokens ``[t0, t1)`` (absolute indices, the sink first) of every slice, float64
+    ``[S, t1 - t0, D]``."""
     g = cache.group
-    kq, ks, kz, vq, vs, vz = cache.quantized()
-    nq = cache.n_quant
+    ns = cache.n_sink
     S, D = cache.slices, cache.head_dim
     K = np.empty((S, t1 - t0, D), np.float64)
     V = np.empty((S, t1 - t0, D), np.float64)
-    a, b = t0, min(t1, nq)
+    if ns and t0 == 0 and t1 > 0:      # token 0 is the sink
+        vq, vs, vz = cache.v_sink
+        K[:, 0] = cache.k_sink.astype(np.float64)
+        V[:, 0] = quant.dequantize_values(vq[:, None], vs[:, None], vz[:, None], g)[:, 0]
+    a0, b0 = max(t0, ns), t1            # absolute range after the sink
+    if b0 <= a0:
+        return K, V
+    kq, ks, kz, vq, vs, vz = cache.quantized()
+    nq = cache.n_quant
+    a, b = a0 - ns, min(b0 - ns, nq)    # indices into the quantized part
+    off = a0 - t0
     if b > a:
-        # expand to whole key groups so the per-channel scale of each token is indexed by t // 32
+        # expand to whole key groups so the per-channel scale of each token is indexed by its group
         ga, gb = a // g, (b + g - 1) // g
         kh = quant.dequantize_keys(kq[:, ga * g:gb * g], ks[:, ga:gb], kz[:, ga:gb], g)
-        K[:, :b - a] = kh[:, a - ga * g:b - ga * g]
-        V[:, :b - a] = quant.dequantize_values(vq[:, a:b], vs[:, a:b], vz[:, a:b], g)
-    a2 = max(t0, nq)
-    if t1 > a2:
-        K[:, a2 - t0:] = cache.k_res[:, a2 - nq:t1 - nq].astype(np.float64)
-        V[:, a2 - t0:] = cache.v_res[:, a2 - nq:t1 - nq].astype(np.float64)
+        K[:, off:off + b - a] = kh[:, a - ga * g:b - ga * g]
+        V[:, off:off + b - a] = quant.dequantize_values(vq[:, a:b], vs[:, a:b], vz[:, a:b], g)
+    a2 = max(a0 - ns, nq)
+    if b0 - ns > a2:
+        o2 = a2 + ns - t0
+        K[:, o2:] = cache.k_res[:, a2 - nq:b0 - ns - nq].astype(np.float64)
+        V[:, o2:] = cache.v_res[:, a2 - nq:b0 - ns - nq].astype(np.float64)
     return K, V
 
 
@@ -56,11 +71,18 @@ def _q_for_slices(q: np.ndarray, batch: int, kv_heads: int) -> np.ndarray:
 
 
 def decode_attention(cache: SliceCache, q: np.ndarray, batch: int, kv_heads: int, sm_scale: float | None = None,
-                     chunk: int = CHUNK) -> np.ndarray:
+                     chunk: int = CHUNK, rope_base: float | None = None) -> np.ndarray:
     """Attention output float64 ``[B, Hq, D]`` of query ``q`` (float16 ``[B, Hq, D]``) over the whole cache.
 
-    Slice index of (b, hkv) is ``b * kv_heads + hkv``.
+    Slice index of (b, hkv) is ``b * kv_heads + hkv``. With ``rope_base`` the decoded keys are rotated by their
+    absolute positions (pre-RoPE key cache).
     """
+    def keys(t0, t1):
+        K, V = decoded_range(cache, t0, t1)
+        if rope_base is not None:
+            K = rope.rotate(K, np.arange(t0, t1), rope_base)
+        return K, V
+
     B, Hq, D = q.shape
     if cache.slices != batch * kv_heads or Hq % kv_heads:
         raise ValueError("cache slices must be batch * kv_heads and Hq a multiple of kv_heads")
@@ -73,14 +95,14 @@ def decode_attention(cache: SliceCache, q: np.ndarray, batch: int, kv_heads: int
     # pass 1: global maximum of the scores
     m = np.full((S, G), -np.inf)
     for t0 in range(0, N, chunk):
-        K, _ = decoded_range(cache, t0, min(N, t0 + chunk))
+        K, _ = keys(t0, min(N, t0 + chunk))
         sc = sigma * np.matmul(qs, np.swapaxes(K, 1, 2))
         m = np.maximum(m, sc.max(axis=-1))
     # pass 2: exponential sums and the weighted sum of values
     l = np.zeros((S, G))
     acc = np.zeros((S, G, D))
     for t0 in range(0, N, chunk):
-        K, V = decoded_range(cache, t0, min(N, t0 + chunk))
+        K, V = keys(t0, min(N, t0 + chunk))
         sc = sigma * np.matmul(qs, np.swapaxes(K, 1, 2))
         p = np.exp(sc - m[..., None])
         l += p.sum(axis=-1)

@@ -15,6 +15,11 @@ Readings taken where the pages are silent:
 - the flushed block is quantized with the same group quantizer as everywhere else.
 
 A ``SliceCache`` holds any number S of independent (batch row, KV head) slices that share their lengths.
+
+KVQuant variant (``sink=True``; KVQuant page, on the attention sink: the first token's keys stay in full
+precision). Reading taken (listed in the design notes): token 0 is held apart as the sink, its key in float16 and
+its value quantized per token like any other value; the grouped and residual parts start at token 1, so key
+groups cover tokens 1..32, 33..64, and so on, and the window logic above applies to the tokens after the sink.
 """
 from __future__ import annotations
 
@@ -43,6 +48,9 @@ class SliceCache:
     n_quant: int = 0
     k_res: np.ndarray = None
     v_res: np.ndarray = None
+    sink: bool = False
+    k_sink: np.ndarray = None          # float16 [S, D] once the sink holds token 0
+    v_sink: tuple = None               # (codes uint8 [S, D], scale float16 [S, D/32], zero float16 [S, D/32])
 
     def __post_init__(self):
         if self.residual_cap % self.group:
@@ -56,8 +64,18 @@ class SliceCache:
         return self.k_res.shape[1]
 
     @property
+    def n_sink(self) -> int:
+        return 0 if self.k_sink is None else 1
+
+    @property
     def n_tokens(self) -> int:
-        return self.n_quant + self.n_resid
+        return self.n_sink + self.n_quant + self.n_resid
+
+    def _take_sink(self, k_tok: np.ndarray, v_tok: np.ndarray):
+        """Token 0 of a sink cache: key kept as float16, value quantized per token."""
+        self.k_sink = np.asarray(k_tok, np.float16).copy()
+        vq, vs, vz = quant.quantize_values_per_token(np.asarray(v_tok, np.float16)[:, None, :], self.group, self.bits)
+        self.v_sink = (vq[:, 0], vs[:, 0], vz[:, 0])
 
     def quantized(self):
         """(k_codes [S,n_q,D], k_scale [S,n_q/32,D], k_zero, v_codes [S,n_q,D], v_scale [S,n_q,D/32], v_zero)."""
@@ -87,7 +105,11 @@ class SliceCache:
         self.v_res = self.v_res[:, :0]
 
     def append_token(self, k_tok: np.ndarray, v_tok: np.ndarray):
-        """One token per slice (float16 ``[S, D]``): flush a full window first, then store the token."""
+        """One token per slice (float16 ``[S, D]``): flush a full window first, then store the token (the first
+        token of a sink cache goes to the sink)."""
+        if self.sink and self.k_sink is None:
+            self._take_sink(k_tok, v_tok)
+            return
         if self.n_resid == self.residual_cap:
             self.flush()
         self.k_res = np.concatenate([self.k_res, np.asarray(k_tok, np.float16)[:, None, :]], axis=1)
@@ -120,6 +142,11 @@ def append_block(cache: SliceCache, k_new: np.ndarray, v_new: np.ndarray):
     t = k_new.shape[1]
     if t == 0:
         return
+    if cache.sink and cache.k_sink is None:
+        cache._take_sink(k_new[:, 0], v_new[:, 0])
+        k_new, v_new, t = k_new[:, 1:], v_new[:, 1:], t - 1
+        if t == 0:
+            return
     f = flushed_tokens(cache.n_resid, t, cache.residual_cap)
     k_all = np.concatenate([cache.k_res, np.asarray(k_new, np.float16)], axis=1)
     v_all = np.concatenate([cache.v_res, np.asarray(v_new, np.float16)], axis=1)

@@ -144,9 +144,10 @@ def test_workload_lengths():
         cases = json.load(f)["cases"]
     for case in cases:
         R = case["residual_cap"]
+        sink = case.get("sink", 0)        # the first `sink` tokens are held apart before the window logic
         nr, nq = 0, 0
         flush_steps = []
-        for i in range(case["prefill"]):
+        for i in range(case["prefill"] - sink):
             if nr == R:
                 nq, nr = nq + R, 0
             nr += 1
@@ -158,5 +159,5 @@ def test_workload_lengths():
             nr += 1
         assert [nq, nr] == case["final"], case["name"]
         assert flush_steps == case["flush_steps"], case["name"]
-        f = oc.flushed_tokens(0, case["prefill"] + case["steps"], R)
+        f = oc.flushed_tokens(0, case["prefill"] + case["steps"] - sink, R)
         assert f == case["final"][0]
