@@ -11,6 +11,9 @@ timed region starts. The default workload is the GQA decode at 32K context (batc
 Printed (one JSON line on stdout): KV tokens/s over the timed steps (value), the decode-attention call's achieved
 algorithmic HBM bandwidth against the 8 TB/s peak (roofline), and the CPU oracle timed on a sample of the same
 workload (cpu_baseline). Progress goes to stderr.
+
+`--workload kvquant_4bit_16k` measures the 4-bit KVQuant-style variant the same way (batch 16, 32 heads, 16K
+context, keys cached before RoPE and rotated at decode time, token 0 held as an fp16-key sink).
 """
 from __future__ import annotations
 
@@ -23,21 +26,30 @@ import sys
 import time
 
 METRIC = "2-bit KV decode attention: KV tokens/s and achieved HBM GB/s (% of peak)"
+METRIC_4BIT = "4-bit pre-RoPE KV decode attention with sink: KV tokens/s and achieved HBM GB/s (% of peak)"
 PEAK_GBS = 8000.0          # MI355X HBM3E
 ROOT = os.path.dirname(os.path.abspath(__file__))
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_pass1_traffic_llama3_8b_gqa_32k.json")
-KERNEL_SOURCE = os.path.join(ROOT, "decode_attention_quant_amd", "csrc", "kvq_kernels.hip")
+CSRC = os.path.join(ROOT, "decode_attention_quant_amd", "csrc")
+# per workload: the committed HBM byte-counter summary of its pass-1 kernel and that kernel's source file
+TRAFFIC = {
+    "llama3_8b_gqa_32k": (os.path.join(ROOT, "profiles", "decode_pass1_traffic_llama3_8b_gqa_32k.json"),
+                          os.path.join(CSRC, "kvq_kernels.hip")),
+    "kvquant_4bit_16k": (os.path.join(ROOT, "profiles", "decode_b4_pass1_traffic_kvquant_4bit_16k.json"),
+                         os.path.join(CSRC, "kvq_kernels_b4.hip")),
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(batch, kv_heads, q_heads, n_quant, n_resid, head_dim=128):
-    """Bytes one decode-attention call must move: per quantized token and KV head 96 B (32 B key codes, 32 B value
-    codes, 16 B key scale/zero, 16 B value scale/zero), per window token 512 B of fp16 K and V, the fp16 query
-    and the fp32 output."""
-    return (batch * kv_heads * (n_quant * 96 + n_resid * 2 * head_dim * 2)
+def algorithmic_bytes(batch, kv_heads, q_heads, n_quant, n_resid, head_dim=128, bits=2, n_sink=0):
+    """Bytes one decode-attention call must move: per quantized token and KV head 96 B at 2 bits (32 B key codes,
+    32 B value codes, 16 B key scale/zero, 16 B value scale/zero) or 160 B at 4 bits (64 + 64 + 16 + 16), per
+    window token 512 B of fp16 K and V, per sink token 336 B (fp16 key, value codes, value scale/zero), the fp16
+    query and the fp32 output. Each KV slice counts once, however many query heads read it."""
+    per_q = 96 if bits == 2 else 160
+    return (batch * kv_heads * (n_quant * per_q + n_resid * 2 * head_dim * 2 + n_sink * 336)
             + batch * q_heads * head_dim * 2 + batch * q_heads * head_dim * 4)
 
 
@@ -50,12 +62,15 @@ def lengths_after(n_quant, n_resid, appended, R):
     return n_quant, n_resid
 
 
-def traffic_per_launch():
+def traffic_per_launch(workload):
     """HBM bytes per decode pass-1 launch from the committed counter summary, if the kernel source still matches."""
+    if workload not in TRAFFIC:
+        return None
+    traffic_file, kernel_source = TRAFFIC[workload]
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(traffic_file) as f:
             rec = json.load(f)
-        with open(KERNEL_SOURCE, "rb") as f:
+        with open(kernel_source, "rb") as f:
             sha = hashlib.sha256(f.read()).hexdigest()
         if rec.get("kernel_source_sha256") == sha:
             return rec.get("traffic_bytes_per_launch")
@@ -86,14 +101,14 @@ def cpu_baseline(w, queries, n_slices, context):
     k = np.stack([kvsynth.slice_tokens(w.seed, kvsynth.K_ID, b, h, 0, context, w.head_dim, w.k_outliers,
                                        w.k_factor) for b, h in slices])
     v = np.stack([kvsynth.slice_tokens(w.seed, kvsynth.V_ID, b, h, 0, context, w.head_dim) for b, h in slices])
-    c = oc.SliceCache(len(slices), residual_cap=w.residual)
+    c = oc.SliceCache(len(slices), residual_cap=w.residual, bits=w.bits, sink=w.sink)
     oc.append_block(c, k, v)
     del k, v
     dt = 0.0
     for qs in queries:
         q = np.stack([qs[b, h * G:(h + 1) * G] for b, h in slices])       # [S, G, D]
         t = time.perf_counter()
-        oa.decode_attention(c, q, len(slices), 1)
+        oa.decode_attention(c, q, len(slices), 1, rope_base=w.rope_base)
         dt += time.perf_counter() - t
     kv_tokens = len(slices) / w.kv_heads * context * len(queries)
     return {"value": kv_tokens / dt, "unit": "KV tokens/s", "cores": int(blas_threads), "kind": "oracle",
@@ -177,7 +192,9 @@ def main(argv=None):
     W, K, R = args.warmup, args.steps, w.residual
     P = w.context - W - 1                      # first timed step attends over exactly w.context tokens
     total = P + W + K
-    shape = kvq.Shape(w.batch, w.kv_heads, w.q_heads, residual_cap=R, max_tokens=((total + 31) // 32) * 32)
+    flags = (kvq.FLAG_SINK if w.sink else 0) | (kvq.FLAG_PRE_ROPE if w.rope_base else 0)
+    shape = kvq.Shape(w.batch, w.kv_heads, w.q_heads, residual_cap=R, max_tokens=((total + 31) // 32) * 32,
+                      bits=w.bits, flags=flags, rope_base=w.rope_base or 0.0)
     cache = kvq.KVCache(shape)
     t0 = time.time()
     Kd = kdev.kv_to_device(w, kvsynth.K_ID, 0, total)
@@ -187,14 +204,14 @@ def main(argv=None):
         f"in {time.time() - t0:.1f}s")
     kvq.kv_append_and_flush(cache, Kd[:, :, :P], Vd[:, :, :P])
     torch.cuda.synchronize()
-    log(f"[bench] prefill {P} tokens: n_quant={cache.n_quant} n_resid={cache.n_resid}")
+    log(f"[bench] prefill {P} tokens: n_sink={cache.n_sink} n_quant={cache.n_quant} n_resid={cache.n_resid}")
 
     # workspace for the largest split count any step will use (host-side length simulation only)
     ws_bytes = 16
     nq, nr = cache.n_quant, cache.n_resid
     for i in range(W + K):
         nq, nr = lengths_after(nq, nr, 1, R)
-        probe = kvq.KvqCache(cache.c.tiles, cache.c.k_res, cache.c.v_res, nq, nr, 0)
+        probe = kvq.KvqCache(cache.c.tiles, cache.c.k_res, cache.c.v_res, nq, nr, cache.c.n_sink, cache.c.sink)
         ws_bytes = max(ws_bytes, int(kvq.library().kv_decode_attention_workspace_bytes(
             kvq.ctypes.byref(cache._cshape), kvq.ctypes.byref(probe))))
     workspace = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
@@ -222,7 +239,8 @@ def main(argv=None):
         n = cache.n_tokens
         contexts.append(n)
         kv_tokens += w.batch * n
-        call_bytes.append(algorithmic_bytes(w.batch, w.kv_heads, w.q_heads, cache.n_quant, cache.n_resid))
+        call_bytes.append(algorithmic_bytes(w.batch, w.kv_heads, w.q_heads, cache.n_quant, cache.n_resid,
+                                            bits=w.bits, n_sink=cache.n_sink))
     ev[3 * K + 1].record()
     torch.cuda.synchronize()
     total_ms = ev[0].elapsed_time(ev[3 * K + 1])
@@ -237,8 +255,15 @@ def main(argv=None):
         f"({achieved:.0f} GB/s); append avg {1e3 * sum(append_ms) / K:.1f} us, max {1e3 * max(append_ms):.1f} us; "
         f"splits={splits}")
 
+    if w.bits == 2:
+        detail = "2-bit codes expanded to fp16 MFMA operands (scales folded as fp16 hi+lo), fp32 accumulation"
+        kernel = "decode_pass1_kernel + decode_pass2_kernel (one kv_decode_attention call)"
+    else:
+        detail = ("4-bit codes: scores on the fp32 VALU (per-pair rotation by angle addition, binary32 cos/sin), "
+                  "P V on fp16 MFMA (probabilities as fp16 hi+lo), fp32 accumulation")
+        kernel = "decode_b4_pass1_kernel + decode_pass2_kernel (one kv_decode_attention call)"
     res = {
-        "metric": METRIC,
+        "metric": METRIC if w.bits == 2 else METRIC_4BIT,
         "value": value,
         "unit": "KV tokens/s",
         "n_gpus": 1,
@@ -252,7 +277,8 @@ def main(argv=None):
         "data": "synthetic",
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
                    "context_first_timed_step": contexts[0], "context_last_timed_step": contexts[-1],
-                   "bits": w.bits, "group": w.group, "residual": R, "head_dim": w.head_dim},
+                   "bits": w.bits, "group": w.group, "residual": R, "head_dim": w.head_dim,
+                   "sink": bool(w.sink), "rope_base": w.rope_base},
         "hbm_gb_s": achieved,
         "pct_of_peak": 100.0 * achieved / PEAK_GBS,
         "decode_call_us": 1e3 * sum(decode_ms) / K,
@@ -260,13 +286,12 @@ def main(argv=None):
         "append_us_max": 1e3 * max(append_ms),
         "splits": splits,
         "decode_call_us_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
-        "dtype_detail": "2-bit codes expanded to fp16 MFMA operands (scales folded as fp16 hi+lo), fp32 accumulation",
+        "dtype_detail": detail,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / PEAK_GBS, "traffic": traffic_per_launch(),
-                     "kernel": "decode_pass1_kernel + decode_pass2_kernel (one kv_decode_attention call)",
-                     "bytes_per_call": sum(call_bytes) / K},
+                     "frac": achieved / PEAK_GBS, "traffic": traffic_per_launch(w.name),
+                     "kernel": kernel, "bytes_per_call": sum(call_bytes) / K},
     }
-    if not args.no_fp16_comparator:
+    if not args.no_fp16_comparator and w.bits == 2:
         res["fp16_comparator"] = fp16_comparator(kvq, w, Kd, Vd, Q[W], contexts[0], res["decode_call_us"],
                                                  args.fp16_calls)
     if not args.no_cpu_baseline:

@@ -1,4 +1,5 @@
-"""Python binding of the 2-bit KV-cache library (``libkvq.so``, C ABI in ``include/kvq.h``).
+"""Python binding of the quantized KV-cache library (``libkvq.so``, C ABI in ``include/kvq.h``): 2-bit KIVI-style
+caches and the 4-bit KVQuant-style variant (optional pre-RoPE keys and attention-sink token).
 
 Argument marshalling only: every step of quantization, window management and attention runs in the library's HIP
 kernels. PyTorch provides device memory and the current HIP stream. The library must be built
@@ -21,17 +22,23 @@ HEAD_DIM = 128
 GROUP = 32
 TILE_TOKENS = 32
 RECORD_BYTES = 3072
+RECORD_BYTES_4BIT = 5120
+SINK_BYTES = 512
+FLAG_SINK = 1
+FLAG_PRE_ROPE = 2
 
 
 class KvqShape(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("q_heads", ctypes.c_int32),
                 ("head_dim", ctypes.c_int32), ("bits", ctypes.c_int32), ("group", ctypes.c_int32),
-                ("residual_cap", ctypes.c_int32), ("reserved", ctypes.c_int32), ("max_tokens", ctypes.c_int64)]
+                ("residual_cap", ctypes.c_int32), ("flags", ctypes.c_int32), ("max_tokens", ctypes.c_int64),
+                ("rope_base", ctypes.c_double)]
 
 
 class KvqCache(ctypes.Structure):
     _fields_ = [("tiles", ctypes.c_void_p), ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
-                ("n_quant", ctypes.c_int64), ("n_resid", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("n_quant", ctypes.c_int64), ("n_resid", ctypes.c_int32), ("n_sink", ctypes.c_int32),
+                ("sink", ctypes.c_void_p)]
 
 
 class KvqError(RuntimeError):
@@ -104,10 +111,16 @@ class Shape:
     bits: int = 2
     head_dim: int = HEAD_DIM
     group: int = GROUP
+    flags: int = 0              # FLAG_SINK | FLAG_PRE_ROPE (4-bit only)
+    rope_base: float = 0.0      # rotary base when FLAG_PRE_ROPE is set
+
+    @property
+    def record_bytes(self) -> int:
+        return RECORD_BYTES_4BIT if self.bits == 4 else RECORD_BYTES
 
     def c(self) -> KvqShape:
         return KvqShape(self.batch, self.kv_heads, self.q_heads, self.head_dim, self.bits, self.group,
-                        self.residual_cap, 0, self.max_tokens)
+                        self.residual_cap, self.flags, self.max_tokens, float(self.rope_base))
 
 
 class KVCache:
@@ -117,11 +130,16 @@ class KVCache:
         self.shape = shape
         self._cshape = shape.c()
         tiles = shape.max_tokens // TILE_TOKENS
-        self.tiles = torch.zeros((shape.batch, shape.kv_heads, tiles, RECORD_BYTES), dtype=torch.uint8, device=device)
+        self.tiles = torch.zeros((shape.batch, shape.kv_heads, tiles, shape.record_bytes), dtype=torch.uint8,
+                                 device=device)
         self.k_res = torch.zeros((shape.batch, shape.kv_heads, shape.residual_cap, HEAD_DIM), dtype=torch.float16,
                                  device=device)
         self.v_res = torch.zeros_like(self.k_res)
-        self.c = KvqCache(self.tiles.data_ptr(), self.k_res.data_ptr(), self.v_res.data_ptr(), 0, 0, 0)
+        self.sink = None
+        if shape.flags & FLAG_SINK:
+            self.sink = torch.zeros((shape.batch, shape.kv_heads, SINK_BYTES), dtype=torch.uint8, device=device)
+        self.c = KvqCache(self.tiles.data_ptr(), self.k_res.data_ptr(), self.v_res.data_ptr(), 0, 0, 0,
+                          self.sink.data_ptr() if self.sink is not None else None)
 
     @property
     def n_quant(self) -> int:
@@ -132,8 +150,12 @@ class KVCache:
         return int(self.c.n_resid)
 
     @property
+    def n_sink(self) -> int:
+        return int(self.c.n_sink)
+
+    @property
     def n_tokens(self) -> int:
-        return self.n_quant + self.n_resid
+        return self.n_sink + self.n_quant + self.n_resid
 
 
 def kv_quant_keys_per_channel(shape: Shape, k: torch.Tensor, tile0: int, tiles: torch.Tensor, stream=None):

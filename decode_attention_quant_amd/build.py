@@ -9,7 +9,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvq.so")
-SOURCES = ["kvq_kernels.hip", "kvq_api.hip"]
+SOURCES = ["kvq_kernels.hip", "kvq_kernels_b4.hip", "kvq_api.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -22,8 +22,9 @@ HIPCC_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     # correctly rounded fp32 division (the quantizer depends on it)
     "-fhip-fp32-correctly-rounded-divide-sqrt",
-    # no IEEE-mode NaN quieting: inputs are finite by contract, and min/max then need no canonicalization
-    "-mno-amdgpu-ieee", "-fno-honor-nans",
+    # device code only: no IEEE-mode NaN quieting (inputs are finite by contract, and min/max then need no
+    # canonicalization); host validation keeps full NaN semantics
+    "-mno-amdgpu-ieee", "-Xarch_device", "-fno-honor-nans",
     "-Wno-unused-command-line-argument",
 ]
 

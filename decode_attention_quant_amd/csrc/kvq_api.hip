@@ -1,40 +1,63 @@
 // C-ABI entry points declared in include/kvq.h: host-side validation, the residual-window state machine and the
-// split-K sizing; every step of the computation runs in the kernels of kvq_kernels.hip.
+// split-K sizing; every step of the computation runs in the kernels of kvq_kernels.hip (2-bit) and
+// kvq_kernels_b4.hip (4-bit).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
+#include <string.h>
 
 #include "kvq.h"
 #include "kvq_kernels.h"
 
 namespace {
 
-// One wavefront per resident slot: the decode kernel holds four wavefronts per SIMD (its register budget), so
-// 256 CUs x 4 SIMDs x 4 = 4096 wavefronts run as a single round with no tail of partly filled rounds.
+// One wavefront per resident slot: the 2-bit decode kernel holds four wavefronts per SIMD (its register budget), so
+// 256 CUs x 4 SIMDs x 4 = 4096 wavefronts run as a single round with no tail of partly filled rounds. The 4-bit
+// kernel keeps its rotation tables in registers and holds two per SIMD.
 constexpr int64_t kTargetWaves = 4096;
+constexpr int64_t kTargetWavesB4 = 2048;
 constexpr int64_t kMinTilesPerSplit = 4;
 constexpr int64_t kMaxSplits = 1024;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// decided on the bit pattern, so that it holds whatever floating-point assumptions the compiler is given
+bool finite_above_one(double x) {
+    uint64_t u;
+    memcpy(&u, &x, sizeof u);
+    if (((u >> 52) & 0x7ff) == 0x7ff) return false;   // infinity or NaN
+    return x > 1.0;
+}
+
 int check_shape(const kvq_shape *s) {
     if (!s) return KVQ_E_NULL;
-    if (s->bits != 2) return KVQ_E_BITS;
+    if (s->bits != 2 && s->bits != 4) return KVQ_E_BITS;
     if (s->batch <= 0 || s->kv_heads <= 0 || s->q_heads <= 0 || s->head_dim != KVQ_HEAD_DIM ||
         s->group != KVQ_GROUP || s->q_heads % s->kv_heads != 0 || s->residual_cap <= 0 ||
-        s->residual_cap % KVQ_TILE_TOKENS != 0 || s->reserved != 0 || s->max_tokens <= 0 ||
-        s->max_tokens % KVQ_TILE_TOKENS != 0 || s->batch > 65535 || s->kv_heads > 65535)
+        s->residual_cap % KVQ_TILE_TOKENS != 0 || s->max_tokens <= 0 || s->max_tokens % KVQ_TILE_TOKENS != 0 ||
+        s->batch > 65535 || s->kv_heads > 65535 || (int64_t)s->batch * s->q_heads > 0x7fffffff)
         return KVQ_E_SHAPE;
+    if ((s->flags & ~(KVQ_FLAG_SINK | KVQ_FLAG_PRE_ROPE)) != 0 || (s->flags != 0 && s->bits != 4))
+        return KVQ_E_SHAPE;
+    if ((s->flags & KVQ_FLAG_PRE_ROPE) && !finite_above_one(s->rope_base)) return KVQ_E_SHAPE;
     return KVQ_OK;
 }
+
+bool has_sink(const kvq_shape *s) { return (s->flags & KVQ_FLAG_SINK) != 0; }
 
 int check_cache(const kvq_shape *s, const kvq_cache *c) {
     if (!c) return KVQ_E_NULL;
     if (!c->tiles || !c->k_res || !c->v_res) return KVQ_E_NULL;
+    if (has_sink(s) && !c->sink) return KVQ_E_NULL;
     if (!aligned16(c->tiles) || !aligned16(c->k_res) || !aligned16(c->v_res)) return KVQ_E_ALIGN;
-    if (c->reserved != 0 || c->n_quant < 0 || c->n_quant % KVQ_TILE_TOKENS != 0 || c->n_quant > s->max_tokens ||
-        c->n_resid < 0 || c->n_resid > s->residual_cap)
+    if (has_sink(s) && !aligned16(c->sink)) return KVQ_E_ALIGN;
+    if (c->n_quant < 0 || c->n_quant % KVQ_TILE_TOKENS != 0 || c->n_quant > s->max_tokens || c->n_resid < 0 ||
+        c->n_resid > s->residual_cap)
         return KVQ_E_STATE;
+    if (c->n_sink != 0 && c->n_sink != 1) return KVQ_E_STATE;
+    if (!has_sink(s) && c->n_sink != 0) return KVQ_E_STATE;
+    // with a sink, token 0 always goes to the sink first
+    if (has_sink(s) && c->n_sink == 0 && (c->n_quant != 0 || c->n_resid != 0)) return KVQ_E_STATE;
     return KVQ_OK;
 }
 
@@ -56,6 +79,16 @@ kvq::TokSrc single_src(const void *p, int64_t sb, int64_t sh, int64_t st) {
     return s;
 }
 
+hipError_t quant_launch(const kvq_shape *shape, bool keys, const kvq::TokSrc &src, int64_t nt, uint8_t *tiles,
+                        int64_t max_tiles, int64_t tile0, hipStream_t st) {
+    const int B = shape->batch, H = shape->kv_heads;
+    if (shape->bits == 4)
+        return keys ? kvq::launch_quant_keys_b4(src, 0, nt, B, H, tiles, max_tiles, tile0, st)
+                    : kvq::launch_quant_values_b4(src, 0, nt, B, H, tiles, max_tiles, tile0, st);
+    return keys ? kvq::launch_quant_keys(src, 0, nt, B, H, tiles, max_tiles, tile0, st)
+                : kvq::launch_quant_values(src, 0, nt, B, H, tiles, max_tiles, tile0, st);
+}
+
 int quant_common(const kvq_shape *shape, const void *x, int64_t sb, int64_t sh, int64_t st, int64_t n_tokens,
                  int64_t tile0, void *tiles, bool keys, void *stream) {
     int e = check_shape(shape);
@@ -70,8 +103,7 @@ int quant_common(const kvq_shape *shape, const void *x, int64_t sb, int64_t sh, 
     hipStream_t s = static_cast<hipStream_t>(stream);
     uint8_t *t = static_cast<uint8_t *>(tiles);
     const int64_t nt = n_tokens / KVQ_TILE_TOKENS;
-    return launched(keys ? kvq::launch_quant_keys(src, 0, nt, shape->batch, shape->kv_heads, t, max_tiles, tile0, s)
-                         : kvq::launch_quant_values(src, 0, nt, shape->batch, shape->kv_heads, t, max_tiles, tile0, s));
+    return launched(quant_launch(shape, keys, src, nt, t, max_tiles, tile0, s));
 }
 
 struct SplitPlan {
@@ -81,13 +113,17 @@ struct SplitPlan {
     int32_t chunks;
 };
 
+// Splits along the virtual tiles (quantized, then window). A work unit is one wavefront's (batch row, KV head,
+// chunk of 4 query heads) in the 2-bit kernel and one (batch row, query head) in the 4-bit kernel; the sink token,
+// when present, is taken by split 0 on top of its tiles.
 SplitPlan plan(const kvq_shape *s, const kvq_cache *c) {
     SplitPlan p;
     p.n_vt = c->n_quant / KVQ_TILE_TOKENS + (c->n_resid + KVQ_TILE_TOKENS - 1) / KVQ_TILE_TOKENS;
     const int G = s->q_heads / s->kv_heads;
     p.chunks = (G + 3) / 4;
-    const int64_t units = (int64_t)s->batch * s->kv_heads * p.chunks;
-    int64_t S = (kTargetWaves + units - 1) / units;
+    const int64_t units = s->bits == 4 ? (int64_t)s->batch * s->q_heads : (int64_t)s->batch * s->kv_heads * p.chunks;
+    const int64_t target = s->bits == 4 ? kTargetWavesB4 : kTargetWaves;
+    int64_t S = (target + units - 1) / units;
     const int64_t by_len = (p.n_vt + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
     if (S > by_len) S = by_len;
     if (S > kMaxSplits) S = kMaxSplits;
@@ -95,7 +131,7 @@ SplitPlan plan(const kvq_shape *s, const kvq_cache *c) {
     int64_t tps = (p.n_vt + S - 1) / S;
     if (tps < 1) tps = 1;
     S = (p.n_vt + tps - 1) / tps;
-    if (S < 1) S = 1;
+    if (S < 1) S = 1;   // also a cache that holds only the sink token: one split, no tiles
     p.splits = (int32_t)S;
     p.tiles_per_split = (int32_t)tps;
     return p;
@@ -139,18 +175,28 @@ int kv_append_and_flush(const kvq_shape *shape, kvq_cache *cache, const void *k_
     if ((e = check_src(k_new, stride_b, stride_h, stride_t))) return e;
     if ((e = check_src(v_new, stride_b, stride_h, stride_t))) return e;
     if (n_tokens <= 0) return KVQ_E_SHAPE;
+    // with a sink, the first token of an empty cache becomes the sink; the rest follows the window rule
+    const int64_t take_sink = (has_sink(shape) && cache->n_sink == 0) ? 1 : 0;
+    const int64_t n_rest = n_tokens - take_sink;
     const int64_t R = shape->residual_cap;
     const int64_t nr0 = cache->n_resid;
-    const int64_t flushed = R * ((nr0 + n_tokens - 1) / R);
+    const int64_t flushed = n_rest > 0 ? R * ((nr0 + n_rest - 1) / R) : 0;
     if (cache->n_quant + flushed > shape->max_tokens) return KVQ_E_CAPACITY;
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     const int B = shape->batch, H = shape->kv_heads;
+    kvq::TokSrc knew = single_src(k_new, stride_b, stride_h, stride_t);
+    kvq::TokSrc vnew = single_src(v_new, stride_b, stride_h, stride_t);
+    if (take_sink) {
+        if ((e = launched(kvq::launch_sink_b4(knew, vnew, B, H, static_cast<uint8_t *>(cache->sink), s)))) return e;
+        cache->n_sink = 1;
+        if (n_rest == 0) return KVQ_OK;
+        knew = single_src(static_cast<const _Float16 *>(k_new) + stride_t, stride_b, stride_h, stride_t);
+        vnew = single_src(static_cast<const _Float16 *>(v_new) + stride_t, stride_b, stride_h, stride_t);
+    }
     const int64_t max_tiles = shape->max_tokens / KVQ_TILE_TOKENS;
     _Float16 *kres = static_cast<_Float16 *>(cache->k_res);
     _Float16 *vres = static_cast<_Float16 *>(cache->v_res);
-    const kvq::TokSrc knew = single_src(k_new, stride_b, stride_h, stride_t);
-    const kvq::TokSrc vnew = single_src(v_new, stride_b, stride_h, stride_t);
     int64_t copy_from, dst0;
     if (flushed > 0) {
         // the flushed tokens: the whole window, then the first flushed - nr0 new tokens
@@ -162,15 +208,15 @@ int kv_append_and_flush(const kvq_shape *shape, kvq_cache *cache, const void *k_
         ksrc.n_a = vsrc.n_a = nr0;
         uint8_t *tiles = static_cast<uint8_t *>(cache->tiles);
         const int64_t tile0 = cache->n_quant / KVQ_TILE_TOKENS, nt = flushed / KVQ_TILE_TOKENS;
-        if ((e = launched(kvq::launch_quant_keys(ksrc, 0, nt, B, H, tiles, max_tiles, tile0, s)))) return e;
-        if ((e = launched(kvq::launch_quant_values(vsrc, 0, nt, B, H, tiles, max_tiles, tile0, s)))) return e;
+        if ((e = launched(quant_launch(shape, true, ksrc, nt, tiles, max_tiles, tile0, s)))) return e;
+        if ((e = launched(quant_launch(shape, false, vsrc, nt, tiles, max_tiles, tile0, s)))) return e;
         copy_from = flushed - nr0;
         dst0 = 0;
     } else {
         copy_from = 0;
         dst0 = nr0;
     }
-    const int64_t n_copy = n_tokens - copy_from;
+    const int64_t n_copy = n_rest - copy_from;
     if ((e = launched(kvq::launch_copy_rows(knew, copy_from, n_copy, B, H, kres, (int)R, (int)dst0, s)))) return e;
     if ((e = launched(kvq::launch_copy_rows(vnew, copy_from, n_copy, B, H, vres, (int)R, (int)dst0, s)))) return e;
     cache->n_quant += flushed;
@@ -181,7 +227,7 @@ int kv_append_and_flush(const kvq_shape *shape, kvq_cache *cache, const void *k_
 int32_t kv_decode_attention_splits(const kvq_shape *shape, const kvq_cache *cache) {
     if (check_shape(shape) || check_cache(shape, cache)) return 0;
     const SplitPlan p = plan(shape, cache);
-    return p.n_vt > 0 ? p.splits : 0;
+    return (p.n_vt > 0 || cache->n_sink > 0) ? p.splits : 0;
 }
 
 size_t kv_decode_attention_workspace_bytes(const kvq_shape *shape, const kvq_cache *cache) {
@@ -198,19 +244,46 @@ int kv_decode_attention(const kvq_shape *shape, const kvq_cache *cache, const vo
     if (!q || !out) return KVQ_E_NULL;
     if (!aligned16(q) || !aligned16(out)) return KVQ_E_ALIGN;
     const SplitPlan p = plan(shape, cache);
-    if (p.n_vt == 0) return KVQ_E_EMPTY;
+    if (p.n_vt == 0 && cache->n_sink == 0) return KVQ_E_EMPTY;
     const size_t need = (size_t)shape->batch * shape->q_heads * p.splits * (KVQ_HEAD_DIM + 2) * sizeof(float);
     if (!workspace || workspace_bytes < need) return KVQ_E_WORKSPACE;
     if (!aligned16(workspace)) return KVQ_E_ALIGN;
     if (!(sm_scale > 0.0f)) sm_scale = 1.0f / sqrtf((float)KVQ_HEAD_DIM);
+    float *part_o = static_cast<float *>(workspace);
+    float *part_ml = part_o + (size_t)shape->batch * shape->q_heads * p.splits * KVQ_HEAD_DIM;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+
+    if (shape->bits == 4) {
+        kvq::DecodeB4Args a;
+        a.tiles = static_cast<const uint8_t *>(cache->tiles);
+        a.sink = static_cast<const uint8_t *>(cache->sink);
+        a.k_res = static_cast<const _Float16 *>(cache->k_res);
+        a.v_res = static_cast<const _Float16 *>(cache->v_res);
+        a.q = static_cast<const _Float16 *>(q);
+        a.part_o = part_o;
+        a.part_ml = part_ml;
+        a.max_tiles = shape->max_tokens / KVQ_TILE_TOKENS;
+        a.n_sink = cache->n_sink;
+        a.n_qtiles = (int)(cache->n_quant / KVQ_TILE_TOKENS);
+        a.n_resid = cache->n_resid;
+        a.res_cap = shape->residual_cap;
+        a.batch = shape->batch;
+        a.kv_heads = shape->kv_heads;
+        a.q_heads = shape->q_heads;
+        a.tiles_per_split = p.tiles_per_split;
+        a.sm_log2 = sm_scale * 1.4426950408889634f;
+        a.rope = (shape->flags & KVQ_FLAG_PRE_ROPE) ? 1 : 0;
+        a.log2_base = a.rope ? log2(shape->rope_base) : 0.0;
+        return launched(kvq::launch_decode_b4(a, out, p.splits, st));
+    }
 
     kvq::DecodeArgs a;
     a.tiles = static_cast<const uint8_t *>(cache->tiles);
     a.k_res = static_cast<const _Float16 *>(cache->k_res);
     a.v_res = static_cast<const _Float16 *>(cache->v_res);
     a.q = static_cast<const _Float16 *>(q);
-    a.part_o = static_cast<float *>(workspace);
-    a.part_ml = a.part_o + (size_t)shape->batch * shape->q_heads * p.splits * KVQ_HEAD_DIM;
+    a.part_o = part_o;
+    a.part_ml = part_ml;
     a.out = out;
     a.max_tiles = shape->max_tokens / KVQ_TILE_TOKENS;
     a.n_qtiles = (int)(cache->n_quant / KVQ_TILE_TOKENS);
@@ -222,7 +295,7 @@ int kv_decode_attention(const kvq_shape *shape, const kvq_cache *cache, const vo
     a.chunks = p.chunks;
     a.tiles_per_split = p.tiles_per_split;
     a.sm_log2 = sm_scale * 1.4426950408889634f;
-    return launched(kvq::launch_decode(a, p.splits, static_cast<hipStream_t>(stream)));
+    return launched(kvq::launch_decode(a, p.splits, st));
 }
 
 }  // extern "C"

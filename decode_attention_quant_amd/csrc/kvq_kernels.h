@@ -36,6 +36,39 @@ struct DecodeArgs {
     float sm_log2;        // softmax scale * log2(e)
 };
 
+// 4-bit (KVQuant-style) decode: one wavefront per (batch row, query head, token split). Virtual tiles v of a
+// slice: [0, n_sink) the sink token (position 0), then n_qtiles quantized tiles, then the window tiles.
+struct DecodeB4Args {
+    const uint8_t *tiles;   // [B][Hkv][max_tiles][5120]
+    const uint8_t *sink;    // [B][Hkv][512] (read only when n_sink = 1)
+    const _Float16 *k_res;
+    const _Float16 *v_res;
+    const _Float16 *q;
+    float *part_o;          // [B][Hq][splits][128]
+    float *part_ml;         // [B][Hq][splits][2]
+    int64_t max_tiles;
+    int n_sink;
+    int n_qtiles;
+    int n_resid;
+    int res_cap;
+    int batch;
+    int kv_heads;
+    int q_heads;
+    int tiles_per_split;
+    float sm_log2;
+    int rope;               // keys are cached before RoPE: rotate by the absolute position
+    double log2_base;       // log2 of the RoPE base
+};
+
+hipError_t launch_quant_keys_b4(const TokSrc &src, int64_t t_begin, int64_t n_tiles, int batch, int kv_heads,
+                                uint8_t *tiles, int64_t max_tiles, int64_t tile0, hipStream_t st);
+hipError_t launch_quant_values_b4(const TokSrc &src, int64_t t_begin, int64_t n_tiles, int batch, int kv_heads,
+                                  uint8_t *tiles, int64_t max_tiles, int64_t tile0, hipStream_t st);
+hipError_t launch_sink_b4(const TokSrc &ksrc, const TokSrc &vsrc, int batch, int kv_heads, uint8_t *sink,
+                          hipStream_t st);
+hipError_t launch_decode_b4(const DecodeB4Args &a, float *out, int splits, hipStream_t st);
+hipError_t launch_pass2(const float *part_o, const float *part_ml, float *out, int rows, int splits, hipStream_t st);
+
 hipError_t launch_quant_keys(const TokSrc &src, int64_t t_begin, int64_t n_tiles, int batch, int kv_heads,
                              uint8_t *tiles, int64_t max_tiles, int64_t tile0, hipStream_t st);
 hipError_t launch_quant_values(const TokSrc &src, int64_t t_begin, int64_t n_tiles, int batch, int kv_heads,

@@ -9,6 +9,8 @@
 #include <stdint.h>
 
 #include "kvq_kernels.h"
+#include "kvq_quantizer.h"
+#include "kvq_lanes.h"
 
 namespace kvq {
 
@@ -19,41 +21,6 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;
 constexpr int REC = 3072;
-
-// ------------------------------------------------------------------------------------------------ token sources
-__device__ __forceinline__ const _Float16 *tok_row(const TokSrc &s, int b, int h, int64_t t) {
-    if (t < s.n_a) return s.a + b * s.a_sb + h * s.a_sh + t * s.a_st;
-    t -= s.n_a;
-    return s.b + b * s.b_sb + h * s.b_sh + t * s.b_st;
-}
-
-// ------------------------------------------------------------------------------------------------ group quantizer
-// Asymmetric min/max quantizer with binary16 scale/zero (see kvq.h for the exact rule). Contraction is switched
-// off so every binary32 operation rounds on its own.
-__device__ __forceinline__ void group_params(float mn, float mx, float levels, _Float16 &s_out, _Float16 &z_out) {
-#pragma clang fp contract(off)
-    float r = mx - mn;
-    float s32 = r / levels;
-    _Float16 s = (_Float16)s32;
-    if ((levels + 0.5f) * (float)s < r) {
-        uint16_t bits = __builtin_bit_cast(uint16_t, s);
-        s = __builtin_bit_cast(_Float16, (uint16_t)(bits + 1));
-    }
-    _Float16 z = (_Float16)mn;
-    if (mn == 0.0f) z = (_Float16)0.0f;
-    s_out = s;
-    z_out = z;
-}
-
-__device__ __forceinline__ uint32_t code_of(float x, float z, float s, float levels) {
-#pragma clang fp contract(off)
-    if (s == 0.0f) return 0u;
-    float d = x - z;
-    float t = d / s;
-    float q = __builtin_rintf(t);
-    q = fminf(fmaxf(q, 0.0f), levels);
-    return (uint32_t)q;
-}
 
 // Keys: one workgroup of 64 lanes per tile; lane l owns channels 2l and 2l+1 over the tile's 32 tokens.
 __global__ __launch_bounds__(64) void quant_keys_kernel(TokSrc src, int64_t t_begin, int kv_heads, uint8_t *tiles,
@@ -190,39 +157,6 @@ __device__ __forceinline__ void split_pair(float pa, float pb, uint32_t s, uint3
         : "v"(pa), "v"(pb), "v"(s));
 }
 
-// Cross-row reductions over the four 16-lane rows of a wavefront with the gfx950 row swaps. Two compiler traps
-// are avoided here: the second operand goes through an empty asm statement (a swap whose operands the compiler
-// can prove equal is folded into the identity), and the result pair is copied into named integers before use
-// (reading element 1 of the pair through a bit cast was lowered as element 0).
-__device__ __forceinline__ uint32_t opaque(uint32_t v) {
-    asm volatile("" : "+v"(v));
-    return v;
-}
-__device__ __forceinline__ void swap16(uint32_t u, uint32_t &a, uint32_t &b) {
-    auto p = __builtin_amdgcn_permlane16_swap(u, opaque(u), false, false);   // rows (0,1) and (2,3)
-    a = p[0];
-    b = p[1];
-}
-__device__ __forceinline__ void swap32(uint32_t u, uint32_t &a, uint32_t &b) {
-    auto p = __builtin_amdgcn_permlane32_swap(u, opaque(u), false, false);   // halves (0,1) and (2,3)
-    a = p[0];
-    b = p[1];
-}
-__device__ __forceinline__ float rows_max(float v) {
-    uint32_t a, b;
-    swap16(__builtin_bit_cast(uint32_t, v), a, b);
-    v = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
-    swap32(__builtin_bit_cast(uint32_t, v), a, b);
-    return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
-}
-__device__ __forceinline__ float rows_sum(float v) {
-    uint32_t a, b;
-    swap16(__builtin_bit_cast(uint32_t, v), a, b);
-    v = __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
-    swap32(__builtin_bit_cast(uint32_t, v), a, b);
-    return __builtin_bit_cast(float, a) + __builtin_bit_cast(float, b);
-}
-
 // LDS-DMA load: 16 bytes per lane from `src` into LDS at lds_base + 16 * lane (lds_base goes through M0, which
 // the statement saves and restores). Issued from inline asm so that the compiler's wait insertion, which cannot tell
 // the destination from the other LDS buffers, does not drain the vector-memory counter before every LDS access; the
@@ -247,41 +181,6 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 __device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
-
-// Sum over the 16 lanes of each row with DPP lane permutations (every lane of the row ends with the same value:
-// each step adds a lane and its mirror, an exchange that gives both the same rounded sum).
-template <int CTRL>
-__device__ __forceinline__ float dpp_xadd(float v) {
-    const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
-    return v + __builtin_bit_cast(float, s);
-}
-constexpr int DPP_QUAD_1032 = 0xB1;      // quad_perm [1, 0, 3, 2]: lane pairs (0,1), (2,3)
-constexpr int DPP_QUAD_2301 = 0x4E;      // quad_perm [2, 3, 0, 1]
-constexpr int DPP_ROW_HALF_MIRROR = 0x141;
-constexpr int DPP_ROW_MIRROR = 0x140;
-__device__ __forceinline__ float row16_sum(float v) {
-    v = dpp_xadd<DPP_QUAD_1032>(v);
-    v = dpp_xadd<DPP_QUAD_2301>(v);
-    v = dpp_xadd<DPP_ROW_HALF_MIRROR>(v);
-    return dpp_xadd<DPP_ROW_MIRROR>(v);
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_xmax(float v) {
-    const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
-    return fmaxf(v, __builtin_bit_cast(float, s));
-}
-__device__ __forceinline__ float row16_max(float v) {
-    v = dpp_xmax<DPP_QUAD_1032>(v);
-    v = dpp_xmax<DPP_QUAD_2301>(v);
-    v = dpp_xmax<DPP_ROW_HALF_MIRROR>(v);
-    return dpp_xmax<DPP_ROW_MIRROR>(v);
-}
-
-// Cross-lane exchange through LDS inside one wavefront (every workgroup of the decode kernel is a single
-// wavefront). LDS operations are performed in one order per CU and complete in a wavefront's execution order, so a
-// read issued after a write sees it without draining the LDS counter first; only the compiler must not reorder them.
-__device__ __forceinline__ void wave_lds_order() { asm volatile("" : : : "memory"); }
 
 // One wavefront per (split, batch row, KV head, chunk of up to 4 query heads of that KV head); lane l = n + 16 kc.
 //
@@ -633,6 +532,11 @@ hipError_t launch_copy_rows(const TokSrc &src, int64_t t_begin, int64_t n, int b
                             int res_cap, int dst0, hipStream_t st) {
     dim3 grid((unsigned)((n + 3) / 4), (unsigned)kv_heads, (unsigned)batch);
     hipLaunchKernelGGL(copy_rows_kernel, grid, dim3(64), 0, st, src, t_begin, n, kv_heads, res, res_cap, dst0);
+    return hipGetLastError();
+}
+
+hipError_t launch_pass2(const float *part_o, const float *part_ml, float *out, int rows, int splits, hipStream_t st) {
+    hipLaunchKernelGGL(decode_pass2_kernel, dim3((unsigned)rows), dim3(64), 0, st, part_o, part_ml, out, splits);
     return hipGetLastError();
 }
 

@@ -1,0 +1,525 @@
+// HIP kernels for gfx950 (CDNA4): the 4-bit KVQuant-style variant of the cache. Keys are quantized per channel and
+// values per token with 4-bit codes in 5120-byte tile records; keys may be cached before the rotary embedding and are
+// then rotated at decode time by their absolute position; token 0 may be held apart as an attention sink whose key
+// stays in fp16. Decode pass 2 (the split merge) is shared with the 2-bit path.
+//
+// Sources: KVQuant page (fdeinterviews.com, "KVQuant: Towards 10 Million Context Length LLM Inference with KV Cache
+// Quantization"): per-channel keys, per-token values, keys quantized before RoPE with the rotation applied after
+// dequantization, and the first token's keys kept in full precision (attention sink); RoFormer form of the rotary
+// embedding for the pair layout (adjacent channels 2i, 2i+1, angle m * base^(-2i/D)).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq_kernels.h"
+#include "kvq_lanes.h"
+#include "kvq_quantizer.h"
+
+namespace kvq {
+
+namespace {
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr int HD = 128;
+constexpr int REC4 = 5120;
+constexpr int K4_SCALE = 4096, K4_ZERO = 4352;
+constexpr int V4_CODES = 2048, V4_SCALE = 4608, V4_ZERO = 4864;
+constexpr int SINK_REC = 512;
+constexpr float L4 = 15.0f;   // highest 4-bit level
+
+}  // namespace
+
+// ------------------------------------------------------------------------------------------------ quantizers
+// Keys: one workgroup of 64 lanes per tile; lane l owns channels 2l, 2l+1 over the tile's 32 tokens. Key code of
+// token t, channel c sits in word 8 (c/8 + 16 (t/8)) + t%8 at bit 4 (c%8): the two channels of lane l fill byte
+// l%4 of that word, so every byte of the 2 KB code region is written exactly once, by a byte store into LDS.
+__global__ __launch_bounds__(64) void quant_keys_b4_kernel(TokSrc src, int64_t t_begin, int kv_heads, uint8_t *tiles,
+                                                           int64_t max_tiles, int64_t tile0) {
+    __shared__ __align__(16) uint32_t words[512];
+    uint8_t *bytes = reinterpret_cast<uint8_t *>(words);
+    const int l = threadIdx.x;
+    const int64_t tile = blockIdx.x;
+    const int h = blockIdx.y, b = blockIdx.z;
+
+    float x0[32], x1[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const _Float16 *row = tok_row(src, b, h, t_begin + tile * 32 + i);
+        const h2 v = *reinterpret_cast<const h2 *>(row + 2 * l);
+        x0[i] = (float)v[0];
+        x1[i] = (float)v[1];
+    }
+    float mn0 = x0[0], mx0 = x0[0], mn1 = x1[0], mx1 = x1[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) {
+        mn0 = fminf(mn0, x0[i]); mx0 = fmaxf(mx0, x0[i]);
+        mn1 = fminf(mn1, x1[i]); mx1 = fmaxf(mx1, x1[i]);
+    }
+    _Float16 s0, z0, s1, z1;
+    group_params(mn0, mx0, L4, s0, z0);
+    group_params(mn1, mx1, L4, s1, z1);
+    const float fs0 = (float)s0, fz0 = (float)z0, fs1 = (float)s1, fz1 = (float)z1;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const uint32_t byte = code_of(x0[i], fz0, fs0, L4) | (code_of(x1[i], fz1, fs1, L4) << 4);
+        const int w = 8 * ((l >> 2) + 16 * (i >> 3)) + (i & 7);
+        bytes[4 * w + (l & 3)] = (uint8_t)byte;
+    }
+    __syncthreads();
+    uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * REC4;
+    reinterpret_cast<uint4 *>(rec)[2 * l] = reinterpret_cast<const uint4 *>(words)[2 * l];
+    reinterpret_cast<uint4 *>(rec)[2 * l + 1] = reinterpret_cast<const uint4 *>(words)[2 * l + 1];
+    const h2 sp = {s0, s1}, zp = {z0, z1};
+    reinterpret_cast<h2 *>(rec + K4_SCALE)[l] = sp;
+    reinterpret_cast<h2 *>(rec + K4_ZERO)[l] = zp;
+}
+
+// Values: groups are 32 channels of one token; lane l owns channels 2l, 2l+1 (group l/16). Value code of channel c,
+// token t sits in word 4c + t/8 at bit 4 (t%8), so lane l owns words 8l .. 8l+7 whole and builds them in registers.
+__global__ __launch_bounds__(64) void quant_values_b4_kernel(TokSrc src, int64_t t_begin, int kv_heads,
+                                                             uint8_t *tiles, int64_t max_tiles, int64_t tile0) {
+    __shared__ __align__(16) _Float16 sv[128], zv[128];
+    const int l = threadIdx.x;
+    const int64_t tile = blockIdx.x;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int g = l >> 4;
+    uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const _Float16 *row = tok_row(src, b, h, t_begin + tile * 32 + i);
+        const h2 v = *reinterpret_cast<const h2 *>(row + 2 * l);
+        const float a0 = (float)v[0], a1 = (float)v[1];
+        float mn = fminf(a0, a1), mx = fmaxf(a0, a1);
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) {
+            mn = fminf(mn, __shfl_xor(mn, off, 16));
+            mx = fmaxf(mx, __shfl_xor(mx, off, 16));
+        }
+        _Float16 s, z;
+        group_params(mn, mx, L4, s, z);
+        const float fs = (float)s, fz = (float)z;
+        w[i >> 3] |= code_of(a0, fz, fs, L4) << (4 * (i & 7));
+        w[4 + (i >> 3)] |= code_of(a1, fz, fs, L4) << (4 * (i & 7));
+        if ((l & 15) == 0) { sv[32 * g + i] = s; zv[32 * g + i] = z; }
+    }
+    __syncthreads();
+    uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * REC4;
+    uint4 *dst = reinterpret_cast<uint4 *>(rec + V4_CODES);
+    dst[2 * l] = uint4{w[0], w[1], w[2], w[3]};
+    dst[2 * l + 1] = uint4{w[4], w[5], w[6], w[7]};
+    reinterpret_cast<uint32_t *>(rec + V4_SCALE)[l] = reinterpret_cast<const uint32_t *>(sv)[l];
+    reinterpret_cast<uint32_t *>(rec + V4_ZERO)[l] = reinterpret_cast<const uint32_t *>(zv)[l];
+}
+
+// Sink record of one slice from token 0 of the sources: the key copied as fp16 into bytes [0, 256), the value
+// quantized per token (4 groups of 32 channels) with codes at byte 256 + c/2 (bit 4 (c%2)), scales at 320 + 2g,
+// zeros at 328 + 2g; bytes [336, 512) zero. One wavefront per slice, lane l owns channels 2l, 2l+1.
+__global__ __launch_bounds__(64) void sink_b4_kernel(TokSrc ksrc, TokSrc vsrc, int kv_heads, uint8_t *sink) {
+    const int l = threadIdx.x;
+    const int h = blockIdx.x, b = blockIdx.y;
+    const int g = l >> 4;
+    uint8_t *out = sink + (int64_t)(b * kv_heads + h) * SINK_REC;
+    const _Float16 *krow = tok_row(ksrc, b, h, 0);
+    const _Float16 *vrow = tok_row(vsrc, b, h, 0);
+    reinterpret_cast<uint32_t *>(out)[l] = reinterpret_cast<const uint32_t *>(krow)[l];
+    const h2 v = *reinterpret_cast<const h2 *>(vrow + 2 * l);
+    const float a0 = (float)v[0], a1 = (float)v[1];
+    float mn = fminf(a0, a1), mx = fmaxf(a0, a1);
+#pragma unroll
+    for (int off = 1; off < 16; off <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, off, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, off, 16));
+    }
+    _Float16 s, z;
+    group_params(mn, mx, L4, s, z);
+    const float fs = (float)s, fz = (float)z;
+    out[256 + l] = (uint8_t)(code_of(a0, fz, fs, L4) | (code_of(a1, fz, fs, L4) << 4));
+    if ((l & 15) == 0) {
+        reinterpret_cast<_Float16 *>(out + 320)[g] = s;
+        reinterpret_cast<_Float16 *>(out + 328)[g] = z;
+    }
+    if (l < 44) reinterpret_cast<uint32_t *>(out + 336)[l] = 0u;
+}
+
+// ------------------------------------------------------------------------------------------------ decode pass 1
+namespace {
+
+// cos and sin of pi * m * thp, with the product reduced modulo 2 in binary64 first (m up to 2^31, so the binary32
+// argument of sincospi keeps its full relative precision)
+__device__ __forceinline__ void half_turns(double m, double thp, float &c, float &s) {
+    double t = m * thp;
+    t -= 2.0 * floor(0.5 * t);
+    sincospif((float)t, &s, &c);
+}
+
+__device__ __forceinline__ float ubyte(uint32_t w, int k) { return (float)((w >> (8 * k)) & 0xFFu); }
+
+__device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
+
+// Eight 4-bit codes of one word as fp16, in the order of nibbles 0, 2, 4, 6, 1, 3, 5, 7. The even and odd nibbles
+// are spread into bytes; a byte b < 16 read as an fp8 e4m3 value is b * 2^-9 (subnormal for b < 8, exponent 1
+// otherwise), so the gfx950 fp8 converter with scale 2^9 yields b exactly.
+__device__ __forceinline__ h8 expand8_b4(uint32_t w) {
+    const uint32_t ev = w & 0x0F0F0F0Fu, od = (w >> 4) & 0x0F0F0F0Fu;
+    const h2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ev, 512.0f, false);
+    const h2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ev, 512.0f, true);
+    const h2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(od, 512.0f, false);
+    const h2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(od, 512.0f, true);
+    h8 r = {a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+    return r;
+}
+
+// x = (pa * sa.lo, pb * sb.lo) (or the high halves), hi = RN16(x), lo = RN16(x - hi); every element is one
+// mixed-precision fma with a single rounding, written into the packed halves.
+__device__ __forceinline__ void split_lo(float pa, float pb, uint32_t sa, uint32_t sb, uint32_t &hi, uint32_t &lo) {
+    asm("v_fma_mixlo_f16 %0, %2, %4, 0 op_sel_hi:[0,1,0]\n\t"
+        "v_fma_mixhi_f16 %0, %3, %5, 0 op_sel_hi:[0,1,0]\n\t"
+        "v_fma_mixlo_f16 %1, %2, %4, -%0 op_sel_hi:[0,1,1]\n\t"
+        "v_fma_mixhi_f16 %1, %3, %5, -%0 op_sel:[0,0,1] op_sel_hi:[0,1,1]"
+        : "=&v"(hi), "=&v"(lo)
+        : "v"(pa), "v"(pb), "v"(sa), "v"(sb));
+}
+__device__ __forceinline__ void split_hi(float pa, float pb, uint32_t sa, uint32_t sb, uint32_t &hi, uint32_t &lo) {
+    asm("v_fma_mixlo_f16 %0, %2, %4, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]\n\t"
+        "v_fma_mixhi_f16 %0, %3, %5, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]\n\t"
+        "v_fma_mixlo_f16 %1, %2, %4, -%0 op_sel:[0,1,0] op_sel_hi:[0,1,1]\n\t"
+        "v_fma_mixhi_f16 %1, %3, %5, -%0 op_sel:[0,1,1] op_sel_hi:[0,1,1]"
+        : "=&v"(hi), "=&v"(lo)
+        : "v"(pa), "v"(pb), "v"(sa), "v"(sb));
+}
+
+}  // namespace
+
+// One wavefront per (batch row, query head, token split). Virtual tiles of a slice: the quantized tiles
+// 0 .. n_qtiles - 1, then the window tiles (32 rows each, the last one partial); token u of virtual tile v sits at
+// absolute position n_sink + 32 v + u. Split 0 also takes the sink token (position 0) when there is one.
+//
+// Scores (VALU). Lane l = pq + 16 to owns channels 8pq .. 8pq+7 (rotation pairs i = 4pq .. 4pq+3) of tokens
+// 8to .. 8to+7: exactly the 32 contiguous bytes of key-code words 8l .. 8l+7. For a pair (x0, x1) of codes with
+// per-channel scales (s0, s1) and zeros (z0, z1), and the query pair (q0, q1) rotated back by the tile start
+// position m0 (qr = R(-m0 theta) q), the pair's share of the score of token u is
+//     cos(u theta) (a0 x0 + a1 x1 + alpha) + sin(u theta) (b0 x0 + b1 x1 + beta)
+// with a0 = qr0 s0, a1 = qr1 s1, alpha = qr0 z0 + qr1 z1, b0 = qr1 s0, b1 = -qr0 s1, beta = qr1 z0 - qr0 z1: the
+// dot product of the query with the dequantized key rotated by m0 + u, expanded by angle addition. The cos/sin of
+// u theta for the lane's 32 (token, pair) combinations are the same for every tile and stay in registers; the
+// rotation by the tile start advances by 32 theta per tile (recomputed exactly every 64 tiles). Window tiles use
+// the same expansion with the fp16 keys (s = 1, z = 0). Partial sums of the 16 lanes of a token are added through
+// LDS. The query carries the softmax scale times log2(e), so scores are in the log2 domain.
+//
+// Softmax. Lagged maximum: the running maximum is raised (and every accumulator rescaled) only when some score of
+// the tile exceeds it.
+//
+// PV (MFMA). 16x16x32 fp16: B = the value codes of 16 channels (column n = channel 16j + n) and the tile's 32
+// tokens, one code word per lane (expanded exactly by the fp8 converter); A row g = p~[t] = p[t] s_V[g][t] for value
+// group g, split into fp16 high and low parts contracted in turn (rows 4..15 repeat rows 0..3). For channel block j
+// only row g = j/2 is kept. The zero-point term sum_t p z_V[g][t] is accumulated on the VALU; window tiles and the
+// sink add their values on the VALU.
+template <bool ROPE>
+__global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
+    __shared__ __align__(16) float red[32 * 16];
+    __shared__ __align__(16) float pbuf[32];
+    __shared__ __align__(16) float obuf[HD];
+    __shared__ float gbuf[4];
+
+    const int l = threadIdx.x;
+    const int pq = l & 15, to = l >> 4;
+    const int n = l & 15, kg = l >> 4;
+    const int u = l >> 1, uh = l & 1;
+    const int bh = blockIdx.x;
+    const int split = blockIdx.y;
+    const int S = gridDim.y;
+    const int b = bh / a.q_heads, hq = bh - b * a.q_heads;
+    const int G = a.q_heads / a.kv_heads;
+    const int64_t slice = (int64_t)b * a.kv_heads + hq / G;
+    const int n_vt = a.n_qtiles + (a.n_resid + 31) / 32;
+    const int v0 = split * a.tiles_per_split;
+    const int v1 = min(n_vt, v0 + a.tiles_per_split);
+    const float C = a.sm_log2;
+    const float NEG_INF = -__builtin_inff();
+
+    // ---- query pairs of this lane (channels 8pq + 2j, 8pq + 2j + 1), in log2 units
+    const _Float16 *qrow = a.q + (int64_t)bh * HD;
+    const h8 qh = __builtin_bit_cast(h8, *reinterpret_cast<const uint4 *>(qrow + 8 * pq));
+    float q0[4], q1[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        q0[j] = C * (float)qh[2 * j];
+        q1[j] = C * (float)qh[2 * j + 1];
+    }
+
+    // ---- rotation tables: cos/sin of (8to + v) theta_i for this lane's pairs, one tile's step, tile start
+    float tc[8][4], ts[8][4], rc[4], rs[4], ec[4], es[4];
+    double thp[4];
+    if constexpr (ROPE) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = 4 * pq + j;
+            thp[j] = exp2(-(2.0 * i / HD) * a.log2_base) * 0.31830988618379067154;   // theta_i / pi
+            float c1, s1;
+            half_turns(1.0, thp[j], c1, s1);
+            half_turns(8.0 * to, thp[j], tc[0][j], ts[0][j]);
+#pragma unroll
+            for (int v = 1; v < 8; ++v) {
+                tc[v][j] = tc[v - 1][j] * c1 - ts[v - 1][j] * s1;
+                ts[v][j] = ts[v - 1][j] * c1 + tc[v - 1][j] * s1;
+            }
+            half_turns(32.0, thp[j], rc[j], rs[j]);
+            half_turns((double)a.n_sink + 32.0 * v0, thp[j], ec[j], es[j]);
+        }
+    }
+    auto advance = [&](int v_next) {
+        if constexpr (ROPE) {
+            if (((v_next - v0) & 63) == 0) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) half_turns((double)a.n_sink + 32.0 * v_next, thp[j], ec[j], es[j]);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float c = ec[j] * rc[j] - es[j] * rs[j];
+                    es[j] = es[j] * rc[j] + ec[j] * rs[j];
+                    ec[j] = c;
+                }
+            }
+        }
+    };
+
+    // ---- online softmax state
+    float m = NEG_INF, lsum = 0.0f, gam = 0.0f, ws = 0.0f, ow0 = 0.0f, ow1 = 0.0f, vs0 = 0.0f, vs1 = 0.0f;
+    f4 acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = f4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    if (split == 0 && a.n_sink) {   // sink token at position 0 (no rotation); lane l: channels 2l, 2l+1
+        const uint8_t *sk = a.sink + slice * SINK_REC;
+        const h2 kk = reinterpret_cast<const h2 *>(sk)[l];
+        const h2 qq = reinterpret_cast<const h2 *>(qrow)[l];
+        float d = (C * (float)qq[0]) * (float)kk[0] + (C * (float)qq[1]) * (float)kk[1];
+        d = rows_sum(row16_sum(d));
+        const uint32_t byte = sk[256 + l];
+        const int g = l >> 4;
+        const float s = (float)reinterpret_cast<const _Float16 *>(sk + 320)[g];
+        const float z = (float)reinterpret_cast<const _Float16 *>(sk + 328)[g];
+        vs0 = fmaf((float)(byte & 15u), s, z);
+        vs1 = fmaf((float)(byte >> 4), s, z);
+        m = d;
+        ws = 1.0f;
+        lsum = (l == 0) ? 1.0f : 0.0f;
+    }
+
+    // partial scores -> full score of token u in lanes 2u, 2u+1 (tokens >= nv masked), then the softmax step
+    auto softmax_step = [&](const float (&part)[8], int nv) -> float {
+#pragma unroll
+        for (int v = 0; v < 8; ++v) red[(8 * to + v) * 16 + pq] = part[v];
+        wave_lds_order();
+        const float4 r0 = *reinterpret_cast<const float4 *>(red + 16 * u + 8 * uh);
+        const float4 r1 = *reinterpret_cast<const float4 *>(red + 16 * u + 8 * uh + 4);
+        float s = ((r0.x + r0.y) + (r0.z + r0.w)) + ((r1.x + r1.y) + (r1.z + r1.w));
+        s = dpp_xadd<DPP_QUAD_1032>(s);
+        if (u >= nv) s = NEG_INF;
+        if (__any(s > m)) {
+            const float mn = fmaxf(m, rows_max(row16_max(s)));
+            const float sc = __builtin_amdgcn_exp2f(m - mn);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] *= sc;
+            gam *= sc; lsum *= sc; ws *= sc; ow0 *= sc; ow1 *= sc;
+            m = mn;
+        }
+        const float p = __builtin_amdgcn_exp2f(s - m);
+        lsum += uh ? 0.0f : p;
+        pbuf[u] = p;
+        wave_lds_order();
+        return p;
+    };
+
+    const uint8_t *recs = a.tiles + slice * a.max_tiles * REC4;
+    const int vq_end = min(v1, a.n_qtiles);
+    int v = v0;
+
+    // ---- quantized tiles
+    for (; v < vq_end; ++v) {
+        const uint8_t *rec = recs + (int64_t)v * REC4;
+        const uint4 k03 = reinterpret_cast<const uint4 *>(rec)[2 * l];
+        const uint4 k47 = reinterpret_cast<const uint4 *>(rec)[2 * l + 1];
+        const h8 skh = __builtin_bit_cast(h8, *reinterpret_cast<const uint4 *>(rec + K4_SCALE + 16 * pq));
+        const h8 zkh = __builtin_bit_cast(h8, *reinterpret_cast<const uint4 *>(rec + K4_ZERO + 16 * pq));
+        uint32_t vw[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) vw[j] = reinterpret_cast<const uint32_t *>(rec + V4_CODES)[4 * (16 * j + n) + kg];
+        const int gA = n & 3;
+        const uint4 svr = *reinterpret_cast<const uint4 *>(rec + V4_SCALE + 2 * (32 * gA + 8 * kg));
+        const h8 zvh = __builtin_bit_cast(h8, *reinterpret_cast<const uint4 *>(rec + V4_ZERO + 2 * (32 * gA + 8 * kg)));
+
+        // per-tile coefficients of the lane's pairs
+        float a0[4], a1[4], al[4], b0[4], b1[4], be[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float r0 = q0[j], r1 = q1[j];
+            if constexpr (ROPE) {
+                r0 = q0[j] * ec[j] + q1[j] * es[j];
+                r1 = q1[j] * ec[j] - q0[j] * es[j];
+            }
+            const float s0 = (float)skh[2 * j], s1 = (float)skh[2 * j + 1];
+            const float z0 = (float)zkh[2 * j], z1 = (float)zkh[2 * j + 1];
+            a0[j] = r0 * s0;
+            a1[j] = r1 * s1;
+            al[j] = r0 * z0 + r1 * z1;
+            b0[j] = r1 * s0;
+            b1[j] = -(r0 * s1);
+            be[j] = r1 * z0 - r0 * z1;
+        }
+        advance(v + 1);
+
+        const uint32_t kw[8] = {k03.x, k03.y, k03.z, k03.w, k47.x, k47.y, k47.z, k47.w};
+        float part[8];
+        if constexpr (ROPE) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const uint32_t ev = kw[t] & 0x0F0F0F0Fu, od = (kw[t] >> 4) & 0x0F0F0F0Fu;
+                float sacc = 0.0f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float x0 = ubyte(ev, j), x1 = ubyte(od, j);
+                    const float P = fmaf(a1[j], x1, fmaf(a0[j], x0, al[j]));
+                    const float Q = fmaf(b1[j], x1, fmaf(b0[j], x0, be[j]));
+                    sacc = fmaf(tc[t][j], P, fmaf(ts[t][j], Q, sacc));
+                }
+                part[t] = sacc;
+            }
+        } else {
+            const float alpha = (al[0] + al[1]) + (al[2] + al[3]);
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const uint32_t ev = kw[t] & 0x0F0F0F0Fu, od = (kw[t] >> 4) & 0x0F0F0F0Fu;
+                float sacc = alpha;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sacc = fmaf(a1[j], ubyte(od, j), fmaf(a0[j], ubyte(ev, j), sacc));
+                part[t] = sacc;
+            }
+        }
+        softmax_step(part, 32);
+
+        // PV: A rows g = n & 3 over tokens 8kg .. 8kg+7 in the expand8_b4 order (t0 t2 t4 t6 t1 t3 t5 t7)
+        const float4 pa = *reinterpret_cast<const float4 *>(pbuf + 8 * kg);
+        const float4 pb = *reinterpret_cast<const float4 *>(pbuf + 8 * kg + 4);
+        uint32_t ah[4], alo[4];
+        split_lo(pa.x, pa.z, svr.x, svr.y, ah[0], alo[0]);
+        split_lo(pb.x, pb.z, svr.z, svr.w, ah[1], alo[1]);
+        split_hi(pa.y, pa.w, svr.x, svr.y, ah[2], alo[2]);
+        split_hi(pb.y, pb.w, svr.z, svr.w, ah[3], alo[3]);
+        const h8 Ahi = __builtin_bit_cast(h8, uint4{ah[0], ah[1], ah[2], ah[3]});
+        const h8 Alo = __builtin_bit_cast(h8, uint4{alo[0], alo[1], alo[2], alo[3]});
+        gam += ((pa.x * (float)zvh[0] + pa.y * (float)zvh[1]) + (pa.z * (float)zvh[2] + pa.w * (float)zvh[3])) +
+               ((pb.x * (float)zvh[4] + pb.y * (float)zvh[5]) + (pb.z * (float)zvh[6] + pb.w * (float)zvh[7]));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const h8 B = expand8_b4(vw[j]);
+            acc[j] = mfma(Ahi, B, acc[j]);
+            acc[j] = mfma(Alo, B, acc[j]);
+        }
+    }
+
+    // ---- window tiles (fp16 rows; keys rotated like the quantized ones)
+    for (; v < v1; ++v) {
+        const int w = v - a.n_qtiles;
+        const int nv = min(32, a.n_resid - 32 * w);
+        const _Float16 *kr = a.k_res + (slice * a.res_cap + 32 * w) * HD;
+        const _Float16 *vr = a.v_res + (slice * a.res_cap + 32 * w) * HD;
+        h8 kx[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) kx[t] = __builtin_bit_cast(h8, *reinterpret_cast<const uint4 *>(kr + (8 * to + t) * HD + 8 * pq));
+        float r0[4], r1[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            r0[j] = q0[j];
+            r1[j] = q1[j];
+            if constexpr (ROPE) {
+                r0[j] = q0[j] * ec[j] + q1[j] * es[j];
+                r1[j] = q1[j] * ec[j] - q0[j] * es[j];
+            }
+        }
+        advance(v + 1);
+        float part[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            float sacc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float x0 = (float)kx[t][2 * j], x1 = (float)kx[t][2 * j + 1];
+                const float P = fmaf(r1[j], x1, r0[j] * x0);
+                if constexpr (ROPE) {
+                    const float Q = fmaf(-r0[j], x1, r1[j] * x0);
+                    sacc = fmaf(tc[t][j], P, fmaf(ts[t][j], Q, sacc));
+                } else {
+                    sacc += P;
+                }
+            }
+            part[t] = sacc;
+        }
+        softmax_step(part, nv);
+        for (int t = 0; t < nv; ++t) {   // lane l: channels 2l, 2l+1
+            const float p = pbuf[t];
+            const h2 vv = reinterpret_cast<const h2 *>(vr + t * HD)[l];
+            ow0 = fmaf(p, (float)vv[0], ow0);
+            ow1 = fmaf(p, (float)vv[1], ow1);
+        }
+    }
+
+    // ---- partials of this split: lanes 0..15 hold channel 16j + n of the MFMA sums in acc[j][j / 2]
+    lsum = rows_sum(row16_sum(lsum));
+    gam = rows_sum(gam);   // lane n (any row): value group n & 3
+    if (l < 16) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) obuf[16 * j + l] = acc[j][j >> 1];
+    }
+    if (l < 4) gbuf[l] = gam;
+    wave_lds_order();
+    const float2 ov = reinterpret_cast<const float2 *>(obuf)[l];
+    const float gz = gbuf[l >> 4];
+    const int64_t row = (int64_t)bh * S + split;
+    float2 res;
+    res.x = ov.x + gz + ws * vs0 + ow0;
+    res.y = ov.y + gz + ws * vs1 + ow1;
+    reinterpret_cast<float2 *>(a.part_o + row * HD)[l] = res;
+    if (l == 0) {
+        a.part_ml[2 * row] = m;
+        a.part_ml[2 * row + 1] = lsum;
+    }
+}
+
+// ------------------------------------------------------------------------------------------------ launchers
+hipError_t launch_quant_keys_b4(const TokSrc &src, int64_t t_begin, int64_t n_tiles, int batch, int kv_heads,
+                                uint8_t *tiles, int64_t max_tiles, int64_t tile0, hipStream_t st) {
+    dim3 grid((unsigned)n_tiles, (unsigned)kv_heads, (unsigned)batch);
+    hipLaunchKernelGGL(quant_keys_b4_kernel, grid, dim3(64), 0, st, src, t_begin, kv_heads, tiles, max_tiles, tile0);
+    return hipGetLastError();
+}
+
+hipError_t launch_quant_values_b4(const TokSrc &src, int64_t t_begin, int64_t n_tiles, int batch, int kv_heads,
+                                  uint8_t *tiles, int64_t max_tiles, int64_t tile0, hipStream_t st) {
+    dim3 grid((unsigned)n_tiles, (unsigned)kv_heads, (unsigned)batch);
+    hipLaunchKernelGGL(quant_values_b4_kernel, grid, dim3(64), 0, st, src, t_begin, kv_heads, tiles, max_tiles,
+                       tile0);
+    return hipGetLastError();
+}
+
+hipError_t launch_sink_b4(const TokSrc &ksrc, const TokSrc &vsrc, int batch, int kv_heads, uint8_t *sink,
+                          hipStream_t st) {
+    hipLaunchKernelGGL(sink_b4_kernel, dim3((unsigned)kv_heads, (unsigned)batch), dim3(64), 0, st, ksrc, vsrc,
+                       kv_heads, sink);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_b4(const DecodeB4Args &a, float *out, int splits, hipStream_t st) {
+    const dim3 grid((unsigned)(a.batch * a.q_heads), (unsigned)splits);
+    if (a.rope)
+        hipLaunchKernelGGL(decode_b4_pass1_kernel<true>, grid, dim3(64), 0, st, a);
+    else
+        hipLaunchKernelGGL(decode_b4_pass1_kernel<false>, grid, dim3(64), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_pass2(a.part_o, a.part_ml, out, a.batch * a.q_heads, splits, st);
+}
+
+}  // namespace kvq

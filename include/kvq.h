@@ -1,7 +1,9 @@
 /*
- * kvq.h — C ABI of a 2-bit KV-cache library for AMD MI355X (gfx950): KIVI-style asymmetric quantization of keys
- * per channel and values per token, a full-precision window of the newest tokens, and decode attention computed
- * straight from the packed codes plus that window.
+ * kvq.h — C ABI of a quantized KV-cache library for AMD MI355X (gfx950): KIVI-style asymmetric quantization of keys
+ * per channel and values per token (2-bit, or 4-bit in the KVQuant-style variant), a full-precision window of the
+ * newest tokens, and decode attention computed straight from the packed codes plus that window. The 4-bit variant
+ * can also keep keys cached before the rotary embedding (rotated at decode time) and hold token 0 apart as an
+ * attention sink with a full-precision key.
  *
  * Sources (the pages this library follows):
  *  - KIVI page, fdeinterviews.com "KIVI: A Tuning-Free Asymmetric 2bit Quantization for KV Cache": keys grouped per
@@ -10,6 +12,9 @@
  *  - synthetic.wiki "KV cache quantization", section "Keys are harder than values": per-channel keys, per-token
  *    values, and a key cache split into a grouped part and a residual part that are combined when computing
  *    attention scores.
+ *  - KVQuant page, fdeinterviews.com "KVQuant: Towards 10 Million Context Length LLM Inference with KV Cache
+ *    Quantization": per-channel keys quantized before the rotary embedding (RoPE applied after dequantization),
+ *    per-token values, and the first token's keys kept in full precision (attention sink); 4-bit codes.
  *
  * Conventions for every call:
  *  - All pointers named as device pointers refer to memory on the current HIP device; host pointers are named so.
@@ -43,8 +48,9 @@ extern "C" {
 #define KVQ_OK 0
 #define KVQ_E_NULL (-1)      /* a required pointer is NULL */
 #define KVQ_E_SHAPE (-2)     /* head_dim != 128, group != 32, q_heads % kv_heads != 0, R not a positive multiple
-                                of 32, non-positive sizes, or a token count/offset that is not a multiple of 32 */
-#define KVQ_E_BITS (-3)      /* bits != 2 */
+                                of 32, non-positive sizes, a token count/offset that is not a multiple of 32,
+                                unknown flags, flags with bits != 4, or KVQ_FLAG_PRE_ROPE with rope_base <= 1 */
+#define KVQ_E_BITS (-3)      /* bits not 2 or 4 */
 #define KVQ_E_ALIGN (-4)     /* a device pointer is not 16-byte aligned, or a token/head/batch stride is not a
                                 multiple of 8 elements (rows must be 16-byte aligned; the channel stride is 1) */
 #define KVQ_E_CAPACITY (-5)  /* the quantized part would exceed max_tokens, or a tile range exceeds it */
@@ -52,21 +58,36 @@ extern "C" {
 #define KVQ_E_EMPTY (-7)     /* attention over a cache that holds no token */
 #define KVQ_E_LAUNCH (-8)    /* the HIP runtime reported an error when launching */
 #define KVQ_E_STATE (-9)     /* cache host fields inconsistent: n_quant not a multiple of 32 or outside
-                                [0, max_tokens], n_resid outside [0, R] */
+                                [0, max_tokens], n_resid outside [0, R], n_sink not 0/1, n_sink = 1 without
+                                KVQ_FLAG_SINK, or (with KVQ_FLAG_SINK) n_sink = 0 while the cache holds tokens */
 
-/* Fixed sizes of the 2-bit layout. */
+/* Fixed sizes of the layouts. */
 #define KVQ_HEAD_DIM 128
 #define KVQ_GROUP 32
 #define KVQ_TILE_TOKENS 32
-#define KVQ_RECORD_BYTES 3072
+#define KVQ_RECORD_BYTES 3072       /* one 32-token tile, 2-bit codes */
+#define KVQ_RECORD_BYTES_4BIT 5120  /* one 32-token tile, 4-bit codes */
+#define KVQ_SINK_BYTES 512          /* the sink record of one (batch row, KV head) slice */
+
+/* kvq_shape.flags (4-bit only). */
+#define KVQ_FLAG_SINK 1      /* token 0 is held apart: fp16 key, per-token 4-bit value (KVQuant page, attention sink) */
+#define KVQ_FLAG_PRE_ROPE 2  /* keys are given and cached before the rotary embedding; attention rotates every key
+                                (sink, quantized and window alike) by its absolute position (KVQuant page, pre-RoPE
+                                key quantization) */
 
 /*
  * Shape of one cache (one attention layer).
  *   batch, kv_heads, q_heads: B, Hkv, Hq (Hq a multiple of Hkv; query head hq uses KV head hq / (Hq / Hkv), i.e.
  *   consecutive query heads share a KV head — the usual grouped-query layout);
- *   head_dim: must be 128; bits: must be 2; group: must be 32 (tokens per key group, channels per value group);
+ *   head_dim: must be 128; bits: 2 or 4; group: must be 32 (tokens per key group, channels per value group);
  *   residual_cap: R, the number of newest tokens kept in fp16 (a positive multiple of 32; 128 on the pages);
- *   max_tokens: capacity of the quantized part in tokens (a positive multiple of 32).
+ *   flags: 0, or (bits = 4 only) an OR of KVQ_FLAG_SINK and KVQ_FLAG_PRE_ROPE;
+ *   max_tokens: capacity of the quantized part in tokens (a positive multiple of 32);
+ *   rope_base: with KVQ_FLAG_PRE_ROPE, the rotary base (10000 in the usual models; must be > 1); ignored otherwise.
+ *     Rotary form: channel pairs (2i, 2i+1), i = 0..63, turned by the angle m * theta_i with
+ *     theta_i = rope_base^(-2i/128) at absolute position m (the sink is position 0, token k of the quantized part is
+ *     position n_sink + k, window row r is position n_sink + n_quant + r): (x0, x1) -> (x0 cos - x1 sin,
+ *     x0 sin + x1 cos). The query passed to kv_decode_attention is already rotated for its own position.
  */
 typedef struct kvq_shape {
     int32_t batch;
@@ -76,14 +97,15 @@ typedef struct kvq_shape {
     int32_t bits;
     int32_t group;
     int32_t residual_cap;
-    int32_t reserved; /* must be 0 */
+    int32_t flags;
     int64_t max_tokens;
+    double rope_base;
 } kvq_shape;
 
 /*
- * One cache: caller-owned device buffers plus two host integers.
- *   tiles: device, uint8 [B][Hkv][max_tokens / 32][3072]: the quantized part. Tile j of slice (b, h) holds tokens
- *     32 j .. 32 j + 31 as one 3072-byte record:
+ * One cache: caller-owned device buffers plus three host integers.
+ *   tiles: device, uint8 [B][Hkv][max_tokens / 32][record]: the quantized part. Tile j of slice (b, h) holds
+ *     quantized tokens 32 j .. 32 j + 31 as one record. 2-bit: a 3072-byte record
  *       bytes    0..1023  key codes,   256 little-endian uint32 words (16 two-bit codes each)
  *       bytes 1024..2047  value codes, 256 uint32 words
  *       bytes 2048..2303  key scale s_K[c] (fp16, c = 0..127; one per channel of the tile)
@@ -95,9 +117,22 @@ typedef struct kvq_shape {
  *     Value code of channel c, token t: with (kc, e) = (t/4, t%4) for t < 16 and ((t-16)/4, 4 + (t-16)%4) otherwise,
  *       word 4 (c%16 + 16 kc) + (c/16)/2, bit 4 e + 2 ((c/16)%2).
  *     Decoding: x = code * s + z.
- *   k_res, v_res: device, fp16 [B][Hkv][R][128]: the residual window; rows 0 .. n_resid-1 hold tokens
- *     n_quant .. n_quant + n_resid - 1 exactly as appended.
+ *     4-bit: a 5120-byte record (a library layout; the pages fix only the code width)
+ *       bytes    0..2047  key codes,   512 little-endian uint32 words (8 four-bit codes each)
+ *       bytes 2048..4095  value codes, 512 words
+ *       bytes 4096..4351  key scale s_K[c];  4352..4607 key zero z_K[c]
+ *       bytes 4608..4863  value scale s_V[g][t] (index 32 g + t);  4864..5119 value zero z_V[g][t]
+ *     Key code of token t, channel c: word 8 (c/8 + 16 (t/8)) + t%8, bit 4 (c%8).
+ *     Value code of channel c, token t: word 4 c + t/8, bit 4 (t%8).
+ *   k_res, v_res: device, fp16 [B][Hkv][R][128]: the residual window; rows 0 .. n_resid-1 hold the newest tokens
+ *     exactly as appended.
  *   n_quant (host): tokens in the quantized part (a multiple of 32). n_resid (host): tokens in the window (0..R).
+ *   n_sink (host): 1 once the sink holds token 0 (KVQ_FLAG_SINK), else 0. The cache then holds
+ *     n_sink + n_quant + n_resid tokens, in that order.
+ *   sink: device, uint8 [B][Hkv][512], required with KVQ_FLAG_SINK (else ignored): bytes 0..255 the fp16 key of
+ *     token 0; bytes 256..319 its value codes (channel c at byte 256 + c/2, bit 4 (c%2)); bytes 320..327 value scales
+ *     s_V[g] and 328..335 value zeros z_V[g] (fp16, g = 0..3); bytes 336..511 zero.
+ * A new cache starts with n_quant = n_resid = n_sink = 0.
  */
 typedef struct kvq_cache {
     void *tiles;
@@ -105,7 +140,8 @@ typedef struct kvq_cache {
     void *v_res;
     int64_t n_quant;
     int32_t n_resid;
-    int32_t reserved; /* must be 0 */
+    int32_t n_sink;
+    void *sink;
 } kvq_cache;
 
 /*
@@ -115,7 +151,7 @@ typedef struct kvq_cache {
  *   n_tokens: a positive multiple of 32. tile0: first destination tile index (tokens 32*tile0 ...).
  *   tiles: device, the tile array of a cache of this shape; for tiles tile0 .. tile0 + n_tokens/32 - 1 of every
  *     slice, the key codes and key scale/zero fields are written; the value fields are left untouched.
- * Per group (32 tokens of one channel), with x the fp16 inputs and L = 3:
+ * Per group (32 tokens of one channel), with x the fp16 inputs and L = 2^bits - 1 (3 or 15):
  *   r = RN32(max - min); s = RN16(RN32(r / L)); if (L + 1/2) * s < r then s = next binary16 above s;
  *   z = min (a zero minimum stored as +0); code = 0 if s == 0, else
  *   clamp(round_half_even(RN32(RN32(x - z) / s)), 0, L); RN32/RN16 = round to nearest even into binary32/binary16,
@@ -140,6 +176,8 @@ KVQ_API int kv_quant_values_per_token(const kvq_shape *shape, const void *v, int
  * (quantizing its R tokens into R/32 tiles, keys per channel and values per token) and then stores the token:
  *   F = R * floor((n_resid + n_tokens - 1) / R) tokens are flushed: the first F of (window, new tokens);
  *   the remaining tokens become the window.
+ *   With KVQ_FLAG_SINK and n_sink = 0, the first new token is written to the sink record instead (n_sink becomes 1)
+ *   and the rule above applies to the other n_tokens - 1 tokens.
  *   k_new, v_new: device fp16 with the same stride convention as kv_quant_keys_per_channel; n_tokens >= 1.
  *   cache: host struct; on success cache->n_quant and cache->n_resid are updated at enqueue time.
  * Errors: KVQ_E_NULL, KVQ_E_SHAPE, KVQ_E_BITS, KVQ_E_ALIGN, KVQ_E_STATE, KVQ_E_CAPACITY (n_quant + F > max_tokens),
@@ -150,7 +188,8 @@ KVQ_API int kv_append_and_flush(const kvq_shape *shape, kvq_cache *cache, const 
 
 /*
  * Number of token splits kv_decode_attention uses for the cache's current length (split-K along tokens; each
- * split covers a contiguous range of 32-token tiles, the residual window being the last tiles), and the workspace
+ * split covers a contiguous range of 32-token tiles, the residual window being the last tiles; the sink token goes
+ * with the first split), and the workspace
  * it needs: batch * q_heads * splits * (128 + 2) * 4 bytes. Return 0 when the arguments are invalid.
  */
 KVQ_API int32_t kv_decode_attention_splits(const kvq_shape *shape, const kvq_cache *cache);
@@ -160,7 +199,9 @@ KVQ_API size_t kv_decode_attention_workspace_bytes(const kvq_shape *shape, const
  * Decode attention of one query per (batch row, query head) over the whole cache: grouped part and residual
  * window (synthetic.wiki "Keys are harder than values", last bullet). For query head hq of batch row b, with
  * KV head h = hq / (Hq / Hkv) and decoded keys/values K, V (codes * scale + zero; window tokens as stored):
- *   out[b][hq][c] = sum_t softmax_t(sm_scale * q . K[t]) V[t][c].
+ *   out[b][hq][c] = sum_t softmax_t(sm_scale * q . K[t]) V[t][c],
+ * over the sink token (if any), the quantized part and the window. With KVQ_FLAG_PRE_ROPE, K[t] is the decoded key
+ * rotated by its absolute position (see kvq_shape).
  *   q: device fp16 [B][Hq][128], contiguous. sm_scale: softmax scale; a value <= 0 selects 1/sqrt(128).
  *   out: device fp32 [B][Hq][128], contiguous.
  *   workspace: device, >= kv_decode_attention_workspace_bytes(shape, cache) bytes, 16-byte aligned (split

@@ -49,3 +49,40 @@ def workload_tokens(w: kvsynth.Workload, tensor_id: int, t0: int, t1: int, b=Non
         return kvsynth.slice_tokens(w.seed, tensor_id, b, h, t0, t1, w.head_dim, n_out, factor)
     return kvsynth.kv_tensor(w.seed, tensor_id, w.batch, w.kv_heads, t0, t1, w.head_dim, n_out, factor,
                              threads=threads)
+
+
+def oracle_records4(cache: oc.SliceCache) -> np.ndarray:
+    """4-bit tile records [S, n_quant / 32, 5120] of the oracle's quantized part, packed by the oracle."""
+    from oracle import layout4
+    kq, ks, kz, vq, vs, vz = cache.quantized()
+    S, nq, D = kq.shape
+    nt = nq // 32
+    return layout4.pack_tiles(kq.reshape(S, nt, 32, D), ks, kz, vq.reshape(S, nt, 32, D),
+                              vs.reshape(S, nt, 32, 4), vz.reshape(S, nt, 32, 4))
+
+
+def oracle_sink(cache: oc.SliceCache) -> np.ndarray:
+    """Sink records [S, 512] of the oracle's sink token, packed by the oracle."""
+    from oracle import layout4
+    vq, vs, vz = cache.v_sink
+    return layout4.pack_sink(cache.k_sink, vq, vs, vz)
+
+
+def records4_from_device(tiles, n_tiles: int, slices=None) -> np.ndarray:
+    """GPU 4-bit tile array [B, H, max_tiles, 5120] -> numpy [S, n_tiles, 5120]."""
+    B, H = tiles.shape[:2]
+    t = tiles[:, :, :n_tiles].reshape(B * H, n_tiles, 5120)
+    if slices is not None:
+        t = t[list(slices)]
+    return t.cpu().numpy()
+
+
+def first_mismatch4(a: np.ndarray, b: np.ndarray) -> str:
+    """First differing byte of two 4-bit record arrays (slice, tile, field, byte)."""
+    idx = np.argwhere(a != b)
+    if len(idx) == 0:
+        return "identical"
+    off = idx[0][-1]
+    field = ["k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"][
+        0 if off < 2048 else 1 if off < 4096 else 2 + (off - 4096) // 256]
+    return f"{len(idx)} bytes differ; first at {tuple(idx[0])} ({field}): gpu {a[tuple(idx[0])]} oracle {b[tuple(idx[0])]}"

@@ -46,8 +46,8 @@ def kvq():
 
 
 def _shape(kvq, **kw):
-    d = dict(batch=2, kv_heads=2, q_heads=4, head_dim=128, bits=2, group=32, residual_cap=128, reserved=0,
-             max_tokens=1024)
+    d = dict(batch=2, kv_heads=2, q_heads=4, head_dim=128, bits=2, group=32, residual_cap=128, flags=0,
+             max_tokens=1024, rope_base=0.0)
     d.update(kw)
     return kvq.KvqShape(**d)
 
@@ -55,8 +55,8 @@ def _shape(kvq, **kw):
 FAKE = 0x7f0000000000     # 16-byte aligned, never dereferenced: every call below fails validation first
 
 
-def _cache(kvq, n_quant=0, n_resid=0, tiles=FAKE, k_res=FAKE + 4096, v_res=FAKE + 8192):
-    return kvq.KvqCache(tiles, k_res, v_res, n_quant, n_resid, 0)
+def _cache(kvq, n_quant=0, n_resid=0, tiles=FAKE, k_res=FAKE + 4096, v_res=FAKE + 8192, n_sink=0, sink=None):
+    return kvq.KvqCache(tiles, k_res, v_res, n_quant, n_resid, n_sink, sink)
 
 
 def test_status_strings(kvq):
@@ -68,9 +68,14 @@ def test_status_strings(kvq):
 def test_shape_validation(kvq):
     lib = kvq.library()
     cases = [
-        (dict(bits=4), kvq.E_BITS), (dict(head_dim=64), kvq.E_SHAPE), (dict(group=16), kvq.E_SHAPE),
-        (dict(q_heads=3), kvq.E_SHAPE), (dict(residual_cap=100), kvq.E_SHAPE), (dict(residual_cap=0), kvq.E_SHAPE),
-        (dict(max_tokens=1000), kvq.E_SHAPE), (dict(batch=0), kvq.E_SHAPE), (dict(reserved=1), kvq.E_SHAPE),
+        (dict(bits=3), kvq.E_BITS), (dict(bits=8), kvq.E_BITS), (dict(head_dim=64), kvq.E_SHAPE),
+        (dict(group=16), kvq.E_SHAPE), (dict(q_heads=3), kvq.E_SHAPE), (dict(residual_cap=100), kvq.E_SHAPE),
+        (dict(residual_cap=0), kvq.E_SHAPE), (dict(max_tokens=1000), kvq.E_SHAPE), (dict(batch=0), kvq.E_SHAPE),
+        # flags belong to the 4-bit variant; unknown bits and a missing rotary base are rejected
+        (dict(flags=kvq.FLAG_SINK), kvq.E_SHAPE), (dict(bits=4, flags=4), kvq.E_SHAPE),
+        (dict(bits=4, flags=kvq.FLAG_PRE_ROPE, rope_base=0.0), kvq.E_SHAPE),
+        (dict(bits=4, flags=kvq.FLAG_PRE_ROPE, rope_base=1.0), kvq.E_SHAPE),
+        (dict(bits=4, flags=kvq.FLAG_PRE_ROPE, rope_base=float("nan")), kvq.E_SHAPE),
     ]
     for kw, code in cases:
         s = _shape(kvq, **kw)
@@ -151,3 +156,45 @@ def test_split_plan_covers_every_tile(kvq, B, Hq, Hkv, n_q, n_r, min_splits):
     assert min_splits <= S <= n_vt
     tps = -(-n_vt // S)
     assert (S - 1) * tps < n_vt <= S * tps       # no empty split, every tile covered
+
+
+def test_sink_cache_validation(kvq):
+    """The sink record is required with FLAG_SINK; n_sink is 0/1, only with the flag, and 1 before any other token."""
+    lib = kvq.library()
+    s = _shape(kvq, bits=4, flags=kvq.FLAG_SINK | kvq.FLAG_PRE_ROPE, rope_base=10000.0)
+    ap = lambda c, n=1: lib.kv_append_and_flush(ctypes.byref(s), ctypes.byref(c), FAKE, FAKE, 0, 0, 128, n, None)
+    assert ap(_cache(kvq)) == kvq.E_NULL                                    # no sink buffer
+    assert ap(_cache(kvq, sink=FAKE + 8)) == kvq.E_ALIGN
+    assert ap(_cache(kvq, n_sink=2, sink=FAKE + 16384)) == kvq.E_STATE
+    assert ap(_cache(kvq, 32, 1, n_sink=0, sink=FAKE + 16384)) == kvq.E_STATE   # tokens but no sink yet
+    plain = _shape(kvq, bits=4)
+    c = _cache(kvq, 0, 1, n_sink=1)
+    assert lib.kv_append_and_flush(ctypes.byref(plain), ctypes.byref(c), FAKE, FAKE, 0, 0, 128, 1,
+                                   None) == kvq.E_STATE                     # n_sink without the flag
+    # capacity: the first token of an empty sink cache goes to the sink, the other 1024 + 128 fit exactly
+    c = _cache(kvq, sink=FAKE + 16384)
+    assert ap(c, 1024 + 130) == kvq.E_CAPACITY
+    assert (c.n_quant, c.n_resid, c.n_sink) == (0, 0, 0)
+
+
+def test_sink_only_cache_has_one_split(kvq):
+    lib = kvq.library()
+    s = _shape(kvq, bits=4, flags=kvq.FLAG_SINK)
+    c = _cache(kvq, n_sink=1, sink=FAKE + 16384)
+    assert lib.kv_decode_attention_splits(ctypes.byref(s), ctypes.byref(c)) == 1
+    assert lib.kv_decode_attention_workspace_bytes(ctypes.byref(s), ctypes.byref(c)) == 2 * 4 * 130 * 4
+    empty = _cache(kvq, sink=FAKE + 16384)
+    assert lib.kv_decode_attention_splits(ctypes.byref(s), ctypes.byref(empty)) == 0
+    assert lib.kv_decode_attention(ctypes.byref(s), ctypes.byref(empty), FAKE, 0.0, FAKE, FAKE, 1 << 30,
+                                   None) == kvq.E_EMPTY
+
+
+def test_four_bit_splits_cover_every_query_head(kvq):
+    """4-bit work units are (batch row, query head): the split count follows B * Hq, not B * Hkv."""
+    lib = kvq.library()
+    s = _shape(kvq, bits=4, batch=16, kv_heads=32, q_heads=32, max_tokens=16384)
+    c = _cache(kvq, 16256, 127)
+    S = lib.kv_decode_attention_splits(ctypes.byref(s), ctypes.byref(c))
+    n_vt = 16256 // 32 + 4
+    tps = -(-n_vt // S)
+    assert S >= 1 and -(-n_vt // tps) == S and 16 * 32 * S <= 4096
