@@ -25,6 +25,8 @@ HIPCC_FLAGS = [
     # device code only: no IEEE-mode NaN quieting (inputs are finite by contract, and min/max then need no
     # canonicalization); host validation keeps full NaN semantics
     "-mno-amdgpu-ieee", "-Xarch_device", "-fno-honor-nans",
+    # MFMA accumulators in ordinary VGPRs (no copies to and from the accumulation registers around VALU rescales)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-command-line-argument",
 ]
 

@@ -157,30 +157,12 @@ __device__ __forceinline__ void split_pair(float pa, float pb, uint32_t s, uint3
         : "v"(pa), "v"(pb), "v"(s));
 }
 
-// LDS-DMA load: 16 bytes per lane from `src` into LDS at lds_base + 16 * lane (lds_base goes through M0, which
-// the statement saves and restores). Issued from inline asm so that the compiler's wait insertion, which cannot tell
-// the destination from the other LDS buffers, does not drain the vector-memory counter before every LDS access; the
-// destination's readers wait explicitly (wait_vmcnt), and loads complete in order, so these extra loads can only
-// make the compiler's own counted waits stricter.
-__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds_base) {
-    uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-                 : "=&s"(saved)
-                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "memory");
-}
 // gfx950 LDS transpose read of 16-bit elements: within each 16-lane row, lane i receives element i % 4 of the 8-byte
 // chunks read by lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 (in that order)
 typedef short s4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ h4 read_tr16(const _Float16 *lds) {
     return __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4 *)lds));
 }
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
 // One wavefront per (split, batch row, KV head, chunk of up to 4 query heads of that KV head); lane l = n + 16 kc.
 //

@@ -154,7 +154,13 @@ __device__ __forceinline__ void half_turns(double m, double thp, float &c, float
     sincospif((float)t, &s, &c);
 }
 
-__device__ __forceinline__ float ubyte(uint32_t w, int k) { return (float)((w >> (8 * k)) & 0xFFu); }
+// Two 4-bit codes held in bytes 2 sel and 2 sel + 1 of w (each byte < 16) as exact fp32 values: a byte b < 16
+// read as fp8 e4m3 is b * 2^-9 (subnormal for b < 8, exponent 1 otherwise), and the converter's scale 2^9 makes it b.
+typedef float f2 __attribute__((ext_vector_type(2)));
+template <bool SEL>
+__device__ __forceinline__ f2 codes2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 512.0f, SEL);
+}
 
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
@@ -196,17 +202,23 @@ __device__ __forceinline__ void split_hi(float pa, float pb, uint32_t sa, uint32
 // 0 .. n_qtiles - 1, then the window tiles (32 rows each, the last one partial); token u of virtual tile v sits at
 // absolute position n_sink + 32 v + u. Split 0 also takes the sink token (position 0) when there is one.
 //
+// Staging. Quantized tiles are copied whole into an LDS ring of three 5120-byte slots by global-to-LDS DMA, two
+// tiles ahead of the one being computed, so a wavefront keeps up to 10 KB of loads in flight without spending
+// registers on them. The key codes are scattered on the way in so that lane l later reads its 32 bytes as two
+// bank-conflict-free 16-byte reads.
+//
 // Scores (VALU). Lane l = pq + 16 to owns channels 8pq .. 8pq+7 (rotation pairs i = 4pq .. 4pq+3) of tokens
-// 8to .. 8to+7: exactly the 32 contiguous bytes of key-code words 8l .. 8l+7. For a pair (x0, x1) of codes with
-// per-channel scales (s0, s1) and zeros (z0, z1), and the query pair (q0, q1) rotated back by the tile start
-// position m0 (qr = R(-m0 theta) q), the pair's share of the score of token u is
+// 8to .. 8to+7: key-code words 8l .. 8l+7. For a pair (x0, x1) of codes with per-channel scales (s0, s1) and zeros
+// (z0, z1), and the query pair (q0, q1) rotated back by the tile start position m0 (qr = R(-m0 theta) q), the
+// pair's share of the score of token u is
 //     cos(u theta) (a0 x0 + a1 x1 + alpha) + sin(u theta) (b0 x0 + b1 x1 + beta)
 // with a0 = qr0 s0, a1 = qr1 s1, alpha = qr0 z0 + qr1 z1, b0 = qr1 s0, b1 = -qr0 s1, beta = qr1 z0 - qr0 z1: the
-// dot product of the query with the dequantized key rotated by m0 + u, expanded by angle addition. The cos/sin of
-// u theta for the lane's 32 (token, pair) combinations are the same for every tile and stay in registers; the
-// rotation by the tile start advances by 32 theta per tile (recomputed exactly every 64 tiles). Window tiles use
-// the same expansion with the fp16 keys (s = 1, z = 0). Partial sums of the 16 lanes of a token are added through
-// LDS. The query carries the softmax scale times log2(e), so scores are in the log2 domain.
+// dot product of the query with the dequantized key rotated by m0 + u, expanded by angle addition. Lane l computes
+// the six coefficients of pair l once per tile and shares them through LDS. The cos/sin of u theta for a lane's 32
+// (token, pair) combinations are the same for every tile and stay in registers; the rotation by the tile start
+// advances by 32 theta per tile (recomputed exactly every 64 tiles). Window tiles use the same expansion with the
+// fp16 keys (s = 1, z = 0). Partial sums of the 16 lanes of a token are added through LDS. The query carries the
+// softmax scale times log2(e), so scores are in the log2 domain.
 //
 // Softmax. Lagged maximum: the running maximum is raised (and every accumulator rescaled) only when some score of
 // the tile exceeds it.
@@ -216,12 +228,25 @@ __device__ __forceinline__ void split_hi(float pa, float pb, uint32_t sa, uint32
 // group g, split into fp16 high and low parts contracted in turn (rows 4..15 repeat rows 0..3). For channel block j
 // only row g = j/2 is kept. The zero-point term sum_t p z_V[g][t] is accumulated on the VALU; window tiles and the
 // sink add their values on the VALU.
+namespace {
+constexpr int NBUF = 3;                        // LDS ring slots (tiles in flight + the one being computed)
+constexpr int RING = 0;                        // [NBUF][5120]: K codes scattered (see dma_tile), rest as stored
+constexpr int RED = NBUF * REC4;               // f32 rows of 16 (one per token, row 9 (u/8) + u%8); reused for the
+                                               // output at the end
+constexpr int PBUF = RED + 36 * 64;            // f32 [32]; reused for the zero-point sums at the end
+constexpr int COEF4 = PBUF + 128;              // f32x4 [4 (pair % 4)][16 (pair / 4)]: a0 a1 alpha b0
+constexpr int COEF2 = COEF4 + 1024;            // f32x2 [4][16]: b1 beta
+constexpr int B4_LDS = COEF2 + 512;
+}  // namespace
+
 template <bool ROPE>
 __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
-    __shared__ __align__(16) float red[32 * 16];
-    __shared__ __align__(16) float pbuf[32];
-    __shared__ __align__(16) float obuf[HD];
-    __shared__ float gbuf[4];
+    __shared__ __align__(16) unsigned char smem[B4_LDS];
+    float *red = reinterpret_cast<float *>(smem + RED);
+    float *pbuf = reinterpret_cast<float *>(smem + PBUF);
+    float4 *coef4 = reinterpret_cast<float4 *>(smem + COEF4);
+    float2 *coef2 = reinterpret_cast<float2 *>(smem + COEF2);
+    const uint32_t ring_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)smem + RING;
 
     const int l = threadIdx.x;
     const int pq = l & 15, to = l >> 4;
@@ -239,49 +264,78 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
     const float C = a.sm_log2;
     const float NEG_INF = -__builtin_inff();
 
-    // ---- query pairs of this lane (channels 8pq + 2j, 8pq + 2j + 1), in log2 units
+    // ---- query pair l (channels 2l, 2l+1) in log2 units: the pair whose coefficients this lane computes
     const _Float16 *qrow = a.q + (int64_t)bh * HD;
-    const h8 qh = __builtin_bit_cast(h8, *reinterpret_cast<const uint4 *>(qrow + 8 * pq));
-    float q0[4], q1[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        q0[j] = C * (float)qh[2 * j];
-        q1[j] = C * (float)qh[2 * j + 1];
-    }
+    const h2 qq = reinterpret_cast<const h2 *>(qrow)[l];
+    const float qp0 = C * (float)qq[0], qp1 = C * (float)qq[1];
 
-    // ---- rotation tables: cos/sin of (8to + v) theta_i for this lane's pairs, one tile's step, tile start
-    float tc[8][4], ts[8][4], rc[4], rs[4], ec[4], es[4];
-    double thp[4];
+    // ---- rotation state: cos/sin of (8to + t) theta_i for the lane's score pairs i = 4pq + j (fixed tables); the
+    // tile-start rotation of pair l and its per-tile step
+    float tc[8][4], ts[8][4], ec = 1.0f, es = 0.0f, rc = 1.0f, rs = 0.0f;
+    double thl = 0.0;   // theta_l / pi
     if constexpr (ROPE) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int i = 4 * pq + j;
-            thp[j] = exp2(-(2.0 * i / HD) * a.log2_base) * 0.31830988618379067154;   // theta_i / pi
+            const double th = exp2(-(2.0 * (4 * pq + j) / HD) * a.log2_base) * 0.31830988618379067154;
             float c1, s1;
-            half_turns(1.0, thp[j], c1, s1);
-            half_turns(8.0 * to, thp[j], tc[0][j], ts[0][j]);
+            half_turns(1.0, th, c1, s1);
+            half_turns(8.0 * to, th, tc[0][j], ts[0][j]);
 #pragma unroll
-            for (int v = 1; v < 8; ++v) {
-                tc[v][j] = tc[v - 1][j] * c1 - ts[v - 1][j] * s1;
-                ts[v][j] = ts[v - 1][j] * c1 + tc[v - 1][j] * s1;
+            for (int t = 1; t < 8; ++t) {
+                tc[t][j] = tc[t - 1][j] * c1 - ts[t - 1][j] * s1;
+                ts[t][j] = ts[t - 1][j] * c1 + tc[t - 1][j] * s1;
             }
-            half_turns(32.0, thp[j], rc[j], rs[j]);
-            half_turns((double)a.n_sink + 32.0 * v0, thp[j], ec[j], es[j]);
         }
+        thl = exp2(-(2.0 * l / HD) * a.log2_base) * 0.31830988618379067154;
+        half_turns(32.0, thl, rc, rs);
+        half_turns((double)a.n_sink + 32.0 * v0, thl, ec, es);
     }
-    auto advance = [&](int v_next) {
+    auto advance = [&](int v_next) {   // rotation of pair l for the start of tile v_next
         if constexpr (ROPE) {
             if (((v_next - v0) & 63) == 0) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) half_turns((double)a.n_sink + 32.0 * v_next, thp[j], ec[j], es[j]);
+                half_turns((double)a.n_sink + 32.0 * v_next, thl, ec, es);
             } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float c = ec[j] * rc[j] - es[j] * rs[j];
-                    es[j] = es[j] * rc[j] + ec[j] * rs[j];
-                    ec[j] = c;
-                }
+                const float c = ec * rc - es * rs;
+                es = es * rc + ec * rs;
+                ec = c;
             }
+        }
+    };
+
+    // coefficients of pair l for the current tile (scales/zeros of its two channels) -> LDS; then the lane's four
+    // score pairs are read back
+    float a0[4], a1[4], al[4], b0[4], b1[4], be[4];
+    auto share_coefficients = [&](float s0, float s1, float z0, float z1) {
+        const float r0 = qp0 * ec + qp1 * es;
+        const float r1 = qp1 * ec - qp0 * es;
+        const int at = (l & 3) * 16 + (l >> 2);
+        coef4[at] = float4{r0 * s0, r1 * s1, r0 * z0 + r1 * z1, r1 * s0};
+        coef2[at] = float2{-(r0 * s1), r1 * z0 - r0 * z1};
+        wave_lds_order();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float4 c0 = coef4[j * 16 + pq];
+            const float2 c1 = coef2[j * 16 + pq];
+            a0[j] = c0.x; a1[j] = c0.y; al[j] = c0.z; b0[j] = c0.w; b1[j] = c1.x; be[j] = c1.y;
+        }
+    };
+
+    // partial score of token 8to + t from x pairs (x0, x1) of the lane's four pairs
+    auto token_score = [&](int t, const float (&x0)[4], const float (&x1)[4]) -> float {
+        if constexpr (ROPE) {
+            float sacc = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float P = fmaf(a1[j], x1[j], fmaf(a0[j], x0[j], al[j]));
+                const float Q = fmaf(b1[j], x1[j], fmaf(b0[j], x0[j], be[j]));
+                sacc = (j == 0) ? fmaf(tc[t][0], P, ts[t][0] * Q) : fmaf(tc[t][j], P, fmaf(ts[t][j], Q, sacc));
+            }
+            return sacc;
+        } else {
+            float sacc = (al[0] + al[1]) + (al[2] + al[3]);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sacc = fmaf(a1[j], x1[j], fmaf(a0[j], x0[j], sacc));
+            return sacc;
         }
     };
 
@@ -294,9 +348,7 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
     if (split == 0 && a.n_sink) {   // sink token at position 0 (no rotation); lane l: channels 2l, 2l+1
         const uint8_t *sk = a.sink + slice * SINK_REC;
         const h2 kk = reinterpret_cast<const h2 *>(sk)[l];
-        const h2 qq = reinterpret_cast<const h2 *>(qrow)[l];
-        float d = (C * (float)qq[0]) * (float)kk[0] + (C * (float)qq[1]) * (float)kk[1];
-        d = rows_sum(row16_sum(d));
+        const float d = rows_sum(row16_sum(qp0 * (float)kk[0] + qp1 * (float)kk[1]));
         const uint32_t byte = sk[256 + l];
         const int g = l >> 4;
         const float s = (float)reinterpret_cast<const _Float16 *>(sk + 320)[g];
@@ -309,12 +361,14 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
     }
 
     // partial scores -> full score of token u in lanes 2u, 2u+1 (tokens >= nv masked), then the softmax step
-    auto softmax_step = [&](const float (&part)[8], int nv) -> float {
+    auto softmax_step = [&](const float (&part)[8], int nv) {
+        // token 8to + t in row 9to + t: the 16 lanes of each `to` group land in distinct banks
 #pragma unroll
-        for (int v = 0; v < 8; ++v) red[(8 * to + v) * 16 + pq] = part[v];
+        for (int t = 0; t < 8; ++t) red[(9 * to + t) * 16 + pq] = part[t];
         wave_lds_order();
-        const float4 r0 = *reinterpret_cast<const float4 *>(red + 16 * u + 8 * uh);
-        const float4 r1 = *reinterpret_cast<const float4 *>(red + 16 * u + 8 * uh + 4);
+        const float *rr = red + (9 * (u >> 3) + (u & 7)) * 16 + 4 * uh;   // partials 4uh..4uh+3 and 8+4uh..11+4uh
+        const float4 r0 = *reinterpret_cast<const float4 *>(rr);
+        const float4 r1 = *reinterpret_cast<const float4 *>(rr + 8);
         float s = ((r0.x + r0.y) + (r0.z + r0.w)) + ((r1.x + r1.y) + (r1.z + r1.w));
         s = dpp_xadd<DPP_QUAD_1032>(s);
         if (u >= nv) s = NEG_INF;
@@ -330,77 +384,79 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
         lsum += uh ? 0.0f : p;
         pbuf[u] = p;
         wave_lds_order();
-        return p;
     };
 
     const uint8_t *recs = a.tiles + slice * a.max_tiles * REC4;
     const int vq_end = min(v1, a.n_qtiles);
-    int v = v0;
 
-    // ---- quantized tiles
-    for (; v < vq_end; ++v) {
+    // one tile record -> ring slot, scales and zeros first (the coefficients of a tile need only those): key-code
+    // bytes [32 l, 32 l + 16) go to slot + 16 l and [32 l + 16, 32 l + 32) to slot + 1024 + 16 l; value codes,
+    // scales and zeros at their record offsets
+    auto dma_tile = [&](int v, int slot) {
         const uint8_t *rec = recs + (int64_t)v * REC4;
-        const uint4 k03 = reinterpret_cast<const uint4 *>(rec)[2 * l];
-        const uint4 k47 = reinterpret_cast<const uint4 *>(rec)[2 * l + 1];
-        const h8 skh = __builtin_bit_cast(h8, *reinterpret_cast<const uint4 *>(rec + K4_SCALE + 16 * pq));
-        const h8 zkh = __builtin_bit_cast(h8, *reinterpret_cast<const uint4 *>(rec + K4_ZERO + 16 * pq));
-        uint32_t vw[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) vw[j] = reinterpret_cast<const uint32_t *>(rec + V4_CODES)[4 * (16 * j + n) + kg];
-        const int gA = n & 3;
-        const uint4 svr = *reinterpret_cast<const uint4 *>(rec + V4_SCALE + 2 * (32 * gA + 8 * kg));
-        const h8 zvh = __builtin_bit_cast(h8, *reinterpret_cast<const uint4 *>(rec + V4_ZERO + 2 * (32 * gA + 8 * kg)));
+        const uint32_t base = ring_base + slot * REC4;
+        lds_dma16(rec + K4_SCALE + 16 * l, base + K4_SCALE);
+        lds_dma16(rec + 32 * l, base);
+        lds_dma16(rec + 32 * l + 16, base + 1024);
+        lds_dma16(rec + V4_CODES + 16 * l, base + V4_CODES);
+        lds_dma16(rec + V4_CODES + 1024 + 16 * l, base + V4_CODES + 1024);
+    };
+    auto tile_coefficients = [&](int slot) {
+        const unsigned char *tl = smem + RING + slot * REC4;
+        const h2 skp = reinterpret_cast<const h2 *>(tl + K4_SCALE)[l];
+        const h2 zkp = reinterpret_cast<const h2 *>(tl + K4_ZERO)[l];
+        share_coefficients((float)skp[0], (float)skp[1], (float)zkp[0], (float)zkp[1]);
+    };
 
-        // per-tile coefficients of the lane's pairs
-        float a0[4], a1[4], al[4], b0[4], b1[4], be[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float r0 = q0[j], r1 = q1[j];
-            if constexpr (ROPE) {
-                r0 = q0[j] * ec[j] + q1[j] * es[j];
-                r1 = q1[j] * ec[j] - q0[j] * es[j];
-            }
-            const float s0 = (float)skh[2 * j], s1 = (float)skh[2 * j + 1];
-            const float z0 = (float)zkh[2 * j], z1 = (float)zkh[2 * j + 1];
-            a0[j] = r0 * s0;
-            a1[j] = r1 * s1;
-            al[j] = r0 * z0 + r1 * z1;
-            b0[j] = r1 * s0;
-            b1[j] = -(r0 * s1);
-            be[j] = r1 * z0 - r0 * z1;
+    // ---- quantized tiles: two tiles in flight; the coefficients of tile v + 1 are shared at the end of
+    // iteration v (after its scales, the first chunk of its DMA, have landed)
+    int v = v0;
+    if (v < vq_end) {
+        dma_tile(v, 0);
+        if (v + 1 < vq_end) {
+            dma_tile(v + 1, 1);
+            wait_vmcnt<9>();
+        } else {
+            wait_vmcnt<4>();
         }
+        tile_coefficients(0);
         advance(v + 1);
+    }
+    int slot = 0;
+    for (; v < vq_end; ++v) {
+        // issue tile v + 2 into the slot tile v - 1 used (its reads are complete), then wait for tile v (DMA loads
+        // complete in order)
+        const bool ahead2 = v + 2 < vq_end, ahead1 = v + 1 < vq_end;
+        if (ahead2) {
+            dma_tile(v + 2, slot == 0 ? 2 : slot - 1);
+            wait_vmcnt<10>();
+        } else if (ahead1) {
+            wait_vmcnt<5>();
+        } else {
+            wait_vmcnt<0>();
+        }
+        const unsigned char *tl = smem + RING + slot * REC4;
+        slot = (slot == NBUF - 1) ? 0 : slot + 1;
 
+        const uint4 k03 = reinterpret_cast<const uint4 *>(tl)[l];
+        const uint4 k47 = reinterpret_cast<const uint4 *>(tl + 1024)[l];
         const uint32_t kw[8] = {k03.x, k03.y, k03.z, k03.w, k47.x, k47.y, k47.z, k47.w};
         float part[8];
-        if constexpr (ROPE) {
 #pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const uint32_t ev = kw[t] & 0x0F0F0F0Fu, od = (kw[t] >> 4) & 0x0F0F0F0Fu;
-                float sacc = 0.0f;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float x0 = ubyte(ev, j), x1 = ubyte(od, j);
-                    const float P = fmaf(a1[j], x1, fmaf(a0[j], x0, al[j]));
-                    const float Q = fmaf(b1[j], x1, fmaf(b0[j], x0, be[j]));
-                    sacc = fmaf(tc[t][j], P, fmaf(ts[t][j], Q, sacc));
-                }
-                part[t] = sacc;
-            }
-        } else {
-            const float alpha = (al[0] + al[1]) + (al[2] + al[3]);
-#pragma unroll
-            for (int t = 0; t < 8; ++t) {
-                const uint32_t ev = kw[t] & 0x0F0F0F0Fu, od = (kw[t] >> 4) & 0x0F0F0F0Fu;
-                float sacc = alpha;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sacc = fmaf(a1[j], ubyte(od, j), fmaf(a0[j], ubyte(ev, j), sacc));
-                part[t] = sacc;
-            }
+        for (int t = 0; t < 8; ++t) {
+            // even channels in the bytes of ev, odd channels in the bytes of od; two bytes per fp8 convert
+            const uint32_t ev = kw[t] & 0x0F0F0F0Fu, od = (kw[t] >> 4) & 0x0F0F0F0Fu;
+            const f2 e01 = codes2<false>(ev), e23 = codes2<true>(ev), o01 = codes2<false>(od), o23 = codes2<true>(od);
+            const float x0[4] = {e01[0], e01[1], e23[0], e23[1]};
+            const float x1[4] = {o01[0], o01[1], o23[0], o23[1]};
+            part[t] = token_score(t, x0, x1);
         }
         softmax_step(part, 32);
 
         // PV: A rows g = n & 3 over tokens 8kg .. 8kg+7 in the expand8_b4 order (t0 t2 t4 t6 t1 t3 t5 t7)
+        const int gA = n & 3;
+        const uint4 svr = *reinterpret_cast<const uint4 *>(tl + V4_SCALE + 2 * (32 * gA + 8 * kg));
+        const h8 zvh = __builtin_bit_cast(h8, *reinterpret_cast<const uint4 *>(tl + V4_ZERO + 2 * (32 * gA + 8 * kg)));
         const float4 pa = *reinterpret_cast<const float4 *>(pbuf + 8 * kg);
         const float4 pb = *reinterpret_cast<const float4 *>(pbuf + 8 * kg + 4);
         uint32_t ah[4], alo[4];
@@ -412,11 +468,25 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
         const h8 Alo = __builtin_bit_cast(h8, uint4{alo[0], alo[1], alo[2], alo[3]});
         gam += ((pa.x * (float)zvh[0] + pa.y * (float)zvh[1]) + (pa.z * (float)zvh[2] + pa.w * (float)zvh[3])) +
                ((pb.x * (float)zvh[4] + pb.y * (float)zvh[5]) + (pb.z * (float)zvh[6] + pb.w * (float)zvh[7]));
+        const uint32_t *vwl = reinterpret_cast<const uint32_t *>(tl + V4_CODES);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const h8 B = expand8_b4(vw[j]);
-            acc[j] = mfma(Ahi, B, acc[j]);
-            acc[j] = mfma(Alo, B, acc[j]);
+        for (int j0 = 0; j0 < 8; j0 += 4) {   // high parts of four blocks, then their low parts (no back-to-back
+            h8 B[4];                          // dependence on one accumulator)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                B[j] = expand8_b4(vwl[4 * (16 * (j0 + j) + n) + kg]);
+                acc[j0 + j] = mfma(Ahi, B[j], acc[j0 + j]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j0 + j] = mfma(Alo, B[j], acc[j0 + j]);
+        }
+        if (ahead1) {   // coefficients of tile v + 1: its scale chunk is the oldest load still counted
+            if (ahead2)
+                wait_vmcnt<9>();
+            else
+                wait_vmcnt<4>();
+            tile_coefficients(slot);
+            advance(v + 2);
         }
     }
 
@@ -428,34 +498,20 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
         const _Float16 *vr = a.v_res + (slice * a.res_cap + 32 * w) * HD;
         h8 kx[8];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) kx[t] = __builtin_bit_cast(h8, *reinterpret_cast<const uint4 *>(kr + (8 * to + t) * HD + 8 * pq));
-        float r0[4], r1[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            r0[j] = q0[j];
-            r1[j] = q1[j];
-            if constexpr (ROPE) {
-                r0[j] = q0[j] * ec[j] + q1[j] * es[j];
-                r1[j] = q1[j] * ec[j] - q0[j] * es[j];
-            }
-        }
+        for (int t = 0; t < 8; ++t)
+            kx[t] = __builtin_bit_cast(h8, *reinterpret_cast<const uint4 *>(kr + (8 * to + t) * HD + 8 * pq));
+        share_coefficients(1.0f, 1.0f, 0.0f, 0.0f);
         advance(v + 1);
         float part[8];
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            float sacc = 0.0f;
+            float x0[4], x1[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float x0 = (float)kx[t][2 * j], x1 = (float)kx[t][2 * j + 1];
-                const float P = fmaf(r1[j], x1, r0[j] * x0);
-                if constexpr (ROPE) {
-                    const float Q = fmaf(-r0[j], x1, r1[j] * x0);
-                    sacc = fmaf(tc[t][j], P, fmaf(ts[t][j], Q, sacc));
-                } else {
-                    sacc += P;
-                }
+                x0[j] = (float)kx[t][2 * j];
+                x1[j] = (float)kx[t][2 * j + 1];
             }
-            part[t] = sacc;
+            part[t] = token_score(t, x0, x1);
         }
         softmax_step(part, nv);
         for (int t = 0; t < nv; ++t) {   // lane l: channels 2l, 2l+1
@@ -467,8 +523,11 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
     }
 
     // ---- partials of this split: lanes 0..15 hold channel 16j + n of the MFMA sums in acc[j][j / 2]
+    float *obuf = red;
+    float *gbuf = pbuf;
     lsum = rows_sum(row16_sum(lsum));
     gam = rows_sum(gam);   // lane n (any row): value group n & 3
+    wave_lds_order();
     if (l < 16) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) obuf[16 * j + l] = acc[j][j >> 1];

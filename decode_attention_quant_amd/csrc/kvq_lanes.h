@@ -1,5 +1,5 @@
 // Wavefront-level helpers shared by the decode kernels: cross-row swaps and reductions (gfx950 row permutes and
-// DPP), and ordering of LDS exchanges inside a single-wavefront workgroup.
+// DPP), ordering of LDS exchanges inside a single-wavefront workgroup, global-to-LDS DMA loads and explicit waits.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -74,5 +74,24 @@ __device__ __forceinline__ float row16_max(float v) {
 // wavefront). LDS operations are performed in one order per CU and complete in a wavefront's execution order, so a
 // read issued after a write sees it without draining the LDS counter first; only the compiler must not reorder them.
 __device__ __forceinline__ void wave_lds_order() { asm volatile("" : : : "memory"); }
+
+// LDS-DMA load: 16 bytes per lane from `src` into LDS at lds_base + 16 * lane (lds_base goes through M0, which
+// the statement saves and restores). Issued from inline asm so that the compiler's wait insertion, which cannot tell
+// the destination from the other LDS buffers, does not drain the vector-memory counter before every LDS access; the
+// destination's readers wait explicitly (wait_vmcnt), and loads complete in order, so these extra loads can only
+// make the compiler's own counted waits stricter.
+__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkmcnt0() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
 
 }  // namespace kvq
