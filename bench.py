@@ -30,12 +30,13 @@ METRIC_4BIT = "4-bit pre-RoPE KV decode attention with sink: KV tokens/s and ach
 PEAK_GBS = 8000.0          # MI355X HBM3E
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "decode_attention_quant_amd", "csrc")
-# per workload: the committed HBM byte-counter summary of its pass-1 kernel and that kernel's source file
+# per workload: the committed HBM byte-counter summary of its pass-1 kernel and the sources that kernel is built from
+_COMMON = [os.path.join(CSRC, f) for f in ("kvq_kernels.h", "kvq_lanes.h", "kvq_quantizer.h")]
 TRAFFIC = {
     "llama3_8b_gqa_32k": (os.path.join(ROOT, "profiles", "decode_pass1_traffic_llama3_8b_gqa_32k.json"),
-                          os.path.join(CSRC, "kvq_kernels.hip")),
+                          [os.path.join(CSRC, "kvq_kernels.hip")] + _COMMON),
     "kvquant_4bit_16k": (os.path.join(ROOT, "profiles", "decode_b4_pass1_traffic_kvquant_4bit_16k.json"),
-                         os.path.join(CSRC, "kvq_kernels_b4.hip")),
+                         [os.path.join(CSRC, "kvq_kernels_b4.hip")] + _COMMON),
 }
 
 
@@ -62,17 +63,23 @@ def lengths_after(n_quant, n_resid, appended, R):
     return n_quant, n_resid
 
 
+def kernel_source_sha256(workload):
+    """sha256 over the sources of the workload's pass-1 kernel, in order (a changed kernel voids its counters)."""
+    h = hashlib.sha256()
+    for path in TRAFFIC[workload][1]:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def traffic_per_launch(workload):
-    """HBM bytes per decode pass-1 launch from the committed counter summary, if the kernel source still matches."""
+    """HBM bytes per decode pass-1 launch from the committed counter summary, if the kernel sources still match."""
     if workload not in TRAFFIC:
         return None
-    traffic_file, kernel_source = TRAFFIC[workload]
     try:
-        with open(traffic_file) as f:
+        with open(TRAFFIC[workload][0]) as f:
             rec = json.load(f)
-        with open(kernel_source, "rb") as f:
-            sha = hashlib.sha256(f.read()).hexdigest()
-        if rec.get("kernel_source_sha256") == sha:
+        if rec.get("kernel_source_sha256") == kernel_source_sha256(workload):
             return rec.get("traffic_bytes_per_launch")
     except (OSError, ValueError):
         pass
