@@ -41,6 +41,11 @@ class KvqCache(ctypes.Structure):
                 ("sink", ctypes.c_void_p)]
 
 
+class KvqRagged(ctypes.Structure):
+    _fields_ = [("tiles", ctypes.c_void_p), ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
+                ("sink", ctypes.c_void_p), ("lens", ctypes.c_void_p)]
+
+
 class KvqError(RuntimeError):
     def __init__(self, fn: str, status: int):
         super().__init__(f"{fn}: {status_string(status)} (status {status})")
@@ -52,7 +57,7 @@ def _load():
         raise ImportError(f"{_LIB_PATH} is missing: build it with `python -m decode_attention_quant_amd.build`")
     lib = ctypes.CDLL(_LIB_PATH)
     P, I64, I32, F = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_float
-    SP, CP = ctypes.POINTER(KvqShape), ctypes.POINTER(KvqCache)
+    SP, CP, RP = ctypes.POINTER(KvqShape), ctypes.POINTER(KvqCache), ctypes.POINTER(KvqRagged)
     sigs = {
         "kv_quant_keys_per_channel": (ctypes.c_int, [SP, P, I64, I64, I64, I64, I64, P, P]),
         "kv_quant_values_per_token": (ctypes.c_int, [SP, P, I64, I64, I64, I64, I64, P, P]),
@@ -61,6 +66,12 @@ def _load():
         "kv_decode_attention_workspace_bytes": (ctypes.c_size_t, [SP, CP]),
         "kv_decode_attention": (ctypes.c_int, [SP, CP, P, F, P, P, ctypes.c_size_t, P]),
         "kvq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "kv_ragged_prefill": (ctypes.c_int, [SP, RP, I32, P, P, I64, I64, I64, P]),
+        "kv_ragged_append": (ctypes.c_int, [SP, RP, P, P, I64, I64, P]),
+        "kv_ragged_splits": (I32, [SP]),
+        "kv_ragged_workspace_bytes": (ctypes.c_size_t, [SP]),
+        "kv_ragged_decode_attention": (ctypes.c_int, [SP, RP, P, F, P, P, ctypes.c_size_t, P]),
+        "kv_ragged_decode_step": (ctypes.c_int, [SP, RP, P, P, I64, I64, P, F, P, P, ctypes.c_size_t, P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -72,7 +83,8 @@ def _load():
 _lib = _load()
 EXPORTS = ("kv_quant_keys_per_channel", "kv_quant_values_per_token", "kv_append_and_flush",
            "kv_decode_attention_splits", "kv_decode_attention_workspace_bytes", "kv_decode_attention",
-           "kvq_status_string")
+           "kvq_status_string", "kv_ragged_prefill", "kv_ragged_append", "kv_ragged_splits",
+           "kv_ragged_workspace_bytes", "kv_ragged_decode_attention", "kv_ragged_decode_step")
 
 
 def library():
@@ -203,5 +215,110 @@ def kv_decode_attention(cache: KVCache, q: torch.Tensor, out: torch.Tensor | Non
     _check("kv_decode_attention", _lib.kv_decode_attention(
         ctypes.byref(cache._cshape), ctypes.byref(cache.c), ctypes.c_void_p(q.data_ptr()), float(sm_scale),
         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+# ---------------------------------------------------------------------------------------------------- ragged caches
+class RaggedCache:
+    """A 2-bit cache whose sequences sit at their own lengths, held on the device in ``lens`` (int32 [B, 4]:
+    n_quant, n_resid, n_sink, status); every call enqueues fixed arguments, so decode steps can be graph-captured."""
+
+    def __init__(self, shape: Shape, device="cuda"):
+        if shape.bits != 2 or shape.flags:
+            raise ValueError("ragged caches are 2-bit without flags")
+        self.shape = shape
+        self._cshape = shape.c()
+        tiles = shape.max_tokens // TILE_TOKENS
+        self.tiles = torch.zeros((shape.batch, shape.kv_heads, tiles, RECORD_BYTES), dtype=torch.uint8, device=device)
+        self.k_res = torch.zeros((shape.batch, shape.kv_heads, shape.residual_cap, HEAD_DIM), dtype=torch.float16,
+                                 device=device)
+        self.v_res = torch.zeros_like(self.k_res)
+        self.lens = torch.zeros((shape.batch, 4), dtype=torch.int32, device=device)
+        self.c = KvqRagged(self.tiles.data_ptr(), self.k_res.data_ptr(), self.v_res.data_ptr(), None,
+                           self.lens.data_ptr())
+
+    def lengths(self):
+        """Host copy of the per-sequence (n_quant, n_resid, n_sink, status) rows (synchronizes)."""
+        return self.lens.cpu().tolist()
+
+
+def _f16_tokens(t: torch.Tensor, name: str):
+    """One token per (sequence, KV head): [B, Hkv, 128] or [B, Hkv, 1, 128] -> (pointer, stride_b, stride_h)."""
+    if t.dim() == 4:
+        if t.shape[2] != 1:
+            raise ValueError(f"{name}: one token per sequence")
+        t = t[:, :, 0]
+    if t.dtype != torch.float16 or not t.is_cuda or t.dim() != 3 or t.shape[-1] != HEAD_DIM or t.stride(-1) != 1:
+        raise ValueError(f"{name} must be a CUDA float16 tensor [B, Hkv, 128] with unit channel stride")
+    return ctypes.c_void_p(t.data_ptr()), t.stride(0), t.stride(1)
+
+
+def kv_ragged_prefill(cache: RaggedCache, b: int, k: torch.Tensor, v: torch.Tensor, stream=None):
+    """Replace sequence b with the tokens of k, v ([Hkv, T, 128], unit channel stride)."""
+    for t, nm in ((k, "k"), (v, "v")):
+        if t.dtype != torch.float16 or not t.is_cuda or t.dim() != 3 or t.shape[-1] != HEAD_DIM or \
+                (t.numel() and t.stride(-1) != 1):
+            raise ValueError(f"{nm} must be a CUDA float16 tensor [Hkv, T, 128] with unit channel stride")
+    if k.shape != v.shape or (k.numel() and k.stride() != v.stride()):
+        raise ValueError("k and v must have the same shape and strides")
+    n = k.shape[1]
+    sh, st = (k.stride(0), k.stride(1)) if n else (0, 0)   # no token: nothing is read
+    _check("kv_ragged_prefill", _lib.kv_ragged_prefill(
+        ctypes.byref(cache._cshape), ctypes.byref(cache.c), int(b), ctypes.c_void_p(k.data_ptr() if n else None),
+        ctypes.c_void_p(v.data_ptr() if n else None), sh, st, n, _stream(stream)))
+
+
+def kv_ragged_append(cache: RaggedCache, k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
+    pk, sb, sh = _f16_tokens(k_new, "k_new")
+    pv, sb2, sh2 = _f16_tokens(v_new, "v_new")
+    if (sb, sh) != (sb2, sh2):
+        raise ValueError("k_new and v_new must have the same strides")
+    _check("kv_ragged_append", _lib.kv_ragged_append(
+        ctypes.byref(cache._cshape), ctypes.byref(cache.c), pk, pv, sb, sh, _stream(stream)))
+
+
+def kv_ragged_workspace_bytes(cache: RaggedCache) -> int:
+    return int(_lib.kv_ragged_workspace_bytes(ctypes.byref(cache._cshape)))
+
+
+def kv_ragged_splits(cache: RaggedCache) -> int:
+    return int(_lib.kv_ragged_splits(ctypes.byref(cache._cshape)))
+
+
+def _ragged_io(cache, q, out, workspace):
+    s = cache.shape
+    if q.dtype != torch.float16 or not q.is_cuda or tuple(q.shape) != (s.batch, s.q_heads, HEAD_DIM) \
+            or not q.is_contiguous():
+        raise ValueError("q must be a contiguous CUDA float16 tensor [B, Hq, 128]")
+    if out is None:
+        out = torch.empty((s.batch, s.q_heads, HEAD_DIM), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        workspace = torch.empty(max(kv_ragged_workspace_bytes(cache), 16), dtype=torch.uint8, device=q.device)
+    return out, workspace
+
+
+def kv_ragged_decode_attention(cache: RaggedCache, q: torch.Tensor, out: torch.Tensor | None = None,
+                               sm_scale: float = 0.0, workspace: torch.Tensor | None = None, stream=None):
+    out, workspace = _ragged_io(cache, q, out, workspace)
+    _check("kv_ragged_decode_attention", _lib.kv_ragged_decode_attention(
+        ctypes.byref(cache._cshape), ctypes.byref(cache.c), ctypes.c_void_p(q.data_ptr()), float(sm_scale),
+        ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
+        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def kv_ragged_decode_step(cache: RaggedCache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
+                          out: torch.Tensor | None = None, sm_scale: float = 0.0,
+                          workspace: torch.Tensor | None = None, stream=None):
+    """Append one token per sequence, then attend (three launches, no host state: graph-capturable)."""
+    pk, sb, sh = _f16_tokens(k_new, "k_new")
+    pv, sb2, sh2 = _f16_tokens(v_new, "v_new")
+    if (sb, sh) != (sb2, sh2):
+        raise ValueError("k_new and v_new must have the same strides")
+    out, workspace = _ragged_io(cache, q, out, workspace)
+    _check("kv_ragged_decode_step", _lib.kv_ragged_decode_step(
+        ctypes.byref(cache._cshape), ctypes.byref(cache.c), pk, pv, sb, sh, ctypes.c_void_p(q.data_ptr()),
+        float(sm_scale), ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
         workspace.numel() * workspace.element_size(), _stream(stream)))
     return out

@@ -137,6 +137,62 @@ SplitPlan plan(const kvq_shape *s, const kvq_cache *c) {
     return p;
 }
 
+int check_ragged(const kvq_shape *s, const kvq_ragged *c) {
+    int e = check_shape(s);
+    if (e) return e;
+    if (s->bits != 2 || s->flags != 0) return KVQ_E_BITS;
+    if (!c) return KVQ_E_NULL;
+    if (!c->tiles || !c->k_res || !c->v_res || !c->lens) return KVQ_E_NULL;
+    if (!aligned16(c->tiles) || !aligned16(c->k_res) || !aligned16(c->v_res) || !aligned16(c->lens))
+        return KVQ_E_ALIGN;
+    if (s->max_tokens > 0x7fffffffLL - s->residual_cap) return KVQ_E_SHAPE;   // lengths are int32 on the device
+    return KVQ_OK;
+}
+
+// Split plan of a ragged cache: fixed by the capacity (every sequence could be full), so a captured step stays
+// valid as lengths grow; each sequence spreads its own tiles over these splits.
+SplitPlan ragged_plan(const kvq_shape *s) {
+    kvq_cache full{};
+    full.n_quant = s->max_tokens;
+    full.n_resid = s->residual_cap;
+    return plan(s, &full);
+}
+
+kvq::DecodeArgs ragged_args(const kvq_shape *shape, const kvq_ragged *cache, const SplitPlan &p, const void *q,
+                            float sm_scale, float *out, void *workspace, int appended) {
+    kvq::DecodeArgs a;
+    a.tiles = static_cast<const uint8_t *>(cache->tiles);
+    a.k_res = static_cast<const _Float16 *>(cache->k_res);
+    a.v_res = static_cast<const _Float16 *>(cache->v_res);
+    a.q = static_cast<const _Float16 *>(q);
+    a.part_o = static_cast<float *>(workspace);
+    a.part_ml = a.part_o + (size_t)shape->batch * shape->q_heads * p.splits * KVQ_HEAD_DIM;
+    a.out = out;
+    a.max_tiles = shape->max_tokens / KVQ_TILE_TOKENS;
+    a.n_qtiles = 0;
+    a.n_resid = 0;
+    a.res_cap = shape->residual_cap;
+    a.batch = shape->batch;
+    a.kv_heads = shape->kv_heads;
+    a.q_heads = shape->q_heads;
+    a.chunks = p.chunks;
+    a.tiles_per_split = 0;
+    a.sm_log2 = (sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)KVQ_HEAD_DIM)) * 1.4426950408889634f;
+    a.lens = cache->lens;
+    a.appended = appended;
+    return a;
+}
+
+int check_decode_io(const kvq_shape *shape, const SplitPlan &p, const void *q, const float *out, const void *ws,
+                    size_t ws_bytes) {
+    if (!q || !out) return KVQ_E_NULL;
+    if (!aligned16(q) || !aligned16(out)) return KVQ_E_ALIGN;
+    const size_t need = (size_t)shape->batch * shape->q_heads * p.splits * (KVQ_HEAD_DIM + 2) * sizeof(float);
+    if (!ws || ws_bytes < need) return KVQ_E_WORKSPACE;
+    if (!aligned16(ws)) return KVQ_E_ALIGN;
+    return KVQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -295,7 +351,99 @@ int kv_decode_attention(const kvq_shape *shape, const kvq_cache *cache, const vo
     a.chunks = p.chunks;
     a.tiles_per_split = p.tiles_per_split;
     a.sm_log2 = sm_scale * 1.4426950408889634f;
+    a.lens = nullptr;
+    a.appended = 0;
     return launched(kvq::launch_decode(a, p.splits, st));
+}
+
+int kv_ragged_prefill(const kvq_shape *shape, const kvq_ragged *cache, int32_t b, const void *k, const void *v,
+                      int64_t stride_h, int64_t stride_t, int64_t n_tokens, void *stream) {
+    int e = check_ragged(shape, cache);
+    if (e) return e;
+    if (b < 0 || b >= shape->batch || n_tokens < 0) return KVQ_E_SHAPE;
+    const int64_t R = shape->residual_cap;
+    const int64_t flushed = n_tokens > 0 ? R * ((n_tokens - 1) / R) : 0;
+    if (flushed > shape->max_tokens) return KVQ_E_CAPACITY;
+    if (n_tokens > 0) {
+        if ((e = check_src(k, 0, stride_h, stride_t))) return e;
+        if ((e = check_src(v, 0, stride_h, stride_t))) return e;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const int H = shape->kv_heads;
+    const int64_t max_tiles = shape->max_tokens / KVQ_TILE_TOKENS;
+    // sequence b alone, as a batch of one
+    uint8_t *tiles = static_cast<uint8_t *>(cache->tiles) + (int64_t)b * H * max_tiles * KVQ_RECORD_BYTES;
+    _Float16 *kres = static_cast<_Float16 *>(cache->k_res) + (int64_t)b * H * R * KVQ_HEAD_DIM;
+    _Float16 *vres = static_cast<_Float16 *>(cache->v_res) + (int64_t)b * H * R * KVQ_HEAD_DIM;
+    if (n_tokens > 0) {
+        const kvq::TokSrc ks = single_src(k, 0, stride_h, stride_t), vs = single_src(v, 0, stride_h, stride_t);
+        if (flushed > 0) {
+            const int64_t nt = flushed / KVQ_TILE_TOKENS;
+            if ((e = launched(kvq::launch_quant_keys(ks, 0, nt, 1, H, tiles, max_tiles, 0, s)))) return e;
+            if ((e = launched(kvq::launch_quant_values(vs, 0, nt, 1, H, tiles, max_tiles, 0, s)))) return e;
+        }
+        const int64_t n_copy = n_tokens - flushed;
+        if ((e = launched(kvq::launch_copy_rows(ks, flushed, n_copy, 1, H, kres, (int)R, 0, s)))) return e;
+        if ((e = launched(kvq::launch_copy_rows(vs, flushed, n_copy, 1, H, vres, (int)R, 0, s)))) return e;
+    }
+    return launched(kvq::launch_ragged_set(cache->lens, b, (int)flushed, (int)(n_tokens - flushed), 0, s));
+}
+
+int kv_ragged_append(const kvq_shape *shape, const kvq_ragged *cache, const void *k_new, const void *v_new,
+                     int64_t stride_b, int64_t stride_h, void *stream) {
+    int e = check_ragged(shape, cache);
+    if (e) return e;
+    if ((e = check_src(k_new, stride_b, stride_h, 0))) return e;
+    if ((e = check_src(v_new, stride_b, stride_h, 0))) return e;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const kvq::TokSrc kn = single_src(k_new, stride_b, stride_h, 0), vn = single_src(v_new, stride_b, stride_h, 0);
+    if ((e = launched(kvq::launch_ragged_flush_append(
+             kn, vn, shape->batch, shape->kv_heads, static_cast<uint8_t *>(cache->tiles),
+             shape->max_tokens / KVQ_TILE_TOKENS, static_cast<_Float16 *>(cache->k_res),
+             static_cast<_Float16 *>(cache->v_res), shape->residual_cap, cache->lens, s))))
+        return e;
+    return launched(kvq::launch_ragged_commit(cache->lens, shape->batch, shape->residual_cap, s));
+}
+
+int32_t kv_ragged_splits(const kvq_shape *shape) {
+    if (check_shape(shape) || shape->bits != 2 || shape->flags != 0) return 0;
+    return ragged_plan(shape).splits;
+}
+
+size_t kv_ragged_workspace_bytes(const kvq_shape *shape) {
+    const int32_t S = kv_ragged_splits(shape);
+    if (S <= 0) return 0;
+    return (size_t)shape->batch * shape->q_heads * S * (KVQ_HEAD_DIM + 2) * sizeof(float);
+}
+
+int kv_ragged_decode_attention(const kvq_shape *shape, const kvq_ragged *cache, const void *q, float sm_scale,
+                               float *out, void *workspace, size_t workspace_bytes, void *stream) {
+    int e = check_ragged(shape, cache);
+    if (e) return e;
+    const SplitPlan p = ragged_plan(shape);
+    if ((e = check_decode_io(shape, p, q, out, workspace, workspace_bytes))) return e;
+    const kvq::DecodeArgs a = ragged_args(shape, cache, p, q, sm_scale, out, workspace, 0);
+    return launched(kvq::launch_decode_ragged(a, p.splits, cache->lens, 0, static_cast<hipStream_t>(stream)));
+}
+
+int kv_ragged_decode_step(const kvq_shape *shape, const kvq_ragged *cache, const void *k_new, const void *v_new,
+                          int64_t stride_b, int64_t stride_h, const void *q, float sm_scale, float *out,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    int e = check_ragged(shape, cache);
+    if (e) return e;
+    if ((e = check_src(k_new, stride_b, stride_h, 0))) return e;
+    if ((e = check_src(v_new, stride_b, stride_h, 0))) return e;
+    const SplitPlan p = ragged_plan(shape);
+    if ((e = check_decode_io(shape, p, q, out, workspace, workspace_bytes))) return e;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const kvq::TokSrc kn = single_src(k_new, stride_b, stride_h, 0), vn = single_src(v_new, stride_b, stride_h, 0);
+    if ((e = launched(kvq::launch_ragged_flush_append(
+             kn, vn, shape->batch, shape->kv_heads, static_cast<uint8_t *>(cache->tiles),
+             shape->max_tokens / KVQ_TILE_TOKENS, static_cast<_Float16 *>(cache->k_res),
+             static_cast<_Float16 *>(cache->v_res), shape->residual_cap, cache->lens, s))))
+        return e;
+    const kvq::DecodeArgs a = ragged_args(shape, cache, p, q, sm_scale, out, workspace, 1);
+    return launched(kvq::launch_decode_ragged(a, p.splits, cache->lens, 1, s));
 }
 
 }  // extern "C"

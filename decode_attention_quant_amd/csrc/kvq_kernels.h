@@ -34,6 +34,8 @@ struct DecodeArgs {
     int chunks;           // ceil(G / 4): query heads are processed four per wavefront
     int tiles_per_split;  // 32-token tiles (quantized, then residual) per split
     float sm_log2;        // softmax scale * log2(e)
+    const int32_t *lens;  // ragged caches: per-sequence {n_quant, n_resid, n_sink, status}; else null
+    int appended;         // ragged: the lengths predate the append of one token per sequence (decode step)
 };
 
 // 4-bit (KVQuant-style) decode: one wavefront per (batch row, query head, token split). Virtual tiles v of a
@@ -76,5 +78,14 @@ hipError_t launch_quant_values(const TokSrc &src, int64_t t_begin, int64_t n_til
 hipError_t launch_copy_rows(const TokSrc &src, int64_t t_begin, int64_t n, int batch, int kv_heads, _Float16 *res,
                             int res_cap, int dst0, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs &a, int splits, hipStream_t st);
+
+// Ragged caches (per-sequence lengths in device memory, see kvq_kernels.hip).
+hipError_t launch_ragged_flush_append(const TokSrc &knew, const TokSrc &vnew, int batch, int kv_heads,
+                                      uint8_t *tiles, int64_t max_tiles, _Float16 *k_res, _Float16 *v_res,
+                                      int res_cap, int32_t *lens, hipStream_t st);
+hipError_t launch_ragged_commit(int32_t *lens, int batch, int res_cap, hipStream_t st);
+hipError_t launch_ragged_set(int32_t *lens, int b, int nq, int nr, int ns, hipStream_t st);
+// pass 1 over per-sequence lengths, then pass 2 (which commits the appended token's lengths when `commit`)
+hipError_t launch_decode_ragged(const DecodeArgs &a, int splits, int32_t *lens, int commit, hipStream_t st);
 
 }  // namespace kvq

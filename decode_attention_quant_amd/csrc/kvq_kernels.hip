@@ -22,19 +22,17 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 constexpr int D = 128;
 constexpr int REC = 3072;
 
-// Keys: one workgroup of 64 lanes per tile; lane l owns channels 2l and 2l+1 over the tile's 32 tokens.
-__global__ __launch_bounds__(64) void quant_keys_kernel(TokSrc src, int64_t t_begin, int kv_heads, uint8_t *tiles,
-                                                        int64_t max_tiles, int64_t tile0) {
-    __shared__ uint32_t words[256];
+// Keys of one tile (tokens t_first .. t_first + 31 of slice (b, h)) into the record at `rec`: one workgroup of 64
+// lanes; lane l owns channels 2l and 2l+1 over the tile's 32 tokens. `words` is 1 KB of LDS.
+__device__ __forceinline__ void quant_keys_tile(const TokSrc &src, int64_t t_first, int b, int h, uint8_t *rec,
+                                                uint32_t *words) {
     const int l = threadIdx.x;
-    const int64_t tile = blockIdx.x;
-    const int h = blockIdx.y, b = blockIdx.z;
     for (int i = l; i < 256; i += 64) words[i] = 0u;
 
     float x0[32], x1[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-        const _Float16 *row = tok_row(src, b, h, t_begin + tile * 32 + i);
+        const _Float16 *row = tok_row(src, b, h, t_first + i);
         h2 v = *reinterpret_cast<const h2 *>(row + 2 * l);
         x0[i] = (float)v[0];
         x1[i] = (float)v[1];
@@ -62,29 +60,24 @@ __global__ __launch_bounds__(64) void quant_keys_kernel(TokSrc src, int64_t t_be
         atomicOr(&words[w], bits);
     }
     __syncthreads();
-    uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * REC;
     reinterpret_cast<uint4 *>(rec)[l] = reinterpret_cast<const uint4 *>(words)[l];
     h2 sp = {s0, s1}, zp = {z0, z1};
     reinterpret_cast<h2 *>(rec + 2048)[l] = sp;
     reinterpret_cast<h2 *>(rec + 2304)[l] = zp;
 }
 
-// Values: one workgroup of 64 lanes per tile; for each token, lane l owns channels 2l and 2l+1 and the 16 lanes
-// of row g = l / 16 together own channel group g (channels 32g .. 32g+31).
-__global__ __launch_bounds__(64) void quant_values_kernel(TokSrc src, int64_t t_begin, int kv_heads,
-                                                          uint8_t *tiles, int64_t max_tiles, int64_t tile0) {
-    __shared__ uint32_t words[256];
-    __shared__ _Float16 sv[128], zv[128];
+// Values of one tile into the record at `rec`: for each token, lane l owns channels 2l and 2l+1 and the 16 lanes
+// of row g = l / 16 together own channel group g (channels 32g .. 32g+31). `words` 1 KB, `sv`/`zv` 256 B of LDS.
+__device__ __forceinline__ void quant_values_tile(const TokSrc &src, int64_t t_first, int b, int h, uint8_t *rec,
+                                                  uint32_t *words, _Float16 *sv, _Float16 *zv) {
     const int l = threadIdx.x;
-    const int64_t tile = blockIdx.x;
-    const int h = blockIdx.y, b = blockIdx.z;
     for (int i = l; i < 256; i += 64) words[i] = 0u;
     __syncthreads();
 
     const int c = 2 * l, j = c >> 4, cc = c & 15, g = l >> 4;
 #pragma unroll 4
     for (int i = 0; i < 32; ++i) {
-        const _Float16 *row = tok_row(src, b, h, t_begin + tile * 32 + i);
+        const _Float16 *row = tok_row(src, b, h, t_first + i);
         h2 v = *reinterpret_cast<const h2 *>(row + c);
         const float a0 = (float)v[0], a1 = (float)v[1];
         float mn = fminf(a0, a1), mx = fmaxf(a0, a1);
@@ -105,10 +98,28 @@ __global__ __launch_bounds__(64) void quant_values_kernel(TokSrc src, int64_t t_
         if ((l & 15) == 0) { sv[32 * g + i] = s; zv[32 * g + i] = z; }
     }
     __syncthreads();
-    uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * REC;
     reinterpret_cast<uint4 *>(rec + 1024)[l] = reinterpret_cast<const uint4 *>(words)[l];
     reinterpret_cast<uint32_t *>(rec + 2560)[l] = reinterpret_cast<const uint32_t *>(sv)[l];
     reinterpret_cast<uint32_t *>(rec + 2816)[l] = reinterpret_cast<const uint32_t *>(zv)[l];
+}
+
+__global__ __launch_bounds__(64) void quant_keys_kernel(TokSrc src, int64_t t_begin, int kv_heads, uint8_t *tiles,
+                                                        int64_t max_tiles, int64_t tile0) {
+    __shared__ uint32_t words[256];
+    const int64_t tile = blockIdx.x;
+    const int h = blockIdx.y, b = blockIdx.z;
+    uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * REC;
+    quant_keys_tile(src, t_begin + tile * 32, b, h, rec, words);
+}
+
+__global__ __launch_bounds__(64) void quant_values_kernel(TokSrc src, int64_t t_begin, int kv_heads,
+                                                          uint8_t *tiles, int64_t max_tiles, int64_t tile0) {
+    __shared__ uint32_t words[256];
+    __shared__ _Float16 sv[128], zv[128];
+    const int64_t tile = blockIdx.x;
+    const int h = blockIdx.y, b = blockIdx.z;
+    uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * REC;
+    quant_values_tile(src, t_begin + tile * 32, b, h, rec, words, sv, zv);
 }
 
 // ------------------------------------------------------------------------------------------------ window append
@@ -123,6 +134,81 @@ __global__ __launch_bounds__(64) void copy_rows_kernel(TokSrc src, int64_t t_beg
     const _Float16 *row = tok_row(src, b, h, t_begin + r);
     _Float16 *dst = res + ((int64_t)(b * kv_heads + h) * res_cap + dst0 + r) * D;
     reinterpret_cast<uint4 *>(dst)[l & 15] = reinterpret_cast<const uint4 *>(row)[l & 15];
+}
+
+// ------------------------------------------------------------------------------------------------ ragged caches
+// Per-sequence state in device memory, lens[b] = {n_quant, n_resid, n_sink, status}. status 1 (sticky until the
+// sequence is prefilled again) marks a sequence whose flush did not fit the tile capacity: its appends are refused
+// and its lengths stay. Effective state after appending one token: a full window is flushed (R tokens more in the
+// quantized part), then the token opens or extends the window.
+__device__ __forceinline__ void ragged_after_append(const int32_t *ln, int res_cap, int &nq, int &nr) {
+    nq = ln[0];
+    nr = ln[1];
+    if (ln[3] != 0) return;
+    if (nr == res_cap) {
+        nq += nr;
+        nr = 1;
+    } else {
+        nr += 1;
+    }
+}
+
+// One decode-step append for every sequence: workgroup (i, h, b) quantizes window tile i of slice (b, h) into tile
+// n_quant / 32 + i when the window is full (lazy flush), and workgroup (0, h, b) then copies the new token into
+// window row n_resid (row 0 after a flush, once its own tile's reads are done; the other tiles never read row 0).
+__global__ __launch_bounds__(64) void ragged_flush_append_kernel(TokSrc knew, TokSrc vnew, int kv_heads,
+                                                                 uint8_t *tiles, int64_t max_tiles, _Float16 *k_res,
+                                                                 _Float16 *v_res, int res_cap, int32_t *lens) {
+    __shared__ uint32_t words[256];
+    __shared__ _Float16 sv[128], zv[128];
+    const int l = threadIdx.x;
+    const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    int32_t *ln = lens + 4 * b;
+    const int nq = ln[0], nr = ln[1];
+    const bool flush = nr == res_cap;
+    if (ln[3] != 0) return;   // full sequence: appends refused
+    if (flush && (int64_t)nq + res_cap > max_tiles * 32) {   // no room for the flushed tiles: refuse the token
+        if (i == 0 && h == 0 && l == 0) ln[3] = 1;           // (workgroups reading 1 here also return)
+        return;
+    }
+    if (flush) {
+        TokSrc wk;
+        wk.a = k_res; wk.a_sb = (int64_t)kv_heads * res_cap * D; wk.a_sh = (int64_t)res_cap * D; wk.a_st = D;
+        wk.n_a = INT64_MAX;
+        wk.b = wk.a; wk.b_sb = wk.a_sb; wk.b_sh = wk.a_sh; wk.b_st = wk.a_st;
+        TokSrc wv = wk;
+        wv.a = v_res; wv.b = v_res;
+        uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + nq / 32 + i) * REC;
+        quant_keys_tile(wk, 32 * i, b, h, rec, words);
+        quant_values_tile(wv, 32 * i, b, h, rec, words, sv, zv);
+        __syncthreads();
+    }
+    if (i == 0) {
+        const int row = flush ? 0 : nr;
+        const int64_t dst = ((int64_t)(b * kv_heads + h) * res_cap + row) * D;
+        reinterpret_cast<uint32_t *>(k_res + dst)[l] = reinterpret_cast<const uint32_t *>(tok_row(knew, b, h, 0))[l];
+        reinterpret_cast<uint32_t *>(v_res + dst)[l] = reinterpret_cast<const uint32_t *>(tok_row(vnew, b, h, 0))[l];
+    }
+}
+
+// Makes the append of the last ragged_flush_append_kernel visible in the lengths.
+__global__ __launch_bounds__(256) void ragged_commit_kernel(int32_t *lens, int batch, int res_cap) {
+    for (int b = blockIdx.x * blockDim.x + threadIdx.x; b < batch; b += gridDim.x * blockDim.x) {
+        int32_t *ln = lens + 4 * b;
+        int nq, nr;
+        ragged_after_append(ln, res_cap, nq, nr);
+        ln[0] = nq;
+        ln[1] = nr;
+    }
+}
+
+// Sets the lengths of sequence b (after a prefill of that sequence alone).
+__global__ void ragged_set_kernel(int32_t *lens, int b, int nq, int nr, int ns) {
+    int32_t *ln = lens + 4 * b;
+    ln[0] = nq;
+    ln[1] = nr;
+    ln[2] = ns;
+    ln[3] = 0;
 }
 
 // ------------------------------------------------------------------------------------------------ decode pass 1
@@ -195,6 +281,7 @@ constexpr int LDS_ZERO = 3088;       // 256 zero bytes: A-operand rows 4 h + 2, 
 constexpr int LDS_P = 8192;          // fp32 [4 heads][16][2]: p of tokens i and 16 + i
 constexpr int LDS_BYTES = 8704;      // [0, 8192) also holds the fp16 window value tile [32][128]
 
+template <bool RAGGED>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void decode_pass1_kernel(DecodeArgs a) {
     __shared__ __align__(16) unsigned char smem[LDS_BYTES];
     uint32_t *sz_lds = reinterpret_cast<uint32_t *>(smem + LDS_SZ);
@@ -244,10 +331,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    const int n_vt = a.n_qtiles + (a.n_resid + 31) / 32;
-    const int v0 = split * a.tiles_per_split;
-    const int v1 = min(v0 + a.tiles_per_split, n_vt);
-    const int qend = min(v1, a.n_qtiles);
+    int n_qtiles = a.n_qtiles, n_resid = a.n_resid, tiles_per_split = a.tiles_per_split;
+    if constexpr (RAGGED) {   // this sequence's lengths; the splits share its tiles evenly
+        int nq = a.lens[4 * b], nr = a.lens[4 * b + 1];
+        if (a.appended) ragged_after_append(a.lens + 4 * b, a.res_cap, nq, nr);
+        n_qtiles = nq / 32;
+        n_resid = nr;
+        tiles_per_split = (n_qtiles + (n_resid + 31) / 32 + (int)gridDim.y - 1) / (int)gridDim.y;
+    }
+    const int n_vt = n_qtiles + (n_resid + 31) / 32;
+    const int v0 = split * tiles_per_split;
+    const int v1 = min(v0 + tiles_per_split, n_vt);
+    const int qend = min(v1, n_qtiles);
     const uint8_t *base = a.tiles + ((int64_t)b * a.kv_heads + hkv) * a.max_tiles * (int64_t)REC;
 
     // s0, s1: raw score minus mr of head kc for tokens n and 16 + n of the tile (-inf for absent tokens).
@@ -368,7 +463,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     // loads (issued for the next tile once PV has read the current one) and reach the PV B layout through transpose
     // reads; p~ = p (no scales). Window tiles (at most four per split in the normal case) and all-fp16 caches (the
     // fp16 comparator, bandwidth-bound: 16 KB per tile and wavefront) share this loop.
-    const int w0 = max(v0, a.n_qtiles);
+    const int w0 = max(v0, n_qtiles);
     if (w0 < v1) {
         h8 qw[4];
         __syncthreads();
@@ -385,14 +480,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
         // the buffer's capacity, which is a multiple of 32 rows, and zeroed in LDS before use)
         auto v_dma = [&](int v) {
             const unsigned char *src =
-                reinterpret_cast<const unsigned char *>(vres + (int64_t)(v - a.n_qtiles) * 32 * D) + 16 * l;
+                reinterpret_cast<const unsigned char *>(vres + (int64_t)(v - n_qtiles) * 32 * D) + 16 * l;
 #pragma unroll
             for (int i = 0; i < 8; ++i) lds_dma16(src + 1024 * i, vt_base + 1024 * i);
         };
         // key rows of tokens n and 16 + n (clamped to the window's length), channels 32 ks + 8 kc ..
         auto k_load = [&](int v, h8 kr[8]) {
-            const int r0 = (v - a.n_qtiles) * 32;
-            const int nv = min(32, a.n_resid - r0);
+            const int r0 = (v - n_qtiles) * 32;
+            const int nv = min(32, n_resid - r0);
             const _Float16 *k0 = kres + (int64_t)(r0 + min(n, nv - 1)) * D + 8 * kc;
             const _Float16 *k1 = kres + (int64_t)(r0 + min(16 + n, nv - 1)) * D + 8 * kc;
 #pragma unroll
@@ -407,8 +502,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
         const _Float16 *vt1 = vt0 + 16 * 128;
         v_dma(w0);
         for (int v = w0; v < v1; ++v) {
-            const int r0 = (v - a.n_qtiles) * 32;
-            const int nv = min(32, a.n_resid - r0);
+            const int r0 = (v - n_qtiles) * 32;
+            const int nv = min(32, n_resid - r0);
             h8 kr[8];
             k_load(v, kr);
             const f4 ci = {-mr, 0.0f, 0.0f, 0.0f};
@@ -476,10 +571,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
 
 // ------------------------------------------------------------------------------------------------ decode pass 2
 // One wavefront per (batch row, query head): out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// Ragged caches: a sequence with no token gives zeros, and with `commit` the workgroup of each sequence's first query
+// head makes the appended token visible in its lengths (every pass-1 read of them is complete by now).
+template <bool RAGGED>
 __global__ __launch_bounds__(64) void decode_pass2_kernel(const float *part_o, const float *part_ml, float *out,
-                                                          int splits) {
+                                                          int splits, int32_t *lens, int q_heads, int res_cap,
+                                                          int commit) {
     const int64_t bh = blockIdx.x;
     const int l = threadIdx.x;
+    if constexpr (RAGGED) {
+        if (commit && l == 0 && bh % q_heads == 0) {
+            int32_t *ln = lens + 4 * (bh / q_heads);
+            int nq, nr;
+            ragged_after_append(ln, res_cap, nq, nr);
+            ln[0] = nq;
+            ln[1] = nr;
+        }
+    }
     const float *pm = part_ml + bh * splits * 2;
     float M = -__builtin_inff();
     for (int s = 0; s < splits; ++s) M = fmaxf(M, pm[2 * s]);
@@ -491,6 +599,10 @@ __global__ __launch_bounds__(64) void decode_pass2_kernel(const float *part_o, c
         const float2 ov = reinterpret_cast<const float2 *>(part_o + (bh * splits + s) * D)[l];
         o0 += w * ov.x;
         o1 += w * ov.y;
+    }
+    if (RAGGED && !(L > 0.0f)) {
+        reinterpret_cast<float2 *>(out + bh * D)[l] = float2{0.0f, 0.0f};
+        return;
     }
     reinterpret_cast<float2 *>(out + bh * D)[l] = float2{o0 / L, o1 / L};
 }
@@ -518,17 +630,46 @@ hipError_t launch_copy_rows(const TokSrc &src, int64_t t_begin, int64_t n, int b
 }
 
 hipError_t launch_pass2(const float *part_o, const float *part_ml, float *out, int rows, int splits, hipStream_t st) {
-    hipLaunchKernelGGL(decode_pass2_kernel, dim3((unsigned)rows), dim3(64), 0, st, part_o, part_ml, out, splits);
+    hipLaunchKernelGGL(decode_pass2_kernel<false>, dim3((unsigned)rows), dim3(64), 0, st, part_o, part_ml, out, splits,
+                       nullptr, 1, 0, 0);
     return hipGetLastError();
 }
 
 hipError_t launch_decode(const DecodeArgs &a, int splits, hipStream_t st) {
     const int units = a.batch * a.kv_heads * a.chunks;
-    hipLaunchKernelGGL(decode_pass1_kernel, dim3((unsigned)units, (unsigned)splits), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(decode_pass1_kernel<false>, dim3((unsigned)units, (unsigned)splits), dim3(64), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_pass2_kernel, dim3((unsigned)(a.batch * a.q_heads)), dim3(64), 0, st, a.part_o,
-                       a.part_ml, a.out, splits);
+    return launch_pass2(a.part_o, a.part_ml, a.out, a.batch * a.q_heads, splits, st);
+}
+
+hipError_t launch_decode_ragged(const DecodeArgs &a, int splits, int32_t *lens, int commit, hipStream_t st) {
+    const int units = a.batch * a.kv_heads * a.chunks;
+    hipLaunchKernelGGL(decode_pass1_kernel<true>, dim3((unsigned)units, (unsigned)splits), dim3(64), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_pass2_kernel<true>, dim3((unsigned)(a.batch * a.q_heads)), dim3(64), 0, st, a.part_o,
+                       a.part_ml, a.out, splits, lens, a.q_heads, a.res_cap, commit);
+    return hipGetLastError();
+}
+
+hipError_t launch_ragged_flush_append(const TokSrc &knew, const TokSrc &vnew, int batch, int kv_heads,
+                                      uint8_t *tiles, int64_t max_tiles, _Float16 *k_res, _Float16 *v_res,
+                                      int res_cap, int32_t *lens, hipStream_t st) {
+    dim3 grid((unsigned)(res_cap / 32), (unsigned)kv_heads, (unsigned)batch);
+    hipLaunchKernelGGL(ragged_flush_append_kernel, grid, dim3(64), 0, st, knew, vnew, kv_heads, tiles, max_tiles,
+                       k_res, v_res, res_cap, lens);
+    return hipGetLastError();
+}
+
+hipError_t launch_ragged_commit(int32_t *lens, int batch, int res_cap, hipStream_t st) {
+    hipLaunchKernelGGL(ragged_commit_kernel, dim3((unsigned)((batch + 255) / 256)), dim3(256), 0, st, lens, batch,
+                       res_cap);
+    return hipGetLastError();
+}
+
+hipError_t launch_ragged_set(int32_t *lens, int b, int nq, int nr, int ns, hipStream_t st) {
+    hipLaunchKernelGGL(ragged_set_kernel, dim3(1), dim3(1), 0, st, lens, b, nq, nr, ns);
     return hipGetLastError();
 }
 

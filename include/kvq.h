@@ -212,6 +212,69 @@ KVQ_API size_t kv_decode_attention_workspace_bytes(const kvq_shape *shape, const
 KVQ_API int kv_decode_attention(const kvq_shape *shape, const kvq_cache *cache, const void *q, float sm_scale, float *out,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Ragged caches: every sequence (batch row) at its own length, the lengths held in device memory, so a whole
+ * decode step is enqueued with fixed arguments and can be captured once in a HIP graph and replayed (no host state
+ * changes between steps). Serving batches hold sequences at different positions; the pages' per-sequence cache
+ * (KIVI page, paragraph on the recent-token window) is applied to each sequence on its own. 2-bit caches only
+ * (bits = 2, flags = 0; otherwise KVQ_E_BITS).
+ *   tiles, k_res, v_res: as in kvq_cache; sink: unused (may be NULL).
+ *   lens: device int32 [B][4], 16-byte aligned: {n_quant, n_resid, n_sink (0), status} of sequence b. A new cache
+ *     has all zeros. status 1 marks a sequence whose flush did not fit max_tokens: its appends are refused from then
+ *     on and its lengths stay, until it is prefilled again.
+ * Calls on one ragged cache must be issued on one stream, in order.
+ */
+typedef struct kvq_ragged {
+    void *tiles;
+    void *k_res;
+    void *v_res;
+    void *sink;
+    int32_t *lens;
+} kvq_ragged;
+
+/*
+ * Replaces sequence b's contents with n_tokens tokens (n_tokens >= 0; 0 empties it): k, v fp16 [Hkv][n_tokens][128]
+ * with element strides stride_h, stride_t (16-byte aligned rows). Same state as n_tokens single appends to an empty
+ * sequence (KIVI page, paragraph on the recent-token window); writes lens[b] = {flushed, n_tokens - flushed, 0, 0}.
+ * Other sequences are untouched.
+ * Errors: KVQ_E_NULL, KVQ_E_SHAPE (b outside [0, B), n_tokens < 0), KVQ_E_BITS, KVQ_E_ALIGN, KVQ_E_CAPACITY
+ *   (flushed tokens > max_tokens), KVQ_E_LAUNCH.
+ */
+KVQ_API int kv_ragged_prefill(const kvq_shape *shape, const kvq_ragged *cache, int32_t b, const void *k,
+                              const void *v, int64_t stride_h, int64_t stride_t, int64_t n_tokens, void *stream);
+
+/*
+ * Appends one token to every sequence: k_new, v_new fp16 [B][Hkv][128] with element strides stride_b, stride_h.
+ * Per sequence on the device: a full window is first quantized into R/32 tiles (lazy flush), then the token is
+ * stored; equals kv_append_and_flush with one token applied to each sequence at its own length.
+ * Errors: KVQ_E_NULL, KVQ_E_SHAPE, KVQ_E_BITS, KVQ_E_ALIGN, KVQ_E_LAUNCH.
+ */
+KVQ_API int kv_ragged_append(const kvq_shape *shape, const kvq_ragged *cache, const void *k_new, const void *v_new,
+                             int64_t stride_b, int64_t stride_h, void *stream);
+
+/* Splits and workspace of the ragged decode calls: fixed by the capacity (max_tokens + R per sequence), so one
+ * workspace serves every step; workspace = B * q_heads * splits * (128 + 2) * 4 bytes. 0 on invalid arguments. */
+KVQ_API int32_t kv_ragged_splits(const kvq_shape *shape);
+KVQ_API size_t kv_ragged_workspace_bytes(const kvq_shape *shape);
+
+/*
+ * Decode attention of one query per (sequence, query head) over that sequence's tokens (same definition and
+ * arguments as kv_decode_attention). A sequence that holds no token gets zeros.
+ * Errors: KVQ_E_NULL, KVQ_E_SHAPE, KVQ_E_BITS, KVQ_E_ALIGN, KVQ_E_WORKSPACE, KVQ_E_LAUNCH.
+ */
+KVQ_API int kv_ragged_decode_attention(const kvq_shape *shape, const kvq_ragged *cache, const void *q,
+                                       float sm_scale, float *out, void *workspace, size_t workspace_bytes,
+                                       void *stream);
+
+/*
+ * One decode step: kv_ragged_append(k_new, v_new) then kv_ragged_decode_attention(q), in three launches (flush and
+ * append, pass 1 over the lengths after the append, pass 2 which also commits the new lengths).
+ * Errors: as kv_ragged_append and kv_ragged_decode_attention.
+ */
+KVQ_API int kv_ragged_decode_step(const kvq_shape *shape, const kvq_ragged *cache, const void *k_new,
+                                  const void *v_new, int64_t stride_b, int64_t stride_h, const void *q,
+                                  float sm_scale, float *out, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Human-readable name of a status code (static string, never NULL). */
 KVQ_API const char *kvq_status_string(int status);
 

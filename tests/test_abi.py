@@ -198,3 +198,43 @@ def test_four_bit_splits_cover_every_query_head(kvq):
     n_vt = 16256 // 32 + 4
     tps = -(-n_vt // S)
     assert S >= 1 and -(-n_vt // tps) == S and 16 * 32 * S <= 4096
+
+
+def _ragged(kvq, tiles=FAKE, k_res=FAKE + 4096, v_res=FAKE + 8192, lens=FAKE + 12288):
+    return kvq.KvqRagged(tiles, k_res, v_res, None, lens)
+
+
+def test_ragged_validation(kvq):
+    """Ragged calls reject bad arguments before launching: 2-bit without flags only, device lengths required and
+    16-byte aligned, b inside the batch, flushed prefill tokens within max_tokens, a large enough workspace."""
+    lib = kvq.library()
+    s = _shape(kvq)
+    r = _ragged(kvq)
+    pre = lambda sh, c, b, n: lib.kv_ragged_prefill(ctypes.byref(sh), ctypes.byref(c), b, FAKE, FAKE, 0, 128, n, None)
+    assert pre(_shape(kvq, bits=4), r, 0, 1) == kvq.E_BITS
+    assert pre(s, _ragged(kvq, lens=0), 0, 1) == kvq.E_NULL
+    assert pre(s, _ragged(kvq, lens=FAKE + 12292), 0, 1) == kvq.E_ALIGN
+    assert pre(s, r, 2, 1) == kvq.E_SHAPE and pre(s, r, -1, 1) == kvq.E_SHAPE and pre(s, r, 0, -1) == kvq.E_SHAPE
+    assert pre(s, r, 0, 1024 + 129) == kvq.E_CAPACITY          # 1152 tokens would be flushed, 1024 fit
+    assert lib.kv_ragged_prefill(ctypes.byref(s), ctypes.byref(r), 0, None, FAKE, 0, 128, 5, None) == kvq.E_NULL
+    ap = lambda c, kn: lib.kv_ragged_append(ctypes.byref(s), ctypes.byref(c), kn, FAKE, 256, 128, None)
+    assert ap(r, None) == kvq.E_NULL and ap(r, FAKE + 2) == kvq.E_ALIGN
+    S = lib.kv_ragged_splits(ctypes.byref(s))
+    need = lib.kv_ragged_workspace_bytes(ctypes.byref(s))
+    assert S >= 1 and need == 2 * 4 * S * 130 * 4
+    dec = lambda ws, nbytes: lib.kv_ragged_decode_attention(ctypes.byref(s), ctypes.byref(r), FAKE, 0.0, FAKE, ws,
+                                                            nbytes, None)
+    assert dec(FAKE, need - 1) == kvq.E_WORKSPACE and dec(None, need) == kvq.E_WORKSPACE
+    step = lib.kv_ragged_decode_step(ctypes.byref(s), ctypes.byref(r), FAKE, FAKE, 256, 128, FAKE, 0.0, FAKE, FAKE,
+                                     need - 1, None)
+    assert step == kvq.E_WORKSPACE
+    assert lib.kv_ragged_splits(ctypes.byref(_shape(kvq, bits=4))) == 0
+
+
+def test_ragged_splits_follow_capacity(kvq):
+    """The ragged split count is the uniform plan of a full cache (max_tokens quantized + R window), whatever the
+    lengths: one workspace and one captured step serve every length."""
+    lib = kvq.library()
+    s = _shape(kvq, batch=3, kv_heads=2, q_heads=8, max_tokens=1024)
+    full = _cache(kvq, 1024, 128)
+    assert lib.kv_ragged_splits(ctypes.byref(s)) == lib.kv_decode_attention_splits(ctypes.byref(s), ctypes.byref(full))
