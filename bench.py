@@ -14,6 +14,11 @@ workload (cpu_baseline). Progress goes to stderr.
 
 `--workload kvquant_4bit_16k` measures the 4-bit KVQuant-style variant the same way (batch 16, 32 heads, 16K
 context, keys cached before RoPE and rotated at decode time, token 0 held as an fp16-key sink).
+
+`--step-graph` measures whole decode steps (append + attention) three ways on the same inputs: the host-length
+calls issued eagerly, the ragged-cache step (lengths in device memory, three launches) issued eagerly, and the
+ragged step with all timed steps captured in one HIP graph and replayed once. Default workload for it:
+llama2_7b_stream (batch 8, 32 heads, 4096-token prefill), whose steps are short enough for launch costs to show.
 """
 from __future__ import annotations
 
@@ -157,6 +162,103 @@ def fp16_comparator(kvq, w, Kd, Vd, q, context, call_us_2bit, calls):
             "note": "same library and kernel over a window as large as the context (no quantized tiles)"}
 
 
+def step_graph(args, kvq, kdev, kvsynth, torch):
+    """Decode-step time (append + attention) on one workload: host-length API eager, ragged step eager, ragged step
+    captured in one graph of all timed steps. Prints one JSON line."""
+    w = kvsynth.WORKLOADS[args.workload]
+    if w.bits != 2:
+        raise SystemExit("--step-graph: ragged caches are 2-bit")
+    W, K, R = args.warmup, args.steps, w.residual
+    P = w.prefill if w.steps >= W + K else w.context - W - K   # prefill, then W warm-up and K timed steps
+    total = P + W + K
+    cap = ((total + 31) // 32) * 32
+    t0 = time.time()
+    Kd = kdev.kv_to_device(w, kvsynth.K_ID, 0, total)
+    Vd = kdev.kv_to_device(w, kvsynth.V_ID, 0, total)
+    Q = kdev.queries_to_device(w, range(1, W + K + 1))
+    log(f"[step-graph] {w.name}: prefill {P}, {W} warm-up + {K} timed steps; data in {time.time() - t0:.1f}s")
+    shape = kvq.Shape(w.batch, w.kv_heads, w.q_heads, residual_cap=R, max_tokens=cap)
+    out = torch.empty((w.batch, w.q_heads, 128), dtype=torch.float32, device="cuda")
+
+    def timed(run_steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        run_steps()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / K   # us per step
+
+    # host-length calls
+    hc = kvq.KVCache(shape)
+    kvq.kv_append_and_flush(hc, Kd[:, :, :P], Vd[:, :, :P])
+    ws_h = torch.empty(max(16, kvq.kv_decode_attention_workspace_bytes(hc) * 2), dtype=torch.uint8, device="cuda")
+
+    def host_step(i):
+        t = P + i
+        kvq.kv_append_and_flush(hc, Kd[:, :, t:t + 1], Vd[:, :, t:t + 1])
+        kvq.kv_decode_attention(hc, Q[i], out=out, workspace=ws_h)
+
+    for i in range(W):
+        host_step(i)
+    us_host = timed(lambda: [host_step(W + j) for j in range(K)])
+    ctx = hc.n_tokens
+
+    # ragged step, eager
+    def ragged_cache():
+        rc = kvq.RaggedCache(shape)
+        for b in range(w.batch):
+            kvq.kv_ragged_prefill(rc, b, Kd[b, :, :P], Vd[b, :, :P])
+        return rc
+
+    rc = ragged_cache()
+    ws_r = torch.empty(kvq.kv_ragged_workspace_bytes(rc), dtype=torch.uint8, device="cuda")
+
+    def ragged_step(c, i, o):
+        t = P + i
+        kvq.kv_ragged_decode_step(c, Kd[:, :, t], Vd[:, :, t], Q[i], out=o, workspace=ws_r)
+
+    for i in range(W):
+        ragged_step(rc, i, out)
+    us_ragged = timed(lambda: [ragged_step(rc, W + j, out) for j in range(K)])
+
+    # ragged steps captured once (every timed step its own inputs and output row), replayed once
+    gc = ragged_cache()
+    outs = torch.empty((K, w.batch, w.q_heads, 128), dtype=torch.float32, device="cuda")
+    for i in range(W):
+        ragged_step(gc, i, outs[0])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for j in range(K):
+            ragged_step(gc, W + j, outs[j])
+    us_graph = timed(graph.replay)
+    # the replayed graph and the eager ragged steps ran the same kernels on the same inputs
+    same = bool(torch.equal(outs[K - 1], out)) and bool(torch.equal(gc.lens, rc.lens))
+    nbytes = algorithmic_bytes(w.batch, w.kv_heads, w.q_heads, hc.n_quant, hc.n_resid)
+    log(f"[step-graph] per step: host API {us_host:.1f} us, ragged eager {us_ragged:.1f} us, ragged graph "
+        f"{us_graph:.1f} us (graph == eager: {same})")
+    res = {
+        "metric": "2-bit decode step (append + attention), per-step time and KV tokens/s",
+        "value": w.batch * ctx / (us_graph * 1e-6),
+        "unit": "KV tokens/s",
+        "n_gpus": 1, "steps": K, "warmup": W, "ms_per_step": us_graph / 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16", "data": "synthetic",
+        "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+                   "prefill": P, "context_last_timed_step": ctx, "bits": 2, "residual": R},
+        "modes_us_per_step": {"host_api_eager": us_host, "ragged_step_eager": us_ragged,
+                              "ragged_step_graph": us_graph},
+        "graph_equals_eager": same,
+        "bytes_last_step": nbytes,
+        "hbm_gb_s_graph_last_step_bytes": nbytes / us_graph / 1e3,
+        "note": "host_api_eager: kv_append_and_flush + kv_decode_attention per step (4 launches, 6 on a flush step); "
+                "ragged_step_*: kv_ragged_decode_step (3 launches); graph: all timed steps captured in one HIP "
+                "graph, replayed once",
+    }
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -168,6 +270,9 @@ def main(argv=None):
     ap.add_argument("--cpu-queries", type=int, default=12)
     ap.add_argument("--no-fp16-comparator", action="store_true")
     ap.add_argument("--fp16-calls", type=int, default=20)
+    ap.add_argument("--step-graph", action="store_true",
+                    help="decode-step time: host API vs ragged step vs ragged step in a HIP graph "
+                         "(default workload llama2_7b_stream)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (5 times), the reference for HBM byte counters")
     args = ap.parse_args(argv)
@@ -194,6 +299,11 @@ def main(argv=None):
     import decode_attention_quant_amd as kvq
     import kvsynth
     from kvsynth import device as kdev
+
+    if args.step_graph:
+        if args.workload == "llama3_8b_gqa_32k" and "--workload" not in (argv or sys.argv):
+            args.workload = "llama2_7b_stream"
+        return step_graph(args, kvq, kdev, kvsynth, torch)
 
     w = kvsynth.WORKLOADS[args.workload]
     W, K, R = args.warmup, args.steps, w.residual

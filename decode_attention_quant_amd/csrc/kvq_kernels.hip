@@ -570,13 +570,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
 }
 
 // ------------------------------------------------------------------------------------------------ decode pass 2
-// One wavefront per (batch row, query head): out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// One wavefront per (batch row, query head): out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s. The splits'
+// (m, l) are read by all lanes at once (lane l takes splits l, l + 64, ...), M and the weighted sum of l are wave
+// reductions, and the weights go through LDS to the lanes that sum the partial outputs (lane l: channels 2l, 2l+1),
+// eight splits per batch of loads. Empty splits carry m = -inf and weight 0.
 // Ragged caches: a sequence with no token gives zeros, and with `commit` the workgroup of each sequence's first query
 // head makes the appended token visible in its lengths (every pass-1 read of them is complete by now).
+constexpr int PASS2_MAX_SPLITS = 1024;
 template <bool RAGGED>
 __global__ __launch_bounds__(64) void decode_pass2_kernel(const float *part_o, const float *part_ml, float *out,
                                                           int splits, int32_t *lens, int q_heads, int res_cap,
                                                           int commit) {
+    __shared__ float wts[PASS2_MAX_SPLITS];
     const int64_t bh = blockIdx.x;
     const int l = threadIdx.x;
     if constexpr (RAGGED) {
@@ -589,20 +594,42 @@ __global__ __launch_bounds__(64) void decode_pass2_kernel(const float *part_o, c
         }
     }
     const float *pm = part_ml + bh * splits * 2;
-    float M = -__builtin_inff();
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, pm[2 * s]);
-    float L = 0.0f, o0 = 0.0f, o1 = 0.0f;
-    for (int s = 0; s < splits; ++s) {
-        const float ms = pm[2 * s];
-        const float w = (ms == -__builtin_inff()) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-        L += w * pm[2 * s + 1];
-        const float2 ov = reinterpret_cast<const float2 *>(part_o + (bh * splits + s) * D)[l];
-        o0 += w * ov.x;
-        o1 += w * ov.y;
+    const float NEG_INF = -__builtin_inff();
+    float M = NEG_INF;
+    for (int sp = l; sp < splits; sp += 64) M = fmaxf(M, pm[2 * sp]);
+    M = rows_max(row16_max(M));
+    float L = 0.0f;
+    for (int sp = l; sp < splits; sp += 64) {
+        const float ms = pm[2 * sp];
+        const float w = (ms == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+        wts[sp] = w;
+        L += w * pm[2 * sp + 1];
     }
+    L = rows_sum(row16_sum(L));
+    __syncthreads();
     if (RAGGED && !(L > 0.0f)) {
         reinterpret_cast<float2 *>(out + bh * D)[l] = float2{0.0f, 0.0f};
         return;
+    }
+    const float2 *po = reinterpret_cast<const float2 *>(part_o + bh * splits * D) + l;
+    float o0 = 0.0f, o1 = 0.0f;
+    int sp = 0;
+    for (; sp + 8 <= splits; sp += 8) {
+        float2 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = po[(sp + k) * (D / 2)];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float w = wts[sp + k];
+            o0 = fmaf(w, v[k].x, o0);
+            o1 = fmaf(w, v[k].y, o1);
+        }
+    }
+    for (; sp < splits; ++sp) {
+        const float2 v = po[sp * (D / 2)];
+        const float w = wts[sp];
+        o0 = fmaf(w, v.x, o0);
+        o1 = fmaf(w, v.y, o1);
     }
     reinterpret_cast<float2 *>(out + bh * D)[l] = float2{o0 / L, o1 / L};
 }
