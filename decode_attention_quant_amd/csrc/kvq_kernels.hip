@@ -27,16 +27,9 @@ constexpr int REC = 3072;
 __device__ __forceinline__ void quant_keys_tile(const TokSrc &src, int64_t t_first, int b, int h, uint8_t *rec,
                                                 uint32_t *words) {
     const int l = threadIdx.x;
-    for (int i = l; i < 256; i += 64) words[i] = 0u;
 
     float x0[32], x1[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const _Float16 *row = tok_row(src, b, h, t_first + i);
-        h2 v = *reinterpret_cast<const h2 *>(row + 2 * l);
-        x0[i] = (float)v[0];
-        x1[i] = (float)v[1];
-    }
+    load_pairs32(src, t_first, b, h, 2 * l, x0, x1);
     float mn0 = x0[0], mx0 = x0[0], mn1 = x1[0], mx1 = x1[0];
 #pragma unroll
     for (int i = 1; i < 32; ++i) {
@@ -47,17 +40,25 @@ __device__ __forceinline__ void quant_keys_tile(const TokSrc &src, int64_t t_fir
     group_params(mn0, mx0, 3.0f, s0, z0);
     group_params(mn1, mx1, 3.0f, s1, z1);
     const float fs0 = (float)s0, fz0 = (float)z0, fs1 = (float)s1, fz1 = (float)z1;
-    __syncthreads();
+    // a constant group (s = 0) gets rs = 0, hence t' = 0 and code 0
+    const float rs0 = fs0 > 0.0f ? __builtin_amdgcn_rcpf(fs0) : 0.0f;
+    const float rs1 = fs1 > 0.0f ? __builtin_amdgcn_rcpf(fs1) : 0.0f;
 
-    // channel c = 2l: ks = c / 32, kc = (c % 32) / 8, e = c % 8 (even, so c + 1 sits in the next nibble)
+    // channel c = 2l: ks = c / 32, kc = (c % 32) / 8, e = c % 8 (even, so c + 1 sits in the next nibble). The 16
+    // codes of a word come from the 8 lanes 32 (ks / 2) + 16 (ks % 2) + 4 kc + 0..3: OR over the lane quad, then with
+    // the other row of the row pair; lane 32 (ks / 2) + 4 kc writes the word.
     const int c = 2 * l, ks = c >> 5, kc = (c & 31) >> 3, e = c & 7;
     const int shift = 4 * e + 2 * (ks & 1);
+    const bool writer = (l & 3) == 0 && (ks & 1) == 0;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
         const int m = i >> 4, n = i & 15;
         const int w = 4 * (n + 16 * kc) + 2 * m + (ks >> 1);
-        uint32_t bits = (code_of(x0[i], fz0, fs0, 3.0f) << shift) | (code_of(x1[i], fz1, fs1, 3.0f) << (shift + 4));
-        atomicOr(&words[w], bits);
+        const uint32_t bits = quad_or((code_fast(x0[i], fz0, fs0, rs0, 3.0f) << shift) |
+                                      (code_fast(x1[i], fz1, fs1, rs1, 3.0f) << (shift + 4)));
+        uint32_t lo, hi;
+        swap16(bits, lo, hi);
+        if (writer) words[w] = lo | hi;
     }
     __syncthreads();
     reinterpret_cast<uint4 *>(rec)[l] = reinterpret_cast<const uint4 *>(words)[l];
@@ -66,36 +67,57 @@ __device__ __forceinline__ void quant_keys_tile(const TokSrc &src, int64_t t_fir
     reinterpret_cast<h2 *>(rec + 2304)[l] = zp;
 }
 
-// Values of one tile into the record at `rec`: for each token, lane l owns channels 2l and 2l+1 and the 16 lanes
-// of row g = l / 16 together own channel group g (channels 32g .. 32g+31). `words` 1 KB, `sv`/`zv` 256 B of LDS.
+// Values of one tile into the record at `rec`: lane l owns channels 2l and 2l+1 of every token, and the 16 lanes of
+// row g = l / 16 together own channel group g (channels 32g .. 32g+31). The min/max of the 128 (token, group)
+// groups are row reductions; each lane then derives the parameters of two groups, shared through LDS.
+// LDS: `words` 1 KB, `sv`/`zv` 256 B each, `gp` 1 KB.
 __device__ __forceinline__ void quant_values_tile(const TokSrc &src, int64_t t_first, int b, int h, uint8_t *rec,
-                                                  uint32_t *words, _Float16 *sv, _Float16 *zv) {
+                                                  uint32_t *words, _Float16 *sv, _Float16 *zv, float *gp) {
     const int l = threadIdx.x;
-    for (int i = l; i < 256; i += 64) words[i] = 0u;
-    __syncthreads();
-
     const int c = 2 * l, j = c >> 4, cc = c & 15, g = l >> 4;
-#pragma unroll 4
-    for (int i = 0; i < 32; ++i) {
-        const _Float16 *row = tok_row(src, b, h, t_first + i);
-        h2 v = *reinterpret_cast<const h2 *>(row + c);
-        const float a0 = (float)v[0], a1 = (float)v[1];
-        float mn = fminf(a0, a1), mx = fmaxf(a0, a1);
+    float x0[32], x1[32];
+    load_pairs32(src, t_first, b, h, c, x0, x1);
+    float *gmn = gp, *gmx = gp + 128;   // [token][group]; gmx then holds the reciprocal scales
 #pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-            mn = fminf(mn, __shfl_xor(mn, off, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, off, 16));
+    for (int i = 0; i < 32; ++i) {
+        const float mn = row16_min(fminf(x0[i], x1[i]));
+        const float mx = row16_max(fmaxf(x0[i], x1[i]));
+        if ((l & 15) == 0) {
+            gmn[4 * i + g] = mn;
+            gmx[4 * i + g] = mx;
         }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {   // groups e = l and l + 64: token e / 4, channel group e % 4
+        const int ge = l + 64 * k, t = ge >> 2, gg = ge & 3;
         _Float16 s, z;
-        group_params(mn, mx, 3.0f, s, z);
-        const float fs = (float)s, fz = (float)z;
+        group_params(gmn[ge], gmx[ge], 3.0f, s, z);
+        sv[32 * gg + t] = s;
+        zv[32 * gg + t] = z;
+        const float fs = (float)s;
+        gmx[ge] = fs > 0.0f ? __builtin_amdgcn_rcpf(fs) : 0.0f;
+    }
+    __syncthreads();
+    // lane l's channels fill words 4 (cc + 16 kc) + j / 2 (channel 2l) and the next-but-three (channel 2l + 1) for
+    // kc = 0..3, built in registers over the tokens; lane l ^ 8 fills the other half of each word
+    uint32_t wv[4][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}, {0u, 0u}};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const float fs = (float)sv[32 * g + i], fz = (float)zv[32 * g + i], rs = gmx[4 * i + g];
         int kc, e;
         if (i < 16) { kc = i >> 2; e = i & 3; } else { kc = (i - 16) >> 2; e = 4 + ((i - 16) & 3); }
-        const int w0 = 4 * (cc + 16 * kc) + (j >> 1);
         const int shift = 4 * e + 2 * (j & 1);
-        atomicOr(&words[w0], code_of(a0, fz, fs, 3.0f) << shift);
-        atomicOr(&words[w0 + 4], code_of(a1, fz, fs, 3.0f) << shift);
-        if ((l & 15) == 0) { sv[32 * g + i] = s; zv[32 * g + i] = z; }
+        wv[kc][0] |= code_fast(x0[i], fz, fs, rs, 3.0f) << shift;
+        wv[kc][1] |= code_fast(x1[i], fz, fs, rs, 3.0f) << shift;
+    }
+#pragma unroll
+    for (int kc = 0; kc < 4; ++kc) {
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const uint32_t word = dpp_xor_or<DPP_ROW_ROR8>(wv[kc][q]);
+            if ((j & 1) == 0) words[4 * (cc + q + 16 * kc) + (j >> 1)] = word;
+        }
     }
     __syncthreads();
     reinterpret_cast<uint4 *>(rec + 1024)[l] = reinterpret_cast<const uint4 *>(words)[l];
@@ -116,10 +138,11 @@ __global__ __launch_bounds__(64) void quant_values_kernel(TokSrc src, int64_t t_
                                                           uint8_t *tiles, int64_t max_tiles, int64_t tile0) {
     __shared__ uint32_t words[256];
     __shared__ _Float16 sv[128], zv[128];
+    __shared__ float gp[256];
     const int64_t tile = blockIdx.x;
     const int h = blockIdx.y, b = blockIdx.z;
     uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * REC;
-    quant_values_tile(src, t_begin + tile * 32, b, h, rec, words, sv, zv);
+    quant_values_tile(src, t_begin + tile * 32, b, h, rec, words, sv, zv, gp);
 }
 
 // ------------------------------------------------------------------------------------------------ window append
@@ -161,6 +184,7 @@ __global__ __launch_bounds__(64) void ragged_flush_append_kernel(TokSrc knew, To
                                                                  _Float16 *v_res, int res_cap, int32_t *lens) {
     __shared__ uint32_t words[256];
     __shared__ _Float16 sv[128], zv[128];
+    __shared__ float gp[256];
     const int l = threadIdx.x;
     const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     int32_t *ln = lens + 4 * b;
@@ -180,7 +204,7 @@ __global__ __launch_bounds__(64) void ragged_flush_append_kernel(TokSrc knew, To
         wv.a = v_res; wv.b = v_res;
         uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + nq / 32 + i) * REC;
         quant_keys_tile(wk, 32 * i, b, h, rec, words);
-        quant_values_tile(wv, 32 * i, b, h, rec, words, sv, zv);
+        quant_values_tile(wv, 32 * i, b, h, rec, words, sv, zv, gp);
         __syncthreads();
     }
     if (i == 0) {

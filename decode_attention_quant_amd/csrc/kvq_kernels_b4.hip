@@ -34,23 +34,16 @@ constexpr float L4 = 15.0f;   // highest 4-bit level
 // ------------------------------------------------------------------------------------------------ quantizers
 // Keys: one workgroup of 64 lanes per tile; lane l owns channels 2l, 2l+1 over the tile's 32 tokens. Key code of
 // token t, channel c sits in word 8 (c/8 + 16 (t/8)) + t%8 at bit 4 (c%8): the two channels of lane l fill byte
-// l%4 of that word, so every byte of the 2 KB code region is written exactly once, by a byte store into LDS.
+// l%4 of that word, so the four lanes of a quad make one word, written once into LDS.
 __global__ __launch_bounds__(64) void quant_keys_b4_kernel(TokSrc src, int64_t t_begin, int kv_heads, uint8_t *tiles,
                                                            int64_t max_tiles, int64_t tile0) {
     __shared__ __align__(16) uint32_t words[512];
-    uint8_t *bytes = reinterpret_cast<uint8_t *>(words);
     const int l = threadIdx.x;
     const int64_t tile = blockIdx.x;
     const int h = blockIdx.y, b = blockIdx.z;
 
     float x0[32], x1[32];
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const _Float16 *row = tok_row(src, b, h, t_begin + tile * 32 + i);
-        const h2 v = *reinterpret_cast<const h2 *>(row + 2 * l);
-        x0[i] = (float)v[0];
-        x1[i] = (float)v[1];
-    }
+    load_pairs32(src, t_begin + tile * 32, b, h, 2 * l, x0, x1);
     float mn0 = x0[0], mx0 = x0[0], mn1 = x1[0], mx1 = x1[0];
 #pragma unroll
     for (int i = 1; i < 32; ++i) {
@@ -61,11 +54,16 @@ __global__ __launch_bounds__(64) void quant_keys_b4_kernel(TokSrc src, int64_t t
     group_params(mn0, mx0, L4, s0, z0);
     group_params(mn1, mx1, L4, s1, z1);
     const float fs0 = (float)s0, fz0 = (float)z0, fs1 = (float)s1, fz1 = (float)z1;
+    const float rs0 = fs0 > 0.0f ? __builtin_amdgcn_rcpf(fs0) : 0.0f;   // s = 0: t' = 0, code 0
+    const float rs1 = fs1 > 0.0f ? __builtin_amdgcn_rcpf(fs1) : 0.0f;
+    // the word of token i and channels 8 (l/4) .. 8 (l/4) + 7 takes one byte from each lane of the quad: OR over
+    // the quad, the quad's first lane writes it
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-        const uint32_t byte = code_of(x0[i], fz0, fs0, L4) | (code_of(x1[i], fz1, fs1, L4) << 4);
+        const uint32_t byte = code_fast(x0[i], fz0, fs0, rs0, L4) | (code_fast(x1[i], fz1, fs1, rs1, L4) << 4);
+        const uint32_t word = quad_or(byte << (8 * (l & 3)));
         const int w = 8 * ((l >> 2) + 16 * (i >> 3)) + (i & 7);
-        bytes[4 * w + (l & 3)] = (uint8_t)byte;
+        if ((l & 3) == 0) words[w] = word;
     }
     __syncthreads();
     uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * REC4;
@@ -78,33 +76,46 @@ __global__ __launch_bounds__(64) void quant_keys_b4_kernel(TokSrc src, int64_t t
 
 // Values: groups are 32 channels of one token; lane l owns channels 2l, 2l+1 (group l/16). Value code of channel c,
 // token t sits in word 4c + t/8 at bit 4 (t%8), so lane l owns words 8l .. 8l+7 whole and builds them in registers.
+// The min/max of the 128 (token, group) groups are row reductions; each lane derives the parameters of two groups,
+// shared through LDS.
 __global__ __launch_bounds__(64) void quant_values_b4_kernel(TokSrc src, int64_t t_begin, int kv_heads,
                                                              uint8_t *tiles, int64_t max_tiles, int64_t tile0) {
     __shared__ __align__(16) _Float16 sv[128], zv[128];
+    __shared__ float gmn[128], gmx[128];
     const int l = threadIdx.x;
     const int64_t tile = blockIdx.x;
     const int h = blockIdx.y, b = blockIdx.z;
     const int g = l >> 4;
+    float x0[32], x1[32];
+    load_pairs32(src, t_begin + tile * 32, b, h, 2 * l, x0, x1);
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const float mn = row16_min(fminf(x0[i], x1[i]));
+        const float mx = row16_max(fmaxf(x0[i], x1[i]));
+        if ((l & 15) == 0) {
+            gmn[4 * i + g] = mn;
+            gmx[4 * i + g] = mx;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {   // groups e = l and l + 64: token e / 4, channel group e % 4
+        const int ge = l + 64 * k, t = ge >> 2, gg = ge & 3;
+        _Float16 s, z;
+        group_params(gmn[ge], gmx[ge], L4, s, z);
+        sv[32 * gg + t] = s;
+        zv[32 * gg + t] = z;
+        const float fs = (float)s;
+        gmx[ge] = fs > 0.0f ? __builtin_amdgcn_rcpf(fs) : 0.0f;   // the reciprocal scale from here on
+    }
+    __syncthreads();
     uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-        const _Float16 *row = tok_row(src, b, h, t_begin + tile * 32 + i);
-        const h2 v = *reinterpret_cast<const h2 *>(row + 2 * l);
-        const float a0 = (float)v[0], a1 = (float)v[1];
-        float mn = fminf(a0, a1), mx = fmaxf(a0, a1);
-#pragma unroll
-        for (int off = 1; off < 16; off <<= 1) {
-            mn = fminf(mn, __shfl_xor(mn, off, 16));
-            mx = fmaxf(mx, __shfl_xor(mx, off, 16));
-        }
-        _Float16 s, z;
-        group_params(mn, mx, L4, s, z);
-        const float fs = (float)s, fz = (float)z;
-        w[i >> 3] |= code_of(a0, fz, fs, L4) << (4 * (i & 7));
-        w[4 + (i >> 3)] |= code_of(a1, fz, fs, L4) << (4 * (i & 7));
-        if ((l & 15) == 0) { sv[32 * g + i] = s; zv[32 * g + i] = z; }
+        const float fs = (float)sv[32 * g + i], fz = (float)zv[32 * g + i], rs = gmx[4 * i + g];
+        w[i >> 3] |= code_fast(x0[i], fz, fs, rs, L4) << (4 * (i & 7));
+        w[4 + (i >> 3)] |= code_fast(x1[i], fz, fs, rs, L4) << (4 * (i & 7));
     }
-    __syncthreads();
     uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * REC4;
     uint4 *dst = reinterpret_cast<uint4 *>(rec + V4_CODES);
     dst[2 * l] = uint4{w[0], w[1], w[2], w[3]};

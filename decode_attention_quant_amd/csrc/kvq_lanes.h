@@ -70,6 +70,28 @@ __device__ __forceinline__ float row16_max(float v) {
     return dpp_xmax<DPP_ROW_MIRROR>(v);
 }
 
+template <int CTRL>
+__device__ __forceinline__ float dpp_xmin(float v) {
+    const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
+    return fminf(v, __builtin_bit_cast(float, s));
+}
+__device__ __forceinline__ float row16_min(float v) {
+    v = dpp_xmin<DPP_QUAD_1032>(v);
+    v = dpp_xmin<DPP_QUAD_2301>(v);
+    v = dpp_xmin<DPP_ROW_HALF_MIRROR>(v);
+    return dpp_xmin<DPP_ROW_MIRROR>(v);
+}
+
+// Bitwise OR with the value of another lane of the same 16-lane row (DPP), and over each lane quad
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_xor_or(uint32_t v) {
+    return v | (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int DPP_ROW_ROR8 = 0x128;   // row_ror:8: lane i reads lane (i + 8) % 16 of its row
+__device__ __forceinline__ uint32_t quad_or(uint32_t v) {
+    return dpp_xor_or<DPP_QUAD_2301>(dpp_xor_or<DPP_QUAD_1032>(v));
+}
+
 // Cross-lane exchange through LDS inside one wavefront (every workgroup of the decode kernel is a single
 // wavefront). LDS operations are performed in one order per CU and complete in a wavefront's execution order, so a
 // read issued after a write sees it without draining the LDS counter first; only the compiler must not reorder them.

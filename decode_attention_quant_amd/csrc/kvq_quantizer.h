@@ -10,6 +10,8 @@
 
 namespace kvq {
 
+typedef _Float16 h2v __attribute__((ext_vector_type(2)));
+
 // ------------------------------------------------------------------------------------------------ token sources
 __device__ __forceinline__ const _Float16 *tok_row(const TokSrc &s, int b, int h, int64_t t) {
     if (t < s.n_a) return s.a + b * s.a_sb + h * s.a_sh + t * s.a_st;
@@ -33,6 +35,54 @@ __device__ __forceinline__ void group_params(float mn, float mx, float levels, _
     if (mn == 0.0f) z = (_Float16)0.0f;
     s_out = s;
     z_out = z;
+}
+
+// Channels c, c + 1 of the tokens t0 .. t0 + 31 of slice (b, h): x0[i], x1[i]. A tile normally lies in one source
+// (one pointer walk); a tile that straddles the two sources selects per row.
+__device__ __forceinline__ void load_pairs32(const TokSrc &s, int64_t t0, int b, int h, int c, float (&x0)[32],
+                                             float (&x1)[32]) {
+    const int64_t lim = s.n_a - t0;   // rows i < lim come from source a
+    if (lim >= 32 || lim <= 0) {
+        const bool in_a = lim >= 32;
+        const _Float16 *p = in_a ? s.a + b * s.a_sb + h * s.a_sh + t0 * s.a_st + c
+                                 : s.b + b * s.b_sb + h * s.b_sh + (t0 - s.n_a) * s.b_st + c;
+        const int64_t st = in_a ? s.a_st : s.b_st;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const h2v v = *reinterpret_cast<const h2v *>(p);
+            x0[i] = (float)v[0];
+            x1[i] = (float)v[1];
+            p += st;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const h2v v = *reinterpret_cast<const h2v *>(tok_row(s, b, h, t0 + i) + c);
+            x0[i] = (float)v[0];
+            x1[i] = (float)v[1];
+        }
+    }
+}
+
+// The level of one element, equal to code_of (the stated rule) for s > 0, with the division replaced by a product
+// with rs ~ 1/s (within 1 ulp): t' = RN32(d * rs) is within 4 * 2^-24 * t' of the correctly rounded quotient t, at
+// most 2^-18 for t <= 16, so rint(t') = rint(t) unless t' lies within 2^-16 of a half-integer, where the correctly
+// rounded division decides.
+// The division sits behind a wavefront vote, so it is a scalar branch taken only when some lane needs it (a lane-level
+// condition lets the compiler compute the division for every element and select).
+__device__ __forceinline__ uint32_t code_fast(float x, float z, float s, float rs, float levels) {
+#pragma clang fp contract(off)
+    const float d = x - z;
+    float t = d * rs;
+    const float f = t - __builtin_floorf(t);
+    const bool near = __builtin_fabsf(f - 0.5f) < 0x1p-16f;
+    if (__builtin_amdgcn_ballot_w64(near) != 0) {
+        const float te = d / s;
+        t = near ? te : t;
+    }
+    float q = __builtin_rintf(t);
+    q = fminf(fmaxf(q, 0.0f), levels);
+    return (uint32_t)q;
 }
 
 __device__ __forceinline__ uint32_t code_of(float x, float z, float s, float levels) {

@@ -86,3 +86,25 @@ def first_mismatch4(a: np.ndarray, b: np.ndarray) -> str:
     field = ["k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"][
         0 if off < 2048 else 1 if off < 4096 else 2 + (off - 4096) // 256]
     return f"{len(idx)} bytes differ; first at {tuple(idx[0])} ({field}): gpu {a[tuple(idx[0])]} oracle {b[tuple(idx[0])]}"
+
+
+def tie_groups(rng, n_groups: int, levels: int) -> np.ndarray:
+    """float16 [n_groups, 32]: groups whose quotients (x - min) / s land exactly on a half level k + 1/2 or one
+    binary16 ulp beside it. The scale is a power of two 2^e and the minimum c a multiple of it, with max - min =
+    levels * 2^e, so the quantizer's s is exactly 2^e (r / L is exact and a binary16 value); every value is exactly
+    representable. Used to exercise the rounding-boundary path of the kernels' quotient."""
+    out = np.empty((n_groups, 32), np.float32)
+    for gi in range(n_groups):
+        e = int(rng.integers(-10, 4))
+        s = 2.0 ** e
+        c = s * int(rng.integers(-6, 7))
+        k = rng.integers(0, levels, 30)
+        x = c + (k + 0.5) * s
+        ulp = np.spacing(np.abs(x).astype(np.float16)).astype(np.float32)
+        x = x + rng.integers(-1, 2, 30) * ulp
+        x = np.clip(x, c, c + levels * s)
+        row = np.concatenate([[c, c + levels * s], x])
+        out[gi] = rng.permutation(row)
+    h = out.astype(np.float16)
+    assert np.array_equal(h.astype(np.float32), out), "tie groups must be exact binary16 values"
+    return h

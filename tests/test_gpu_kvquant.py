@@ -97,13 +97,18 @@ def _family(rng, kind, shape):
     return np.asarray(x).astype(np.float16)
 
 
-@pytest.mark.parametrize("kind", ["normal_outliers", "wide", "tiny", "const_and_zero"])
+@pytest.mark.parametrize("kind", ["normal_outliers", "wide", "tiny", "const_and_zero", "ties"])
 def test_quantize_4bit_entry_points_bit_exact(kvq, kind):
     say(f"[quant4] kind={kind}")
     rng = np.random.default_rng(zlib.crc32(kind.encode()) + 4)
     B, H, T, tile0 = 2, 3, 256, 2
-    k = _family(rng, kind, (B, H, T, 128))
-    v = _family(rng, kind, (B, H, T, 128))
+    if kind == "ties":   # key groups along tokens, value groups along channels, all at or beside half levels
+        k = helpers.tie_groups(rng, B * H * (T // 32) * 128, 15).reshape(B, H, T // 32, 128, 32)
+        k = np.ascontiguousarray(k.transpose(0, 1, 2, 4, 3)).reshape(B, H, T, 128)
+        v = helpers.tie_groups(rng, B * H * T * 4, 15).reshape(B, H, T, 128)
+    else:
+        k = _family(rng, kind, (B, H, T, 128))
+        v = _family(rng, kind, (B, H, T, 128))
     shape = kvq.Shape(B, H, H, max_tokens=T + 32 * tile0 + 64, bits=4)
     tiles = torch.zeros((B, H, shape.max_tokens // 32, 5120), dtype=torch.uint8, device="cuda")
     k_store = _dev(np.ascontiguousarray(k.transpose(0, 2, 1, 3)))

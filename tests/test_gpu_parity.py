@@ -57,13 +57,18 @@ def _family(rng, kind, shape):
     return x.astype(np.float16)
 
 
-@pytest.mark.parametrize("kind", ["normal_outliers", "wide", "tiny", "const_and_zero"])
+@pytest.mark.parametrize("kind", ["normal_outliers", "wide", "tiny", "const_and_zero", "ties"])
 def test_quantize_entry_points_bit_exact(kvq, kind):
     say(f"[quant] kind={kind}")
     rng = np.random.default_rng(zlib.crc32(kind.encode()))
     B, H, T, tile0 = 2, 3, 256, 2
-    k = _family(rng, kind, (B, H, T, 128))
-    v = _family(rng, kind, (B, H, T, 128))
+    if kind == "ties":   # key groups along tokens, value groups along channels, all at or beside half levels
+        k = helpers.tie_groups(rng, B * H * (T // 32) * 128, 3).reshape(B, H, T // 32, 128, 32)
+        k = np.ascontiguousarray(k.transpose(0, 1, 2, 4, 3)).reshape(B, H, T, 128)
+        v = helpers.tie_groups(rng, B * H * T * 4, 3).reshape(B, H, T, 128)
+    else:
+        k = _family(rng, kind, (B, H, T, 128))
+        v = _family(rng, kind, (B, H, T, 128))
     shape = kvq.Shape(B, H, H, max_tokens=T + 32 * tile0 + 64)
     tiles = torch.zeros((B, H, shape.max_tokens // 32, 3072), dtype=torch.uint8, device="cuda")
     # keys through a non-contiguous view ([B, T, H, D] storage), values contiguous
