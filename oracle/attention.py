@@ -15,7 +15,8 @@ here and float32 in the library.
 
 KVQuant variant: with a sink, token 0 is the sink (its float16 key, its value decoded from per-token codes); with
 ``rope_base`` set the cached keys are pre-RoPE and every decoded key is rotated by its absolute position before the
-dot product (see ``rope``): score_t = sigma * sum_c q_c (R(t) K_hat[t])_c.
+dot product (see ``rope``): score_t = sigma * sum_c q_c (R(t) K_hat[t])_c. With dense-and-sparse groups the decoded
+keys and values hold each group's outlier at its index (``oracle.sparse``).
 
 Long caches are processed in token chunks (two passes: the global maximum first, then the exponential sums), so
 a million-token slice never materializes in float64 all at once.
@@ -24,7 +25,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import quant, rope
+from . import quant, rope, sparse as dsq
 from .cache import SliceCache
 
 CHUNK = 65536
@@ -41,7 +42,12 @@ def decoded_range(cache: SliceCache, t0: int, t1: int):
     if ns and t0 == 0 and t1 > 0:      # token 0 is the sink
         vq, vs, vz = cache.v_sink
         K[:, 0] = cache.k_sink.astype(np.float64)
-        V[:, 0] = quant.dequantize_values(vq[:, None], vs[:, None], vz[:, None], g)[:, 0]
+        if cache.sparse:
+            vo, vi = cache.v_sink_out
+            V[:, 0] = dsq.dequantize_values_sparse(vq[:, None], vs[:, None], vz[:, None], vo[:, None], vi[:, None],
+                                                   g)[:, 0]
+        else:
+            V[:, 0] = quant.dequantize_values(vq[:, None], vs[:, None], vz[:, None], g)[:, 0]
     a0, b0 = max(t0, ns), t1            # absolute range after the sink
     if b0 <= a0:
         return K, V
@@ -52,9 +58,16 @@ def decoded_range(cache: SliceCache, t0: int, t1: int):
     if b > a:
         # expand to whole key groups so the per-channel scale of each token is indexed by its group
         ga, gb = a // g, (b + g - 1) // g
-        kh = quant.dequantize_keys(kq[:, ga * g:gb * g], ks[:, ga:gb], kz[:, ga:gb], g)
+        if cache.sparse:
+            ko, ki, vo, vi = cache.outliers()
+            kh = dsq.dequantize_keys_sparse(kq[:, ga * g:gb * g], ks[:, ga:gb], kz[:, ga:gb], ko[:, ga:gb],
+                                            ki[:, ga:gb], g)
+            V[:, off:off + b - a] = dsq.dequantize_values_sparse(vq[:, a:b], vs[:, a:b], vz[:, a:b], vo[:, a:b],
+                                                                 vi[:, a:b], g)
+        else:
+            kh = quant.dequantize_keys(kq[:, ga * g:gb * g], ks[:, ga:gb], kz[:, ga:gb], g)
+            V[:, off:off + b - a] = quant.dequantize_values(vq[:, a:b], vs[:, a:b], vz[:, a:b], g)
         K[:, off:off + b - a] = kh[:, a - ga * g:b - ga * g]
-        V[:, off:off + b - a] = quant.dequantize_values(vq[:, a:b], vs[:, a:b], vz[:, a:b], g)
     a2 = max(a0 - ns, nq)
     if b0 - ns > a2:
         o2 = a2 + ns - t0

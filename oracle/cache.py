@@ -20,6 +20,9 @@ KVQuant variant (``sink=True``; KVQuant page, on the attention sink: the first t
 precision). Reading taken (listed in the design notes): token 0 is held apart as the sink, its key in float16 and
 its value quantized per token like any other value; the grouped and residual parts start at token 1, so key
 groups cover tokens 1..32, 33..64, and so on, and the window logic above applies to the tokens after the sink.
+
+Dense-and-sparse groups (``sparse=True``, ``oracle.sparse``): every flushed group, and the sink's value groups, keep
+their largest-magnitude element apart (value and index) and quantize the rest; ``outliers()`` returns them.
 """
 from __future__ import annotations
 
@@ -27,7 +30,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-from . import quant
+from . import quant, sparse as dsq
 
 
 @dataclass
@@ -51,6 +54,12 @@ class SliceCache:
     sink: bool = False
     k_sink: np.ndarray = None          # float16 [S, D] once the sink holds token 0
     v_sink: tuple = None               # (codes uint8 [S, D], scale float16 [S, D/32], zero float16 [S, D/32])
+    sparse: bool = False               # per-vector dense-and-sparse groups (oracle.sparse)
+    v_sink_out: tuple = None           # sparse: (outlier values float16 [S, D/32], channels uint8 [S, D/32])
+    _ko: list = field(default_factory=list)
+    _ki: list = field(default_factory=list)
+    _vo: list = field(default_factory=list)
+    _vi: list = field(default_factory=list)
 
     def __post_init__(self):
         if self.residual_cap % self.group:
@@ -74,7 +83,12 @@ class SliceCache:
     def _take_sink(self, k_tok: np.ndarray, v_tok: np.ndarray):
         """Token 0 of a sink cache: key kept as float16, value quantized per token."""
         self.k_sink = np.asarray(k_tok, np.float16).copy()
-        vq, vs, vz = quant.quantize_values_per_token(np.asarray(v_tok, np.float16)[:, None, :], self.group, self.bits)
+        v1 = np.asarray(v_tok, np.float16)[:, None, :]
+        if self.sparse:
+            vq, vs, vz, vo, vi = dsq.quantize_values_per_token_sparse(v1, self.group, self.bits)
+            self.v_sink_out = (vo[:, 0], vi[:, 0])
+        else:
+            vq, vs, vz = quant.quantize_values_per_token(v1, self.group, self.bits)
         self.v_sink = (vq[:, 0], vs[:, 0], vz[:, 0])
 
     def quantized(self):
@@ -89,9 +103,26 @@ class SliceCache:
                 setattr(self, name, [np.concatenate(getattr(self, name), axis=1)])
         return self._kq[0], self._ks[0], self._kz[0], self._vq[0], self._vs[0], self._vz[0]
 
+    def outliers(self):
+        """Sparse caches: (key outlier values float16 [S, n_q/32, D], their tokens uint8, value outlier values
+        float16 [S, n_q, D/32], their channels uint8)."""
+        S, D, g = self.slices, self.head_dim, self.group
+        if not self._ko:
+            return (np.zeros((S, 0, D), np.float16), np.zeros((S, 0, D), np.uint8),
+                    np.zeros((S, 0, D // g), np.float16), np.zeros((S, 0, D // g), np.uint8))
+        if len(self._ko) > 1:
+            for name in ("_ko", "_ki", "_vo", "_vi"):
+                setattr(self, name, [np.concatenate(getattr(self, name), axis=1)])
+        return self._ko[0], self._ki[0], self._vo[0], self._vi[0]
+
     def _push_quantized(self, k_tok: np.ndarray, v_tok: np.ndarray):
-        kq, ks, kz = quant.quantize_keys_per_channel(k_tok, self.group, self.bits)
-        vq, vs, vz = quant.quantize_values_per_token(v_tok, self.group, self.bits)
+        if self.sparse:
+            kq, ks, kz, ko, ki = dsq.quantize_keys_per_channel_sparse(k_tok, self.group, self.bits)
+            vq, vs, vz, vo, vi = dsq.quantize_values_per_token_sparse(v_tok, self.group, self.bits)
+            self._ko.append(ko); self._ki.append(ki); self._vo.append(vo); self._vi.append(vi)
+        else:
+            kq, ks, kz = quant.quantize_keys_per_channel(k_tok, self.group, self.bits)
+            vq, vs, vz = quant.quantize_values_per_token(v_tok, self.group, self.bits)
         self._kq.append(kq); self._ks.append(ks); self._kz.append(kz)
         self._vq.append(vq); self._vs.append(vs); self._vz.append(vz)
         self.n_quant += k_tok.shape[1]

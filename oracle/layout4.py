@@ -28,6 +28,15 @@ The sink record (one per slice, 512 bytes) holds token 0 when the first token's 
     bytes 320..327  its value scales s_V[g], g = 0..3 (binary16)
     bytes 328..335  its value zeros z_V[g] (binary16)
     bytes 336..511  zero
+
+With per-vector dense-and-sparse quantization (``oracle.sparse``), each tile record grows to 5888 bytes with a
+section after the metadata, and the sink record keeps its value outliers in its padding:
+
+    bytes 5120..5375  key outlier values   o_K[c],    c = 0..127          (binary16)
+    bytes 5376..5503  key outlier tokens   i_K[c]     (uint8, 0..31, the token within the tile)
+    bytes 5504..5759  value outlier values o_V[g][t]  (binary16, index 32*g + t)
+    bytes 5760..5887  value outlier channels i_V[g][t] (uint8, 0..31, the channel within group g)
+    sink: bytes 336..343 value outlier values o_V[g] (binary16), bytes 344..347 their channels i_V[g] (uint8)
 """
 from __future__ import annotations
 
@@ -40,6 +49,8 @@ K_CODES_OFF, V_CODES_OFF = 0, 2048
 K_SCALE_OFF, K_ZERO_OFF = 4096, 4352
 V_SCALE_OFF, V_ZERO_OFF = 4608, 4864
 SINK_BYTES = 512
+RECORD_BYTES_SPARSE = 5888
+K_OUT_OFF, K_IDX_OFF, V_OUT_OFF, V_IDX_OFF = 5120, 5376, 5504, 5760
 
 
 def key_code_position(t: int, c: int) -> tuple[int, int]:
@@ -100,6 +111,33 @@ def pack_tiles(k_codes, k_scale, k_zero, v_codes, v_scale, v_zero) -> np.ndarray
     return rec
 
 
+def pack_tiles_sparse(k_codes, k_scale, k_zero, v_codes, v_scale, v_zero, k_out, k_idx, v_out, v_idx) -> np.ndarray:
+    """5888-byte records: :func:`pack_tiles` plus the outlier section. Key outliers float16 / uint8 ``[..., 128]``
+    (one per channel), value outliers ``[..., 32, 4]`` (one per token and channel group)."""
+    base = pack_tiles(k_codes, k_scale, k_zero, v_codes, v_scale, v_zero)
+    lead = base.shape[:-1]
+    rec = np.zeros(lead + (RECORD_BYTES_SPARSE,), dtype=np.uint8)
+    rec[..., :RECORD_BYTES] = base
+    rec[..., K_OUT_OFF:K_OUT_OFF + 256] = np.ascontiguousarray(np.broadcast_to(np.asarray(k_out, np.float16), lead + (128,))).view(np.uint8).reshape(lead + (256,))
+    rec[..., K_IDX_OFF:K_IDX_OFF + 128] = np.broadcast_to(np.asarray(k_idx, np.uint8), lead + (128,))
+    vo = np.ascontiguousarray(np.swapaxes(np.asarray(v_out, np.float16), -1, -2))          # [..., 4, 32]
+    rec[..., V_OUT_OFF:V_OUT_OFF + 256] = vo.view(np.uint8).reshape(lead + (256,))
+    rec[..., V_IDX_OFF:V_IDX_OFF + 128] = np.ascontiguousarray(np.swapaxes(np.asarray(v_idx, np.uint8), -1, -2)).reshape(lead + (128,))
+    return rec
+
+
+def unpack_tiles_sparse(rec: np.ndarray):
+    """Inverse of :func:`pack_tiles_sparse`: the six dense fields, then (k_out, k_idx, v_out, v_idx)."""
+    rec = np.ascontiguousarray(rec, dtype=np.uint8)
+    lead = rec.shape[:-1]
+    dense = unpack_tiles(rec[..., :RECORD_BYTES])
+    k_out = rec[..., K_OUT_OFF:K_OUT_OFF + 256].copy().view(np.float16).reshape(lead + (128,))
+    k_idx = rec[..., K_IDX_OFF:K_IDX_OFF + 128].copy()
+    v_out = np.swapaxes(rec[..., V_OUT_OFF:V_OUT_OFF + 256].copy().view(np.float16).reshape(lead + (4, 32)), -1, -2)
+    v_idx = np.swapaxes(rec[..., V_IDX_OFF:V_IDX_OFF + 128].copy().reshape(lead + (4, 32)), -1, -2)
+    return dense + (k_out, k_idx, np.ascontiguousarray(v_out), np.ascontiguousarray(v_idx))
+
+
 def unpack_tiles(rec: np.ndarray):
     """Inverse of :func:`pack_tiles`: (k_codes, k_scale, k_zero, v_codes, v_scale, v_zero)."""
     rec = np.ascontiguousarray(rec, dtype=np.uint8)
@@ -115,9 +153,10 @@ def unpack_tiles(rec: np.ndarray):
     return k_codes, k_scale, k_zero, v_codes, np.ascontiguousarray(v_scale), np.ascontiguousarray(v_zero)
 
 
-def pack_sink(k_sink, v_codes, v_scale, v_zero) -> np.ndarray:
+def pack_sink(k_sink, v_codes, v_scale, v_zero, v_out=None, v_idx=None) -> np.ndarray:
     """Sink records uint8 ``[..., 512]`` from the fp16 key ``[..., 128]``, value codes uint8 ``[..., 128]`` (0..15)
-    and value scale / zero float16 ``[..., 4]``."""
+    and value scale / zero float16 ``[..., 4]``; with dense-and-sparse values also the outlier values float16 and
+    channels uint8 ``[..., 4]``."""
     k_sink = np.asarray(k_sink, np.float16)
     lead = k_sink.shape[:-1]
     rec = np.zeros(lead + (SINK_BYTES,), np.uint8)
@@ -126,6 +165,9 @@ def pack_sink(k_sink, v_codes, v_scale, v_zero) -> np.ndarray:
     rec[..., 256:320] = (vc[..., 0::2] | (vc[..., 1::2] << 4)).astype(np.uint8)
     rec[..., 320:328] = np.ascontiguousarray(np.asarray(v_scale, np.float16)).view(np.uint8).reshape(lead + (8,))
     rec[..., 328:336] = np.ascontiguousarray(np.asarray(v_zero, np.float16)).view(np.uint8).reshape(lead + (8,))
+    if v_out is not None:
+        rec[..., 336:344] = np.ascontiguousarray(np.asarray(v_out, np.float16)).view(np.uint8).reshape(lead + (8,))
+        rec[..., 344:348] = np.asarray(v_idx, np.uint8)
     return rec
 
 
