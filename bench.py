@@ -32,6 +32,8 @@ import time
 
 METRIC = "2-bit KV decode attention: KV tokens/s and achieved HBM GB/s (% of peak)"
 METRIC_4BIT = "4-bit pre-RoPE KV decode attention with sink: KV tokens/s and achieved HBM GB/s (% of peak)"
+METRIC_4BIT_SPARSE = ("4-bit pre-RoPE KV decode attention with sink and dense-and-sparse groups: KV tokens/s and "
+                      "achieved HBM GB/s (% of peak)")
 PEAK_GBS = 8000.0          # MI355X HBM3E
 ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "decode_attention_quant_amd", "csrc")
@@ -42,6 +44,9 @@ TRAFFIC = {
                           [os.path.join(CSRC, "kvq_kernels.hip")] + _COMMON),
     "kvquant_4bit_16k": (os.path.join(ROOT, "profiles", "decode_b4_pass1_traffic_kvquant_4bit_16k.json"),
                          [os.path.join(CSRC, "kvq_kernels_b4.hip")] + _COMMON),
+    "kvquant_4bit_sparse_16k": (os.path.join(ROOT, "profiles",
+                                             "decode_b4_pass1_traffic_kvquant_4bit_sparse_16k.json"),
+                                [os.path.join(CSRC, "kvq_kernels_b4.hip")] + _COMMON),
 }
 
 
@@ -49,13 +54,15 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(batch, kv_heads, q_heads, n_quant, n_resid, head_dim=128, bits=2, n_sink=0):
+def algorithmic_bytes(batch, kv_heads, q_heads, n_quant, n_resid, head_dim=128, bits=2, n_sink=0, sparse=False):
     """Bytes one decode-attention call must move: per quantized token and KV head 96 B at 2 bits (32 B key codes,
-    32 B value codes, 16 B key scale/zero, 16 B value scale/zero) or 160 B at 4 bits (64 + 64 + 16 + 16), per
-    window token 512 B of fp16 K and V, per sink token 336 B (fp16 key, value codes, value scale/zero), the fp16
+    32 B value codes, 16 B key scale/zero, 16 B value scale/zero) or 160 B at 4 bits (64 + 64 + 16 + 16), plus 24 B
+    with dense-and-sparse groups (a tile's 768-byte outlier section over 32 tokens), per window token 512 B of fp16
+    K and V, per sink token 336 B (fp16 key, value codes, value scale/zero; 348 B with the value outliers), the fp16
     query and the fp32 output. Each KV slice counts once, however many query heads read it."""
-    per_q = 96 if bits == 2 else 160
-    return (batch * kv_heads * (n_quant * per_q + n_resid * 2 * head_dim * 2 + n_sink * 336)
+    per_q = 96 if bits == 2 else (184 if sparse else 160)
+    per_sink = 348 if sparse else 336
+    return (batch * kv_heads * (n_quant * per_q + n_resid * 2 * head_dim * 2 + n_sink * per_sink)
             + batch * q_heads * head_dim * 2 + batch * q_heads * head_dim * 4)
 
 
@@ -113,7 +120,7 @@ def cpu_baseline(w, queries, n_slices, context):
     k = np.stack([kvsynth.slice_tokens(w.seed, kvsynth.K_ID, b, h, 0, context, w.head_dim, w.k_outliers,
                                        w.k_factor) for b, h in slices])
     v = np.stack([kvsynth.slice_tokens(w.seed, kvsynth.V_ID, b, h, 0, context, w.head_dim) for b, h in slices])
-    c = oc.SliceCache(len(slices), residual_cap=w.residual, bits=w.bits, sink=w.sink)
+    c = oc.SliceCache(len(slices), residual_cap=w.residual, bits=w.bits, sink=w.sink, sparse=w.sparse)
     oc.append_block(c, k, v)
     del k, v
     dt = 0.0
@@ -309,7 +316,8 @@ def main(argv=None):
     W, K, R = args.warmup, args.steps, w.residual
     P = w.context - W - 1                      # first timed step attends over exactly w.context tokens
     total = P + W + K
-    flags = (kvq.FLAG_SINK if w.sink else 0) | (kvq.FLAG_PRE_ROPE if w.rope_base else 0)
+    flags = ((kvq.FLAG_SINK if w.sink else 0) | (kvq.FLAG_PRE_ROPE if w.rope_base else 0)
+             | (kvq.FLAG_SPARSE if w.sparse else 0))
     shape = kvq.Shape(w.batch, w.kv_heads, w.q_heads, residual_cap=R, max_tokens=((total + 31) // 32) * 32,
                       bits=w.bits, flags=flags, rope_base=w.rope_base or 0.0)
     cache = kvq.KVCache(shape)
@@ -332,7 +340,7 @@ def main(argv=None):
     pe[1].record()
     torch.cuda.synchronize()
     prefill_us = pe[0].elapsed_time(pe[1]) * 1e3
-    rec_bytes = 3072 if w.bits == 2 else 5120
+    rec_bytes = shape.record_bytes
     # prefill traffic: every token's fp16 K and V read once; tiles, window rows (and the sink record) written
     prefill_bytes = (w.batch * w.kv_heads * (P * 512 + cache.n_quant // 32 * rec_bytes + cache.n_resid * 512
                                              + cache.n_sink * 512))
@@ -373,7 +381,7 @@ def main(argv=None):
         contexts.append(n)
         kv_tokens += w.batch * n
         call_bytes.append(algorithmic_bytes(w.batch, w.kv_heads, w.q_heads, cache.n_quant, cache.n_resid,
-                                            bits=w.bits, n_sink=cache.n_sink))
+                                            bits=w.bits, n_sink=cache.n_sink, sparse=w.sparse))
     ev[3 * K + 1].record()
     torch.cuda.synchronize()
     total_ms = ev[0].elapsed_time(ev[3 * K + 1])
@@ -396,7 +404,7 @@ def main(argv=None):
                   "P V on fp16 MFMA (probabilities as fp16 hi+lo), fp32 accumulation")
         kernel = "decode_b4_pass1_kernel + decode_pass2_kernel (one kv_decode_attention call)"
     res = {
-        "metric": METRIC if w.bits == 2 else METRIC_4BIT,
+        "metric": METRIC if w.bits == 2 else (METRIC_4BIT_SPARSE if w.sparse else METRIC_4BIT),
         "value": value,
         "unit": "KV tokens/s",
         "n_gpus": 1,
@@ -411,7 +419,7 @@ def main(argv=None):
         "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
                    "context_first_timed_step": contexts[0], "context_last_timed_step": contexts[-1],
                    "bits": w.bits, "group": w.group, "residual": R, "head_dim": w.head_dim,
-                   "sink": bool(w.sink), "rope_base": w.rope_base},
+                   "sink": bool(w.sink), "rope_base": w.rope_base, "sparse": bool(w.sparse)},
         "hbm_gb_s": achieved,
         "pct_of_peak": 100.0 * achieved / PEAK_GBS,
         "decode_call_us": 1e3 * sum(decode_ms) / K,

@@ -23,9 +23,11 @@ GROUP = 32
 TILE_TOKENS = 32
 RECORD_BYTES = 3072
 RECORD_BYTES_4BIT = 5120
+RECORD_BYTES_4BIT_SPARSE = 5888
 SINK_BYTES = 512
 FLAG_SINK = 1
 FLAG_PRE_ROPE = 2
+FLAG_SPARSE = 4
 
 
 class KvqShape(ctypes.Structure):
@@ -123,12 +125,14 @@ class Shape:
     bits: int = 2
     head_dim: int = HEAD_DIM
     group: int = GROUP
-    flags: int = 0              # FLAG_SINK | FLAG_PRE_ROPE (4-bit only)
+    flags: int = 0              # FLAG_SINK | FLAG_PRE_ROPE | FLAG_SPARSE (4-bit only)
     rope_base: float = 0.0      # rotary base when FLAG_PRE_ROPE is set
 
     @property
     def record_bytes(self) -> int:
-        return RECORD_BYTES_4BIT if self.bits == 4 else RECORD_BYTES
+        if self.bits != 4:
+            return RECORD_BYTES
+        return RECORD_BYTES_4BIT_SPARSE if self.flags & FLAG_SPARSE else RECORD_BYTES_4BIT
 
     def c(self) -> KvqShape:
         return KvqShape(self.batch, self.kv_heads, self.q_heads, self.head_dim, self.bits, self.group,

@@ -37,13 +37,14 @@ int check_shape(const kvq_shape *s) {
         s->residual_cap % KVQ_TILE_TOKENS != 0 || s->max_tokens <= 0 || s->max_tokens % KVQ_TILE_TOKENS != 0 ||
         s->batch > 65535 || s->kv_heads > 65535 || (int64_t)s->batch * s->q_heads > 0x7fffffff)
         return KVQ_E_SHAPE;
-    if ((s->flags & ~(KVQ_FLAG_SINK | KVQ_FLAG_PRE_ROPE)) != 0 || (s->flags != 0 && s->bits != 4))
+    if ((s->flags & ~(KVQ_FLAG_SINK | KVQ_FLAG_PRE_ROPE | KVQ_FLAG_SPARSE)) != 0 || (s->flags != 0 && s->bits != 4))
         return KVQ_E_SHAPE;
     if ((s->flags & KVQ_FLAG_PRE_ROPE) && !finite_above_one(s->rope_base)) return KVQ_E_SHAPE;
     return KVQ_OK;
 }
 
 bool has_sink(const kvq_shape *s) { return (s->flags & KVQ_FLAG_SINK) != 0; }
+bool is_sparse(const kvq_shape *s) { return (s->flags & KVQ_FLAG_SPARSE) != 0; }
 
 int check_cache(const kvq_shape *s, const kvq_cache *c) {
     if (!c) return KVQ_E_NULL;
@@ -83,8 +84,8 @@ hipError_t quant_launch(const kvq_shape *shape, bool keys, const kvq::TokSrc &sr
                         int64_t max_tiles, int64_t tile0, hipStream_t st) {
     const int B = shape->batch, H = shape->kv_heads;
     if (shape->bits == 4)
-        return keys ? kvq::launch_quant_keys_b4(src, 0, nt, B, H, tiles, max_tiles, tile0, st)
-                    : kvq::launch_quant_values_b4(src, 0, nt, B, H, tiles, max_tiles, tile0, st);
+        return keys ? kvq::launch_quant_keys_b4(src, 0, nt, B, H, tiles, max_tiles, tile0, is_sparse(shape), st)
+                    : kvq::launch_quant_values_b4(src, 0, nt, B, H, tiles, max_tiles, tile0, is_sparse(shape), st);
     return keys ? kvq::launch_quant_keys(src, 0, nt, B, H, tiles, max_tiles, tile0, st)
                 : kvq::launch_quant_values(src, 0, nt, B, H, tiles, max_tiles, tile0, st);
 }
@@ -244,7 +245,9 @@ int kv_append_and_flush(const kvq_shape *shape, kvq_cache *cache, const void *k_
     kvq::TokSrc knew = single_src(k_new, stride_b, stride_h, stride_t);
     kvq::TokSrc vnew = single_src(v_new, stride_b, stride_h, stride_t);
     if (take_sink) {
-        if ((e = launched(kvq::launch_sink_b4(knew, vnew, B, H, static_cast<uint8_t *>(cache->sink), s)))) return e;
+        if ((e = launched(kvq::launch_sink_b4(knew, vnew, B, H, static_cast<uint8_t *>(cache->sink), is_sparse(shape),
+                                              s))))
+            return e;
         cache->n_sink = 1;
         if (n_rest == 0) return KVQ_OK;
         knew = single_src(static_cast<const _Float16 *>(k_new) + stride_t, stride_b, stride_h, stride_t);
@@ -329,6 +332,7 @@ int kv_decode_attention(const kvq_shape *shape, const kvq_cache *cache, const vo
         a.tiles_per_split = p.tiles_per_split;
         a.sm_log2 = sm_scale * 1.4426950408889634f;
         a.rope = (shape->flags & KVQ_FLAG_PRE_ROPE) ? 1 : 0;
+        a.sparse = is_sparse(shape) ? 1 : 0;
         a.log2_base = a.rope ? log2(shape->rope_base) : 0.0;
         return launched(kvq::launch_decode_b4(a, out, p.splits, st));
     }

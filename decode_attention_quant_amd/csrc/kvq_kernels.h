@@ -41,7 +41,7 @@ struct DecodeArgs {
 // 4-bit (KVQuant-style) decode: one wavefront per (batch row, query head, token split). Virtual tiles v of a
 // slice: [0, n_sink) the sink token (position 0), then n_qtiles quantized tiles, then the window tiles.
 struct DecodeB4Args {
-    const uint8_t *tiles;   // [B][Hkv][max_tiles][5120]
+    const uint8_t *tiles;   // [B][Hkv][max_tiles][5120, or 5888 with outliers]
     const uint8_t *sink;    // [B][Hkv][512] (read only when n_sink = 1)
     const _Float16 *k_res;
     const _Float16 *v_res;
@@ -59,15 +59,16 @@ struct DecodeB4Args {
     int tiles_per_split;
     float sm_log2;
     int rope;               // keys are cached before RoPE: rotate by the absolute position
+    int sparse;             // dense-and-sparse records (5888 bytes) and sink
     double log2_base;       // log2 of the RoPE base
 };
 
 hipError_t launch_quant_keys_b4(const TokSrc &src, int64_t t_begin, int64_t n_tiles, int batch, int kv_heads,
-                                uint8_t *tiles, int64_t max_tiles, int64_t tile0, hipStream_t st);
+                                uint8_t *tiles, int64_t max_tiles, int64_t tile0, bool sparse, hipStream_t st);
 hipError_t launch_quant_values_b4(const TokSrc &src, int64_t t_begin, int64_t n_tiles, int batch, int kv_heads,
-                                  uint8_t *tiles, int64_t max_tiles, int64_t tile0, hipStream_t st);
+                                  uint8_t *tiles, int64_t max_tiles, int64_t tile0, bool sparse, hipStream_t st);
 hipError_t launch_sink_b4(const TokSrc &ksrc, const TokSrc &vsrc, int batch, int kv_heads, uint8_t *sink,
-                          hipStream_t st);
+                          bool sparse, hipStream_t st);
 hipError_t launch_decode_b4(const DecodeB4Args &a, float *out, int splits, hipStream_t st);
 hipError_t launch_pass2(const float *part_o, const float *part_ml, float *out, int rows, int splits, hipStream_t st);
 

@@ -28,6 +28,31 @@ constexpr int K4_SCALE = 4096, K4_ZERO = 4352;
 constexpr int V4_CODES = 2048, V4_SCALE = 4608, V4_ZERO = 4864;
 constexpr int SINK_REC = 512;
 constexpr float L4 = 15.0f;   // highest 4-bit level
+// dense-and-sparse records: the 5120 bytes above, then the outlier section
+constexpr int REC4S = 5888;
+constexpr int K4_OUT = 5120, K4_IDX = 5376, V4_OUT = 5504, V4_IDX = 5760;
+constexpr int SINK_VOUT = 336, SINK_VIDX = 344;
+
+template <bool SPARSE>
+constexpr int record_bytes() { return SPARSE ? REC4S : REC4; }
+
+// Order key of an element for the outlier choice of a 32-element group: the binary16 magnitude (the binary32 bits
+// of |x| shifted by 13 keep every bit of a binary16 value and its order) above the reversed index, so the largest
+// key is the largest magnitude and, among equal magnitudes, the lowest index.
+__device__ __forceinline__ uint32_t outlier_key(float x, uint32_t idx) {
+    return ((__builtin_bit_cast(uint32_t, __builtin_fabsf(x)) >> 13) << 5) | (31u - idx);
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_xmax_u32(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+    return v > o ? v : o;
+}
+__device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
+    v = dpp_xmax_u32<DPP_QUAD_1032>(v);
+    v = dpp_xmax_u32<DPP_QUAD_2301>(v);
+    v = dpp_xmax_u32<DPP_ROW_HALF_MIRROR>(v);
+    return dpp_xmax_u32<DPP_ROW_MIRROR>(v);
+}
 
 }  // namespace
 
@@ -35,6 +60,10 @@ constexpr float L4 = 15.0f;   // highest 4-bit level
 // Keys: one workgroup of 64 lanes per tile; lane l owns channels 2l, 2l+1 over the tile's 32 tokens. Key code of
 // token t, channel c sits in word 8 (c/8 + 16 (t/8)) + t%8 at bit 4 (c%8): the two channels of lane l fill byte
 // l%4 of that word, so the four lanes of a quad make one word, written once into LDS.
+// SPARSE (dense-and-sparse groups, KVQuant page, list of methods): each channel's token of largest magnitude (the
+// first on ties) is kept apart as its fp16 value and token index; min and max run over the other 31 tokens and the
+// outlier's code is 0.
+template <bool SPARSE>
 __global__ __launch_bounds__(64) void quant_keys_b4_kernel(TokSrc src, int64_t t_begin, int kv_heads, uint8_t *tiles,
                                                            int64_t max_tiles, int64_t tile0) {
     __shared__ __align__(16) uint32_t words[512];
@@ -44,11 +73,31 @@ __global__ __launch_bounds__(64) void quant_keys_b4_kernel(TokSrc src, int64_t t
 
     float x0[32], x1[32];
     load_pairs32(src, t_begin + tile * 32, b, h, 2 * l, x0, x1);
+    int i0 = -1, i1 = -1;   // outlier tokens (SPARSE)
+    float o0 = 0.0f, o1 = 0.0f;
     float mn0 = x0[0], mx0 = x0[0], mn1 = x1[0], mx1 = x1[0];
+    if constexpr (SPARSE) {
+        float b0 = __builtin_fabsf(x0[0]), b1 = __builtin_fabsf(x1[0]);
+        i0 = 0; i1 = 0; o0 = x0[0]; o1 = x1[0];
 #pragma unroll
-    for (int i = 1; i < 32; ++i) {
-        mn0 = fminf(mn0, x0[i]); mx0 = fmaxf(mx0, x0[i]);
-        mn1 = fminf(mn1, x1[i]); mx1 = fmaxf(mx1, x1[i]);
+        for (int i = 1; i < 32; ++i) {
+            const float a0 = __builtin_fabsf(x0[i]), a1 = __builtin_fabsf(x1[i]);
+            if (a0 > b0) { b0 = a0; i0 = i; o0 = x0[i]; }
+            if (a1 > b1) { b1 = a1; i1 = i; o1 = x1[i]; }
+        }
+        const float inf = __builtin_inff();
+        mn0 = inf; mx0 = -inf; mn1 = inf; mx1 = -inf;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            mn0 = fminf(mn0, i == i0 ? inf : x0[i]); mx0 = fmaxf(mx0, i == i0 ? -inf : x0[i]);
+            mn1 = fminf(mn1, i == i1 ? inf : x1[i]); mx1 = fmaxf(mx1, i == i1 ? -inf : x1[i]);
+        }
+    } else {
+#pragma unroll
+        for (int i = 1; i < 32; ++i) {
+            mn0 = fminf(mn0, x0[i]); mx0 = fmaxf(mx0, x0[i]);
+            mn1 = fminf(mn1, x1[i]); mx1 = fmaxf(mx1, x1[i]);
+        }
     }
     _Float16 s0, z0, s1, z1;
     group_params(mn0, mx0, L4, s0, z0);
@@ -60,38 +109,67 @@ __global__ __launch_bounds__(64) void quant_keys_b4_kernel(TokSrc src, int64_t t
     // the quad, the quad's first lane writes it
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-        const uint32_t byte = code_fast(x0[i], fz0, fs0, rs0, L4) | (code_fast(x1[i], fz1, fs1, rs1, L4) << 4);
-        const uint32_t word = quad_or(byte << (8 * (l & 3)));
+        uint32_t c0 = code_fast(x0[i], fz0, fs0, rs0, L4), c1 = code_fast(x1[i], fz1, fs1, rs1, L4);
+        if constexpr (SPARSE) {
+            c0 = i == i0 ? 0u : c0;
+            c1 = i == i1 ? 0u : c1;
+        }
+        const uint32_t word = quad_or((c0 | (c1 << 4)) << (8 * (l & 3)));
         const int w = 8 * ((l >> 2) + 16 * (i >> 3)) + (i & 7);
         if ((l & 3) == 0) words[w] = word;
     }
     __syncthreads();
-    uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * REC4;
+    uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * record_bytes<SPARSE>();
     reinterpret_cast<uint4 *>(rec)[2 * l] = reinterpret_cast<const uint4 *>(words)[2 * l];
     reinterpret_cast<uint4 *>(rec)[2 * l + 1] = reinterpret_cast<const uint4 *>(words)[2 * l + 1];
     const h2 sp = {s0, s1}, zp = {z0, z1};
     reinterpret_cast<h2 *>(rec + K4_SCALE)[l] = sp;
     reinterpret_cast<h2 *>(rec + K4_ZERO)[l] = zp;
+    if constexpr (SPARSE) {
+        const h2 op = {(_Float16)o0, (_Float16)o1};
+        reinterpret_cast<h2 *>(rec + K4_OUT)[l] = op;
+        reinterpret_cast<uint16_t *>(rec + K4_IDX)[l] = (uint16_t)(i0 | (i1 << 8));
+    }
 }
 
 // Values: groups are 32 channels of one token; lane l owns channels 2l, 2l+1 (group l/16). Value code of channel c,
 // token t sits in word 4c + t/8 at bit 4 (t%8), so lane l owns words 8l .. 8l+7 whole and builds them in registers.
 // The min/max of the 128 (token, group) groups are row reductions; each lane derives the parameters of two groups,
-// shared through LDS.
+// shared through LDS. SPARSE: the outlier of each group (largest magnitude, lowest channel on ties) is found first
+// by a row reduction of its order key; its lane stores it, and min/max/codes skip it.
+template <bool SPARSE>
 __global__ __launch_bounds__(64) void quant_values_b4_kernel(TokSrc src, int64_t t_begin, int kv_heads,
                                                              uint8_t *tiles, int64_t max_tiles, int64_t tile0) {
-    __shared__ __align__(16) _Float16 sv[128], zv[128];
+    __shared__ __align__(16) _Float16 sv[128], zv[128], ov[128];   // [g][t]
+    __shared__ __align__(16) uint8_t oi[128];                        // [g][t]
     __shared__ float gmn[128], gmx[128];
     const int l = threadIdx.x;
     const int64_t tile = blockIdx.x;
     const int h = blockIdx.y, b = blockIdx.z;
     const int g = l >> 4;
+    const uint32_t c0 = 2 * (l & 15);   // the lane's first channel within its group
     float x0[32], x1[32];
     load_pairs32(src, t_begin + tile * 32, b, h, 2 * l, x0, x1);
+    uint32_t om0 = 0u, om1 = 0u;   // bit i: the lane's element of token i is its group's outlier
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-        const float mn = row16_min(fminf(x0[i], x1[i]));
-        const float mx = row16_max(fmaxf(x0[i], x1[i]));
+        float lo0 = x0[i], hi0 = x0[i], lo1 = x1[i], hi1 = x1[i];
+        if constexpr (SPARSE) {
+            const uint32_t k0 = outlier_key(x0[i], c0), k1 = outlier_key(x1[i], c0 + 1);
+            const uint32_t w = 31u - (row16_max_u32(k0 > k1 ? k0 : k1) & 31u);
+            const bool is0 = w == c0, is1 = w == c0 + 1;
+            om0 |= (uint32_t)is0 << i;
+            om1 |= (uint32_t)is1 << i;
+            if (is0 || is1) {
+                ov[32 * g + i] = (_Float16)(is0 ? x0[i] : x1[i]);
+                oi[32 * g + i] = (uint8_t)w;
+            }
+            const float inf = __builtin_inff();
+            lo0 = is0 ? inf : lo0; hi0 = is0 ? -inf : hi0;
+            lo1 = is1 ? inf : lo1; hi1 = is1 ? -inf : hi1;
+        }
+        const float mn = row16_min(fminf(lo0, lo1));
+        const float mx = row16_max(fmaxf(hi0, hi1));
         if ((l & 15) == 0) {
             gmn[4 * i + g] = mn;
             gmx[4 * i + g] = mx;
@@ -113,31 +191,53 @@ __global__ __launch_bounds__(64) void quant_values_b4_kernel(TokSrc src, int64_t
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
         const float fs = (float)sv[32 * g + i], fz = (float)zv[32 * g + i], rs = gmx[4 * i + g];
-        w[i >> 3] |= code_fast(x0[i], fz, fs, rs, L4) << (4 * (i & 7));
-        w[4 + (i >> 3)] |= code_fast(x1[i], fz, fs, rs, L4) << (4 * (i & 7));
+        uint32_t q0 = code_fast(x0[i], fz, fs, rs, L4), q1 = code_fast(x1[i], fz, fs, rs, L4);
+        if constexpr (SPARSE) {
+            q0 = (om0 >> i) & 1u ? 0u : q0;
+            q1 = (om1 >> i) & 1u ? 0u : q1;
+        }
+        w[i >> 3] |= q0 << (4 * (i & 7));
+        w[4 + (i >> 3)] |= q1 << (4 * (i & 7));
     }
-    uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * REC4;
+    uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * record_bytes<SPARSE>();
     uint4 *dst = reinterpret_cast<uint4 *>(rec + V4_CODES);
     dst[2 * l] = uint4{w[0], w[1], w[2], w[3]};
     dst[2 * l + 1] = uint4{w[4], w[5], w[6], w[7]};
     reinterpret_cast<uint32_t *>(rec + V4_SCALE)[l] = reinterpret_cast<const uint32_t *>(sv)[l];
     reinterpret_cast<uint32_t *>(rec + V4_ZERO)[l] = reinterpret_cast<const uint32_t *>(zv)[l];
+    if constexpr (SPARSE) {
+        reinterpret_cast<uint32_t *>(rec + V4_OUT)[l] = reinterpret_cast<const uint32_t *>(ov)[l];
+        reinterpret_cast<uint16_t *>(rec + V4_IDX)[l] = reinterpret_cast<const uint16_t *>(oi)[l];
+    }
 }
 
 // Sink record of one slice from token 0 of the sources: the key copied as fp16 into bytes [0, 256), the value
 // quantized per token (4 groups of 32 channels) with codes at byte 256 + c/2 (bit 4 (c%2)), scales at 320 + 2g,
-// zeros at 328 + 2g; bytes [336, 512) zero. One wavefront per slice, lane l owns channels 2l, 2l+1.
+// zeros at 328 + 2g; bytes [336, 512) zero. SPARSE: each value group's outlier value at 336 + 2g and its channel
+// within the group at 344 + g (its code 0); zero from byte 348. One wavefront per slice, lane l owns channels 2l,
+// 2l+1.
+template <bool SPARSE>
 __global__ __launch_bounds__(64) void sink_b4_kernel(TokSrc ksrc, TokSrc vsrc, int kv_heads, uint8_t *sink) {
     const int l = threadIdx.x;
     const int h = blockIdx.x, b = blockIdx.y;
     const int g = l >> 4;
+    const uint32_t c0 = 2 * (l & 15);
     uint8_t *out = sink + (int64_t)(b * kv_heads + h) * SINK_REC;
     const _Float16 *krow = tok_row(ksrc, b, h, 0);
     const _Float16 *vrow = tok_row(vsrc, b, h, 0);
     reinterpret_cast<uint32_t *>(out)[l] = reinterpret_cast<const uint32_t *>(krow)[l];
     const h2 v = *reinterpret_cast<const h2 *>(vrow + 2 * l);
     const float a0 = (float)v[0], a1 = (float)v[1];
-    float mn = fminf(a0, a1), mx = fmaxf(a0, a1);
+    bool is0 = false, is1 = false;
+    uint32_t w = 0u;
+    if constexpr (SPARSE) {
+        const uint32_t k0 = outlier_key(a0, c0), k1 = outlier_key(a1, c0 + 1);
+        w = 31u - (row16_max_u32(k0 > k1 ? k0 : k1) & 31u);
+        is0 = w == c0;
+        is1 = w == c0 + 1;
+    }
+    const float inf = __builtin_inff();
+    float mn = fminf(is0 ? inf : a0, is1 ? inf : a1), mx = fmaxf(is0 ? -inf : a0, is1 ? -inf : a1);
 #pragma unroll
     for (int off = 1; off < 16; off <<= 1) {
         mn = fminf(mn, __shfl_xor(mn, off, 16));
@@ -146,23 +246,56 @@ __global__ __launch_bounds__(64) void sink_b4_kernel(TokSrc ksrc, TokSrc vsrc, i
     _Float16 s, z;
     group_params(mn, mx, L4, s, z);
     const float fs = (float)s, fz = (float)z;
-    out[256 + l] = (uint8_t)(code_of(a0, fz, fs, L4) | (code_of(a1, fz, fs, L4) << 4));
+    const uint32_t q0 = is0 ? 0u : code_of(a0, fz, fs, L4), q1 = is1 ? 0u : code_of(a1, fz, fs, L4);
+    out[256 + l] = (uint8_t)(q0 | (q1 << 4));
     if ((l & 15) == 0) {
         reinterpret_cast<_Float16 *>(out + 320)[g] = s;
         reinterpret_cast<_Float16 *>(out + 328)[g] = z;
     }
-    if (l < 44) reinterpret_cast<uint32_t *>(out + 336)[l] = 0u;
+    if constexpr (SPARSE) {
+        if (is0 || is1) {
+            reinterpret_cast<_Float16 *>(out + SINK_VOUT)[g] = is0 ? v[0] : v[1];
+            out[SINK_VIDX + g] = (uint8_t)w;
+        }
+        if (l < 41) reinterpret_cast<uint32_t *>(out + 348)[l] = 0u;
+    } else {
+        if (l < 44) reinterpret_cast<uint32_t *>(out + 336)[l] = 0u;
+    }
 }
 
 // ------------------------------------------------------------------------------------------------ decode pass 1
 namespace {
 
-// cos and sin of pi * m * thp, with the product reduced modulo 2 in binary64 first (m up to 2^31, so the binary32
-// argument of sincospi keeps its full relative precision)
+// sin(pi x) and cos(pi x) for x = hi + lo (|hi| < 2^21, |lo| small beside the reduced argument), inline and
+// branch-free: hi = n/2 + r with n = rint(2 hi) and |r| <= 1/4 (r exact), y = pi (r + lo), the Taylor series of
+// sin y and cos y to the y^9 and y^10 terms (the next terms are below 2^-28 for |y| <= pi/4), then the quarter turns
+// n mod 4. Absolute error a few units of 2^-24.
+__device__ __forceinline__ void sincospi2(float hi, float lo, float &sn, float &cs) {
+    const float n = __builtin_rintf(2.0f * hi);
+    const float y = (fmaf(n, -0.5f, hi) + lo) * 3.14159265358979323846f;
+    const float y2 = y * y;
+    float ps = fmaf(y2, 2.75573192239858906526e-6f, -1.98412698412698412698e-4f);
+    ps = fmaf(y2, ps, 8.33333333333333333333e-3f);
+    ps = fmaf(y2, ps, -1.66666666666666666667e-1f);
+    const float sy = fmaf(y * y2, ps, y);
+    float pc = fmaf(y2, -2.75573192239858906526e-7f, 2.48015873015873015873e-5f);
+    pc = fmaf(y2, pc, -1.38888888888888888889e-3f);
+    pc = fmaf(y2, pc, 4.16666666666666666667e-2f);
+    pc = fmaf(y2, pc, -0.5f);
+    const float cy = fmaf(y2, pc, 1.0f);
+    const int q = (int)n;
+    const float a = (q & 1) ? cy : sy, b = (q & 1) ? sy : cy;   // sin, cos of y + (q & 1) pi/2, up to sign
+    sn = (q & 2) ? -a : a;
+    cs = ((q + 1) & 2) ? -b : b;
+}
+
+// cos and sin of pi * m * thp: the product reduced modulo 2 into [-1, 1] in binary64 (m up to 2^31), then passed
+// on as a binary32 pair, so the argument keeps about 2^-48 absolute precision instead of binary32's 2^-25
 __device__ __forceinline__ void half_turns(double m, double thp, float &c, float &s) {
     double t = m * thp;
-    t -= 2.0 * floor(0.5 * t);
-    sincospif((float)t, &s, &c);
+    t -= 2.0 * __builtin_rint(0.5 * t);
+    const float hi = (float)t;
+    sincospi2(hi, (float)(t - (double)hi), s, c);
 }
 
 // Two 4-bit codes held in bytes 2 sel and 2 sel + 1 of w (each byte < 16) as exact fp32 values: a byte b < 16
@@ -227,7 +360,7 @@ __device__ __forceinline__ void split_hi(float pa, float pb, uint32_t sa, uint32
 // dot product of the query with the dequantized key rotated by m0 + u, expanded by angle addition. Lane l computes
 // the six coefficients of pair l once per tile and shares them through LDS. The cos/sin of u theta for a lane's 32
 // (token, pair) combinations are the same for every tile and stay in registers; the rotation by the tile start
-// advances by 32 theta per tile (recomputed exactly every 64 tiles). Window tiles use the same expansion with the
+// advances by 32 theta per tile (recomputed from the position every 16 tiles). Window tiles use the same expansion with the
 // fp16 keys (s = 1, z = 0). Partial sums of the 16 lanes of a token are added through LDS. The query carries the
 // softmax scale times log2(e), so scores are in the log2 domain.
 //
@@ -239,25 +372,82 @@ __device__ __forceinline__ void split_hi(float pa, float pb, uint32_t sa, uint32
 // group g, split into fp16 high and low parts contracted in turn (rows 4..15 repeat rows 0..3). For channel block j
 // only row g = j/2 is kept. The zero-point term sum_t p z_V[g][t] is accumulated on the VALU; window tiles and the
 // sink add their values on the VALU.
+//
+// Dense-and-sparse records (SPARSE). The outlier of a key channel's group decodes as its zero point z (code 0), so
+// the score of its token u misses d (dq/dk_c) with d = o - z: for pair l this is d (cos(u theta) qr0 + sin(u theta)
+// qr1) for the even channel and d (cos(u theta) qr1 - sin(u theta) qr0) for the odd one. Lane l computes the two
+// corrections of pair l with the tile's coefficients; a value outlier adds p[t] (o - z) to its channel. Both are
+// scattered (to tokens, to channels) through LDS as exact integer sums: each correction is split against a power of
+// two 2^K at least the tile's largest one, x = H 2^(K-23) + L 2^(K-46) with integers |H|, |L| < 2^23 (error below
+// 2^(K-46)), and H and L are added with integer LDS atomics (a float LDS atomic costs some thirty times an integer
+// one on this chip). Integer sums do not depend on the order of the adds, so the result is deterministic. The
+// sink's value outliers replace the decoded value of their channels.
 namespace {
-constexpr int NBUF = 3;                        // LDS ring slots (tiles in flight + the one being computed)
-constexpr int RING = 0;                        // [NBUF][5120]: K codes scattered (see dma_tile), rest as stored
-constexpr int RED = NBUF * REC4;               // f32 rows of 16 (one per token, row 9 (u/8) + u%8); reused for the
-                                               // output at the end
-constexpr int PBUF = RED + 36 * 64;            // f32 [32]; reused for the zero-point sums at the end
-constexpr int COEF4 = PBUF + 128;              // f32x4 [4 (pair % 4)][16 (pair / 4)]: a0 a1 alpha b0
-constexpr int COEF2 = COEF4 + 1024;            // f32x2 [4][16]: b1 beta
-constexpr int B4_LDS = COEF2 + 512;
+constexpr int NBUF = 3;   // LDS ring slots (tiles in flight + the one being computed)
+template <bool SPARSE>
+struct B4Lds {
+    static constexpr int REC = record_bytes<SPARSE>();
+    static constexpr int RING = 0;                  // [NBUF][REC]: K codes scattered (see dma_tile), rest as stored
+    static constexpr int RED = NBUF * REC;          // f32 rows of 16 (one per token, row 9 (u/8) + u%8); reused for
+                                                    // the output at the end
+    static constexpr int PBUF = RED + 36 * 64;      // f32 [32]; reused for the zero-point sums at the end
+    // f32x4 [4 (pair % 4)][16 (pair / 4)]: a0 a1 alpha b0, and f32x2 [4][16]: b1 beta. Dense records: after PBUF.
+    // Sparse records (the ring is larger): inside RED, whose rows are dead while the coefficients are shared.
+    static constexpr int COEF4 = SPARSE ? RED : PBUF + 128;
+    static constexpr int COEF2 = COEF4 + 1024;
+    // SPARSE: value-outlier sums, int32 (H, L) [128 channels], inside RED (used between P V and the coefficients);
+    // key-outlier sums, int32 (H, L) [32 tokens], filled with the coefficients and read by the next softmax step
+    static constexpr int VACC = RED;
+    static constexpr int KACC = PBUF + 128;
+    static constexpr int BYTES = SPARSE ? KACC + 256 : COEF2 + 512;
+    static constexpr int ND = SPARSE ? 6 : 5;       // LDS-DMA loads per tile
+    static constexpr int NC = SPARSE ? 2 : 1;       // the first NC of them hold what the coefficients need
+};
+static_assert(B4Lds<true>::COEF2 + 512 <= B4Lds<true>::PBUF && B4Lds<true>::VACC + 1024 <= B4Lds<true>::PBUF,
+              "coefficients and value sums inside the reduction rows");
+static_assert(B4Lds<true>::BYTES <= 20480 && B4Lds<false>::BYTES <= 20480, "eight wavefronts per CU");
+
+__device__ __forceinline__ void lds_add(int32_t *p, int32_t v) {
+    __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+__device__ __forceinline__ float exp2i(int n) { return __builtin_bit_cast(float, (uint32_t)(n + 127) << 23); }
+
+// Fixed-point parts of values x against 2^K > m (m = the wavefront's largest |x|, K clamped to [-60, 100] so every
+// factor below is a normal binary32 power of two): x = H 2^(K-23) + L 2^(K-46) + e, |H|, |L| < 2^23, |e| < 2^(K-46).
+// x 2^(23-K) and H 2^(K-23) are exact, and so is the remainder x - H 2^(K-23) (it keeps the low bits of x).
+struct FixScale {
+    float f1, f2, g1, g2;   // 2^(23-K), 2^(46-K), 2^(K-23), 2^(K-46)
+};
+__device__ __forceinline__ FixScale fix_scale(float m) {
+    int K = (int)((__builtin_bit_cast(uint32_t, m) >> 23) & 0xFFu) - 126;
+    K = K < -60 ? -60 : (K > 100 ? 100 : K);
+    return FixScale{exp2i(23 - K), exp2i(46 - K), exp2i(K - 23), exp2i(K - 46)};
+}
+__device__ __forceinline__ void fix_split(float x, const FixScale &f, int32_t &H, int32_t &L) {
+#pragma clang fp contract(off)
+    H = (int32_t)(x * f.f1);
+    const float r = fmaf(-(float)H, f.g1, x);
+    L = (int32_t)(r * f.f2);
+}
+__device__ __forceinline__ float fix_join(int32_t H, int32_t L, const FixScale &f) {
+    return fmaf((float)H, f.g1, (float)L * f.g2);
+}
+__device__ __forceinline__ float wave_max_abs2(float a, float b) {
+    return rows_max(row16_max(fmaxf(__builtin_fabsf(a), __builtin_fabsf(b))));
+}
 }  // namespace
 
-template <bool ROPE>
+template <bool ROPE, bool SPARSE>
 __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
-    __shared__ __align__(16) unsigned char smem[B4_LDS];
-    float *red = reinterpret_cast<float *>(smem + RED);
-    float *pbuf = reinterpret_cast<float *>(smem + PBUF);
-    float4 *coef4 = reinterpret_cast<float4 *>(smem + COEF4);
-    float2 *coef2 = reinterpret_cast<float2 *>(smem + COEF2);
-    const uint32_t ring_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)smem + RING;
+    typedef B4Lds<SPARSE> L;
+    constexpr int REC = L::REC;
+    __shared__ __align__(16) unsigned char smem[L::BYTES];
+    float *red = reinterpret_cast<float *>(smem + L::RED);
+    float *pbuf = reinterpret_cast<float *>(smem + L::PBUF);
+    float4 *coef4 = reinterpret_cast<float4 *>(smem + L::COEF4);
+    float2 *coef2 = reinterpret_cast<float2 *>(smem + L::COEF2);
+    const uint32_t ring_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)smem + L::RING;
 
     const int l = threadIdx.x;
     const int pq = l & 15, to = l >> 4;
@@ -284,6 +474,7 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
     // tile-start rotation of pair l and its per-tile step
     float tc[8][4], ts[8][4], ec = 1.0f, es = 0.0f, rc = 1.0f, rs = 0.0f;
     double thl = 0.0;   // theta_l / pi
+    float thl_hi = 0.0f, thl_lo = 0.0f;   // theta_l / pi as hi (14 significant bits, so u * hi is exact) + lo
     if constexpr (ROPE) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -298,12 +489,14 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
             }
         }
         thl = exp2(-(2.0 * l / HD) * a.log2_base) * 0.31830988618379067154;
+        thl_hi = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, (float)thl) & 0xFFFFFC00u);
+        thl_lo = (float)(thl - (double)thl_hi);
         half_turns(32.0, thl, rc, rs);
         half_turns((double)a.n_sink + 32.0 * v0, thl, ec, es);
     }
     auto advance = [&](int v_next) {   // rotation of pair l for the start of tile v_next
         if constexpr (ROPE) {
-            if (((v_next - v0) & 63) == 0) {
+            if (((v_next - v0) & 15) == 0) {
                 half_turns((double)a.n_sink + 32.0 * v_next, thl, ec, es);
             } else {
                 const float c = ec * rc - es * rs;
@@ -316,9 +509,9 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
     // coefficients of pair l for the current tile (scales/zeros of its two channels) -> LDS; then the lane's four
     // score pairs are read back
     float a0[4], a1[4], al[4], b0[4], b1[4], be[4];
-    auto share_coefficients = [&](float s0, float s1, float z0, float z1) {
-        const float r0 = qp0 * ec + qp1 * es;
-        const float r1 = qp1 * ec - qp0 * es;
+    auto share_coefficients = [&](float s0, float s1, float z0, float z1, float &r0, float &r1) {
+        r0 = qp0 * ec + qp1 * es;
+        r1 = qp1 * ec - qp0 * es;
         const int at = (l & 3) * 16 + (l >> 2);
         coef4[at] = float4{r0 * s0, r1 * s1, r0 * z0 + r1 * z1, r1 * s0};
         coef2[at] = float2{-(r0 * s1), r1 * z0 - r0 * z1};
@@ -366,13 +559,26 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
         const float z = (float)reinterpret_cast<const _Float16 *>(sk + 328)[g];
         vs0 = fmaf((float)(byte & 15u), s, z);
         vs1 = fmaf((float)(byte >> 4), s, z);
+        if constexpr (SPARSE) {   // the group's outlier replaces its channel's decoded value
+            const float so = (float)reinterpret_cast<const _Float16 *>(sk + SINK_VOUT)[g];
+            const uint32_t si = sk[SINK_VIDX + g] & 31u, c0 = 2 * (l & 15);
+            vs0 = si == c0 ? so : vs0;
+            vs1 = si == c0 + 1 ? so : vs1;
+        }
         m = d;
         ws = 1.0f;
         lsum = (l == 0) ? 1.0f : 0.0f;
     }
 
     // partial scores -> full score of token u in lanes 2u, 2u+1 (tokens >= nv masked), then the softmax step
-    auto softmax_step = [&](const float (&part)[8], int nv) {
+    // SPARSE: key-outlier score corrections of the coming tile, per token as int32 (H, L) in KACC, and their scale
+    int2 *kacc = reinterpret_cast<int2 *>(smem + L::KACC);
+    FixScale kfix{0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (SPARSE) {
+        if (l < 32) kacc[l] = int2{0, 0};
+        wave_lds_order();
+    }
+    auto softmax_step = [&](const float (&part)[8], int nv, bool key_outliers) {
         // token 8to + t in row 9to + t: the 16 lanes of each `to` group land in distinct banks
 #pragma unroll
         for (int t = 0; t < 8; ++t) red[(9 * to + t) * 16 + pq] = part[t];
@@ -382,6 +588,14 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
         const float4 r1 = *reinterpret_cast<const float4 *>(rr + 8);
         float s = ((r0.x + r0.y) + (r0.z + r0.w)) + ((r1.x + r1.y) + (r1.z + r1.w));
         s = dpp_xadd<DPP_QUAD_1032>(s);
+        if constexpr (SPARSE) {
+            if (key_outliers) {   // token u's key-outlier sum, then cleared for the next tile
+                const int2 hl = kacc[u];
+                s += fix_join(hl.x, hl.y, kfix);
+                wave_lds_order();
+                if (uh == 0) kacc[u] = int2{0, 0};
+            }
+        }
         if (u >= nv) s = NEG_INF;
         if (__any(s > m)) {
             const float mn = fmaxf(m, rows_max(row16_max(s)));
@@ -397,26 +611,59 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
         wave_lds_order();
     };
 
-    const uint8_t *recs = a.tiles + slice * a.max_tiles * REC4;
+    const uint8_t *recs = a.tiles + slice * a.max_tiles * REC;
     const int vq_end = min(v1, a.n_qtiles);
 
     // one tile record -> ring slot, scales and zeros first (the coefficients of a tile need only those): key-code
     // bytes [32 l, 32 l + 16) go to slot + 16 l and [32 l + 16, 32 l + 32) to slot + 1024 + 16 l; value codes,
     // scales and zeros at their record offsets
+    // SPARSE: the outlier section (768 bytes, lanes 0..47) right after the scales
     auto dma_tile = [&](int v, int slot) {
-        const uint8_t *rec = recs + (int64_t)v * REC4;
-        const uint32_t base = ring_base + slot * REC4;
+        const uint8_t *rec = recs + (int64_t)v * REC;
+        const uint32_t base = ring_base + slot * REC;
         lds_dma16(rec + K4_SCALE + 16 * l, base + K4_SCALE);
+        if constexpr (SPARSE) {
+            if (l < 48) lds_dma16(rec + K4_OUT + 16 * l, base + K4_OUT);
+        }
         lds_dma16(rec + 32 * l, base);
         lds_dma16(rec + 32 * l + 16, base + 1024);
         lds_dma16(rec + V4_CODES + 16 * l, base + V4_CODES);
         lds_dma16(rec + V4_CODES + 1024 + 16 * l, base + V4_CODES + 1024);
     };
     auto tile_coefficients = [&](int slot) {
-        const unsigned char *tl = smem + RING + slot * REC4;
+        const unsigned char *tl = smem + L::RING + slot * REC;
         const h2 skp = reinterpret_cast<const h2 *>(tl + K4_SCALE)[l];
         const h2 zkp = reinterpret_cast<const h2 *>(tl + K4_ZERO)[l];
-        share_coefficients((float)skp[0], (float)skp[1], (float)zkp[0], (float)zkp[1]);
+        const float z0 = (float)zkp[0], z1 = (float)zkp[1];
+        float r0, r1;
+        share_coefficients((float)skp[0], (float)skp[1], z0, z1, r0, r1);
+        if constexpr (SPARSE) {   // key outliers of channels 2l, 2l+1
+            const h2 kop = reinterpret_cast<const h2 *>(tl + K4_OUT)[l];
+            const uint32_t ki = reinterpret_cast<const uint16_t *>(tl + K4_IDX)[l];
+            const uint32_t u0 = ki & 31u, u1 = (ki >> 8) & 31u;
+            const float d0 = (float)kop[0] - z0, d1 = (float)kop[1] - z1;
+            float kc0, kc1;
+            if constexpr (ROPE) {
+                float c0, s0, c1, s1;
+                sincospi2((float)u0 * thl_hi, (float)u0 * thl_lo, s0, c0);
+                sincospi2((float)u1 * thl_hi, (float)u1 * thl_lo, s1, c1);
+                kc0 = d0 * fmaf(c0, r0, s0 * r1);
+                kc1 = d1 * fmaf(c1, r1, -(s1 * r0));
+            } else {
+                kc0 = d0 * r0;
+                kc1 = d1 * r1;
+            }
+            kfix = fix_scale(wave_max_abs2(kc0, kc1));
+            int32_t h0, l0, h1, l1;
+            fix_split(kc0, kfix, h0, l0);
+            fix_split(kc1, kfix, h1, l1);
+            int32_t *ka = reinterpret_cast<int32_t *>(kacc);
+            wave_lds_order();
+            lds_add(ka + 2 * u0, h0);
+            lds_add(ka + 2 * u0 + 1, l0);
+            lds_add(ka + 2 * u1, h1);
+            lds_add(ka + 2 * u1 + 1, l1);
+        }
     };
 
     // ---- quantized tiles: two tiles in flight; the coefficients of tile v + 1 are shared at the end of
@@ -426,9 +673,9 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
         dma_tile(v, 0);
         if (v + 1 < vq_end) {
             dma_tile(v + 1, 1);
-            wait_vmcnt<9>();
+            wait_vmcnt<2 * L::ND - L::NC>();
         } else {
-            wait_vmcnt<4>();
+            wait_vmcnt<L::ND - L::NC>();
         }
         tile_coefficients(0);
         advance(v + 1);
@@ -440,13 +687,13 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
         const bool ahead2 = v + 2 < vq_end, ahead1 = v + 1 < vq_end;
         if (ahead2) {
             dma_tile(v + 2, slot == 0 ? 2 : slot - 1);
-            wait_vmcnt<10>();
+            wait_vmcnt<2 * L::ND>();
         } else if (ahead1) {
-            wait_vmcnt<5>();
+            wait_vmcnt<L::ND>();
         } else {
             wait_vmcnt<0>();
         }
-        const unsigned char *tl = smem + RING + slot * REC4;
+        const unsigned char *tl = smem + L::RING + slot * REC;
         slot = (slot == NBUF - 1) ? 0 : slot + 1;
 
         const uint4 k03 = reinterpret_cast<const uint4 *>(tl)[l];
@@ -462,7 +709,7 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
             const float x1[4] = {o01[0], o01[1], o23[0], o23[1]};
             part[t] = token_score(t, x0, x1);
         }
-        softmax_step(part, 32);
+        softmax_step(part, 32, true);
 
         // PV: A rows g = n & 3 over tokens 8kg .. 8kg+7 in the expand8_b4 order (t0 t2 t4 t6 t1 t3 t5 t7)
         const int gA = n & 3;
@@ -491,11 +738,35 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[j0 + j] = mfma(Alo, B[j], acc[j0 + j]);
         }
-        if (ahead1) {   // coefficients of tile v + 1: its scale chunk is the oldest load still counted
+        if constexpr (SPARSE) {   // value outliers of entries 2l, 2l+1 ([g][t]): p[t] (o - z) into channel 32 g + idx
+            int32_t *vacc = reinterpret_cast<int32_t *>(smem + L::VACC);   // (H, L) per channel
+            const h2 vo = reinterpret_cast<const h2 *>(tl + V4_OUT)[l];
+            const h2 vz = reinterpret_cast<const h2 *>(tl + V4_ZERO)[l];
+            const uint32_t vi = reinterpret_cast<const uint16_t *>(tl + V4_IDX)[l];
+            const float2 pp = reinterpret_cast<const float2 *>(pbuf)[l & 15];
+            const float w0 = pp.x * ((float)vo[0] - (float)vz[0]), w1 = pp.y * ((float)vo[1] - (float)vz[1]);
+            const FixScale vfix = fix_scale(wave_max_abs2(w0, w1));
+            int32_t h0, l0, h1, l1;
+            fix_split(w0, vfix, h0, l0);
+            fix_split(w1, vfix, h1, l1);
+            int32_t *cg = vacc + 2 * 32 * (l >> 4);
+            wave_lds_order();
+            reinterpret_cast<int4 *>(vacc)[l] = int4{0, 0, 0, 0};
+            wave_lds_order();
+            lds_add(cg + 2 * (vi & 31u), h0);
+            lds_add(cg + 2 * (vi & 31u) + 1, l0);
+            lds_add(cg + 2 * ((vi >> 8) & 31u), h1);
+            lds_add(cg + 2 * ((vi >> 8) & 31u) + 1, l1);
+            wave_lds_order();
+            const int4 cv = reinterpret_cast<const int4 *>(vacc)[l];
+            ow0 += fix_join(cv.x, cv.y, vfix);
+            ow1 += fix_join(cv.z, cv.w, vfix);
+        }
+        if (ahead1) {   // coefficients of tile v + 1: its first NC loads are the oldest still counted
             if (ahead2)
-                wait_vmcnt<9>();
+                wait_vmcnt<2 * L::ND - L::NC>();
             else
-                wait_vmcnt<4>();
+                wait_vmcnt<L::ND - L::NC>();
             tile_coefficients(slot);
             advance(v + 2);
         }
@@ -511,7 +782,8 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
 #pragma unroll
         for (int t = 0; t < 8; ++t)
             kx[t] = __builtin_bit_cast(h8, *reinterpret_cast<const uint4 *>(kr + (8 * to + t) * HD + 8 * pq));
-        share_coefficients(1.0f, 1.0f, 0.0f, 0.0f);
+        float r0, r1;
+        share_coefficients(1.0f, 1.0f, 0.0f, 0.0f, r0, r1);
         advance(v + 1);
         float part[8];
 #pragma unroll
@@ -524,7 +796,7 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
             }
             part[t] = token_score(t, x0, x1);
         }
-        softmax_step(part, nv);
+        softmax_step(part, nv, false);
         for (int t = 0; t < nv; ++t) {   // lane l: channels 2l, 2l+1
             const float p = pbuf[t];
             const h2 vv = reinterpret_cast<const h2 *>(vr + t * HD)[l];
@@ -560,33 +832,52 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
 
 // ------------------------------------------------------------------------------------------------ launchers
 hipError_t launch_quant_keys_b4(const TokSrc &src, int64_t t_begin, int64_t n_tiles, int batch, int kv_heads,
-                                uint8_t *tiles, int64_t max_tiles, int64_t tile0, hipStream_t st) {
+                                uint8_t *tiles, int64_t max_tiles, int64_t tile0, bool sparse, hipStream_t st) {
     dim3 grid((unsigned)n_tiles, (unsigned)kv_heads, (unsigned)batch);
-    hipLaunchKernelGGL(quant_keys_b4_kernel, grid, dim3(64), 0, st, src, t_begin, kv_heads, tiles, max_tiles, tile0);
+    if (sparse)
+        hipLaunchKernelGGL(quant_keys_b4_kernel<true>, grid, dim3(64), 0, st, src, t_begin, kv_heads, tiles,
+                           max_tiles, tile0);
+    else
+        hipLaunchKernelGGL(quant_keys_b4_kernel<false>, grid, dim3(64), 0, st, src, t_begin, kv_heads, tiles,
+                           max_tiles, tile0);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_values_b4(const TokSrc &src, int64_t t_begin, int64_t n_tiles, int batch, int kv_heads,
-                                  uint8_t *tiles, int64_t max_tiles, int64_t tile0, hipStream_t st) {
+                                  uint8_t *tiles, int64_t max_tiles, int64_t tile0, bool sparse, hipStream_t st) {
     dim3 grid((unsigned)n_tiles, (unsigned)kv_heads, (unsigned)batch);
-    hipLaunchKernelGGL(quant_values_b4_kernel, grid, dim3(64), 0, st, src, t_begin, kv_heads, tiles, max_tiles,
-                       tile0);
+    if (sparse)
+        hipLaunchKernelGGL(quant_values_b4_kernel<true>, grid, dim3(64), 0, st, src, t_begin, kv_heads, tiles,
+                           max_tiles, tile0);
+    else
+        hipLaunchKernelGGL(quant_values_b4_kernel<false>, grid, dim3(64), 0, st, src, t_begin, kv_heads, tiles,
+                           max_tiles, tile0);
     return hipGetLastError();
 }
 
 hipError_t launch_sink_b4(const TokSrc &ksrc, const TokSrc &vsrc, int batch, int kv_heads, uint8_t *sink,
-                          hipStream_t st) {
-    hipLaunchKernelGGL(sink_b4_kernel, dim3((unsigned)kv_heads, (unsigned)batch), dim3(64), 0, st, ksrc, vsrc,
-                       kv_heads, sink);
+                          bool sparse, hipStream_t st) {
+    const dim3 grid((unsigned)kv_heads, (unsigned)batch);
+    if (sparse)
+        hipLaunchKernelGGL(sink_b4_kernel<true>, grid, dim3(64), 0, st, ksrc, vsrc, kv_heads, sink);
+    else
+        hipLaunchKernelGGL(sink_b4_kernel<false>, grid, dim3(64), 0, st, ksrc, vsrc, kv_heads, sink);
     return hipGetLastError();
 }
 
 hipError_t launch_decode_b4(const DecodeB4Args &a, float *out, int splits, hipStream_t st) {
     const dim3 grid((unsigned)(a.batch * a.q_heads), (unsigned)splits);
-    if (a.rope)
-        hipLaunchKernelGGL(decode_b4_pass1_kernel<true>, grid, dim3(64), 0, st, a);
-    else
-        hipLaunchKernelGGL(decode_b4_pass1_kernel<false>, grid, dim3(64), 0, st, a);
+    if (a.sparse) {
+        if (a.rope)
+            hipLaunchKernelGGL((decode_b4_pass1_kernel<true, true>), grid, dim3(64), 0, st, a);
+        else
+            hipLaunchKernelGGL((decode_b4_pass1_kernel<false, true>), grid, dim3(64), 0, st, a);
+    } else {
+        if (a.rope)
+            hipLaunchKernelGGL((decode_b4_pass1_kernel<true, false>), grid, dim3(64), 0, st, a);
+        else
+            hipLaunchKernelGGL((decode_b4_pass1_kernel<false, false>), grid, dim3(64), 0, st, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_pass2(a.part_o, a.part_ml, out, a.batch * a.q_heads, splits, st);

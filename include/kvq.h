@@ -2,8 +2,9 @@
  * kvq.h — C ABI of a quantized KV-cache library for AMD MI355X (gfx950): KIVI-style asymmetric quantization of keys
  * per channel and values per token (2-bit, or 4-bit in the KVQuant-style variant), a full-precision window of the
  * newest tokens, and decode attention computed straight from the packed codes plus that window. The 4-bit variant
- * can also keep keys cached before the rotary embedding (rotated at decode time) and hold token 0 apart as an
- * attention sink with a full-precision key.
+ * can also keep keys cached before the rotary embedding (rotated at decode time), hold token 0 apart as an
+ * attention sink with a full-precision key, and keep each group's largest element apart in fp16 (dense-and-sparse
+ * groups).
  *
  * Sources (the pages this library follows):
  *  - KIVI page, fdeinterviews.com "KIVI: A Tuning-Free Asymmetric 2bit Quantization for KV Cache": keys grouped per
@@ -14,7 +15,9 @@
  *    attention scores.
  *  - KVQuant page, fdeinterviews.com "KVQuant: Towards 10 Million Context Length LLM Inference with KV Cache
  *    Quantization": per-channel keys quantized before the rotary embedding (RoPE applied after dequantization),
- *    per-token values, and the first token's keys kept in full precision (attention sink); 4-bit codes.
+ *    per-token values, the first token's keys kept in full precision (attention sink), and per-vector
+ *    dense-and-sparse quantization (outliers held apart so they do not stretch the quantization range); 4-bit
+ *    codes.
  *
  * Conventions for every call:
  *  - All pointers named as device pointers refer to memory on the current HIP device; host pointers are named so.
@@ -49,7 +52,8 @@ extern "C" {
 #define KVQ_E_NULL (-1)      /* a required pointer is NULL */
 #define KVQ_E_SHAPE (-2)     /* head_dim != 128, group != 32, q_heads % kv_heads != 0, R not a positive multiple
                                 of 32, non-positive sizes, a token count/offset that is not a multiple of 32,
-                                unknown flags, flags with bits != 4, or KVQ_FLAG_PRE_ROPE with rope_base <= 1 */
+                                unknown flags, flags with bits != 4, or KVQ_FLAG_PRE_ROPE with rope_base <= 1 (or
+                                not finite) */
 #define KVQ_E_BITS (-3)      /* bits not 2 or 4 */
 #define KVQ_E_ALIGN (-4)     /* a device pointer is not 16-byte aligned, or a token/head/batch stride is not a
                                 multiple of 8 elements (rows must be 16-byte aligned; the channel stride is 1) */
@@ -67,6 +71,7 @@ extern "C" {
 #define KVQ_TILE_TOKENS 32
 #define KVQ_RECORD_BYTES 3072       /* one 32-token tile, 2-bit codes */
 #define KVQ_RECORD_BYTES_4BIT 5120  /* one 32-token tile, 4-bit codes */
+#define KVQ_RECORD_BYTES_4BIT_SPARSE 5888  /* one 32-token tile, 4-bit codes with dense-and-sparse groups */
 #define KVQ_SINK_BYTES 512          /* the sink record of one (batch row, KV head) slice */
 
 /* kvq_shape.flags (4-bit only). */
@@ -74,6 +79,12 @@ extern "C" {
 #define KVQ_FLAG_PRE_ROPE 2  /* keys are given and cached before the rotary embedding; attention rotates every key
                                 (sink, quantized and window alike) by its absolute position (KVQuant page, pre-RoPE
                                 key quantization) */
+#define KVQ_FLAG_SPARSE 4    /* dense-and-sparse groups (KVQuant page, per-vector dense-and-sparse quantization): in
+                                every key group (32 tokens of a channel) and value group (32 channels of a token),
+                                the sink's value groups included, the element of largest magnitude (the lowest index
+                                on ties) is stored apart as its fp16 value and index; the other 31 are quantized by
+                                the rule of kv_quant_keys_per_channel over their own minimum and maximum, and the
+                                outlier's code is 0. Records are 5888 bytes. */
 
 /*
  * Shape of one cache (one attention layer).
@@ -81,7 +92,7 @@ extern "C" {
  *   consecutive query heads share a KV head — the usual grouped-query layout);
  *   head_dim: must be 128; bits: 2 or 4; group: must be 32 (tokens per key group, channels per value group);
  *   residual_cap: R, the number of newest tokens kept in fp16 (a positive multiple of 32; 128 on the pages);
- *   flags: 0, or (bits = 4 only) an OR of KVQ_FLAG_SINK and KVQ_FLAG_PRE_ROPE;
+ *   flags: 0, or (bits = 4 only) an OR of KVQ_FLAG_SINK, KVQ_FLAG_PRE_ROPE and KVQ_FLAG_SPARSE;
  *   max_tokens: capacity of the quantized part in tokens (a positive multiple of 32);
  *   rope_base: with KVQ_FLAG_PRE_ROPE, the rotary base (10000 in the usual models; must be > 1); ignored otherwise.
  *     Rotary form: channel pairs (2i, 2i+1), i = 0..63, turned by the angle m * theta_i with
@@ -124,6 +135,11 @@ typedef struct kvq_shape {
  *       bytes 4608..4863  value scale s_V[g][t] (index 32 g + t);  4864..5119 value zero z_V[g][t]
  *     Key code of token t, channel c: word 8 (c/8 + 16 (t/8)) + t%8, bit 4 (c%8).
  *     Value code of channel c, token t: word 4 c + t/8, bit 4 (t%8).
+ *     4-bit with KVQ_FLAG_SPARSE: a 5888-byte record, the 5120 bytes above followed by
+ *       bytes 5120..5375  key outlier o_K[c] (fp16, one per channel);  5376..5503 its token t (uint8, 0..31)
+ *       bytes 5504..5759  value outlier o_V[g][t] (fp16, index 32 g + t);  5760..5887 its channel within group g
+ *                         (uint8 at 5760 + 32 g + t, 0..31)
+ *     the outlier's code is 0 and it decodes as o instead of code * s + z.
  *   k_res, v_res: device, fp16 [B][Hkv][R][128]: the residual window; rows 0 .. n_resid-1 hold the newest tokens
  *     exactly as appended.
  *   n_quant (host): tokens in the quantized part (a multiple of 32). n_resid (host): tokens in the window (0..R).
@@ -131,7 +147,9 @@ typedef struct kvq_shape {
  *     n_sink + n_quant + n_resid tokens, in that order.
  *   sink: device, uint8 [B][Hkv][512], required with KVQ_FLAG_SINK (else ignored): bytes 0..255 the fp16 key of
  *     token 0; bytes 256..319 its value codes (channel c at byte 256 + c/2, bit 4 (c%2)); bytes 320..327 value scales
- *     s_V[g] and 328..335 value zeros z_V[g] (fp16, g = 0..3); bytes 336..511 zero.
+ *     s_V[g] and 328..335 value zeros z_V[g] (fp16, g = 0..3); bytes 336..511 zero. With KVQ_FLAG_SPARSE: bytes
+ *     336..343 the value outliers o_V[g] (fp16) and 344..347 their channels within the group (uint8); 348..511
+ *     zero.
  * A new cache starts with n_quant = n_resid = n_sink = 0.
  */
 typedef struct kvq_cache {
@@ -155,7 +173,8 @@ typedef struct kvq_cache {
  *   r = RN32(max - min); s = RN16(RN32(r / L)); if (L + 1/2) * s < r then s = next binary16 above s;
  *   z = min (a zero minimum stored as +0); code = 0 if s == 0, else
  *   clamp(round_half_even(RN32(RN32(x - z) / s)), 0, L); RN32/RN16 = round to nearest even into binary32/binary16,
- *   division correctly rounded.
+ *   division correctly rounded. With KVQ_FLAG_SPARSE, min and max run over the group without its outlier, whose
+ *   value and index fill the record's outlier fields (also written).
  * Errors: KVQ_E_NULL, KVQ_E_SHAPE, KVQ_E_BITS, KVQ_E_ALIGN, KVQ_E_CAPACITY (tile range beyond max_tokens/32),
  *   KVQ_E_LAUNCH.
  */

@@ -113,6 +113,7 @@ class Workload:
     residual: int = 128
     sink: bool = False              # token 0's keys kept in fp16 (KVQuant variant)
     rope_base: float | None = None  # keys cached before the rotary embedding, rotated at decode time
+    sparse: bool = False            # dense-and-sparse groups: each group's largest element kept apart in fp16
     notes: str = ""
     extra: dict = field(default_factory=dict)
 
@@ -135,4 +136,9 @@ WORKLOADS = {
                                  sink=True, rope_base=10000.0,
                                  notes="B16 H32 D128 N16384, 4-bit, pre-RoPE keys (base 10000), fp16 sink token 0, "
                                        "K outliers 4 ch x20 (values plain N(0,1))"),
+    # The same cache and data with dense-and-sparse groups (one fp16 outlier per group of 32).
+    "kvquant_4bit_sparse_16k": Workload("kvquant_4bit_sparse_16k", 16, 32, 32, 16384, 16383, 1, 1005, 4, 20.0,
+                                        bits=4, sink=True, rope_base=10000.0, sparse=True,
+                                        notes="kvquant_4bit_16k with dense-and-sparse groups: per key channel and "
+                                              "value token group of 32, the largest element kept in fp16"),
 }

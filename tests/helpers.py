@@ -52,26 +52,33 @@ def workload_tokens(w: kvsynth.Workload, tensor_id: int, t0: int, t1: int, b=Non
 
 
 def oracle_records4(cache: oc.SliceCache) -> np.ndarray:
-    """4-bit tile records [S, n_quant / 32, 5120] of the oracle's quantized part, packed by the oracle."""
+    """4-bit tile records [S, n_quant / 32, 5120 (5888 with dense-and-sparse groups)] of the oracle's quantized
+    part, packed by the oracle."""
     from oracle import layout4
     kq, ks, kz, vq, vs, vz = cache.quantized()
     S, nq, D = kq.shape
     nt = nq // 32
-    return layout4.pack_tiles(kq.reshape(S, nt, 32, D), ks, kz, vq.reshape(S, nt, 32, D),
-                              vs.reshape(S, nt, 32, 4), vz.reshape(S, nt, 32, 4))
+    dense = (kq.reshape(S, nt, 32, D), ks, kz, vq.reshape(S, nt, 32, D), vs.reshape(S, nt, 32, 4),
+             vz.reshape(S, nt, 32, 4))
+    if not cache.sparse:
+        return layout4.pack_tiles(*dense)
+    ko, ki, vo, vi = cache.outliers()
+    return layout4.pack_tiles_sparse(*dense, ko, ki, vo.reshape(S, nt, 32, 4), vi.reshape(S, nt, 32, 4))
 
 
 def oracle_sink(cache: oc.SliceCache) -> np.ndarray:
     """Sink records [S, 512] of the oracle's sink token, packed by the oracle."""
     from oracle import layout4
     vq, vs, vz = cache.v_sink
+    if cache.sparse:
+        return layout4.pack_sink(cache.k_sink, vq, vs, vz, *cache.v_sink_out)
     return layout4.pack_sink(cache.k_sink, vq, vs, vz)
 
 
 def records4_from_device(tiles, n_tiles: int, slices=None) -> np.ndarray:
-    """GPU 4-bit tile array [B, H, max_tiles, 5120] -> numpy [S, n_tiles, 5120]."""
+    """GPU 4-bit tile array [B, H, max_tiles, record] -> numpy [S, n_tiles, record]."""
     B, H = tiles.shape[:2]
-    t = tiles[:, :, :n_tiles].reshape(B * H, n_tiles, 5120)
+    t = tiles[:, :, :n_tiles].reshape(B * H, n_tiles, tiles.shape[-1])
     if slices is not None:
         t = t[list(slices)]
     return t.cpu().numpy()
@@ -83,9 +90,29 @@ def first_mismatch4(a: np.ndarray, b: np.ndarray) -> str:
     if len(idx) == 0:
         return "identical"
     off = idx[0][-1]
-    field = ["k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"][
-        0 if off < 2048 else 1 if off < 4096 else 2 + (off - 4096) // 256]
+    bounds = [(0, "k_codes"), (2048, "v_codes"), (4096, "k_scale"), (4352, "k_zero"), (4608, "v_scale"),
+              (4864, "v_zero"), (5120, "k_outlier"), (5376, "k_outlier_token"), (5504, "v_outlier"),
+              (5760, "v_outlier_channel")]
+    field = [name for start, name in bounds if off >= start][-1]
     return f"{len(idx)} bytes differ; first at {tuple(idx[0])} ({field}): gpu {a[tuple(idx[0])]} oracle {b[tuple(idx[0])]}"
+
+
+def tie_groups_sparse(rng, n_groups: int, levels: int) -> np.ndarray:
+    """float16 [n_groups, 32]: a :func:`tie_groups` group with one of its half-level values dropped, plus one
+    element of strictly largest magnitude (the outlier) at a random position. The 31 dense elements keep the range
+    levels * 2^e, so their quotients land on or beside half levels."""
+    base = tie_groups(rng, n_groups, levels).astype(np.float32)
+    out = np.empty((n_groups, 32), np.float32)
+    for gi in range(n_groups):
+        row = base[gi]
+        lo, hi = row.min(), row.max()
+        inner = np.flatnonzero((row != lo) & (row != hi))
+        rest = np.delete(row, inner[int(rng.integers(0, len(inner)))])
+        o = (max(abs(lo), abs(hi)) + 4 * (hi - lo) / levels) * (1.0 if rng.integers(0, 2) else -1.0)
+        out[gi] = np.insert(rest, int(rng.integers(0, 32)), o)
+    h = out.astype(np.float16)
+    assert np.array_equal(h.astype(np.float32), out), "sparse tie groups must be exact binary16 values"
+    return h
 
 
 def tie_groups(rng, n_groups: int, levels: int) -> np.ndarray:

@@ -72,7 +72,8 @@ def test_shape_validation(kvq):
         (dict(group=16), kvq.E_SHAPE), (dict(q_heads=3), kvq.E_SHAPE), (dict(residual_cap=100), kvq.E_SHAPE),
         (dict(residual_cap=0), kvq.E_SHAPE), (dict(max_tokens=1000), kvq.E_SHAPE), (dict(batch=0), kvq.E_SHAPE),
         # flags belong to the 4-bit variant; unknown bits and a missing rotary base are rejected
-        (dict(flags=kvq.FLAG_SINK), kvq.E_SHAPE), (dict(bits=4, flags=4), kvq.E_SHAPE),
+        (dict(flags=kvq.FLAG_SINK), kvq.E_SHAPE), (dict(flags=kvq.FLAG_SPARSE), kvq.E_SHAPE),
+        (dict(bits=4, flags=8), kvq.E_SHAPE), (dict(bits=4, flags=kvq.FLAG_SPARSE | 16), kvq.E_SHAPE),
         (dict(bits=4, flags=kvq.FLAG_PRE_ROPE, rope_base=0.0), kvq.E_SHAPE),
         (dict(bits=4, flags=kvq.FLAG_PRE_ROPE, rope_base=1.0), kvq.E_SHAPE),
         (dict(bits=4, flags=kvq.FLAG_PRE_ROPE, rope_base=float("nan")), kvq.E_SHAPE),
