@@ -378,10 +378,13 @@ __device__ __forceinline__ void split_hi(float pa, float pb, uint32_t sa, uint32
 // qr1) for the even channel and d (cos(u theta) qr1 - sin(u theta) qr0) for the odd one. Lane l computes the two
 // corrections of pair l with the tile's coefficients; a value outlier adds p[t] (o - z) to its channel. Both are
 // scattered (to tokens, to channels) through LDS as exact integer sums: each correction is split against a power of
-// two 2^K at least the tile's largest one, x = H 2^(K-23) + L 2^(K-46) with integers |H|, |L| < 2^23 (error below
+// two 2^K above every correction it can be, x = H 2^(K-23) + L 2^(K-46) with integers |H|, |L| < 2^23 (error below
 // 2^(K-46)), and H and L are added with integer LDS atomics (a float LDS atomic costs some thirty times an integer
-// one on this chip). Integer sums do not depend on the order of the adds, so the result is deterministic. The
-// sink's value outliers replace the decoded value of their channels.
+// one on this chip). The bounds need no per-tile reduction: |o - z| <= 2 * 65504 for binary16 o and z, a rotation
+// keeps the length of a query pair, and p <= 1 under the lagged maximum, so 2^K comes from the wavefront's largest
+// query pair (keys) or is 2^17 (values); the resolution 2^(K-46) stays far below binary32 rounding of a score or an
+// output. Integer sums do not depend on the order of the adds, so the result is deterministic. The sink's value
+// outliers replace the decoded value of their channels.
 namespace {
 constexpr int NBUF = 3;   // LDS ring slots (tiles in flight + the one being computed)
 template <bool SPARSE>
@@ -433,9 +436,7 @@ __device__ __forceinline__ void fix_split(float x, const FixScale &f, int32_t &H
 __device__ __forceinline__ float fix_join(int32_t H, int32_t L, const FixScale &f) {
     return fmaf((float)H, f.g1, (float)L * f.g2);
 }
-__device__ __forceinline__ float wave_max_abs2(float a, float b) {
-    return rows_max(row16_max(fmaxf(__builtin_fabsf(a), __builtin_fabsf(b))));
-}
+constexpr float OUTLIER_SPAN = 131008.0f;   // |o - z| <= 2 * 65504 for binary16 o, z
 }  // namespace
 
 template <bool ROPE, bool SPARSE>
@@ -571,10 +572,13 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
     }
 
     // partial scores -> full score of token u in lanes 2u, 2u+1 (tokens >= nv masked), then the softmax step
-    // SPARSE: key-outlier score corrections of the coming tile, per token as int32 (H, L) in KACC, and their scale
+    // SPARSE: key-outlier score corrections of the coming tile, per token as int32 (H, L) in KACC; their scale bounds
+    // |o - z| |query pair| over the wavefront, the value corrections' bounds p |o - z|
     int2 *kacc = reinterpret_cast<int2 *>(smem + L::KACC);
-    FixScale kfix{0.0f, 0.0f, 0.0f, 0.0f};
+    FixScale kfix{0.0f, 0.0f, 0.0f, 0.0f}, vfix{0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (SPARSE) {
+        kfix = fix_scale(OUTLIER_SPAN * sqrtf(rows_max(row16_max(qp0 * qp0 + qp1 * qp1))));
+        vfix = fix_scale(OUTLIER_SPAN);
         if (l < 32) kacc[l] = int2{0, 0};
         wave_lds_order();
     }
@@ -653,7 +657,6 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
                 kc0 = d0 * r0;
                 kc1 = d1 * r1;
             }
-            kfix = fix_scale(wave_max_abs2(kc0, kc1));
             int32_t h0, l0, h1, l1;
             fix_split(kc0, kfix, h0, l0);
             fix_split(kc1, kfix, h1, l1);
@@ -711,6 +714,28 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
         }
         softmax_step(part, 32, true);
 
+        // SPARSE: value outliers of entries 2l, 2l+1 ([g][t]): p[t] (o - z) into channel 32 g + idx, added into the
+        // (H, L) sums before P V and read back after it, so the adds complete under the MFMAs
+        int32_t *vacc = reinterpret_cast<int32_t *>(smem + L::VACC);
+        if constexpr (SPARSE) {
+            const h2 vo = reinterpret_cast<const h2 *>(tl + V4_OUT)[l];
+            const h2 vz = reinterpret_cast<const h2 *>(tl + V4_ZERO)[l];
+            const uint32_t vi = reinterpret_cast<const uint16_t *>(tl + V4_IDX)[l];
+            const float2 pp = reinterpret_cast<const float2 *>(pbuf)[l & 15];
+            const float w0 = pp.x * ((float)vo[0] - (float)vz[0]), w1 = pp.y * ((float)vo[1] - (float)vz[1]);
+            int32_t h0, l0, h1, l1;
+            fix_split(w0, vfix, h0, l0);
+            fix_split(w1, vfix, h1, l1);
+            int32_t *cg = vacc + 2 * 32 * (l >> 4);
+            wave_lds_order();
+            reinterpret_cast<int4 *>(vacc)[l] = int4{0, 0, 0, 0};
+            wave_lds_order();
+            lds_add(cg + 2 * (vi & 31u), h0);
+            lds_add(cg + 2 * (vi & 31u) + 1, l0);
+            lds_add(cg + 2 * ((vi >> 8) & 31u), h1);
+            lds_add(cg + 2 * ((vi >> 8) & 31u) + 1, l1);
+        }
+
         // PV: A rows g = n & 3 over tokens 8kg .. 8kg+7 in the expand8_b4 order (t0 t2 t4 t6 t1 t3 t5 t7)
         const int gA = n & 3;
         const uint4 svr = *reinterpret_cast<const uint4 *>(tl + V4_SCALE + 2 * (32 * gA + 8 * kg));
@@ -738,25 +763,7 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[j0 + j] = mfma(Alo, B[j], acc[j0 + j]);
         }
-        if constexpr (SPARSE) {   // value outliers of entries 2l, 2l+1 ([g][t]): p[t] (o - z) into channel 32 g + idx
-            int32_t *vacc = reinterpret_cast<int32_t *>(smem + L::VACC);   // (H, L) per channel
-            const h2 vo = reinterpret_cast<const h2 *>(tl + V4_OUT)[l];
-            const h2 vz = reinterpret_cast<const h2 *>(tl + V4_ZERO)[l];
-            const uint32_t vi = reinterpret_cast<const uint16_t *>(tl + V4_IDX)[l];
-            const float2 pp = reinterpret_cast<const float2 *>(pbuf)[l & 15];
-            const float w0 = pp.x * ((float)vo[0] - (float)vz[0]), w1 = pp.y * ((float)vo[1] - (float)vz[1]);
-            const FixScale vfix = fix_scale(wave_max_abs2(w0, w1));
-            int32_t h0, l0, h1, l1;
-            fix_split(w0, vfix, h0, l0);
-            fix_split(w1, vfix, h1, l1);
-            int32_t *cg = vacc + 2 * 32 * (l >> 4);
-            wave_lds_order();
-            reinterpret_cast<int4 *>(vacc)[l] = int4{0, 0, 0, 0};
-            wave_lds_order();
-            lds_add(cg + 2 * (vi & 31u), h0);
-            lds_add(cg + 2 * (vi & 31u) + 1, l0);
-            lds_add(cg + 2 * ((vi >> 8) & 31u), h1);
-            lds_add(cg + 2 * ((vi >> 8) & 31u) + 1, l1);
+        if constexpr (SPARSE) {   // the value-outlier sums of channels 2l, 2l+1
             wave_lds_order();
             const int4 cv = reinterpret_cast<const int4 *>(vacc)[l];
             ow0 += fix_join(cv.x, cv.y, vfix);
