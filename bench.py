@@ -137,6 +137,40 @@ def cpu_baseline(w, queries, n_slices, context):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def hbm_read_ceiling(nbytes, reps=20):
+    """The box's achievable HBM read bandwidth: a plain streaming read (`libkvq_probe.so`, every 16-byte chunk of
+    the buffer loaded once) of a buffer as large as one decode call's bytes, `reps` back-to-back launches between two
+    HIP events on the current stream."""
+    import ctypes
+
+    import torch
+    lib = ctypes.CDLL(os.path.join(ROOT, "decode_attention_quant_amd", "libkvq_probe.so"))
+    lib.kvq_probe_sink_words.restype = ctypes.c_size_t
+    lib.kvq_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p]
+    nbytes = (int(nbytes) + 15) // 16 * 16
+    buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    nsink = lib.kvq_probe_sink_words()
+    sink = torch.empty(nsink, dtype=torch.int32, device="cuda")
+    st = torch.cuda.current_stream().cuda_stream
+    call = lambda: lib.kvq_probe_hbm_read(buf.data_ptr(), nbytes, sink.data_ptr(), nsink, st)
+    for _ in range(3):
+        if call() != 0:
+            raise RuntimeError("kvq_probe_hbm_read failed")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    gbs = nbytes / us / 1e3
+    del buf, sink
+    return {"gb_s": gbs, "frac_of_peak": gbs / PEAK_GBS, "bytes": nbytes, "us_per_launch": us, "launches": reps,
+            "kernel": "hbm_read_kernel (libkvq_probe.so): 2048 wavefronts, one contiguous segment each, eight "
+                      "1 KB loads in flight"}
+
+
 def fp16_comparator(kvq, w, Kd, Vd, q, context, call_us_2bit, calls):
     """The same decode-attention call over an all-fp16 cache of the same context: a window as large as the context,
     so nothing is quantized (same library, same kernel, fp16 tiles only). Timed with HIP events over `calls` calls
@@ -276,6 +310,7 @@ def main(argv=None):
     ap.add_argument("--cpu-slices", type=int, default=24)
     ap.add_argument("--cpu-queries", type=int, default=12)
     ap.add_argument("--no-fp16-comparator", action="store_true")
+    ap.add_argument("--no-hbm-ceiling", action="store_true")
     ap.add_argument("--fp16-calls", type=int, default=20)
     ap.add_argument("--step-graph", action="store_true",
                     help="decode-step time: host API vs ragged step vs ragged step in a HIP graph "
@@ -436,6 +471,12 @@ def main(argv=None):
                      "frac": achieved / PEAK_GBS, "traffic": traffic_per_launch(w.name),
                      "kernel": kernel, "bytes_per_call": sum(call_bytes) / K},
     }
+    if not args.no_hbm_ceiling:
+        ceil = hbm_read_ceiling(res["roofline"]["bytes_per_call"])
+        ceil["decode_frac_of_ceiling"] = achieved / ceil["gb_s"]
+        res["hbm_read_ceiling"] = ceil
+        log(f"[bench] streaming-read ceiling {ceil['gb_s']:.0f} GB/s ({100 * ceil['frac_of_peak']:.1f}% of "
+            f"{PEAK_GBS:.0f}); the decode call reaches {100 * ceil['decode_frac_of_ceiling']:.1f}% of it")
     if not args.no_fp16_comparator and w.bits == 2:
         res["fp16_comparator"] = fp16_comparator(kvq, w, Kd, Vd, Q[W], contexts[0], res["decode_call_us"],
                                                  args.fp16_calls)

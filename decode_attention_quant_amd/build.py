@@ -10,6 +10,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libkvq.so")
 SOURCES = ["kvq_kernels.hip", "kvq_kernels_b4.hip", "kvq_api.hip"]
+# measurement helper for bench.py (a plain streaming read); not part of the cache library
+PROBE_LIB = os.path.join(PKG, "libkvq_probe.so")
+PROBE_SOURCES = ["kvq_probe.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",
@@ -36,10 +39,9 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source of the library; returns the path of the shared library."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
+def _compile(sources, lib: str, verbose: bool) -> str:
+    srcs = [os.path.join(CSRC, s) for s in sources]
+    tmp = lib + ".tmp"
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", os.path.join(ROOT, "include"), "-I", CSRC, *srcs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -50,8 +52,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source of the library (and the benchmark's read probe); returns the library's path."""
+    path = _compile(SOURCES, LIB, verbose)
+    _compile(PROBE_SOURCES, PROBE_LIB, verbose)
+    return path
 
 
 if __name__ == "__main__":

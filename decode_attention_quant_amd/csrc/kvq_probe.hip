@@ -1,0 +1,56 @@
+// Measurement helper for the benchmark (not part of the cache library): a plain streaming read of a device buffer,
+// the achievable HBM read bandwidth of the box to report next to the published peak. Built as libkvq_probe.so.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr int kWaves = 2048;   // one 64-lane workgroup per wavefront, 8 per CU; one contiguous segment each
+constexpr int kVec = 8;        // 1 KB loads in flight per wavefront
+
+// Wavefront w reads its contiguous segment of src (a multiple of 1 KB, the last one shorter) with 16-byte loads,
+// kVec consecutive kilobytes per iteration, folded by XOR into one word per lane, which is written so the loads are
+// kept. (A shape sweep on MI355X, 2048..65536 wavefronts with 4..16 loads in flight, gave 5.7-6.1 TB/s, best with
+// the fewest wavefronts; a grid-stride order with 8 MB between a wavefront's loads gave 5.5.)
+__global__ __launch_bounds__(64) void hbm_read_kernel(const uint4 *src, size_t n16, size_t per, uint32_t *sink) {
+    const size_t beg = (size_t)blockIdx.x * per;
+    const size_t end = beg + per < n16 ? beg + per : n16;
+    uint32_t acc = 0;
+    size_t i = beg + threadIdx.x;
+    for (; i + (kVec - 1) * 64 < end; i += kVec * 64) {
+        uint4 b[kVec];
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) b[k] = src[i + k * 64];
+#pragma unroll
+        for (int k = 0; k < kVec; ++k) acc ^= b[k].x ^ b[k].y ^ b[k].z ^ b[k].w;
+    }
+    for (; i < end; i += 64) {
+        const uint4 a = src[i];
+        acc ^= a.x ^ a.y ^ a.z ^ a.w;
+    }
+    sink[(size_t)blockIdx.x * 64 + threadIdx.x] = acc;
+}
+
+}  // namespace
+
+extern "C" {
+
+__attribute__((visibility("default"))) size_t kvq_probe_sink_words(void) { return (size_t)kWaves * 64; }
+
+// src: device, 16-byte aligned, bytes a positive multiple of 16; sink: device, at least kvq_probe_sink_words()
+// uint32 words. Returns 0 on success, -1 on bad arguments (nothing launched), -8 on a launch error.
+__attribute__((visibility("default"))) int kvq_probe_hbm_read(const void *src, size_t bytes, uint32_t *sink,
+                                                               size_t sink_words, void *stream) {
+    if (!src || !sink || bytes == 0 || bytes % 16 != 0 || (reinterpret_cast<uintptr_t>(src) & 15u) != 0 ||
+        sink_words < (size_t)kWaves * 64)
+        return -1;
+    const size_t n16 = bytes / 16;
+    const size_t per = ((n16 + kWaves - 1) / kWaves + 63) / 64 * 64;   // 16-byte units per wavefront
+    const unsigned grid = (unsigned)((n16 + per - 1) / per);            // <= kWaves
+    hipLaunchKernelGGL(hbm_read_kernel, dim3(grid), dim3(64), 0, static_cast<hipStream_t>(stream),
+                       static_cast<const uint4 *>(src), n16, per, sink);
+    return hipGetLastError() == hipSuccess ? 0 : -8;
+}
+
+}  // extern "C"

@@ -239,3 +239,23 @@ def test_ragged_splits_follow_capacity(kvq):
     s = _shape(kvq, batch=3, kv_heads=2, q_heads=8, max_tokens=1024)
     full = _cache(kvq, 1024, 128)
     assert lib.kv_ragged_splits(ctypes.byref(s)) == lib.kv_decode_attention_splits(ctypes.byref(s), ctypes.byref(full))
+
+
+def test_read_probe_rejects_bad_arguments_before_launching():
+    """The benchmark's streaming-read probe (a separate library) validates on the host: nothing is launched here."""
+    import os
+    import decode_attention_quant_amd as pkg
+    path = os.path.join(os.path.dirname(pkg.__file__), "libkvq_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("probe library not built")
+    lib = ctypes.CDLL(path)
+    lib.kvq_probe_sink_words.restype = ctypes.c_size_t
+    lib.kvq_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p]
+    n = lib.kvq_probe_sink_words()
+    assert n > 0
+    assert lib.kvq_probe_hbm_read(None, 1 << 20, FAKE, n, None) == -1
+    assert lib.kvq_probe_hbm_read(FAKE, 1 << 20, None, n, None) == -1
+    assert lib.kvq_probe_hbm_read(FAKE, 1000, FAKE, n, None) == -1          # not a multiple of 16
+    assert lib.kvq_probe_hbm_read(FAKE + 8, 1 << 20, FAKE, n, None) == -1   # misaligned
+    assert lib.kvq_probe_hbm_read(FAKE, 1 << 20, FAKE, n - 1, None) == -1   # sink too small
