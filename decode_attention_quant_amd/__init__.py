@@ -45,7 +45,7 @@ class KvqCache(ctypes.Structure):
 
 class KvqRagged(ctypes.Structure):
     _fields_ = [("tiles", ctypes.c_void_p), ("k_res", ctypes.c_void_p), ("v_res", ctypes.c_void_p),
-                ("sink", ctypes.c_void_p), ("lens", ctypes.c_void_p)]
+                ("sink", ctypes.c_void_p), ("lens", ctypes.c_void_p), ("sync", ctypes.c_void_p)]
 
 
 class KvqError(RuntimeError):
@@ -72,6 +72,7 @@ def _load():
         "kv_ragged_append": (ctypes.c_int, [SP, RP, P, P, I64, I64, P]),
         "kv_ragged_splits": (I32, [SP]),
         "kv_ragged_workspace_bytes": (ctypes.c_size_t, [SP]),
+        "kv_ragged_sync_words": (ctypes.c_size_t, [SP]),
         "kv_ragged_decode_attention": (ctypes.c_int, [SP, RP, P, F, P, P, ctypes.c_size_t, P]),
         "kv_ragged_decode_step": (ctypes.c_int, [SP, RP, P, P, I64, I64, P, F, P, P, ctypes.c_size_t, P]),
     }
@@ -86,7 +87,8 @@ _lib = _load()
 EXPORTS = ("kv_quant_keys_per_channel", "kv_quant_values_per_token", "kv_append_and_flush",
            "kv_decode_attention_splits", "kv_decode_attention_workspace_bytes", "kv_decode_attention",
            "kvq_status_string", "kv_ragged_prefill", "kv_ragged_append", "kv_ragged_splits",
-           "kv_ragged_workspace_bytes", "kv_ragged_decode_attention", "kv_ragged_decode_step")
+           "kv_ragged_workspace_bytes", "kv_ragged_sync_words", "kv_ragged_decode_attention",
+           "kv_ragged_decode_step")
 
 
 def library():
@@ -239,8 +241,11 @@ class RaggedCache:
                                  device=device)
         self.v_res = torch.zeros_like(self.k_res)
         self.lens = torch.zeros((shape.batch, 4), dtype=torch.int32, device=device)
+        # completion counters of the single-launch decode step (zero, and left zero by every step)
+        self.sync = torch.zeros(library().kv_ragged_sync_words(ctypes.byref(self._cshape)), dtype=torch.int32,
+                                device=device)
         self.c = KvqRagged(self.tiles.data_ptr(), self.k_res.data_ptr(), self.v_res.data_ptr(), None,
-                           self.lens.data_ptr())
+                           self.lens.data_ptr(), self.sync.data_ptr())
 
     def lengths(self):
         """Host copy of the per-sequence (n_quant, n_resid, n_sink, status) rows (synchronizes)."""

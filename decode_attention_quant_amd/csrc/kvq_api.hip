@@ -181,6 +181,14 @@ kvq::DecodeArgs ragged_args(const kvq_shape *shape, const kvq_ragged *cache, con
     a.sm_log2 = (sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)KVQ_HEAD_DIM)) * 1.4426950408889634f;
     a.lens = cache->lens;
     a.appended = appended;
+    a.k_new = nullptr;
+    a.v_new = nullptr;
+    a.new_sb = a.new_sh = 0;
+    a.tiles_w = nullptr;
+    a.k_res_w = nullptr;
+    a.v_res_w = nullptr;
+    a.lens_w = nullptr;
+    a.sync = nullptr;
     return a;
 }
 
@@ -357,6 +365,14 @@ int kv_decode_attention(const kvq_shape *shape, const kvq_cache *cache, const vo
     a.sm_log2 = sm_scale * 1.4426950408889634f;
     a.lens = nullptr;
     a.appended = 0;
+    a.k_new = nullptr;
+    a.v_new = nullptr;
+    a.new_sb = a.new_sh = 0;
+    a.tiles_w = nullptr;
+    a.k_res_w = nullptr;
+    a.v_res_w = nullptr;
+    a.lens_w = nullptr;
+    a.sync = nullptr;
     return launched(kvq::launch_decode(a, p.splits, st));
 }
 
@@ -439,15 +455,25 @@ int kv_ragged_decode_step(const kvq_shape *shape, const kvq_ragged *cache, const
     if ((e = check_src(v_new, stride_b, stride_h, 0))) return e;
     const SplitPlan p = ragged_plan(shape);
     if ((e = check_decode_io(shape, p, q, out, workspace, workspace_bytes))) return e;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    const kvq::TokSrc kn = single_src(k_new, stride_b, stride_h, 0), vn = single_src(v_new, stride_b, stride_h, 0);
-    if ((e = launched(kvq::launch_ragged_flush_append(
-             kn, vn, shape->batch, shape->kv_heads, static_cast<uint8_t *>(cache->tiles),
-             shape->max_tokens / KVQ_TILE_TOKENS, static_cast<_Float16 *>(cache->k_res),
-             static_cast<_Float16 *>(cache->v_res), shape->residual_cap, cache->lens, s))))
-        return e;
-    const kvq::DecodeArgs a = ragged_args(shape, cache, p, q, sm_scale, out, workspace, 1);
-    return launched(kvq::launch_decode_ragged(a, p.splits, cache->lens, 1, s));
+    if (!cache->sync) return KVQ_E_NULL;
+    if ((reinterpret_cast<uintptr_t>(cache->sync) & 3u) != 0) return KVQ_E_ALIGN;
+    kvq::DecodeArgs a = ragged_args(shape, cache, p, q, sm_scale, out, workspace, 0);
+    a.k_new = static_cast<const _Float16 *>(k_new);
+    a.v_new = static_cast<const _Float16 *>(v_new);
+    a.new_sb = stride_b;
+    a.new_sh = stride_h;
+    a.tiles_w = static_cast<uint8_t *>(cache->tiles);
+    a.k_res_w = static_cast<_Float16 *>(cache->k_res);
+    a.v_res_w = static_cast<_Float16 *>(cache->v_res);
+    a.lens_w = cache->lens;
+    a.sync = cache->sync;
+    return launched(kvq::launch_decode_step(a, p.splits, static_cast<hipStream_t>(stream)));
+}
+
+size_t kv_ragged_sync_words(const kvq_shape *shape) {
+    if (check_shape(shape) || shape->bits != 2 || shape->flags != 0) return 0;
+    const int64_t chunks = (shape->q_heads / shape->kv_heads + 3) / 4;
+    return (size_t)shape->batch * (size_t)(1 + (int64_t)shape->kv_heads * chunks);
 }
 
 }  // extern "C"

@@ -36,6 +36,17 @@ struct DecodeArgs {
     float sm_log2;        // softmax scale * log2(e)
     const int32_t *lens;  // ragged caches: per-sequence {n_quant, n_resid, n_sink, status}; else null
     int appended;         // ragged: the lengths predate the append of one token per sequence (decode step)
+    // single-launch decode step (ragged caches): the new token of every (batch row, KV head) at
+    // k_new/v_new + b new_sb + h new_sh; the launch flushes full windows, attends, merges the splits, writes the
+    // new rows and commits the lengths, counting finished workgroups in `sync` (zero before and after)
+    const _Float16 *k_new;
+    const _Float16 *v_new;
+    int64_t new_sb, new_sh;
+    uint8_t *tiles_w;
+    _Float16 *k_res_w;
+    _Float16 *v_res_w;
+    int32_t *lens_w;
+    uint32_t *sync;
 };
 
 // 4-bit (KVQuant-style) decode: one wavefront per (batch row, query head, token split). Virtual tiles v of a
@@ -88,5 +99,7 @@ hipError_t launch_ragged_commit(int32_t *lens, int batch, int res_cap, hipStream
 hipError_t launch_ragged_set(int32_t *lens, int b, int nq, int nr, int ns, hipStream_t st);
 // pass 1 over per-sequence lengths, then pass 2 (which commits the appended token's lengths when `commit`)
 hipError_t launch_decode_ragged(const DecodeArgs &a, int splits, int32_t *lens, int commit, hipStream_t st);
+// the whole decode step (append with lazy flush, attention, merge, length commit) in one launch
+hipError_t launch_decode_step(const DecodeArgs &a, int splits, hipStream_t st);
 
 }  // namespace kvq

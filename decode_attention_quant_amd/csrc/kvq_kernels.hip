@@ -274,6 +274,87 @@ __device__ __forceinline__ h4 read_tr16(const _Float16 *lds) {
     return __builtin_bit_cast(h4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s4 *)lds));
 }
 
+constexpr int PASS2_MAX_SPLITS = 1024;
+
+// Device-coherent access to split partials that another workgroup of the same launch reads (device-scope relaxed
+// atomics: the store writes through to the device's point of coherence, the load reads from it).
+__device__ __forceinline__ void coherent_store(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float coherent_load(const float *p) {
+    return __hip_atomic_load(const_cast<float *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// The merge of one (batch row, query head) row bh by one wavefront; `wts` is LDS for `splits` floats. With
+// zero_empty, a row with no token (every split empty) gets zeros. COHERENT: the partials were written in this launch
+// (read through coherent loads).
+template <bool COHERENT = false>
+__device__ __forceinline__ void merge_splits(const float *part_o, const float *part_ml, float *out, int splits,
+                                             int64_t bh, float *wts, bool zero_empty) {
+    auto ld = [](const float *p) { return COHERENT ? coherent_load(p) : *p; };
+    const int l = threadIdx.x;
+    const float *pm = part_ml + bh * splits * 2;
+    const float2 *po = reinterpret_cast<const float2 *>(part_o + bh * splits * D) + l;
+    auto ld2 = [&](int k) -> float2 {
+        if constexpr (COHERENT) {
+            const float *f = reinterpret_cast<const float *>(po + k * (D / 2));
+            return float2{coherent_load(f), coherent_load(f + 1)};
+        } else {
+            return po[k * (D / 2)];
+        }
+    };
+    // the first eight splits' partial outputs are loaded together with the (m, l) pairs (one memory round trip
+    // for up to eight splits)
+    float2 first[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) first[k] = k < splits ? ld2(k) : float2{0.0f, 0.0f};
+    const float NEG_INF = -__builtin_inff();
+    float M = NEG_INF;
+    for (int sp = l; sp < splits; sp += 64) M = fmaxf(M, ld(pm + 2 * sp));
+    M = rows_max(row16_max(M));
+    float L = 0.0f;
+    for (int sp = l; sp < splits; sp += 64) {
+        const float ms = ld(pm + 2 * sp);
+        const float w = (ms == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
+        wts[sp] = w;
+        L += w * ld(pm + 2 * sp + 1);
+    }
+    L = rows_sum(row16_sum(L));
+    __syncthreads();
+    if (zero_empty && !(L > 0.0f)) {
+        reinterpret_cast<float2 *>(out + bh * D)[l] = float2{0.0f, 0.0f};
+        return;
+    }
+    float o0 = 0.0f, o1 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        if (k < splits) {
+            const float w = wts[k];
+            o0 = fmaf(w, first[k].x, o0);
+            o1 = fmaf(w, first[k].y, o1);
+        }
+    }
+    int sp = 8;
+    for (; sp + 8 <= splits; sp += 8) {
+        float2 v[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) v[k] = ld2(sp + k);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float w = wts[sp + k];
+            o0 = fmaf(w, v[k].x, o0);
+            o1 = fmaf(w, v[k].y, o1);
+        }
+    }
+    for (; sp < splits; ++sp) {
+        const float2 v = ld2(sp);
+        const float w = wts[sp];
+        o0 = fmaf(w, v.x, o0);
+        o1 = fmaf(w, v.y, o1);
+    }
+    reinterpret_cast<float2 *>(out + bh * D)[l] = float2{o0 / L, o1 / L};
+}
+
 // One wavefront per (split, batch row, KV head, chunk of up to 4 query heads of that KV head); lane l = n + 16 kc.
 //
 // Scores. The query with the tile's key scales folded in, q~[h][c] = q'[h][c] s_K[c], is split into an fp16 high
@@ -305,7 +386,19 @@ constexpr int LDS_ZERO = 3088;       // 256 zero bytes: A-operand rows 4 h + 2, 
 constexpr int LDS_P = 8192;          // fp32 [4 heads][16][2]: p of tokens i and 16 + i
 constexpr int LDS_BYTES = 8704;      // [0, 8192) also holds the fp16 window value tile [32][128]
 
-template <bool RAGGED>
+// MODE: 0 uniform lengths; 1 per-sequence lengths (ragged); 2 the single-launch ragged decode step (below).
+//
+// Decode step (MODE 2). Every workgroup derives the step of its sequence from the lengths before it (append the
+// token; a full window is flushed first; a sequence whose flush would pass the capacity refuses the token and is
+// marked full) and attends over the state after it. A workgroup whose split holds tiles of the flushed window
+// quantizes those tiles itself (the same quantizer functions as the flush kernel; workgroups of the other query-head
+// chunks of that KV head write identical bytes) and reads them back. The new token is attended straight from the
+// input (its window row is written only at the end). After its partials are stored, a workgroup counts itself in
+// sync[(b, KV head, chunk)] behind a device-scope fence; the last of the splits merges them (the pass-2 code) and
+// counts the chunk in sync[b]; the last chunk of the sequence writes the new window rows and the lengths, by when
+// every workgroup of the sequence has read them. Counters are reset by the workgroup that completes them. No
+// workgroup waits for another.
+template <int MODE>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void decode_pass1_kernel(DecodeArgs a) {
     __shared__ __align__(16) unsigned char smem[LDS_BYTES];
     uint32_t *sz_lds = reinterpret_cast<uint32_t *>(smem + LDS_SZ);
@@ -315,16 +408,78 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     float *p_lds = reinterpret_cast<float *>(smem + LDS_P);
     _Float16 *vres_lds = reinterpret_cast<_Float16 *>(smem);
 
+    // MODE 2 keeps the workgroup's uniform indices and lengths in scalar registers (integer division runs on the
+    // vector unit; without this they stay in vector registers and spill around the in-kernel flush)
+    auto uni = [](int x) { return MODE == 2 ? __builtin_amdgcn_readfirstlane(x) : x; };
     const int l = threadIdx.x;
     const int n = l & 15, kc = l >> 4, hl = n >> 2, g = n & 3;
     const int unit = blockIdx.x;
     const int split = gridDim.y - 1 - blockIdx.y;   // the split holding the fp16 window tiles is dispatched first
-    const int chunk = unit % a.chunks;
-    const int hkv = (unit / a.chunks) % a.kv_heads;
-    const int b = unit / (a.chunks * a.kv_heads);
+    const int chunk = uni(unit % a.chunks);
+    const int hkv = uni((unit / a.chunks) % a.kv_heads);
+    const int b = uni(unit / (a.chunks * a.kv_heads));
     const int G = a.q_heads / a.kv_heads;
     const int gc = min(4, G - 4 * chunk);
     const int h0 = hkv * G + 4 * chunk;
+
+    int n_qtiles = a.n_qtiles, n_resid = a.n_resid, tiles_per_split = a.tiles_per_split;
+    int flush_t0 = -1;   // MODE 2: first tile of the window this step flushes (or -1)
+    int new_row = -1;    // MODE 2: window row of the token this step appends (or -1)
+    bool refuse = false; // MODE 2: the flush does not fit: the token is refused and the sequence marked full
+    if constexpr (MODE != 0) {   // this sequence's lengths; the splits share its tiles evenly
+        const int32_t *ln = a.lens + 4 * b;
+        int nq = ln[0], nr = ln[1];
+        if constexpr (MODE == 1) {
+            if (a.appended) ragged_after_append(ln, a.res_cap, nq, nr);
+        } else if (ln[3] == 0) {
+            if (nr == a.res_cap) {
+                if ((int64_t)nq + a.res_cap <= a.max_tiles * 32) {
+                    flush_t0 = nq / 32;
+                    nq += nr;
+                    nr = 1;
+                    new_row = 0;
+                } else {
+                    refuse = true;
+                }
+            } else {
+                new_row = nr;
+                nr += 1;
+            }
+        }
+        n_qtiles = uni(nq / 32);
+        n_resid = uni(nr);
+        tiles_per_split = uni((n_qtiles + (n_resid + 31) / 32 + (int)gridDim.y - 1) / (int)gridDim.y);
+        flush_t0 = uni(flush_t0);
+        new_row = uni(new_row);
+    }
+    const int n_vt = n_qtiles + (n_resid + 31) / 32;
+    const int v0 = uni(split * tiles_per_split);
+    const int v1 = uni(min(v0 + tiles_per_split, n_vt));
+    const int qend = uni(min(v1, n_qtiles));
+    const uint8_t *base = a.tiles + ((int64_t)b * a.kv_heads + hkv) * a.max_tiles * (int64_t)REC;
+
+    if constexpr (MODE == 2) {   // flushed tiles in this split: quantize them from the window (LDS from offset 0)
+        const int f0 = max(v0, flush_t0), f1 = min(qend, flush_t0 + a.res_cap / 32);
+        if (flush_t0 >= 0 && f0 < f1) {
+            TokSrc wk;
+            wk.a = a.k_res; wk.a_sb = (int64_t)a.kv_heads * a.res_cap * D; wk.a_sh = (int64_t)a.res_cap * D;
+            wk.a_st = D; wk.n_a = INT64_MAX;
+            wk.b = wk.a; wk.b_sb = wk.a_sb; wk.b_sh = wk.a_sh; wk.b_st = wk.a_st;
+            TokSrc wv = wk;
+            wv.a = a.v_res; wv.b = a.v_res;
+            uint32_t *words = reinterpret_cast<uint32_t *>(smem);
+            _Float16 *sv = reinterpret_cast<_Float16 *>(smem + 1024), *zv = sv + 128;
+            float *gp = reinterpret_cast<float *>(smem + 1536);
+            for (int t = f0; t < f1; ++t) {
+                uint8_t *rec = a.tiles_w + (((int64_t)b * a.kv_heads + hkv) * a.max_tiles + t) * REC;
+                quant_keys_tile(wk, 32 * (t - flush_t0), b, hkv, rec, words);
+                __syncthreads();
+                quant_values_tile(wv, 32 * (t - flush_t0), b, hkv, rec, words, sv, zv, gp);
+                __syncthreads();
+            }
+            __threadfence_block();   // the records are read back below by this workgroup
+        }
+    }
 
     // ---- query: lane (n, kc) holds head kc of the chunk (if valid), channels 8n .. 8n+7, scaled by 2^-E with
     // 2^E > max |q| of that head (qmax is a float16 value widened, hence a normal binary32 number: its exponent
@@ -355,19 +510,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
 #pragma unroll
     for (int j = 0; j < 8; ++j) o[j] = f4{0.0f, 0.0f, 0.0f, 0.0f};
 
-    int n_qtiles = a.n_qtiles, n_resid = a.n_resid, tiles_per_split = a.tiles_per_split;
-    if constexpr (RAGGED) {   // this sequence's lengths; the splits share its tiles evenly
-        int nq = a.lens[4 * b], nr = a.lens[4 * b + 1];
-        if (a.appended) ragged_after_append(a.lens + 4 * b, a.res_cap, nq, nr);
-        n_qtiles = nq / 32;
-        n_resid = nr;
-        tiles_per_split = (n_qtiles + (n_resid + 31) / 32 + (int)gridDim.y - 1) / (int)gridDim.y;
-    }
-    const int n_vt = n_qtiles + (n_resid + 31) / 32;
-    const int v0 = split * tiles_per_split;
-    const int v1 = min(v0 + tiles_per_split, n_vt);
-    const int qend = min(v1, n_qtiles);
-    const uint8_t *base = a.tiles + ((int64_t)b * a.kv_heads + hkv) * a.max_tiles * (int64_t)REC;
 
     // s0, s1: raw score minus mr of head kc for tokens n and 16 + n of the tile (-inf for absent tokens).
     // Raises mr to the tile maximum where it is exceeded (every head on the first tile) and rescales.
@@ -509,11 +651,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
             for (int i = 0; i < 8; ++i) lds_dma16(src + 1024 * i, vt_base + 1024 * i);
         };
         // key rows of tokens n and 16 + n (clamped to the window's length), channels 32 ks + 8 kc ..
+        // MODE 2: the appended token's row comes from the input
+        const _Float16 *knew_row = (MODE == 2 && new_row >= 0) ? a.k_new + b * a.new_sb + hkv * a.new_sh : nullptr;
+        auto krow = [&](int row) -> const _Float16 * {
+            if constexpr (MODE == 2) {
+                if (row == new_row) return knew_row;
+            }
+            return kres + (int64_t)row * D;
+        };
         auto k_load = [&](int v, h8 kr[8]) {
             const int r0 = (v - n_qtiles) * 32;
             const int nv = min(32, n_resid - r0);
-            const _Float16 *k0 = kres + (int64_t)(r0 + min(n, nv - 1)) * D + 8 * kc;
-            const _Float16 *k1 = kres + (int64_t)(r0 + min(16 + n, nv - 1)) * D + 8 * kc;
+            const _Float16 *k0 = krow(r0 + min(n, nv - 1)) + 8 * kc;
+            const _Float16 *k1 = krow(r0 + min(16 + n, nv - 1)) + 8 * kc;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 kr[ks] = *reinterpret_cast<const h8 *>(k0 + 32 * ks);
@@ -559,6 +709,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
                 }
                 wait_lgkmcnt0();
             }
+            if constexpr (MODE == 2) {   // the appended token's value row, from the input
+                if (new_row >= r0 && new_row < r0 + 32) {
+                    if (l < 16)
+                        reinterpret_cast<uint4 *>(vres_lds + (new_row - r0) * D)[l] =
+                            reinterpret_cast<const uint4 *>(a.v_new + b * a.new_sb + hkv * a.new_sh)[l];
+                    wait_lgkmcnt0();
+                }
+            }
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const h4 lo4 = read_tr16(vt0 + 16 * j);
@@ -583,12 +741,75 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     if (kc < gc) {   // lane (n, kc) holds head h0 + kc, channels n + 16 j
         const int hq = h0 + kc;
         float *po = a.part_o + (((int64_t)b * a.q_heads + hq) * S + split) * D;
+        float *pm = a.part_ml + (((int64_t)b * a.q_heads + hq) * S + split) * 2;
+        const float m_out = seen ? mr * C : -__builtin_inff();
+        if constexpr (MODE == 2) {   // read by the merging workgroup of this launch
 #pragma unroll
-        for (int j = 0; j < 8; ++j) po[n + 16 * j] = o[j][j >> 1] + gr[j >> 1];
-        if (n == 0) {
-            float *pm = a.part_ml + (((int64_t)b * a.q_heads + hq) * S + split) * 2;
-            pm[0] = seen ? mr * C : -__builtin_inff();
-            pm[1] = lsum;
+            for (int j = 0; j < 8; ++j) coherent_store(po + n + 16 * j, o[j][j >> 1] + gr[j >> 1]);
+            if (n == 0) {
+                coherent_store(pm, m_out);
+                coherent_store(pm + 1, lsum);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) po[n + 16 * j] = o[j][j >> 1] + gr[j >> 1];
+            if (n == 0) {
+                pm[0] = m_out;
+                pm[1] = lsum;
+            }
+        }
+    }
+
+    if constexpr (MODE == 2) {
+        // count this split once its partial stores are complete (and every load of this workgroup, so the cache
+        // state it read may be overwritten once all are counted); the last one merges the chunk's heads
+        wait_vmcnt<0>();
+        uint32_t *cnt = a.sync + a.batch + ((int64_t)b * a.kv_heads + hkv) * a.chunks + chunk;
+        uint32_t prev = 0u;
+        if (l == 0) prev = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        prev = __shfl(prev, 0);
+        if (prev + 1u != (uint32_t)S) return;
+        if (l == 0) *cnt = 0u;
+        float *wts = reinterpret_cast<float *>(smem);   // S <= PASS2_MAX_SPLITS floats
+        __syncthreads();
+        for (int k = 0; k < gc; ++k) {
+            merge_splits<true>(a.part_o, a.part_ml, a.out, (int)S, (int64_t)b * a.q_heads + h0 + k, wts, true);
+            __syncthreads();
+        }
+        // the appended token's window rows of KV head h: with one chunk per KV head, every reader of that window
+        // is counted by now, so this workgroup writes them; otherwise the sequence's last workgroup writes all
+        auto write_rows = [&](int h) {
+            const int64_t dst = (((int64_t)b * a.kv_heads + h) * a.res_cap + new_row) * D;
+            const int64_t src = b * a.new_sb + h * a.new_sh;
+            const uint32_t kw = reinterpret_cast<const uint32_t *>(a.k_new + src)[l];
+            const uint32_t vw = reinterpret_cast<const uint32_t *>(a.v_new + src)[l];
+            reinterpret_cast<uint32_t *>(a.k_res_w + dst)[l] = kw;
+            reinterpret_cast<uint32_t *>(a.v_res_w + dst)[l] = vw;
+        };
+        if (a.chunks == 1 && new_row >= 0) write_rows(hkv);
+        // count the chunk; the last chunk of the sequence writes the lengths (every workgroup of the sequence has
+        // finished reading them)
+        wait_vmcnt<0>();
+        uint32_t *cb = a.sync + b;
+        if (l == 0) prev = __hip_atomic_fetch_add(cb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        prev = __shfl(prev, 0);
+        if (prev + 1u != (uint32_t)(a.kv_heads * a.chunks)) return;
+        if (l == 0) *cb = 0u;
+        if (new_row >= 0) {
+            if (a.chunks > 1) {
+                int h = 0;
+                for (; h + 4 <= a.kv_heads; h += 4) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) write_rows(h + k);
+                }
+                for (; h < a.kv_heads; ++h) write_rows(h);
+            }
+            if (l == 0) {
+                a.lens_w[4 * b] = n_qtiles * 32;
+                a.lens_w[4 * b + 1] = n_resid;
+            }
+        } else if (refuse && l == 0) {
+            a.lens_w[4 * b + 3] = 1;
         }
     }
 }
@@ -600,16 +821,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
 // eight splits per batch of loads. Empty splits carry m = -inf and weight 0.
 // Ragged caches: a sequence with no token gives zeros, and with `commit` the workgroup of each sequence's first query
 // head makes the appended token visible in its lengths (every pass-1 read of them is complete by now).
-constexpr int PASS2_MAX_SPLITS = 1024;
 template <bool RAGGED>
 __global__ __launch_bounds__(64) void decode_pass2_kernel(const float *part_o, const float *part_ml, float *out,
                                                           int splits, int32_t *lens, int q_heads, int res_cap,
                                                           int commit) {
     __shared__ float wts[PASS2_MAX_SPLITS];
     const int64_t bh = blockIdx.x;
-    const int l = threadIdx.x;
     if constexpr (RAGGED) {
-        if (commit && l == 0 && bh % q_heads == 0) {
+        if (commit && threadIdx.x == 0 && bh % q_heads == 0) {
             int32_t *ln = lens + 4 * (bh / q_heads);
             int nq, nr;
             ragged_after_append(ln, res_cap, nq, nr);
@@ -617,45 +836,7 @@ __global__ __launch_bounds__(64) void decode_pass2_kernel(const float *part_o, c
             ln[1] = nr;
         }
     }
-    const float *pm = part_ml + bh * splits * 2;
-    const float NEG_INF = -__builtin_inff();
-    float M = NEG_INF;
-    for (int sp = l; sp < splits; sp += 64) M = fmaxf(M, pm[2 * sp]);
-    M = rows_max(row16_max(M));
-    float L = 0.0f;
-    for (int sp = l; sp < splits; sp += 64) {
-        const float ms = pm[2 * sp];
-        const float w = (ms == NEG_INF) ? 0.0f : __builtin_amdgcn_exp2f(ms - M);
-        wts[sp] = w;
-        L += w * pm[2 * sp + 1];
-    }
-    L = rows_sum(row16_sum(L));
-    __syncthreads();
-    if (RAGGED && !(L > 0.0f)) {
-        reinterpret_cast<float2 *>(out + bh * D)[l] = float2{0.0f, 0.0f};
-        return;
-    }
-    const float2 *po = reinterpret_cast<const float2 *>(part_o + bh * splits * D) + l;
-    float o0 = 0.0f, o1 = 0.0f;
-    int sp = 0;
-    for (; sp + 8 <= splits; sp += 8) {
-        float2 v[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = po[(sp + k) * (D / 2)];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float w = wts[sp + k];
-            o0 = fmaf(w, v[k].x, o0);
-            o1 = fmaf(w, v[k].y, o1);
-        }
-    }
-    for (; sp < splits; ++sp) {
-        const float2 v = po[sp * (D / 2)];
-        const float w = wts[sp];
-        o0 = fmaf(w, v.x, o0);
-        o1 = fmaf(w, v.y, o1);
-    }
-    reinterpret_cast<float2 *>(out + bh * D)[l] = float2{o0 / L, o1 / L};
+    merge_splits(part_o, part_ml, out, splits, bh, wts, RAGGED);
 }
 
 // ------------------------------------------------------------------------------------------------ launchers
@@ -688,7 +869,7 @@ hipError_t launch_pass2(const float *part_o, const float *part_ml, float *out, i
 
 hipError_t launch_decode(const DecodeArgs &a, int splits, hipStream_t st) {
     const int units = a.batch * a.kv_heads * a.chunks;
-    hipLaunchKernelGGL(decode_pass1_kernel<false>, dim3((unsigned)units, (unsigned)splits), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(decode_pass1_kernel<0>, dim3((unsigned)units, (unsigned)splits), dim3(64), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_pass2(a.part_o, a.part_ml, a.out, a.batch * a.q_heads, splits, st);
@@ -696,11 +877,17 @@ hipError_t launch_decode(const DecodeArgs &a, int splits, hipStream_t st) {
 
 hipError_t launch_decode_ragged(const DecodeArgs &a, int splits, int32_t *lens, int commit, hipStream_t st) {
     const int units = a.batch * a.kv_heads * a.chunks;
-    hipLaunchKernelGGL(decode_pass1_kernel<true>, dim3((unsigned)units, (unsigned)splits), dim3(64), 0, st, a);
+    hipLaunchKernelGGL(decode_pass1_kernel<1>, dim3((unsigned)units, (unsigned)splits), dim3(64), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_pass2_kernel<true>, dim3((unsigned)(a.batch * a.q_heads)), dim3(64), 0, st, a.part_o,
                        a.part_ml, a.out, splits, lens, a.q_heads, a.res_cap, commit);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode_step(const DecodeArgs &a, int splits, hipStream_t st) {
+    const int units = a.batch * a.kv_heads * a.chunks;
+    hipLaunchKernelGGL(decode_pass1_kernel<2>, dim3((unsigned)units, (unsigned)splits), dim3(64), 0, st, a);
     return hipGetLastError();
 }
 

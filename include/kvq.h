@@ -241,6 +241,9 @@ KVQ_API int kv_decode_attention(const kvq_shape *shape, const kvq_cache *cache, 
  *   lens: device int32 [B][4], 16-byte aligned: {n_quant, n_resid, n_sink (0), status} of sequence b. A new cache
  *     has all zeros. status 1 marks a sequence whose flush did not fit max_tokens: its appends are refused from then
  *     on and its lengths stay, until it is prefilled again.
+ *   sync: device uint32 [kv_ragged_sync_words(shape)], 4-byte aligned, all zero when the cache is created; used by
+ *     kv_ragged_decode_step only (completion counters inside its single launch), which leaves it zero again.
+ *     Required by kv_ragged_decode_step (KVQ_E_NULL), ignored by the other calls.
  * Calls on one ragged cache must be issued on one stream, in order.
  */
 typedef struct kvq_ragged {
@@ -249,7 +252,11 @@ typedef struct kvq_ragged {
     void *v_res;
     void *sink;
     int32_t *lens;
+    uint32_t *sync;
 } kvq_ragged;
+
+/* Words of kvq_ragged.sync: B * (1 + Hkv * ceil((Hq / Hkv) / 4)). 0 on invalid arguments. */
+KVQ_API size_t kv_ragged_sync_words(const kvq_shape *shape);
 
 /*
  * Replaces sequence b's contents with n_tokens tokens (n_tokens >= 0; 0 empties it): k, v fp16 [Hkv][n_tokens][128]
@@ -286,9 +293,13 @@ KVQ_API int kv_ragged_decode_attention(const kvq_shape *shape, const kvq_ragged 
                                        void *stream);
 
 /*
- * One decode step: kv_ragged_append(k_new, v_new) then kv_ragged_decode_attention(q), in three launches (flush and
- * append, pass 1 over the lengths after the append, pass 2 which also commits the new lengths).
- * Errors: as kv_ragged_append and kv_ragged_decode_attention.
+ * One decode step: the result of kv_ragged_append(k_new, v_new) then kv_ragged_decode_attention(q), bit for bit, in a
+ * single launch (KIVI page, paragraphs on the recent-token window and on decoding from the grouped and residual
+ * parts). Every workgroup derives its sequence's step from the lengths before it; the workgroups whose token range
+ * holds a window being flushed quantize it themselves; the new token is attended from k_new/v_new; the last split of
+ * each (sequence, KV head, chunk of four query heads) merges the splits, and the last of a sequence writes the new
+ * window rows and lengths (counted in cache->sync, left zero). k_new, v_new must not alias the cache.
+ * Errors: as kv_ragged_append and kv_ragged_decode_attention; KVQ_E_NULL without cache->sync.
  */
 KVQ_API int kv_ragged_decode_step(const kvq_shape *shape, const kvq_ragged *cache, const void *k_new,
                                   const void *v_new, int64_t stride_b, int64_t stride_h, const void *q,

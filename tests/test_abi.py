@@ -201,8 +201,8 @@ def test_four_bit_splits_cover_every_query_head(kvq):
     assert S >= 1 and -(-n_vt // tps) == S and 16 * 32 * S <= 4096
 
 
-def _ragged(kvq, tiles=FAKE, k_res=FAKE + 4096, v_res=FAKE + 8192, lens=FAKE + 12288):
-    return kvq.KvqRagged(tiles, k_res, v_res, None, lens)
+def _ragged(kvq, tiles=FAKE, k_res=FAKE + 4096, v_res=FAKE + 8192, lens=FAKE + 12288, sync=None):
+    return kvq.KvqRagged(tiles, k_res, v_res, None, lens, sync)
 
 
 def test_ragged_validation(kvq):
@@ -226,10 +226,18 @@ def test_ragged_validation(kvq):
     dec = lambda ws, nbytes: lib.kv_ragged_decode_attention(ctypes.byref(s), ctypes.byref(r), FAKE, 0.0, FAKE, ws,
                                                             nbytes, None)
     assert dec(FAKE, need - 1) == kvq.E_WORKSPACE and dec(None, need) == kvq.E_WORKSPACE
-    step = lib.kv_ragged_decode_step(ctypes.byref(s), ctypes.byref(r), FAKE, FAKE, 256, 128, FAKE, 0.0, FAKE, FAKE,
-                                     need - 1, None)
-    assert step == kvq.E_WORKSPACE
+    step = lambda c, nbytes: lib.kv_ragged_decode_step(ctypes.byref(s), ctypes.byref(c), FAKE, FAKE, 256, 128, FAKE,
+                                                       0.0, FAKE, FAKE, nbytes, None)
+    rs = _ragged(kvq, sync=FAKE + 16384)
+    assert step(rs, need - 1) == kvq.E_WORKSPACE
+    assert step(r, need) == kvq.E_NULL                       # the single-launch step needs its counters
+    assert step(_ragged(kvq, sync=FAKE + 16386), need) == kvq.E_ALIGN
     assert lib.kv_ragged_splits(ctypes.byref(_shape(kvq, bits=4))) == 0
+    # counters: one per sequence plus one per (sequence, KV head, chunk of four query heads)
+    lib.kv_ragged_sync_words.restype = ctypes.c_size_t
+    assert lib.kv_ragged_sync_words(ctypes.byref(_shape(kvq, batch=3, kv_heads=2, q_heads=4))) == 3 * (1 + 2)
+    assert lib.kv_ragged_sync_words(ctypes.byref(_shape(kvq, batch=3, kv_heads=2, q_heads=20))) == 3 * (1 + 2 * 3)
+    assert lib.kv_ragged_sync_words(ctypes.byref(_shape(kvq, bits=4))) == 0
 
 
 def test_ragged_splits_follow_capacity(kvq):

@@ -1,9 +1,10 @@
 """GPU parity of ragged caches: sequences at their own lengths, the lengths in device memory.
 
 Each sequence is checked against its own oracle cache (the oracle's state machine and attention applied to that
-sequence alone): packed tiles and window bytes bit-exact, attention outputs within max-abs 2e-3. The decode step is
-also captured once in a HIP graph and replayed with new inputs; every replay must equal the same step run eagerly on
-a twin cache, bit for bit, and the oracle within 2e-3.
+sequence alone): packed tiles and window bytes bit-exact, attention outputs within max-abs 2e-3. The decode step is a
+single launch (flush, append, attention, merge and length commit inside one kernel); it must equal
+kv_ragged_append + kv_ragged_decode_attention bit for bit, leave its completion counters at zero, and, captured once
+in a HIP graph and replayed with new inputs, equal the same step run eagerly on a twin cache, bit for bit.
 """
 import sys
 
@@ -116,6 +117,7 @@ def test_ragged_decode_steps_cross_flushes_at_different_steps(kvq):
     for i in range(steps):
         flushed = [ref.n_resid == ref.residual_cap for ref in refs]
         out = kvq.kv_ragged_decode_step(cache, _dev(ks[i]), _dev(vs[i]), _dev(qs[i]), workspace=ws)
+        assert not cache.sync.any(), f"step {i}: completion counters not reset"
         for b, ref in enumerate(refs):
             ref.append_token(ks[i, b], vs[i, b])
         got = out.cpu().numpy().astype(np.float64)
@@ -129,12 +131,16 @@ def test_ragged_decode_steps_cross_flushes_at_different_steps(kvq):
     say(f"    worst max_abs={worst:.3e}")
 
 
-def test_ragged_append_then_attention_equals_step(kvq):
-    """kv_ragged_append followed by kv_ragged_decode_attention gives the same bytes as kv_ragged_decode_step."""
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (16, 2), (6, 3)])
+def test_ragged_append_then_attention_equals_step(kvq, Hq, Hkv):
+    """kv_ragged_append followed by kv_ragged_decode_attention gives the same bytes as the single-launch
+    kv_ragged_decode_step, across flushes; with 16 query heads on 2 KV heads two query-head chunks of each KV head
+    quantize the flushed window in the same launch."""
     rng = np.random.default_rng(7)
-    lengths, Hq, Hkv = [127, 128, 255, 3], 8, 2
+    lengths = [127, 128, 255, 3]
     a, _, ks, vs, qs = _setup(kvq, np.random.default_rng(7), lengths, Hkv, Hq, 1024, 4)
     b, _, _, _, _ = _setup(kvq, np.random.default_rng(7), lengths, Hkv, Hq, 1024, 4)
+    say(f"[ragged-step==append+attention] Hq={Hq} Hkv={Hkv} splits={kvq.kv_ragged_splits(a)}")
     for i in range(4):
         oa_ = kvq.kv_ragged_decode_step(a, _dev(ks[i]), _dev(vs[i]), _dev(qs[i]))
         kvq.kv_ragged_append(b, _dev(ks[i]), _dev(vs[i]))
@@ -142,6 +148,7 @@ def test_ragged_append_then_attention_equals_step(kvq):
         torch.cuda.synchronize()
         assert torch.equal(oa_, ob)
         assert torch.equal(a.lens, b.lens) and torch.equal(a.tiles, b.tiles) and torch.equal(a.k_res, b.k_res)
+        assert torch.equal(a.v_res, b.v_res) and not a.sync.any()
     del rng
 
 
@@ -182,6 +189,25 @@ def test_ragged_step_graph_replay(kvq):
     assert torch.equal(g_cache.tiles, e_cache.tiles) and torch.equal(g_cache.v_res, e_cache.v_res)
     _check_state(g_cache, refs, "after replays")
     say(f"    {steps} replays, worst max_abs vs oracle={worst:.3e}")
+
+
+def test_ragged_step_gqa8_crosses_flushes(kvq):
+    """Single-launch steps with two query-head chunks per KV head (G = 8) across every sequence's flush: outputs
+    within 2e-3 of the oracle after each step and the state bit-exact after each flush."""
+    rng = np.random.default_rng(808)
+    lengths, Hq, Hkv = [128, 90, 250], 16, 2
+    steps = 40
+    cache, refs, ks, vs, qs = _setup(kvq, rng, lengths, Hkv, Hq, 512, steps)
+    for i in range(steps):
+        flushed = [ref.n_resid == ref.residual_cap for ref in refs]
+        out = kvq.kv_ragged_decode_step(cache, _dev(ks[i]), _dev(vs[i]), _dev(qs[i]))
+        for b, ref in enumerate(refs):
+            ref.append_token(ks[i, b], vs[i, b])
+        err = np.abs(out.cpu().numpy().astype(np.float64) - _oracle_out(refs, qs[i], Hkv)).max()
+        assert err <= ATOL, f"step {i}: {err}"
+        if any(flushed):
+            _check_state(cache, refs, f"step {i}")
+    assert not cache.sync.any()
 
 
 def test_ragged_full_sequence_is_refused(kvq):
