@@ -321,8 +321,9 @@ def main(argv=None):
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path (every (batch row, KV head) slice "
-              "is independent; sharding is described in the design notes). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (every (batch row, KV head) slice "
+              "is independent, so slices would be split across GPUs with no communication). Run with --gpus 1.",
+              file=sys.stderr)
         return 2
 
     import torch

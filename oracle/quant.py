@@ -4,7 +4,7 @@ What the pages fix: KIVI is an asymmetric quantizer (title of the KIVI page; syn
 grouped per channel over 32 tokens and values per token (KIVI page, paragraph on the cache contents;
 synthetic.wiki "Keys are harder than values"), and 2 bits is the width on the hot path.
 
-What the pages leave open, and the reading taken here (each is listed in the design notes):
+What the pages leave open, and the reading taken here:
 - form: uniform levels between the group minimum and maximum, zero-point z = min, scale s = (max - min) / L with
   L = 2**bits - 1, decoded value x_hat = q * s + z;
 - precision: s and z are stored as binary16; the code arithmetic is binary32 with round-to-nearest-even at every

@@ -6,7 +6,7 @@ KVQuant page (fdeinterviews.com, "KVQuant: Towards 10 Million Context Length LLM
 Quantization"), on pre-RoPE key quantization: the keys are quantized before the rotary embedding is applied, and
 the rotation (which turns pairs of channels by a position-dependent angle) is applied after dequantization.
 
-Readings taken where the page is silent (listed in the design notes): the pairs are adjacent channels (2i, 2i+1)
+Readings taken where the page is silent: the pairs are adjacent channels (2i, 2i+1)
 (the RoFormer form); the angle of pair i at position m is m * theta_i with theta_i = base ** (-2 i / D) and base
 10000 unless given; the position of a cached token is its absolute index in the sequence (the first token is
 position 0). The stored query is already rotated for its own position, so a score is q . R(m) k for the key of

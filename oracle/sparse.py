@@ -4,7 +4,7 @@ KVQuant page (fdeinterviews.com, "KVQuant: Towards 10 Million Context Length LLM
 Quantization"), list of methods: per-vector dense-and-sparse quantization isolates outliers separately for each
 vector, so that they do not skew the quantization ranges.
 
-Readings taken where the page is silent (listed in the design notes):
+Readings taken where the page is silent:
 - a vector is one quantization group of 32 elements (keys: 32 tokens of one channel; values: 32 channels of one
   token), so the outlier handling follows the grouping the rest of the cache uses;
 - the number of outliers is a fixed fraction chosen here, one per group (1/32), with no calibration: the element of
