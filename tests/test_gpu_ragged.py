@@ -236,3 +236,40 @@ def test_ragged_empty_sequence_gives_zeros(kvq):
     out = kvq.kv_ragged_decode_attention(cache, _dev(qs[0])).cpu().numpy()
     assert np.all(out[0] == 0) and np.all(out[2] == 0)
     assert np.abs(out[1] - _oracle_out(refs, qs[0], 2)[1]).max() <= ATOL
+
+
+def test_ragged_step_random_lengths_and_capacity(kvq):
+    """200 single-launch steps over seven sequences of seeded random lengths (some empty) in a cache whose capacity
+    makes some of them full along the way: each step equals kv_ragged_append + kv_ragged_decode_attention on a twin
+    cache bit for bit (outputs, lengths, tiles, window), the counters return to zero, and at the end every sequence
+    matches its oracle cache."""
+    rng = np.random.default_rng(2027)
+    lengths = [int(x) for x in rng.integers(0, 600, 7)]
+    lengths[3] = 0
+    lengths[0] = 630     # fills the capacity of 640 quantized tokens at its second flush
+    Hq, Hkv, steps, cap = 12, 4, 200, 640
+    a, refs, ks, vs, qs = _setup(kvq, np.random.default_rng(11), lengths, Hkv, Hq, cap, steps)
+    b, _, _, _, _ = _setup(kvq, np.random.default_rng(11), lengths, Hkv, Hq, cap, steps)
+    say(f"[ragged-step-fuzz] lengths={lengths} splits={kvq.kv_ragged_splits(a)}")
+    full_seen = set()
+    for i in range(steps):
+        oa_ = kvq.kv_ragged_decode_step(a, _dev(ks[i]), _dev(vs[i]), _dev(qs[i]))
+        kvq.kv_ragged_append(b, _dev(ks[i]), _dev(vs[i]))
+        ob = kvq.kv_ragged_decode_attention(b, _dev(qs[i]))
+        torch.cuda.synchronize()
+        assert torch.equal(oa_, ob), f"step {i}: outputs differ"
+        assert torch.equal(a.lens, b.lens), f"step {i}: lengths differ"
+        assert not a.sync.any(), f"step {i}: counters not reset"
+        for s, row in enumerate(a.lengths()):
+            if row[3]:
+                full_seen.add(s)
+            else:
+                refs[s].append_token(ks[i, s], vs[i, s])
+    assert torch.equal(a.tiles, b.tiles) and torch.equal(a.k_res, b.k_res) and torch.equal(a.v_res, b.v_res)
+    say(f"    sequences marked full: {sorted(full_seen)}")
+    assert full_seen, "the capacity should fill some sequence"
+    for s, row in enumerate(a.lengths()):
+        assert row[:2] == [refs[s].n_quant, refs[s].n_resid], f"seq {s}: {row} vs oracle"
+    err = np.abs(oa_.cpu().numpy().astype(np.float64) - _oracle_out(refs, qs[steps - 1], Hkv)).max()
+    say(f"    last step max_abs vs oracle={err:.3e}")
+    assert err <= ATOL
