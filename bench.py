@@ -296,6 +296,8 @@ def step_graph(args, kvq, kdev, kvsynth, torch):
         us_rot = timed(graph_r.replay)
         del graph_r, copies
     nbytes = algorithmic_bytes(w.batch, w.kv_heads, w.q_heads, hc.n_quant, hc.n_resid)
+    # the step's own bytes: attention over the cache, plus the new token read (fp16 K, V) and its window row written
+    step_bytes = nbytes + w.batch * w.kv_heads * 4 * w.head_dim * 2
     log(f"[step-graph] per step: host API {us_host:.1f} us, ragged eager {us_ragged:.1f} us, ragged graph "
         f"{us_graph:.1f} us (graph == eager: {same}); graph over {rot} cache copies {us_rot:.1f} us")
     res = {
@@ -309,6 +311,12 @@ def step_graph(args, kvq, kdev, kvsynth, torch):
         "modes_us_per_step": {"host_api_eager": us_host, "ragged_step_eager": us_ragged,
                               "ragged_step_graph": us_graph, f"ragged_step_graph_{rot}_copies": us_rot},
         "graph_equals_eager": same,
+        "roofline": {"bound": "hbm", "achieved": step_bytes / us_rot / 1e3, "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": step_bytes / us_rot / 1e3 / PEAK_GBS, "traffic": None,
+                     "kernel": "decode_pass1_kernel<2> (one kv_ragged_decode_step launch: flush, append, attention, "
+                               "merge, length commit)", "bytes_per_step": step_bytes,
+                     "note": "attention bytes of the last timed step plus the new token's K, V read and window row "
+                             "written; a window flush (once per 128 steps) is not counted"},
         "bytes_last_step": nbytes,
         "gb_s_graph_last_step_bytes": nbytes / us_graph / 1e3,
         "hbm_gb_s_graph_copies_last_step_bytes": nbytes / us_rot / 1e3,
@@ -317,6 +325,12 @@ def step_graph(args, kvq, kdev, kvsynth, torch):
                 "graph, replayed once; one cache (about 115 MB) stays in the 256 MB last-level cache, the copies "
                 "in turn do not (value and ms_per_step)",
     }
+    if not args.no_cpu_baseline:
+        log(f"[step-graph] timing the CPU oracle on {args.cpu_slices} slices x {args.cpu_queries} queries")
+        qs = [Q[W + j].cpu().numpy() for j in range(min(args.cpu_queries, K))]
+        res["cpu_baseline"] = cpu_baseline(w, qs, args.cpu_slices, ctx)
+    else:
+        res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)
     return 0
 
