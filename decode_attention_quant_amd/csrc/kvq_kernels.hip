@@ -28,17 +28,13 @@ __device__ __forceinline__ void quant_keys_tile(const TokSrc &src, int64_t t_fir
                                                 uint32_t *words) {
     const int l = threadIdx.x;
 
-    float x0[32], x1[32];
-    load_pairs32(src, t_first, b, h, 2 * l, x0, x1);
-    float mn0 = x0[0], mx0 = x0[0], mn1 = x1[0], mx1 = x1[0];
-#pragma unroll
-    for (int i = 1; i < 32; ++i) {
-        mn0 = fminf(mn0, x0[i]); mx0 = fmaxf(mx0, x0[i]);
-        mn1 = fminf(mn1, x1[i]); mx1 = fmaxf(mx1, x1[i]);
-    }
+    uint32_t xw[32];   // token i: channels 2l (low half) and 2l + 1 (high half), binary16
+    load_pairs32_packed(src, t_first, b, h, 2 * l, xw);
+    h2v mn, mx;
+    minmax_pairs32(xw, mn, mx);
     _Float16 s0, z0, s1, z1;
-    group_params(mn0, mx0, 3.0f, s0, z0);
-    group_params(mn1, mx1, 3.0f, s1, z1);
+    group_params((float)mn[0], (float)mx[0], 3.0f, s0, z0);
+    group_params((float)mn[1], (float)mx[1], 3.0f, s1, z1);
     const float fs0 = (float)s0, fz0 = (float)z0, fs1 = (float)s1, fz1 = (float)z1;
     // a constant group (s = 0) gets rs = 0, hence t' = 0 and code 0
     const float rs0 = fs0 > 0.0f ? __builtin_amdgcn_rcpf(fs0) : 0.0f;
@@ -54,8 +50,8 @@ __device__ __forceinline__ void quant_keys_tile(const TokSrc &src, int64_t t_fir
     for (int i = 0; i < 32; ++i) {
         const int m = i >> 4, n = i & 15;
         const int w = 4 * (n + 16 * kc) + 2 * m + (ks >> 1);
-        const uint32_t bits = quad_or((code_fast(x0[i], fz0, fs0, rs0, 3.0f) << shift) |
-                                      (code_fast(x1[i], fz1, fs1, rs1, 3.0f) << (shift + 4)));
+        const uint32_t bits = quad_or((code_from_diff(diff_half<false>(xw[i], fz0), fs0, rs0, 3u) << shift) |
+                                      (code_from_diff(diff_half<true>(xw[i], fz1), fs1, rs1, 3u) << (shift + 4)));
         uint32_t lo, hi;
         swap16(bits, lo, hi);
         if (writer) words[w] = lo | hi;
@@ -67,36 +63,41 @@ __device__ __forceinline__ void quant_keys_tile(const TokSrc &src, int64_t t_fir
     reinterpret_cast<h2 *>(rec + 2304)[l] = zp;
 }
 
-// Values of one tile into the record at `rec`: lane l owns channels 2l and 2l+1 of every token, and the 16 lanes of
-// row g = l / 16 together own channel group g (channels 32g .. 32g+31). The min/max of the 128 (token, group)
-// groups are row reductions; each lane then derives the parameters of two groups, shared through LDS.
-// LDS: `words` 1 KB, `sv`/`zv` 256 B each, `gp` 1 KB.
+// Values of one tile into the record at `rec`. Parameters: lane l reduces the groups (token l / 4 and 16 + l / 4,
+// channel group l % 4) from their own 64-byte rows (packed binary16 min/max, no cross-lane step) and stores scale,
+// zero and reciprocal scale; codes: lane l owns channels 2l and 2l+1 of every token (the row g = l / 16 of lanes
+// owns channel group g) and builds its code words over the tokens. LDS: `words` 1 KB, `sv`/`zv` 256 B each,
+// `gp` 2 KB ({s, z, 1/s, 0} as binary32 per (token, group)).
 __device__ __forceinline__ void quant_values_tile(const TokSrc &src, int64_t t_first, int b, int h, uint8_t *rec,
                                                   uint32_t *words, _Float16 *sv, _Float16 *zv, float *gp) {
     const int l = threadIdx.x;
     const int c = 2 * l, j = c >> 4, cc = c & 15, g = l >> 4;
-    float x0[32], x1[32];
-    load_pairs32(src, t_first, b, h, c, x0, x1);
-    float *gmn = gp, *gmx = gp + 128;   // [token][group]; gmx then holds the reciprocal scales
+    uint32_t xw[32];
+    load_pairs32_packed(src, t_first, b, h, c, xw);
+    const int gq = l & 3;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        const float mn = row16_min(fminf(x0[i], x1[i]));
-        const float mx = row16_max(fmaxf(x0[i], x1[i]));
-        if ((l & 15) == 0) {
-            gmn[4 * i + g] = mn;
-            gmx[4 * i + g] = mx;
+    for (int k = 0; k < 2; ++k) {
+        const int tk = (l >> 2) + 16 * k;
+        const uint4 *row = reinterpret_cast<const uint4 *>(tok_row(src, b, h, t_first + tk) + 32 * gq);
+        uint4 r4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r4[q] = row[q];
+        h2v mn = __builtin_bit_cast(h2v, r4[0].x), mx = mn;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+#pragma unroll
+            for (int e = (q == 0 ? 1 : 0); e < 4; ++e) {
+                const h2v v = __builtin_bit_cast(h2v, r4[q][e]);
+                mn = __builtin_elementwise_min(mn, v);
+                mx = __builtin_elementwise_max(mx, v);
+            }
         }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k = 0; k < 2; ++k) {   // groups e = l and l + 64: token e / 4, channel group e % 4
-        const int ge = l + 64 * k, t = ge >> 2, gg = ge & 3;
-        _Float16 s, z;
-        group_params(gmn[ge], gmx[ge], 3.0f, s, z);
-        sv[32 * gg + t] = s;
-        zv[32 * gg + t] = z;
-        const float fs = (float)s;
-        gmx[ge] = fs > 0.0f ? __builtin_amdgcn_rcpf(fs) : 0.0f;
+        _Float16 sh, zh;
+        group_params((float)__builtin_fminf16(mn[0], mn[1]), (float)__builtin_fmaxf16(mx[0], mx[1]), 3.0f, sh, zh);
+        sv[32 * gq + tk] = sh;
+        zv[32 * gq + tk] = zh;
+        const float fs = (float)sh;
+        reinterpret_cast<f4 *>(gp)[4 * tk + gq] = f4{fs, (float)zh, fs > 0.0f ? __builtin_amdgcn_rcpf(fs) : 0.0f, 0.0f};
     }
     __syncthreads();
     // lane l's channels fill words 4 (cc + 16 kc) + j / 2 (channel 2l) and the next-but-three (channel 2l + 1) for
@@ -104,12 +105,12 @@ __device__ __forceinline__ void quant_values_tile(const TokSrc &src, int64_t t_f
     uint32_t wv[4][2] = {{0u, 0u}, {0u, 0u}, {0u, 0u}, {0u, 0u}};
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-        const float fs = (float)sv[32 * g + i], fz = (float)zv[32 * g + i], rs = gmx[4 * i + g];
+        const f4 prm = reinterpret_cast<const f4 *>(gp)[4 * i + g];
         int kc, e;
         if (i < 16) { kc = i >> 2; e = i & 3; } else { kc = (i - 16) >> 2; e = 4 + ((i - 16) & 3); }
         const int shift = 4 * e + 2 * (j & 1);
-        wv[kc][0] |= code_fast(x0[i], fz, fs, rs, 3.0f) << shift;
-        wv[kc][1] |= code_fast(x1[i], fz, fs, rs, 3.0f) << shift;
+        wv[kc][0] |= code_from_diff(diff_half<false>(xw[i], prm[1]), prm[0], prm[2], 3u) << shift;
+        wv[kc][1] |= code_from_diff(diff_half<true>(xw[i], prm[1]), prm[0], prm[2], 3u) << shift;
     }
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(64) void quant_values_kernel(TokSrc src, int64_t t_
                                                           uint8_t *tiles, int64_t max_tiles, int64_t tile0) {
     __shared__ uint32_t words[256];
     __shared__ _Float16 sv[128], zv[128];
-    __shared__ float gp[256];
+    __shared__ __align__(16) float gp[512];
     const int64_t tile = blockIdx.x;
     const int h = blockIdx.y, b = blockIdx.z;
     uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * REC;
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(64) void ragged_flush_append_kernel(TokSrc knew, To
                                                                  _Float16 *v_res, int res_cap, int32_t *lens) {
     __shared__ uint32_t words[256];
     __shared__ _Float16 sv[128], zv[128];
-    __shared__ float gp[256];
+    __shared__ __align__(16) float gp[512];
     const int l = threadIdx.x;
     const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     int32_t *ln = lens + 4 * b;

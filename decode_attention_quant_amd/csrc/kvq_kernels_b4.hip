@@ -70,6 +70,35 @@ __global__ __launch_bounds__(64) void quant_keys_b4_kernel(TokSrc src, int64_t t
     const int l = threadIdx.x;
     const int64_t tile = blockIdx.x;
     const int h = blockIdx.y, b = blockIdx.z;
+    uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * record_bytes<SPARSE>();
+
+    if constexpr (!SPARSE) {   // packed binary16 pairs: min/max without conversion, x - z by one mixed fma
+        uint32_t xw[32];
+        load_pairs32_packed(src, t_begin + tile * 32, b, h, 2 * l, xw);
+        h2v mn, mx;
+        minmax_pairs32(xw, mn, mx);
+        _Float16 s0, z0, s1, z1;
+        group_params((float)mn[0], (float)mx[0], L4, s0, z0);
+        group_params((float)mn[1], (float)mx[1], L4, s1, z1);
+        const float fs0 = (float)s0, fz0 = (float)z0, fs1 = (float)s1, fz1 = (float)z1;
+        const float rs0 = fs0 > 0.0f ? __builtin_amdgcn_rcpf(fs0) : 0.0f;   // s = 0: t' = 0, code 0
+        const float rs1 = fs1 > 0.0f ? __builtin_amdgcn_rcpf(fs1) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const uint32_t c0 = code_from_diff(diff_half<false>(xw[i], fz0), fs0, rs0, 15u);
+            const uint32_t c1 = code_from_diff(diff_half<true>(xw[i], fz1), fs1, rs1, 15u);
+            const uint32_t word = quad_or((c0 | (c1 << 4)) << (8 * (l & 3)));
+            const int w = 8 * ((l >> 2) + 16 * (i >> 3)) + (i & 7);
+            if ((l & 3) == 0) words[w] = word;
+        }
+        __syncthreads();
+        reinterpret_cast<uint4 *>(rec)[2 * l] = reinterpret_cast<const uint4 *>(words)[2 * l];
+        reinterpret_cast<uint4 *>(rec)[2 * l + 1] = reinterpret_cast<const uint4 *>(words)[2 * l + 1];
+        const h2 sp = {s0, s1}, zp = {z0, z1};
+        reinterpret_cast<h2 *>(rec + K4_SCALE)[l] = sp;
+        reinterpret_cast<h2 *>(rec + K4_ZERO)[l] = zp;
+        return;
+    }
 
     float x0[32], x1[32];
     load_pairs32(src, t_begin + tile * 32, b, h, 2 * l, x0, x1);
@@ -119,7 +148,6 @@ __global__ __launch_bounds__(64) void quant_keys_b4_kernel(TokSrc src, int64_t t
         if ((l & 3) == 0) words[w] = word;
     }
     __syncthreads();
-    uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * record_bytes<SPARSE>();
     reinterpret_cast<uint4 *>(rec)[2 * l] = reinterpret_cast<const uint4 *>(words)[2 * l];
     reinterpret_cast<uint4 *>(rec)[2 * l + 1] = reinterpret_cast<const uint4 *>(words)[2 * l + 1];
     const h2 sp = {s0, s1}, zp = {z0, z1};
@@ -148,6 +176,54 @@ __global__ __launch_bounds__(64) void quant_values_b4_kernel(TokSrc src, int64_t
     const int h = blockIdx.y, b = blockIdx.z;
     const int g = l >> 4;
     const uint32_t c0 = 2 * (l & 15);   // the lane's first channel within its group
+    uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * record_bytes<SPARSE>();
+    if constexpr (!SPARSE) {
+        // parameters: lane l reduces the groups (token l / 4 and 16 + l / 4, channel group l % 4) from their own
+        // 64-byte rows (packed binary16 min/max) into {s, z, 1/s} per (token, group); codes as below
+        __shared__ __align__(16) float gp[512];
+        uint32_t xw[32];
+        load_pairs32_packed(src, t_begin + tile * 32, b, h, 2 * l, xw);
+        const int gq = l & 3;
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int tk = (l >> 2) + 16 * k;
+            const uint4 *row = reinterpret_cast<const uint4 *>(tok_row(src, b, h, t_begin + tile * 32 + tk) + 32 * gq);
+            uint4 r4[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) r4[q] = row[q];
+            h2v mn = __builtin_bit_cast(h2v, r4[0].x), mx = mn;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+#pragma unroll
+                for (int e = (q == 0 ? 1 : 0); e < 4; ++e) {
+                    const h2v v = __builtin_bit_cast(h2v, r4[q][e]);
+                    mn = __builtin_elementwise_min(mn, v);
+                    mx = __builtin_elementwise_max(mx, v);
+                }
+            }
+            _Float16 sh, zh;
+            group_params((float)__builtin_fminf16(mn[0], mn[1]), (float)__builtin_fmaxf16(mx[0], mx[1]), L4, sh, zh);
+            sv[32 * gq + tk] = sh;
+            zv[32 * gq + tk] = zh;
+            const float fs = (float)sh;
+            reinterpret_cast<f4 *>(gp)[4 * tk + gq] =
+                f4{fs, (float)zh, fs > 0.0f ? __builtin_amdgcn_rcpf(fs) : 0.0f, 0.0f};
+        }
+        __syncthreads();
+        uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const f4 prm = reinterpret_cast<const f4 *>(gp)[4 * i + g];
+            w[i >> 3] |= code_from_diff(diff_half<false>(xw[i], prm[1]), prm[0], prm[2], 15u) << (4 * (i & 7));
+            w[4 + (i >> 3)] |= code_from_diff(diff_half<true>(xw[i], prm[1]), prm[0], prm[2], 15u) << (4 * (i & 7));
+        }
+        uint4 *dst = reinterpret_cast<uint4 *>(rec + V4_CODES);
+        dst[2 * l] = uint4{w[0], w[1], w[2], w[3]};
+        dst[2 * l + 1] = uint4{w[4], w[5], w[6], w[7]};
+        reinterpret_cast<uint32_t *>(rec + V4_SCALE)[l] = reinterpret_cast<const uint32_t *>(sv)[l];
+        reinterpret_cast<uint32_t *>(rec + V4_ZERO)[l] = reinterpret_cast<const uint32_t *>(zv)[l];
+        return;
+    }
     float x0[32], x1[32];
     load_pairs32(src, t_begin + tile * 32, b, h, 2 * l, x0, x1);
     uint32_t om0 = 0u, om1 = 0u;   // bit i: the lane's element of token i is its group's outlier
@@ -199,7 +275,6 @@ __global__ __launch_bounds__(64) void quant_values_b4_kernel(TokSrc src, int64_t
         w[i >> 3] |= q0 << (4 * (i & 7));
         w[4 + (i >> 3)] |= q1 << (4 * (i & 7));
     }
-    uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * record_bytes<SPARSE>();
     uint4 *dst = reinterpret_cast<uint4 *>(rec + V4_CODES);
     dst[2 * l] = uint4{w[0], w[1], w[2], w[3]};
     dst[2 * l + 1] = uint4{w[4], w[5], w[6], w[7]};

@@ -85,6 +85,66 @@ __device__ __forceinline__ uint32_t code_fast(float x, float z, float s, float r
     return (uint32_t)q;
 }
 
+// The same tile load with each token's channel pair kept as one packed binary16 word (channel c in the low half).
+__device__ __forceinline__ void load_pairs32_packed(const TokSrc &s, int64_t t0, int b, int h, int c,
+                                                    uint32_t (&xw)[32]) {
+    const int64_t lim = s.n_a - t0;   // rows i < lim come from source a
+    if (lim >= 32 || lim <= 0) {
+        const bool in_a = lim >= 32;
+        const _Float16 *p = in_a ? s.a + b * s.a_sb + h * s.a_sh + t0 * s.a_st + c
+                                 : s.b + b * s.b_sb + h * s.b_sh + (t0 - s.n_a) * s.b_st + c;
+        const int64_t st = in_a ? s.a_st : s.b_st;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            xw[i] = *reinterpret_cast<const uint32_t *>(p);
+            p += st;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) xw[i] = *reinterpret_cast<const uint32_t *>(tok_row(s, b, h, t0 + i) + c);
+    }
+}
+
+// Element-wise minimum and maximum of 32 packed binary16 pairs (exact: the results are elements).
+__device__ __forceinline__ void minmax_pairs32(const uint32_t (&xw)[32], h2v &mn, h2v &mx) {
+    mn = __builtin_bit_cast(h2v, xw[0]);
+    mx = mn;
+#pragma unroll
+    for (int i = 1; i < 32; ++i) {
+        const h2v v = __builtin_bit_cast(h2v, xw[i]);
+        mn = __builtin_elementwise_min(mn, v);
+        mx = __builtin_elementwise_max(mx, v);
+    }
+}
+
+// RN32(x - z) for the binary16 x in the low (HI = false) or high half of w: one mixed-precision fma x * 1 - z,
+// exact product and a single rounding.
+template <bool HI>
+__device__ __forceinline__ float diff_half(uint32_t w, float z) {
+    float d;
+    if constexpr (HI)
+        asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(z));
+    else
+        asm("v_fma_mix_f32 %0, %1, 1.0, -%2 op_sel_hi:[1,0,0]" : "=v"(d) : "v"(w), "v"(z));
+    return d;
+}
+
+// code_fast from d = RN32(x - z): the same level, the same near-half test (t within 2^-16 of a half-integer, judged
+// from t - rint(t)) and the same correctly rounded division there, with rint shared by the test and the level.
+__device__ __forceinline__ uint32_t code_from_diff(float d, float s, float rs, uint32_t levels) {
+#pragma clang fp contract(off)
+    float t = d * rs;
+    float r = __builtin_rintf(t);
+    const bool near = __builtin_fabsf(t - r) > 0.5f - 0x1p-16f;
+    if (__builtin_amdgcn_ballot_w64(near) != 0) {
+        const float te = d / s;
+        t = near ? te : t;
+        r = __builtin_rintf(t);
+    }
+    const uint32_t q = (uint32_t)r;   // r >= 0 (d >= 0, rs >= 0)
+    return q < levels ? q : levels;
+}
+
 __device__ __forceinline__ uint32_t code_of(float x, float z, float s, float levels) {
 #pragma clang fp contract(off)
     if (s == 0.0f) return 0u;
