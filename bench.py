@@ -130,7 +130,14 @@ def cpu_baseline(w, queries, n_slices, context):
         oa.decode_attention(c, q, len(slices), 1, rope_base=w.rope_base)
         dt += time.perf_counter() - t
     kv_tokens = len(slices) / w.kv_heads * context * len(queries)
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:  # pragma: no cover - no procfs
+        pass
     return {"value": kv_tokens / dt, "unit": "KV tokens/s", "cores": int(blas_threads), "kind": "oracle",
+            "blas_threads": int(blas_threads), "cpu_model": cpu_model,
             "sample": f"{len(slices)} of {w.batch * w.kv_heads} (batch row, KV head) slices of {w.name} at "
                       f"{context} tokens, each attended by the queries of the first {len(queries)} timed steps: "
                       f"float64 decode attention (dequantize + softmax), {dt:.2f} s; quantization not timed",
