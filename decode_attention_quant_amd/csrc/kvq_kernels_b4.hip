@@ -160,117 +160,82 @@ __global__ __launch_bounds__(64) void quant_keys_b4_kernel(TokSrc src, int64_t t
     }
 }
 
-// Values: groups are 32 channels of one token; lane l owns channels 2l, 2l+1 (group l/16). Value code of channel c,
-// token t sits in word 4c + t/8 at bit 4 (t%8), so lane l owns words 8l .. 8l+7 whole and builds them in registers.
-// The min/max of the 128 (token, group) groups are row reductions; each lane derives the parameters of two groups,
-// shared through LDS. SPARSE: the outlier of each group (largest magnitude, lowest channel on ties) is found first
-// by a row reduction of its order key; its lane stores it, and min/max/codes skip it.
+// Values: groups are 32 channels of one token. Parameters: lane l reduces the groups (token l / 4 and 16 + l / 4,
+// channel group l % 4) from their own 64-byte rows (packed binary16 min/max) into {s, z, 1/s} per (token, group) in
+// LDS. Codes: lane l owns channels 2l, 2l+1 (group l/16); the value code of channel c, token t sits in word
+// 4c + t/8 at bit 4 (t%8), so lane l owns words 8l .. 8l+7 whole and builds them in registers.
+// SPARSE: the group's outlier (largest magnitude, lowest channel on ties) is the maximum of an order key (|x| bits,
+// then the lower channel, then the sign bit, which recovers the value); min/max over the other 31 elements run with
+// the outlier's half replaced by the other half of its 32-bit word (an element of the same group, so the extremes
+// are unchanged), and the outlier's code is 0.
 template <bool SPARSE>
 __global__ __launch_bounds__(64) void quant_values_b4_kernel(TokSrc src, int64_t t_begin, int kv_heads,
                                                              uint8_t *tiles, int64_t max_tiles, int64_t tile0) {
     __shared__ __align__(16) _Float16 sv[128], zv[128], ov[128];   // [g][t]
     __shared__ __align__(16) uint8_t oi[128];                        // [g][t]
-    __shared__ float gmn[128], gmx[128];
+    __shared__ __align__(16) float gp[512];                          // [t][g] {s, z, 1/s, 0}
     const int l = threadIdx.x;
     const int64_t tile = blockIdx.x;
     const int h = blockIdx.y, b = blockIdx.z;
     const int g = l >> 4;
     const uint32_t c0 = 2 * (l & 15);   // the lane's first channel within its group
     uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * record_bytes<SPARSE>();
-    if constexpr (!SPARSE) {
-        // parameters: lane l reduces the groups (token l / 4 and 16 + l / 4, channel group l % 4) from their own
-        // 64-byte rows (packed binary16 min/max) into {s, z, 1/s} per (token, group); codes as below
-        __shared__ __align__(16) float gp[512];
-        uint32_t xw[32];
-        load_pairs32_packed(src, t_begin + tile * 32, b, h, 2 * l, xw);
-        const int gq = l & 3;
+    uint32_t xw[32];
+    load_pairs32_packed(src, t_begin + tile * 32, b, h, 2 * l, xw);
+    const int gq = l & 3;
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int tk = (l >> 2) + 16 * k;
-            const uint4 *row = reinterpret_cast<const uint4 *>(tok_row(src, b, h, t_begin + tile * 32 + tk) + 32 * gq);
-            uint4 r4[4];
+    for (int k = 0; k < 2; ++k) {
+        const int tk = (l >> 2) + 16 * k;
+        const uint4 *row = reinterpret_cast<const uint4 *>(tok_row(src, b, h, t_begin + tile * 32 + tk) + 32 * gq);
+        uint32_t rw[16];   // word e: channels 2e (low half) and 2e + 1 of the group
 #pragma unroll
-            for (int q = 0; q < 4; ++q) r4[q] = row[q];
-            h2v mn = __builtin_bit_cast(h2v, r4[0].x), mx = mn;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-#pragma unroll
-                for (int e = (q == 0 ? 1 : 0); e < 4; ++e) {
-                    const h2v v = __builtin_bit_cast(h2v, r4[q][e]);
-                    mn = __builtin_elementwise_min(mn, v);
-                    mx = __builtin_elementwise_max(mx, v);
-                }
-            }
-            _Float16 sh, zh;
-            group_params((float)__builtin_fminf16(mn[0], mn[1]), (float)__builtin_fmaxf16(mx[0], mx[1]), L4, sh, zh);
-            sv[32 * gq + tk] = sh;
-            zv[32 * gq + tk] = zh;
-            const float fs = (float)sh;
-            reinterpret_cast<f4 *>(gp)[4 * tk + gq] =
-                f4{fs, (float)zh, fs > 0.0f ? __builtin_amdgcn_rcpf(fs) : 0.0f, 0.0f};
+        for (int q = 0; q < 4; ++q) {
+            const uint4 r = row[q];
+            rw[4 * q] = r.x; rw[4 * q + 1] = r.y; rw[4 * q + 2] = r.z; rw[4 * q + 3] = r.w;
         }
-        __syncthreads();
-        uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const f4 prm = reinterpret_cast<const f4 *>(gp)[4 * i + g];
-            w[i >> 3] |= code_from_diff(diff_half<false>(xw[i], prm[1]), prm[0], prm[2], 15u) << (4 * (i & 7));
-            w[4 + (i >> 3)] |= code_from_diff(diff_half<true>(xw[i], prm[1]), prm[0], prm[2], 15u) << (4 * (i & 7));
-        }
-        uint4 *dst = reinterpret_cast<uint4 *>(rec + V4_CODES);
-        dst[2 * l] = uint4{w[0], w[1], w[2], w[3]};
-        dst[2 * l + 1] = uint4{w[4], w[5], w[6], w[7]};
-        reinterpret_cast<uint32_t *>(rec + V4_SCALE)[l] = reinterpret_cast<const uint32_t *>(sv)[l];
-        reinterpret_cast<uint32_t *>(rec + V4_ZERO)[l] = reinterpret_cast<const uint32_t *>(zv)[l];
-        return;
-    }
-    float x0[32], x1[32];
-    load_pairs32(src, t_begin + tile * 32, b, h, 2 * l, x0, x1);
-    uint32_t om0 = 0u, om1 = 0u;   // bit i: the lane's element of token i is its group's outlier
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        float lo0 = x0[i], hi0 = x0[i], lo1 = x1[i], hi1 = x1[i];
+        h2v mn = __builtin_bit_cast(h2v, rw[0]), mx = mn;
         if constexpr (SPARSE) {
-            const uint32_t k0 = outlier_key(x0[i], c0), k1 = outlier_key(x1[i], c0 + 1);
-            const uint32_t w = 31u - (row16_max_u32(k0 > k1 ? k0 : k1) & 31u);
-            const bool is0 = w == c0, is1 = w == c0 + 1;
-            om0 |= (uint32_t)is0 << i;
-            om1 |= (uint32_t)is1 << i;
-            if (is0 || is1) {
-                ov[32 * g + i] = (_Float16)(is0 ? x0[i] : x1[i]);
-                oi[32 * g + i] = (uint8_t)w;
-            }
-            const float inf = __builtin_inff();
-            lo0 = is0 ? inf : lo0; hi0 = is0 ? -inf : hi0;
-            lo1 = is1 ? inf : lo1; hi1 = is1 ? -inf : hi1;
-        }
-        const float mn = row16_min(fminf(lo0, lo1));
-        const float mx = row16_max(fmaxf(hi0, hi1));
-        if ((l & 15) == 0) {
-            gmn[4 * i + g] = mn;
-            gmx[4 * i + g] = mx;
-        }
-    }
-    __syncthreads();
+            uint32_t kmax = 0u;
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {   // groups e = l and l + 64: token e / 4, channel group e % 4
-        const int ge = l + 64 * k, t = ge >> 2, gg = ge & 3;
-        _Float16 s, z;
-        group_params(gmn[ge], gmx[ge], L4, s, z);
-        sv[32 * gg + t] = s;
-        zv[32 * gg + t] = z;
-        const float fs = (float)s;
-        gmx[ge] = fs > 0.0f ? __builtin_amdgcn_rcpf(fs) : 0.0f;   // the reciprocal scale from here on
+            for (int e = 0; e < 16; ++e) {
+                const uint32_t klo = ((rw[e] & 0x7FFFu) << 6) | ((31u - 2u * e) << 1) | ((rw[e] >> 15) & 1u);
+                const uint32_t khi = (((rw[e] >> 16) & 0x7FFFu) << 6) | ((30u - 2u * e) << 1) | (rw[e] >> 31);
+                kmax = max(kmax, max(klo, khi));
+            }
+            const uint32_t w = 31u - ((kmax >> 1) & 31u);
+            const uint32_t sel = (w & 1u) ? 0x01000100u : 0x03020302u;   // both halves = the partner half
+            ov[32 * gq + tk] = __builtin_bit_cast(_Float16, (uint16_t)(((kmax >> 6) & 0x7FFFu) | ((kmax & 1u) << 15)));
+            oi[32 * gq + tk] = (uint8_t)w;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if ((uint32_t)e == (w >> 1)) rw[e] = __builtin_amdgcn_perm(rw[e], rw[e], sel);
+            mn = __builtin_bit_cast(h2v, rw[0]);
+            mx = mn;
+        }
+#pragma unroll
+        for (int e = 1; e < 16; ++e) {
+            const h2v v = __builtin_bit_cast(h2v, rw[e]);
+            mn = __builtin_elementwise_min(mn, v);
+            mx = __builtin_elementwise_max(mx, v);
+        }
+        _Float16 sh, zh;
+        group_params((float)__builtin_fminf16(mn[0], mn[1]), (float)__builtin_fmaxf16(mx[0], mx[1]), L4, sh, zh);
+        sv[32 * gq + tk] = sh;
+        zv[32 * gq + tk] = zh;
+        const float fs = (float)sh;
+        reinterpret_cast<f4 *>(gp)[4 * tk + gq] = f4{fs, (float)zh, fs > 0.0f ? __builtin_amdgcn_rcpf(fs) : 0.0f, 0.0f};
     }
     __syncthreads();
     uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-        const float fs = (float)sv[32 * g + i], fz = (float)zv[32 * g + i], rs = gmx[4 * i + g];
-        uint32_t q0 = code_fast(x0[i], fz, fs, rs, L4), q1 = code_fast(x1[i], fz, fs, rs, L4);
+        const f4 prm = reinterpret_cast<const f4 *>(gp)[4 * i + g];
+        uint32_t q0 = code_from_diff(diff_half<false>(xw[i], prm[1]), prm[0], prm[2], 15u);
+        uint32_t q1 = code_from_diff(diff_half<true>(xw[i], prm[1]), prm[0], prm[2], 15u);
         if constexpr (SPARSE) {
-            q0 = (om0 >> i) & 1u ? 0u : q0;
-            q1 = (om1 >> i) & 1u ? 0u : q1;
+            const uint32_t oc = oi[32 * g + i];
+            q0 = oc == c0 ? 0u : q0;
+            q1 = oc == c0 + 1 ? 0u : q1;
         }
         w[i >> 3] |= q0 << (4 * (i & 7));
         w[4 + (i >> 3)] |= q1 << (4 * (i & 7));
