@@ -86,6 +86,14 @@ def test_quantize_entry_points_bit_exact(kvq, kind):
     assert not got[:, :tile0].any() and not got[:, tile0 + T // 32:].any(), "wrote outside the tile range"
     sel = got[:, tile0:tile0 + T // 32]
     assert np.array_equal(sel, want), helpers.first_mismatch(sel, want)
+    # values again through a non-contiguous view ([B, T, H, D] storage): the same value fields
+    tiles2 = torch.zeros_like(tiles)
+    v_store = _dev(np.ascontiguousarray(v.transpose(0, 2, 1, 3)))
+    kvq.kv_quant_values_per_token(shape, v_store.permute(0, 2, 1, 3), tile0, tiles2)
+    torch.cuda.synchronize()
+    got2 = tiles2.cpu().numpy().reshape(B * H, -1, 3072)
+    for lo, hi in ((1024, 2048), (2560, 3072)):
+        assert np.array_equal(got2[..., lo:hi], got[..., lo:hi]), f"strided values differ in bytes {lo}..{hi}"
 
 
 def _check_state(kvq, cache, ref, B, H, what):

@@ -139,6 +139,15 @@ def test_quantize_sparse_entry_points_bit_exact(kvq, kind):
     assert not got[:, :tile0].any() and not got[:, tile0 + T // 32:].any(), "wrote outside the tile range"
     sel = got[:, tile0:tile0 + T // 32]
     assert np.array_equal(sel, want), helpers.first_mismatch4(sel, want)
+    # keys and values again through non-contiguous views ([B, T, H, D] storage): the same records
+    tiles2 = torch.zeros_like(tiles)
+    k_store = _dev(np.ascontiguousarray(k.transpose(0, 2, 1, 3)))
+    v_store = _dev(np.ascontiguousarray(v.transpose(0, 2, 1, 3)))
+    kvq.kv_quant_keys_per_channel(shape, k_store.permute(0, 2, 1, 3), tile0, tiles2)
+    kvq.kv_quant_values_per_token(shape, v_store.permute(0, 2, 1, 3), tile0, tiles2)
+    torch.cuda.synchronize()
+    got2 = tiles2.cpu().numpy().reshape(B * H, -1, 5888)
+    assert np.array_equal(got2, got), helpers.first_mismatch4(got2[:, tile0:tile0 + T // 32], want)
 
 
 def test_append_stream_sparse_with_sink(kvq):
