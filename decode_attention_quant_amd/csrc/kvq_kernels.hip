@@ -135,7 +135,8 @@ __global__ __launch_bounds__(64) void quant_keys_kernel(TokSrc src, int64_t t_be
     quant_keys_tile(src, t_begin + tile * 32, b, h, rec, words);
 }
 
-__global__ __launch_bounds__(64) void quant_values_kernel(TokSrc src, int64_t t_begin, int kv_heads,
+// five wavefronts per SIMD (85 registers): a memory-bound kernel whose loads want more wavefronts in flight
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void quant_values_kernel(TokSrc src, int64_t t_begin, int kv_heads,
                                                           uint8_t *tiles, int64_t max_tiles, int64_t tile0) {
     __shared__ uint32_t words[256];
     __shared__ _Float16 sv[128], zv[128];
@@ -288,8 +289,9 @@ __device__ __forceinline__ float coherent_load(const float *p) {
 
 // The merge of one (batch row, query head) row bh by one wavefront; `wts` is LDS for `splits` floats. With
 // zero_empty, a row with no token (every split empty) gets zeros. COHERENT: the partials were written in this launch
-// (read through coherent loads).
-template <bool COHERENT = false>
+// (read through coherent loads). Splits past the first eight are loaded BATCH at a time, the last batch masked (one
+// memory round trip per batch).
+template <bool COHERENT = false, int BATCH = 8>
 __device__ __forceinline__ void merge_splits(const float *part_o, const float *part_ml, float *out, int splits,
                                              int64_t bh, float *wts, bool zero_empty) {
     auto ld = [](const float *p) { return COHERENT ? coherent_load(p) : *p; };
@@ -335,23 +337,18 @@ __device__ __forceinline__ void merge_splits(const float *part_o, const float *p
             o1 = fmaf(w, first[k].y, o1);
         }
     }
-    int sp = 8;
-    for (; sp + 8 <= splits; sp += 8) {
-        float2 v[8];
+    for (int sp = 8; sp < splits; sp += BATCH) {   // the last batch is masked
+        float2 v[BATCH];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = ld2(sp + k);
+        for (int k = 0; k < BATCH; ++k) v[k] = sp + k < splits ? ld2(sp + k) : float2{0.0f, 0.0f};
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const float w = wts[sp + k];
-            o0 = fmaf(w, v[k].x, o0);
-            o1 = fmaf(w, v[k].y, o1);
+        for (int k = 0; k < BATCH; ++k) {
+            if (sp + k < splits) {
+                const float w = wts[sp + k];
+                o0 = fmaf(w, v[k].x, o0);
+                o1 = fmaf(w, v[k].y, o1);
+            }
         }
-    }
-    for (; sp < splits; ++sp) {
-        const float2 v = ld2(sp);
-        const float w = wts[sp];
-        o0 = fmaf(w, v.x, o0);
-        o1 = fmaf(w, v.y, o1);
     }
     reinterpret_cast<float2 *>(out + bh * D)[l] = float2{o0 / L, o1 / L};
 }
@@ -837,7 +834,7 @@ __global__ __launch_bounds__(64) void decode_pass2_kernel(const float *part_o, c
             ln[1] = nr;
         }
     }
-    merge_splits(part_o, part_ml, out, splits, bh, wts, RAGGED);
+    merge_splits<false, 24>(part_o, part_ml, out, splits, bh, wts, RAGGED);
 }
 
 // ------------------------------------------------------------------------------------------------ launchers

@@ -70,18 +70,6 @@ __device__ __forceinline__ float row16_max(float v) {
     return dpp_xmax<DPP_ROW_MIRROR>(v);
 }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_xmin(float v) {
-    const int s = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
-    return fminf(v, __builtin_bit_cast(float, s));
-}
-__device__ __forceinline__ float row16_min(float v) {
-    v = dpp_xmin<DPP_QUAD_1032>(v);
-    v = dpp_xmin<DPP_QUAD_2301>(v);
-    v = dpp_xmin<DPP_ROW_HALF_MIRROR>(v);
-    return dpp_xmin<DPP_ROW_MIRROR>(v);
-}
-
 // Bitwise OR with the value of another lane of the same 16-lane row (DPP), and over each lane quad
 template <int CTRL>
 __device__ __forceinline__ uint32_t dpp_xor_or(uint32_t v) {
