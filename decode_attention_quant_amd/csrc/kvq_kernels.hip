@@ -289,8 +289,9 @@ __device__ __forceinline__ float coherent_load(const float *p) {
 
 // The merge of one (batch row, query head) row bh by one wavefront; `wts` is LDS for `splits` floats. With
 // zero_empty, a row with no token (every split empty) gets zeros. COHERENT: the partials were written in this launch
-// (read through coherent loads). Splits past the first eight are loaded BATCH at a time, the last batch masked (one
-// memory round trip per batch).
+// (read through coherent loads). Splits past the first eight are loaded BATCH at a time, one memory round trip per
+// batch (the last batch rereads the last split). `wts` holds max(8, BATCH) zero weights after the last split, so
+// every weight read is unconditional and the reads of a batch are contiguous.
 template <bool COHERENT = false, int BATCH = 8>
 __device__ __forceinline__ void merge_splits(const float *part_o, const float *part_ml, float *out, int splits,
                                              int64_t bh, float *wts, bool zero_empty) {
@@ -322,6 +323,8 @@ __device__ __forceinline__ void merge_splits(const float *part_o, const float *p
         wts[sp] = w;
         L += w * ld(pm + 2 * sp + 1);
     }
+    constexpr int PAD = BATCH > 8 ? BATCH : 8;
+    if (l < PAD) wts[splits + l] = 0.0f;
     L = rows_sum(row16_sum(L));
     __syncthreads();
     if (zero_empty && !(L > 0.0f)) {
@@ -330,24 +333,20 @@ __device__ __forceinline__ void merge_splits(const float *part_o, const float *p
     }
     float o0 = 0.0f, o1 = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        if (k < splits) {
-            const float w = wts[k];
-            o0 = fmaf(w, first[k].x, o0);
-            o1 = fmaf(w, first[k].y, o1);
-        }
+    for (int k = 0; k < 8; ++k) {   // weights past the last split are 0 (and so are those partials)
+        const float w = wts[k];
+        o0 = fmaf(w, first[k].x, o0);
+        o1 = fmaf(w, first[k].y, o1);
     }
-    for (int sp = 8; sp < splits; sp += BATCH) {   // the last batch is masked
+    for (int sp = 8; sp < splits; sp += BATCH) {   // the last batch: loads clamped to the last split, weights 0
         float2 v[BATCH];
 #pragma unroll
-        for (int k = 0; k < BATCH; ++k) v[k] = sp + k < splits ? ld2(sp + k) : float2{0.0f, 0.0f};
+        for (int k = 0; k < BATCH; ++k) v[k] = ld2(min(sp + k, splits - 1));
 #pragma unroll
         for (int k = 0; k < BATCH; ++k) {
-            if (sp + k < splits) {
-                const float w = wts[sp + k];
-                o0 = fmaf(w, v[k].x, o0);
-                o1 = fmaf(w, v[k].y, o1);
-            }
+            const float w = wts[sp + k];
+            o0 = fmaf(w, v[k].x, o0);
+            o1 = fmaf(w, v[k].y, o1);
         }
     }
     reinterpret_cast<float2 *>(out + bh * D)[l] = float2{o0 / L, o1 / L};
@@ -768,7 +767,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
         prev = __shfl(prev, 0);
         if (prev + 1u != (uint32_t)S) return;
         if (l == 0) *cnt = 0u;
-        float *wts = reinterpret_cast<float *>(smem);   // S <= PASS2_MAX_SPLITS floats
+        float *wts = reinterpret_cast<float *>(smem);   // S <= PASS2_MAX_SPLITS floats + 8 zero weights
         __syncthreads();
         for (int k = 0; k < gc; ++k) {
             merge_splits<true>(a.part_o, a.part_ml, a.out, (int)S, (int64_t)b * a.q_heads + h0 + k, wts, true);
@@ -823,7 +822,7 @@ template <bool RAGGED>
 __global__ __launch_bounds__(64) void decode_pass2_kernel(const float *part_o, const float *part_ml, float *out,
                                                           int splits, int32_t *lens, int q_heads, int res_cap,
                                                           int commit) {
-    __shared__ float wts[PASS2_MAX_SPLITS];
+    __shared__ float wts[PASS2_MAX_SPLITS + 32];   // + zero weights after the last split
     const int64_t bh = blockIdx.x;
     if constexpr (RAGGED) {
         if (commit && threadIdx.x == 0 && bh % q_heads == 0) {
