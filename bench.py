@@ -302,6 +302,48 @@ def step_graph(args, kvq, kdev, kvsynth, torch):
                 ragged_step(copies[j % rot], W + j // rot, outs[j])
         us_rot = timed(graph_r.replay)
         del graph_r, copies
+    # ragged lengths: sequence b prefilled with P (b + 1) / B tokens (a serving batch at mixed positions), the same
+    # single-launch steps in one graph over enough cache copies in turn to exceed the last-level cache; bytes from
+    # each copy's lengths at its last timed step
+    B = w.batch
+    lens0 = [max(32, (P * (b + 1)) // B) for b in range(B)]
+    kmix = [torch.stack([Kd[b, :, lens0[b] + i] for b in range(B)]) for i in range(W + K)]
+    vmix = [torch.stack([Vd[b, :, lens0[b] + i] for b in range(B)]) for i in range(W + K)]
+
+    def mix_cache():
+        c = kvq.RaggedCache(shape)
+        for b in range(B):
+            kvq.kv_ragged_prefill(c, b, Kd[b, :, :lens0[b]], Vd[b, :, :lens0[b]])
+        return c
+
+    def mix_step(c, i, o):
+        kvq.kv_ragged_decode_step(c, kmix[i], vmix[i], Q[i], out=o, workspace=ws_r)
+
+    def mix_bytes(c):
+        ln = c.lens.cpu().tolist()
+        return sum(algorithmic_bytes(1, w.kv_heads, w.q_heads, nq, nr) for nq, nr, _, _ in ln)
+
+    mc = mix_cache()
+    for i in range(W):
+        mix_step(mc, i, out)
+    us_mix_eager = timed(lambda: [mix_step(mc, W + j, out) for j in range(K)])
+    rot_mix = max(rot, -(-320 * 2 ** 20 // mix_bytes(mc)))
+    mcopies = [mix_cache() for _ in range(rot_mix)]
+    for c in mcopies:
+        for i in range(W):
+            mix_step(c, i, outs[0])
+    torch.cuda.synchronize()
+    graph_m = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_m):
+        for j in range(K):
+            mix_step(mcopies[j % rot_mix], W + j // rot_mix, outs[j])
+    us_mix = timed(graph_m.replay)
+    mix_last = sum(mix_bytes(c) for c in mcopies) / rot_mix
+    mix_tokens = sum(int(c.lens[:, :2].sum()) for c in mcopies) / rot_mix
+    del graph_m, mcopies, mc
+    log(f"[step-graph] ragged lengths {lens0[0]}..{lens0[-1]}: eager {us_mix_eager:.1f} us, graph over {rot_mix} copies "
+        f"{us_mix:.1f} us per step ({mix_last / us_mix / 1e3:.0f} GB/s)")
+
     nbytes = algorithmic_bytes(w.batch, w.kv_heads, w.q_heads, hc.n_quant, hc.n_resid)
     # the step's own bytes: attention over the cache, plus the new token read (fp16 K, V) and its window row written
     step_bytes = nbytes + w.batch * w.kv_heads * 4 * w.head_dim * 2
@@ -324,6 +366,11 @@ def step_graph(args, kvq, kdev, kvsynth, torch):
                                "merge, length commit)", "bytes_per_step": step_bytes,
                      "note": "attention bytes of the last timed step plus the new token's K, V read and window row "
                              "written; a window flush (once per 128 steps) is not counted"},
+        "ragged_lengths": {"prefill_lengths": lens0, "us_per_step_eager": us_mix_eager,
+                           f"us_per_step_graph_{rot_mix}_copies": us_mix, "bytes_last_step": mix_last,
+                           "gb_s": mix_last / us_mix / 1e3, "kv_tokens_per_s": mix_tokens / (us_mix * 1e-6),
+                           "note": "sequence b prefilled with P (b + 1) / B tokens, then the same single-launch "
+                                   "steps; every sequence's tiles are spread over the same fixed number of splits"},
         "bytes_last_step": nbytes,
         "gb_s_graph_last_step_bytes": nbytes / us_graph / 1e3,
         "hbm_gb_s_graph_copies_last_step_bytes": nbytes / us_rot / 1e3,
