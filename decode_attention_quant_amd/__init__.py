@@ -320,7 +320,9 @@ def kv_ragged_decode_attention(cache: RaggedCache, q: torch.Tensor, out: torch.T
 def kv_ragged_decode_step(cache: RaggedCache, k_new: torch.Tensor, v_new: torch.Tensor, q: torch.Tensor,
                           out: torch.Tensor | None = None, sm_scale: float = 0.0,
                           workspace: torch.Tensor | None = None, stream=None):
-    """Append one token per sequence, then attend (three launches, no host state: graph-capturable)."""
+    """Append one token per sequence, then attend: one launch that flushes full windows, attends, merges the splits,
+    writes the new window rows and commits the lengths (no host state: graph-capturable). Needs the cache's
+    ``sync`` counters (zero before and after every launch)."""
     pk, sb, sh = _f16_tokens(k_new, "k_new")
     pv, sb2, sh2 = _f16_tokens(v_new, "v_new")
     if (sb, sh) != (sb2, sh2):
