@@ -7,7 +7,9 @@
   outputs at sampled steps;
 - llama3_8b_gqa_32k (B64, 32 query / 8 KV heads, 32768 tokens): tiles of sampled slices bit-exact, outputs of the
   query heads of those slices within 2e-3, all outputs finite and inside the range of their slice's values;
-- long_1m (B1, 32 heads, 1,048,576 tokens): sampled tiles bit-exact, outputs of sampled heads within 2e-3.
+- long_1m (B1, 32 heads, 1,048,576 tokens): sampled tiles bit-exact, outputs of sampled heads within 2e-3;
+- llama2_7b_stream at the benchmark's mixed lengths (sequence b prefilled with 4096 (b + 1) / 8 tokens) through the
+  single-launch ragged step: sampled outputs at every step, then lengths, tiles and window rows exact.
 The oracle side of the long cases runs on a thread pool over independent token blocks; it only calls oracle
 functions.
 """
@@ -186,6 +188,60 @@ def test_llama2_stream(kvq):
     err = np.abs(out.cpu().numpy() - want).max()
     say(f"    final all-head max_abs={err:.3e} worst sampled={worst:.3e}")
     assert err <= ATOL
+
+
+def test_llama2_stream_mixed_lengths_step(kvq):
+    """The benchmark's mixed-length batch: sequence b of llama2_7b_stream prefilled with 4096 (b + 1) / 8 tokens, then
+    136 single-launch decode steps (two flushes per sequence). Outputs of sampled slices against the oracle at every
+    step; at the end the lengths of every sequence, and the tiles and window rows of the sampled slices, are exact."""
+    w = kvsynth.WORKLOADS["llama2_7b_stream"]
+    B, H, R, steps = w.batch, w.kv_heads, w.residual, 136
+    lens0 = [max(32, (w.prefill * (b + 1)) // B) for b in range(B)]
+    total = lens0[-1] + steps
+    say(f"[workload] {w.name} at mixed lengths {lens0[0]}..{lens0[-1]}, {steps} steps")
+    K = kdev.kv_to_device(w, kvsynth.K_ID, 0, total)
+    V = kdev.kv_to_device(w, kvsynth.V_ID, 0, total)
+    Q = kdev.queries_to_device(w, range(1, steps + 1))
+    shape = kvq.Shape(B, H, w.q_heads, residual_cap=R, max_tokens=((total + 31) // 32) * 32)
+    cache = kvq.RaggedCache(shape)
+    for b in range(B):
+        kvq.kv_ragged_prefill(cache, b, K[b, :, :lens0[b]], V[b, :, :lens0[b]])
+    ws = torch.empty(kvq.kv_ragged_workspace_bytes(cache), dtype=torch.uint8, device="cuda")
+    idx = torch.arange(B, device="cuda")
+    sampled = [(0, 0), (3, 17), (7, 31)]
+    refs = [_oracle_slices(w, [(b, h)], lens0[b]) for b, h in sampled]
+    kt = [helpers.workload_tokens(w, kvsynth.K_ID, lens0[b], lens0[b] + steps, b, h) for b, h in sampled]
+    vt = [helpers.workload_tokens(w, kvsynth.V_ID, lens0[b], lens0[b] + steps, b, h) for b, h in sampled]
+    worst = 0.0
+    for i in range(steps):
+        pos = torch.tensor(lens0, device="cuda") + i
+        k_new = K[idx, :, pos].contiguous()
+        v_new = V[idx, :, pos].contiguous()
+        out = kvq.kv_ragged_decode_step(cache, k_new, v_new, Q[i], workspace=ws)
+        qn = Q[i].cpu().numpy()
+        got = out.cpu().numpy()
+        for j, (b, h) in enumerate(sampled):
+            refs[j].append_token(kt[j][i:i + 1], vt[j][i:i + 1])
+            want = oa.decode_attention(refs[j], qn[b:b + 1, h:h + 1], 1, 1)[0, 0]
+            err = float(np.abs(got[b, h] - want).max())
+            worst = max(worst, err)
+            assert err <= ATOL, (i, b, h, err)
+        assert np.all(np.isfinite(got)), i
+    lens = cache.lens.cpu().numpy()
+    for b in range(B):
+        n_q = oc.flushed_tokens(0, lens0[b] + steps, R)
+        assert tuple(lens[b]) == (n_q, lens0[b] + steps - n_q, 0, 0), (b, lens[b])
+    for j, (b, h) in enumerate(sampled):
+        r = refs[j]
+        assert (int(lens[b][0]), int(lens[b][1])) == (r.n_quant, r.n_resid)
+        g = helpers.records_from_device(cache.tiles, r.n_quant // 32, [b * H + h])
+        wnt = helpers.oracle_records(r)
+        assert np.array_equal(g, wnt), helpers.first_mismatch(g, wnt)
+        kr = cache.k_res[b, h, :r.n_resid].cpu().numpy()
+        vr = cache.v_res[b, h, :r.n_resid].cpu().numpy()
+        assert np.array_equal(kr.view(np.uint16), r.k_res[0].view(np.uint16))
+        assert np.array_equal(vr.view(np.uint16), r.v_res[0].view(np.uint16))
+    say(f"    worst sampled max_abs={worst:.3e}; lengths {lens[:, :2].tolist()}")
 
 
 def _view(c, i):
