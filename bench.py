@@ -374,7 +374,7 @@ def step_graph(args, kvq, kdev, kvsynth, torch):
         "bytes_last_step": nbytes,
         "gb_s_graph_last_step_bytes": nbytes / us_graph / 1e3,
         "hbm_gb_s_graph_copies_last_step_bytes": nbytes / us_rot / 1e3,
-        "note": "host_api_eager: kv_append_and_flush + kv_decode_attention per step (4 launches, 6 on a flush step); "
+        "note": "host_api_eager: kv_append_and_flush + kv_decode_attention per step (3 launches, 5 on a flush step); "
                 "ragged_step_*: kv_ragged_decode_step (one launch); graph: all timed steps captured in one HIP "
                 "graph, replayed once; one cache (about 115 MB) stays in the 256 MB last-level cache, the copies "
                 "in turn do not (value and ms_per_step)",

@@ -284,8 +284,8 @@ int kv_append_and_flush(const kvq_shape *shape, kvq_cache *cache, const void *k_
         dst0 = nr0;
     }
     const int64_t n_copy = n_rest - copy_from;
-    if ((e = launched(kvq::launch_copy_rows(knew, copy_from, n_copy, B, H, kres, (int)R, (int)dst0, s)))) return e;
-    if ((e = launched(kvq::launch_copy_rows(vnew, copy_from, n_copy, B, H, vres, (int)R, (int)dst0, s)))) return e;
+    if ((e = launched(kvq::launch_copy_rows(knew, vnew, copy_from, n_copy, B, H, kres, vres, (int)R, (int)dst0, s))))
+        return e;
     cache->n_quant += flushed;
     cache->n_resid = (int32_t)(dst0 + n_copy);
     return KVQ_OK;
@@ -403,8 +403,7 @@ int kv_ragged_prefill(const kvq_shape *shape, const kvq_ragged *cache, int32_t b
             if ((e = launched(kvq::launch_quant_values(vs, 0, nt, 1, H, tiles, max_tiles, 0, s)))) return e;
         }
         const int64_t n_copy = n_tokens - flushed;
-        if ((e = launched(kvq::launch_copy_rows(ks, flushed, n_copy, 1, H, kres, (int)R, 0, s)))) return e;
-        if ((e = launched(kvq::launch_copy_rows(vs, flushed, n_copy, 1, H, vres, (int)R, 0, s)))) return e;
+        if ((e = launched(kvq::launch_copy_rows(ks, vs, flushed, n_copy, 1, H, kres, vres, (int)R, 0, s)))) return e;
     }
     return launched(kvq::launch_ragged_set(cache->lens, b, (int)flushed, (int)(n_tokens - flushed), 0, s));
 }

@@ -87,8 +87,8 @@ hipError_t launch_quant_keys(const TokSrc &src, int64_t t_begin, int64_t n_tiles
                              uint8_t *tiles, int64_t max_tiles, int64_t tile0, hipStream_t st);
 hipError_t launch_quant_values(const TokSrc &src, int64_t t_begin, int64_t n_tiles, int batch, int kv_heads,
                                uint8_t *tiles, int64_t max_tiles, int64_t tile0, hipStream_t st);
-hipError_t launch_copy_rows(const TokSrc &src, int64_t t_begin, int64_t n, int batch, int kv_heads, _Float16 *res,
-                            int res_cap, int dst0, hipStream_t st);
+hipError_t launch_copy_rows(const TokSrc &ksrc, const TokSrc &vsrc, int64_t t_begin, int64_t n, int batch,
+                            int kv_heads, _Float16 *kres, _Float16 *vres, int res_cap, int dst0, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs &a, int splits, hipStream_t st);
 
 // Ragged caches (per-sequence lengths in device memory, see kvq_kernels.hip).

@@ -148,17 +148,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void qu
 }
 
 // ------------------------------------------------------------------------------------------------ window append
-// Copies n tokens (source tokens t_begin ..) of every slice into window rows dst0 .. ; 16 lanes move one 256-byte
-// row, a workgroup of 64 lanes moves 4 rows.
-__global__ __launch_bounds__(64) void copy_rows_kernel(TokSrc src, int64_t t_begin, int64_t n, int kv_heads,
-                                                       _Float16 *res, int res_cap, int dst0) {
+// Copies n tokens (source tokens t_begin ..) of every slice's keys and values into window rows dst0 .. ; 16 lanes
+// move one 256-byte key row and the matching value row, a workgroup of 64 lanes moves 4 rows of each.
+__global__ __launch_bounds__(64) void copy_rows_kernel(TokSrc ksrc, TokSrc vsrc, int64_t t_begin, int64_t n,
+                                                       int kv_heads, _Float16 *kres, _Float16 *vres, int res_cap,
+                                                       int dst0) {
     const int l = threadIdx.x;
     const int64_t r = blockIdx.x * 4 + (l >> 4);
     const int h = blockIdx.y, b = blockIdx.z;
     if (r >= n) return;
-    const _Float16 *row = tok_row(src, b, h, t_begin + r);
-    _Float16 *dst = res + ((int64_t)(b * kv_heads + h) * res_cap + dst0 + r) * D;
-    reinterpret_cast<uint4 *>(dst)[l & 15] = reinterpret_cast<const uint4 *>(row)[l & 15];
+    const uint4 kw = reinterpret_cast<const uint4 *>(tok_row(ksrc, b, h, t_begin + r))[l & 15];
+    const uint4 vw = reinterpret_cast<const uint4 *>(tok_row(vsrc, b, h, t_begin + r))[l & 15];
+    const int64_t dst = ((int64_t)(b * kv_heads + h) * res_cap + dst0 + r) * D;
+    reinterpret_cast<uint4 *>(kres + dst)[l & 15] = kw;
+    reinterpret_cast<uint4 *>(vres + dst)[l & 15] = vw;
 }
 
 // ------------------------------------------------------------------------------------------------ ragged caches
@@ -785,8 +788,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
         };
         if (a.chunks == 1 && new_row >= 0) write_rows(hkv);
         // count the chunk; the last chunk of the sequence writes the lengths (every workgroup of the sequence has
-        // finished reading them)
-        wait_vmcnt<0>();
+        // finished reading them: its loads were complete before its split ticket). Nothing in this launch reads the
+        // outputs or window rows stored above, so their stores need not be complete before this ticket; the end of
+        // the launch makes them visible.
         uint32_t *cb = a.sync + b;
         if (l == 0) prev = __hip_atomic_fetch_add(cb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         prev = __shfl(prev, 0);
@@ -851,10 +855,11 @@ hipError_t launch_quant_values(const TokSrc &src, int64_t t_begin, int64_t n_til
     return hipGetLastError();
 }
 
-hipError_t launch_copy_rows(const TokSrc &src, int64_t t_begin, int64_t n, int batch, int kv_heads, _Float16 *res,
-                            int res_cap, int dst0, hipStream_t st) {
+hipError_t launch_copy_rows(const TokSrc &ksrc, const TokSrc &vsrc, int64_t t_begin, int64_t n, int batch,
+                            int kv_heads, _Float16 *kres, _Float16 *vres, int res_cap, int dst0, hipStream_t st) {
     dim3 grid((unsigned)((n + 3) / 4), (unsigned)kv_heads, (unsigned)batch);
-    hipLaunchKernelGGL(copy_rows_kernel, grid, dim3(64), 0, st, src, t_begin, n, kv_heads, res, res_cap, dst0);
+    hipLaunchKernelGGL(copy_rows_kernel, grid, dim3(64), 0, st, ksrc, vsrc, t_begin, n, kv_heads, kres, vres,
+                       res_cap, dst0);
     return hipGetLastError();
 }
 
