@@ -3,9 +3,10 @@
 // then rotated at decode time by their absolute position; token 0 may be held apart as an attention sink whose key
 // stays in fp16. Decode pass 2 (the split merge) is shared with the 2-bit path.
 //
-// Sources: KVQuant page (fdeinterviews.com, "KVQuant: Towards 10 Million Context Length LLM Inference with KV Cache
-// Quantization"): per-channel keys, per-token values, keys quantized before RoPE with the rotation applied after
-// dequantization, and the first token's keys kept in full precision (attention sink); RoFormer form of the rotary
+// Sources: synthetic.wiki "KV cache quantization: putting the bits in the cached vectors, not the weights",
+// section "Keys are harder than values" (per-channel keys, per-token values, keys quantized before RoPE with the
+// rotation applied after dequantization) and section "What they report" (the first token's keys kept in full
+// precision: attention sink); RoFormer form of the rotary
 // embedding for the pair layout (adjacent channels 2i, 2i+1, angle m * base^(-2i/D)).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -60,9 +61,9 @@ __device__ __forceinline__ uint32_t row16_max_u32(uint32_t v) {
 // Keys: one workgroup of 64 lanes per tile; lane l owns channels 2l, 2l+1 over the tile's 32 tokens. Key code of
 // token t, channel c sits in word 8 (c/8 + 16 (t/8)) + t%8 at bit 4 (c%8): the two channels of lane l fill byte
 // l%4 of that word, so the four lanes of a quad make one word, written once into LDS.
-// SPARSE (dense-and-sparse groups, KVQuant page, list of methods): each channel's token of largest magnitude (the
-// first on ties) is kept apart as its fp16 value and token index; min and max run over the other 31 tokens and the
-// outlier's code is 0.
+// SPARSE (dense-and-sparse groups; synthetic.wiki "KV cache quantization", section "What they report"): each
+// channel's token of largest magnitude (the first on ties) is kept apart as its fp16 value and token index; min and
+// max run over the other 31 tokens and the outlier's code is 0.
 template <bool SPARSE>
 __global__ __launch_bounds__(64) void quant_keys_b4_kernel(TokSrc src, int64_t t_begin, int kv_heads, uint8_t *tiles,
                                                            int64_t max_tiles, int64_t tile0) {

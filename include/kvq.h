@@ -13,11 +13,11 @@
  *  - synthetic.wiki "KV cache quantization", section "Keys are harder than values": per-channel keys, per-token
  *    values, and a key cache split into a grouped part and a residual part that are combined when computing
  *    attention scores.
- *  - KVQuant page, fdeinterviews.com "KVQuant: Towards 10 Million Context Length LLM Inference with KV Cache
- *    Quantization": per-channel keys quantized before the rotary embedding (RoPE applied after dequantization),
- *    per-token values, the first token's keys kept in full precision (attention sink), and per-vector
- *    dense-and-sparse quantization (outliers held apart so they do not stretch the quantization range); 4-bit
- *    codes.
+ *  - synthetic.wiki "KV cache quantization: putting the bits in the cached vectors, not the weights", on KVQuant:
+ *    section "Keys are harder than values" (per-channel keys quantized before the rotary embedding, RoPE applied
+ *    after dequantization; per-token values) and section "What they report" (the first token's keys kept in full
+ *    precision as an attention sink; per-vector dense-and-sparse quantization, outliers held apart so they do not
+ *    stretch the quantization range). The 4-bit width is the KVQuant-style workload's.
  *
  * Conventions for every call:
  *  - All pointers named as device pointers refer to memory on the current HIP device; host pointers are named so.
@@ -75,16 +75,18 @@ extern "C" {
 #define KVQ_SINK_BYTES 512          /* the sink record of one (batch row, KV head) slice */
 
 /* kvq_shape.flags (4-bit only). */
-#define KVQ_FLAG_SINK 1      /* token 0 is held apart: fp16 key, per-token 4-bit value (KVQuant page, attention sink) */
+#define KVQ_FLAG_SINK 1      /* token 0 is held apart: fp16 key, per-token 4-bit value (synthetic.wiki "KV cache
+                                quantization", section "What they report": KVQuant's attention sink) */
 #define KVQ_FLAG_PRE_ROPE 2  /* keys are given and cached before the rotary embedding; attention rotates every key
-                                (sink, quantized and window alike) by its absolute position (KVQuant page, pre-RoPE
-                                key quantization) */
-#define KVQ_FLAG_SPARSE 4    /* dense-and-sparse groups (KVQuant page, per-vector dense-and-sparse quantization): in
-                                every key group (32 tokens of a channel) and value group (32 channels of a token),
-                                the sink's value groups included, the element of largest magnitude (the lowest index
-                                on ties) is stored apart as its fp16 value and index; the other 31 are quantized by
-                                the rule of kv_quant_keys_per_channel over their own minimum and maximum, and the
-                                outlier's code is 0. Records are 5888 bytes. */
+                                (sink, quantized and window alike) by its absolute position (synthetic.wiki "KV
+                                cache quantization", section "Keys are harder than values": pre-RoPE keys) */
+#define KVQ_FLAG_SPARSE 4    /* dense-and-sparse groups (synthetic.wiki "KV cache quantization", section "What they
+                                report": per-vector dense-and-sparse quantization): in every key group (32 tokens
+                                of a channel) and value group (32 channels of a token), the sink's value groups
+                                included, the element of largest magnitude (the lowest index on ties) is stored
+                                apart as its fp16 value and index; the other 31 are quantized by the rule of
+                                kv_quant_keys_per_channel over their own minimum and maximum, and the outlier's
+                                code is 0. Records are 5888 bytes. */
 
 /*
  * Shape of one cache (one attention layer).

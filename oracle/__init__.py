@@ -25,7 +25,8 @@ Modules:
 - ``layout4``: the 5120-byte 4-bit tile record and the per-slice sink record of the KVQuant variant.
 - ``rope``: the rotary embedding (adjacent channel pairs, theta_i = base ** (-2 i / D), absolute positions).
 
-KVQuant page (fdeinterviews.com, "KVQuant: Towards 10 Million Context Length LLM Inference with KV Cache
-Quantization"): keys quantized before RoPE and rotated after dequantization; the first token's keys kept in full
-precision; 4-bit codes.
+synthetic.wiki "KV cache quantization: putting the bits in the cached vectors, not the weights" on KVQuant:
+section "Keys are harder than values" (keys quantized before RoPE, the rotation applied after dequantization) and
+section "What they report" (the first token's keys kept in full precision; per-vector dense-and-sparse groups);
+4-bit codes are the KVQuant-style workload's width.
 """

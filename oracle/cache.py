@@ -16,7 +16,8 @@ Readings taken where the pages are silent:
 
 A ``SliceCache`` holds any number S of independent (batch row, KV head) slices that share their lengths.
 
-KVQuant variant (``sink=True``; KVQuant page, on the attention sink: the first token's keys stay in full
+KVQuant variant (``sink=True``; synthetic.wiki "KV cache quantization", section "What they report", on the
+attention sink: the first token's keys stay in full
 precision). Reading taken: token 0 is held apart as the sink, its key in float16 and
 its value quantized per token like any other value; the grouped and residual parts start at token 1, so key
 groups cover tokens 1..32, 33..64, and so on, and the window logic above applies to the tokens after the sink.

@@ -2,8 +2,8 @@
 
 TEST INFRASTRUCTURE ONLY.
 
-KVQuant page (fdeinterviews.com, "KVQuant: Towards 10 Million Context Length LLM Inference with KV Cache
-Quantization"), on pre-RoPE key quantization: the keys are quantized before the rotary embedding is applied, and
+synthetic.wiki "KV cache quantization: putting the bits in the cached vectors, not the weights",
+section "Keys are harder than values", on pre-RoPE key quantization (KVQuant): the keys are quantized before the rotary embedding is applied, and
 the rotation (which turns pairs of channels by a position-dependent angle) is applied after dequantization.
 
 Readings taken where the page is silent: the pairs are adjacent channels (2i, 2i+1)

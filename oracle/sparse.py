@@ -1,7 +1,7 @@
 """Per-vector dense-and-sparse group quantization (oracle; test infrastructure only).
 
-KVQuant page (fdeinterviews.com, "KVQuant: Towards 10 Million Context Length LLM Inference with KV Cache
-Quantization"), list of methods: per-vector dense-and-sparse quantization isolates outliers separately for each
+synthetic.wiki "KV cache quantization: putting the bits in the cached vectors, not the weights",
+section "What they report", KVQuant's list of methods: per-vector dense-and-sparse quantization isolates outliers separately for each
 vector, so that they do not skew the quantization ranges.
 
 Readings taken where the page is silent:

@@ -1,4 +1,5 @@
-"""GPU parity of dense-and-sparse groups (KVQuant page, per-vector dense-and-sparse quantization): the 4-bit
+"""GPU parity of dense-and-sparse groups (synthetic.wiki "KV cache quantization", section "What they report":
+per-vector dense-and-sparse quantization): the 4-bit
 records of 5888 bytes and the sink record with value outliers, through the C ABI, against the fp64 CPU oracle.
 
 Bars: codes, fp16 scales, zero points, outlier values and their indices, the sink record and the window bytes

@@ -1,9 +1,9 @@
 """Pins of the KVQuant-style oracle pieces: rotary embedding, 4-bit tile and sink records, the sink cache, and
 attention over a pre-RoPE 4-bit cache with a sink.
 
-Sources: KVQuant page (fdeinterviews.com, "KVQuant: Towards 10 Million Context Length LLM Inference with KV Cache
-Quantization"): keys quantized before RoPE with the rotation applied after dequantization, the first token's keys
-kept in full precision, 4-bit codes. Each pin checks the oracle against something other than its own formula:
+Sources: synthetic.wiki "KV cache quantization: putting the bits in the cached vectors, not the weights": section
+"Keys are harder than values" (keys quantized before RoPE with the rotation applied after dequantization) and
+section "What they report" (the first token's keys kept in full precision); 4-bit codes. Each pin checks the oracle against something other than its own formula:
 closed forms, group laws of rotations, a brute-force per-token loop with explicit 2x2 rotation matrices, and
 special cases that reduce to the plain (already pinned) attention path.
 """

@@ -1,5 +1,6 @@
-"""Pins of the per-vector dense-and-sparse oracle (KVQuant page, list of methods: outliers isolated separately for
-each vector so that they do not skew the quantization ranges).
+"""Pins of the per-vector dense-and-sparse oracle (synthetic.wiki "KV cache quantization", section "What they
+report", KVQuant's list of methods: outliers isolated separately for each vector so that they do not skew the
+quantization ranges).
 
 Each pin checks the oracle against something other than its own code: the dense part against the plain group
 quantizer called on the 31 remaining elements (np.delete, a different path from the oracle's slot filling),
