@@ -111,10 +111,48 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
 
 
-def _f16_4d(t: torch.Tensor, name: str):
-    if t.dtype != torch.float16 or not t.is_cuda or t.dim() != 4 or t.shape[-1] != HEAD_DIM or t.stride(-1) != 1:
-        raise ValueError(f"{name} must be a CUDA float16 tensor [B, H, T, 128] with unit channel stride")
+def _f16_4d(t: torch.Tensor, name: str, batch: int | None = None, heads: int | None = None):
+    """[B, H, T, 128] float16 with unit channel stride -> (pointer, stride_b, stride_h, stride_t). The leading sizes
+    must equal (batch, heads) when given: the library addresses every (batch row, head) slice of the cache's shape,
+    so a smaller tensor would be read past its end."""
+    if t.dtype != torch.float16 or t.dim() != 4 or t.shape[-1] != HEAD_DIM or t.stride(-1) != 1:
+        raise ValueError(f"{name} must be a float16 tensor [B, H, T, 128] with unit channel stride")
+    if batch is not None and (t.shape[0], t.shape[1]) != (batch, heads):
+        raise ValueError(f"{name} has leading sizes {tuple(t.shape[:2])}; the cache shape needs ({batch}, {heads})")
     return ctypes.c_void_p(t.data_ptr()), t.stride(0), t.stride(1), t.stride(2)
+
+
+def _sized_bytes(t: torch.Tensor, name: str, need: int):
+    """A contiguous tensor of at least `need` bytes (any element type)."""
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    have = t.numel() * t.element_size()
+    if have < need:
+        raise ValueError(f"{name} holds {have} bytes; {need} are needed")
+
+
+def _same_cuda_device(device, **tensors):
+    """Every tensor is a CUDA tensor on `device` (checked after the sizes, so size errors name the size)."""
+    for name, t in tensors.items():
+        if not t.is_cuda or t.device != device:
+            raise ValueError(f"{name} must be a CUDA tensor on the cache's device ({device})")
+
+
+def _tiles_bytes(shape) -> int:
+    return shape.batch * shape.kv_heads * (shape.max_tokens // TILE_TOKENS) * shape.record_bytes
+
+
+def _check_out(out: torch.Tensor, shape):
+    """The fp32 output [B, Hq, 128], contiguous."""
+    if out.dtype != torch.float32 or tuple(out.shape) != (shape.batch, shape.q_heads, HEAD_DIM) \
+            or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous float32 tensor [{shape.batch}, {shape.q_heads}, {HEAD_DIM}]")
+
+
+def _check_q(q: torch.Tensor, shape):
+    if q.dtype != torch.float16 or tuple(q.shape) != (shape.batch, shape.q_heads, HEAD_DIM) \
+            or not q.is_contiguous():
+        raise ValueError(f"q must be a contiguous float16 tensor [{shape.batch}, {shape.q_heads}, {HEAD_DIM}]")
 
 
 @dataclass
@@ -176,25 +214,32 @@ class KVCache:
         return self.n_sink + self.n_quant + self.n_resid
 
 
-def kv_quant_keys_per_channel(shape: Shape, k: torch.Tensor, tile0: int, tiles: torch.Tensor, stream=None):
-    p, sb, sh, st = _f16_4d(k, "k")
+def _quant(fn: str, shape: Shape, x: torch.Tensor, name: str, tile0: int, tiles: torch.Tensor, stream):
+    p, sb, sh, st = _f16_4d(x, name, shape.batch, shape.kv_heads)
+    if tiles.dtype != torch.uint8:
+        raise ValueError("tiles must be a uint8 tensor [B, Hkv, max_tokens / 32, record bytes]")
+    _sized_bytes(tiles, "tiles", _tiles_bytes(shape))
+    _same_cuda_device(tiles.device, **{name: x, "tiles": tiles})
     cs = shape.c()
-    _check("kv_quant_keys_per_channel", _lib.kv_quant_keys_per_channel(
-        ctypes.byref(cs), p, sb, sh, st, k.shape[2], tile0, ctypes.c_void_p(tiles.data_ptr()), _stream(stream)))
+    _check(fn, getattr(_lib, fn)(ctypes.byref(cs), p, sb, sh, st, x.shape[2], tile0,
+                                 ctypes.c_void_p(tiles.data_ptr()), _stream(stream)))
+
+
+def kv_quant_keys_per_channel(shape: Shape, k: torch.Tensor, tile0: int, tiles: torch.Tensor, stream=None):
+    _quant("kv_quant_keys_per_channel", shape, k, "k", tile0, tiles, stream)
 
 
 def kv_quant_values_per_token(shape: Shape, v: torch.Tensor, tile0: int, tiles: torch.Tensor, stream=None):
-    p, sb, sh, st = _f16_4d(v, "v")
-    cs = shape.c()
-    _check("kv_quant_values_per_token", _lib.kv_quant_values_per_token(
-        ctypes.byref(cs), p, sb, sh, st, v.shape[2], tile0, ctypes.c_void_p(tiles.data_ptr()), _stream(stream)))
+    _quant("kv_quant_values_per_token", shape, v, "v", tile0, tiles, stream)
 
 
 def kv_append_and_flush(cache: KVCache, k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
-    pk, sb, sh, st = _f16_4d(k_new, "k_new")
-    pv, sb2, sh2, st2 = _f16_4d(v_new, "v_new")
+    s = cache.shape
+    pk, sb, sh, st = _f16_4d(k_new, "k_new", s.batch, s.kv_heads)
+    pv, sb2, sh2, st2 = _f16_4d(v_new, "v_new", s.batch, s.kv_heads)
     if (sb, sh, st) != (sb2, sh2, st2) or k_new.shape != v_new.shape:
         raise ValueError("k_new and v_new must have the same shape and strides")
+    _same_cuda_device(cache.tiles.device, k_new=k_new, v_new=v_new)
     _check("kv_append_and_flush", _lib.kv_append_and_flush(
         ctypes.byref(cache._cshape), ctypes.byref(cache.c), pk, pv, sb, sh, st, k_new.shape[2], _stream(stream)))
 
@@ -210,14 +255,15 @@ def kv_decode_attention_workspace_bytes(cache: KVCache) -> int:
 def kv_decode_attention(cache: KVCache, q: torch.Tensor, out: torch.Tensor | None = None, sm_scale: float = 0.0,
                         workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     s = cache.shape
-    if q.dtype != torch.float16 or not q.is_cuda or tuple(q.shape) != (s.batch, s.q_heads, HEAD_DIM) \
-            or not q.is_contiguous():
-        raise ValueError("q must be a contiguous CUDA float16 tensor [B, Hq, 128]")
+    _check_q(q, s)
     if out is None:
         out = torch.empty((s.batch, s.q_heads, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _check_out(out, s)
     need = kv_decode_attention_workspace_bytes(cache)
     if workspace is None:
         workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _sized_bytes(workspace, "workspace", need)
+    _same_cuda_device(cache.tiles.device, q=q, out=out, workspace=workspace)
     _check("kv_decode_attention", _lib.kv_decode_attention(
         ctypes.byref(cache._cshape), ctypes.byref(cache.c), ctypes.c_void_p(q.data_ptr()), float(sm_scale),
         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
@@ -252,23 +298,33 @@ class RaggedCache:
         return self.lens.cpu().tolist()
 
 
-def _f16_tokens(t: torch.Tensor, name: str):
+def _f16_tokens(t: torch.Tensor, name: str, shape=None, device=None):
     """One token per (sequence, KV head): [B, Hkv, 128] or [B, Hkv, 1, 128] -> (pointer, stride_b, stride_h)."""
     if t.dim() == 4:
         if t.shape[2] != 1:
             raise ValueError(f"{name}: one token per sequence")
         t = t[:, :, 0]
-    if t.dtype != torch.float16 or not t.is_cuda or t.dim() != 3 or t.shape[-1] != HEAD_DIM or t.stride(-1) != 1:
-        raise ValueError(f"{name} must be a CUDA float16 tensor [B, Hkv, 128] with unit channel stride")
+    if t.dtype != torch.float16 or t.dim() != 3 or t.shape[-1] != HEAD_DIM or t.stride(-1) != 1:
+        raise ValueError(f"{name} must be a float16 tensor [B, Hkv, 128] with unit channel stride")
+    if shape is not None and (t.shape[0], t.shape[1]) != (shape.batch, shape.kv_heads):
+        raise ValueError(f"{name} has leading sizes {tuple(t.shape[:2])}; the cache shape needs "
+                         f"({shape.batch}, {shape.kv_heads})")
+    if device is not None:
+        _same_cuda_device(device, **{name: t})
     return ctypes.c_void_p(t.data_ptr()), t.stride(0), t.stride(1)
 
 
 def kv_ragged_prefill(cache: RaggedCache, b: int, k: torch.Tensor, v: torch.Tensor, stream=None):
     """Replace sequence b with the tokens of k, v ([Hkv, T, 128], unit channel stride)."""
     for t, nm in ((k, "k"), (v, "v")):
-        if t.dtype != torch.float16 or not t.is_cuda or t.dim() != 3 or t.shape[-1] != HEAD_DIM or \
+        if t.dtype != torch.float16 or t.dim() != 3 or t.shape[-1] != HEAD_DIM or \
                 (t.numel() and t.stride(-1) != 1):
-            raise ValueError(f"{nm} must be a CUDA float16 tensor [Hkv, T, 128] with unit channel stride")
+            raise ValueError(f"{nm} must be a float16 tensor [Hkv, T, 128] with unit channel stride")
+        if t.shape[0] != cache.shape.kv_heads:
+            raise ValueError(f"{nm} holds {t.shape[0]} KV heads; the cache has {cache.shape.kv_heads}")
+    if not 0 <= int(b) < cache.shape.batch:
+        raise ValueError(f"sequence index {b} outside [0, {cache.shape.batch})")
+    _same_cuda_device(cache.tiles.device, k=k, v=v)
     if k.shape != v.shape or (k.numel() and k.stride() != v.stride()):
         raise ValueError("k and v must have the same shape and strides")
     n = k.shape[1]
@@ -279,8 +335,8 @@ def kv_ragged_prefill(cache: RaggedCache, b: int, k: torch.Tensor, v: torch.Tens
 
 
 def kv_ragged_append(cache: RaggedCache, k_new: torch.Tensor, v_new: torch.Tensor, stream=None):
-    pk, sb, sh = _f16_tokens(k_new, "k_new")
-    pv, sb2, sh2 = _f16_tokens(v_new, "v_new")
+    pk, sb, sh = _f16_tokens(k_new, "k_new", cache.shape, cache.tiles.device)
+    pv, sb2, sh2 = _f16_tokens(v_new, "v_new", cache.shape, cache.tiles.device)
     if (sb, sh) != (sb2, sh2):
         raise ValueError("k_new and v_new must have the same strides")
     _check("kv_ragged_append", _lib.kv_ragged_append(
@@ -297,13 +353,15 @@ def kv_ragged_splits(cache: RaggedCache) -> int:
 
 def _ragged_io(cache, q, out, workspace):
     s = cache.shape
-    if q.dtype != torch.float16 or not q.is_cuda or tuple(q.shape) != (s.batch, s.q_heads, HEAD_DIM) \
-            or not q.is_contiguous():
-        raise ValueError("q must be a contiguous CUDA float16 tensor [B, Hq, 128]")
+    _check_q(q, s)
     if out is None:
         out = torch.empty((s.batch, s.q_heads, HEAD_DIM), dtype=torch.float32, device=q.device)
+    _check_out(out, s)
+    need = kv_ragged_workspace_bytes(cache)
     if workspace is None:
-        workspace = torch.empty(max(kv_ragged_workspace_bytes(cache), 16), dtype=torch.uint8, device=q.device)
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _sized_bytes(workspace, "workspace", need)
+    _same_cuda_device(cache.tiles.device, q=q, out=out, workspace=workspace)
     return out, workspace
 
 
@@ -323,11 +381,12 @@ def kv_ragged_decode_step(cache: RaggedCache, k_new: torch.Tensor, v_new: torch.
     """Append one token per sequence, then attend: one launch that flushes full windows, attends, merges the splits,
     writes the new window rows and commits the lengths (no host state: graph-capturable). Needs the cache's
     ``sync`` counters (zero before and after every launch)."""
-    pk, sb, sh = _f16_tokens(k_new, "k_new")
-    pv, sb2, sh2 = _f16_tokens(v_new, "v_new")
+    pk, sb, sh = _f16_tokens(k_new, "k_new", cache.shape)
+    pv, sb2, sh2 = _f16_tokens(v_new, "v_new", cache.shape)
     if (sb, sh) != (sb2, sh2):
         raise ValueError("k_new and v_new must have the same strides")
     out, workspace = _ragged_io(cache, q, out, workspace)
+    _same_cuda_device(cache.tiles.device, k_new=k_new, v_new=v_new)
     _check("kv_ragged_decode_step", _lib.kv_ragged_decode_step(
         ctypes.byref(cache._cshape), ctypes.byref(cache.c), pk, pv, sb, sh, ctypes.c_void_p(q.data_ptr()),
         float(sm_scale), ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
