@@ -394,10 +394,17 @@ constexpr int LDS_BYTES = 8704;      // [0, 8192) also holds the fp16 window val
 // quantizes those tiles itself (the same quantizer functions as the flush kernel; workgroups of the other query-head
 // chunks of that KV head write identical bytes) and reads them back. The new token is attended straight from the
 // input (its window row is written only at the end). After its partials are stored, a workgroup counts itself in
-// sync[(b, KV head, chunk)] behind a device-scope fence; the last of the splits merges them (the pass-2 code) and
-// counts the chunk in sync[b]; the last chunk of the sequence writes the new window rows and the lengths, by when
-// every workgroup of the sequence has read them. Counters are reset by the workgroup that completes them. No
-// workgroup waits for another.
+// sync[(b, KV head, chunk)]; the last of the splits merges them (the pass-2 code) and counts the chunk in sync[b];
+// the last chunk of the sequence writes the new window rows and the lengths, by when every workgroup of the sequence
+// has read them. Counters are reset by the workgroup that completes them. No workgroup waits for another.
+// Ordering: the tickets are relaxed agent-scope atomics, so they carry no happens-before edge of the HIP memory
+// model. The merge is correct because of three hardware facts this kernel relies on instead: every value another
+// workgroup reads (the split partials) is written with agent-scope atomic stores, which write through to the
+// device's coherence point, and read with agent-scope atomic loads, which read from it (never from a non-coherent
+// per-XCD L2 line); a workgroup waits for all its memory operations (s_waitcnt vmcnt(0): stores acknowledged,
+// loads returned) before taking its ticket; the ticket is itself performed at the coherence point. A plain store
+// that another workgroup of the launch read would need a release/acquire pair instead (at agent scope an L2
+// write-back and invalidate per workgroup, which costs the step several times its length).
 template <int MODE>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void decode_pass1_kernel(DecodeArgs a) {
     __shared__ __align__(16) unsigned char smem[LDS_BYTES];
