@@ -5,19 +5,22 @@ One step = one token appended to every sequence (window append, with the 128-tok
 when the window is full) followed by decode attention of one query per (sequence, query head) over the whole
 cache. The cache is built from seeded synthetic keys/values/queries (kvsynth) and is resident in HBM before the
 timed region starts. The default workload is the GQA decode at 32K context (batch 64, 32 query heads sharing
-8 KV heads); the prefill is sized so the first timed step attends over exactly 32768 tokens, and the default
-128 timed steps contain exactly one flush (the steady-state mix).
+8 KV heads); the prefill is sized so the first timed step attends over exactly 32768 tokens.
 
 Printed (one JSON line on stdout): KV tokens/s over the timed steps (value), the decode-attention call's achieved
-algorithmic HBM bandwidth against the 8 TB/s peak (roofline), and the CPU oracle timed on a sample of the same
-workload (cpu_baseline). Progress goes to stderr.
+algorithmic HBM bandwidth against the 8 TB/s peak (roofline), the engine clock over the timed calls (a probe
+wavefront per XCD beside them), the box's streaming-read ceiling, the same call over an all-fp16 cache (the
+fp16-versus-2-bit comparison), and the CPU oracle timed on a sample of the same workload (cpu_baseline: attention
+rate as the value, quantization rate beside it). With the default workload the line also carries `workloads`:
+sub-records for the 4-bit KVQuant-style variant (kvquant_4bit_16k), the 1M-token single sequence (long_1m), each
+with the same warm-up and timed step counts, and the single-launch decode step of the Llama-2-7B-shaped stream
+(128 steps over three cache copies in turn, eager per-step percentiles and one HIP graph). Progress goes to stderr.
 
-`--workload kvquant_4bit_16k` measures the 4-bit KVQuant-style variant the same way (batch 16, 32 heads, 16K
-context, keys cached before RoPE and rotated at decode time, token 0 held as an fp16-key sink).
+`--workload NAME` measures one workload alone (e.g. kvquant_4bit_16k, kvquant_4bit_sparse_16k, long_1m).
 
-`--step-graph` measures whole decode steps (append + attention) three ways on the same inputs: the host-length
-calls issued eagerly, the ragged-cache step (lengths in device memory, three launches) issued eagerly, and the
-ragged step with all timed steps captured in one HIP graph and replayed once. Default workload for it:
+`--step-graph` measures whole decode steps (append + attention) several ways on the same inputs: the host-length
+calls issued eagerly, the single-launch ragged step issued eagerly, the ragged step with all timed steps captured
+in one HIP graph, the graph over cache copies in turn, and a batch at mixed lengths. Default workload for it:
 llama2_7b_stream (batch 8, 32 heads, 4096-token prefill), whose steps are short enough for launch costs to show.
 """
 from __future__ import annotations
@@ -98,63 +101,136 @@ def traffic_per_launch(workload):
     return None
 
 
-def cpu_baseline(w, queries, n_slices, context):
-    """The oracle (as it stands) on a sample of the same workload: decode attention over `context` tokens of
-    `n_slices` (batch row, KV head) slices, once for each of the given timed steps' queries (the oracle's cost does not
-    depend on the query values, so reusing a quantized slice for several queries only saves untimed set-up). Returns
-    the rate in the metric's unit (KV tokens/s, where one batch row of all heads over N tokens counts N)."""
+def _blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover - threadpoolctl missing
+        return 1
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            return next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
+    except OSError:  # pragma: no cover - no procfs
+        return None
+
+
+def cpu_baseline(w, queries, n_slices, context, quant_threads=None):
+    """The oracle (as it stands) on a sample of the same workload, timed on the host cores.
+
+    Quantization (the oracle's per-channel key and per-token value quantizer, the group rule of every flush) of
+    `n_slices` (batch row, KV head) slices of `context` tokens each, the slices spread over a thread pool; then
+    decode attention (dequantize + softmax attention in float64) of those slices, once for each of the given timed
+    steps' queries (the oracle's cost does not depend on the query values). The attention rate is the value, in the
+    metric's unit (KV tokens/s: one batch row of all heads over N tokens counts N); the quantization rate is
+    reported beside it in tokens of one KV head per second and GB/s of fp16 K and V read."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import numpy as np
 
     import kvsynth
     from oracle import attention as oa
     from oracle import cache as oc
-    try:
-        from threadpoolctl import threadpool_info
-        blas_threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"]
-                           or [1])
-    except Exception:  # pragma: no cover - threadpoolctl missing
-        blas_threads = 1
     G = w.q_heads // w.kv_heads
     step = max(1, (w.batch * w.kv_heads) // n_slices)
     slices = [(i // w.kv_heads, i % w.kv_heads) for i in range(0, w.batch * w.kv_heads, step)][:n_slices]
     k = np.stack([kvsynth.slice_tokens(w.seed, kvsynth.K_ID, b, h, 0, context, w.head_dim, w.k_outliers,
                                        w.k_factor) for b, h in slices])
     v = np.stack([kvsynth.slice_tokens(w.seed, kvsynth.V_ID, b, h, 0, context, w.head_dim) for b, h in slices])
-    c = oc.SliceCache(len(slices), residual_cap=w.residual, bits=w.bits, sink=w.sink, sparse=w.sparse)
-    oc.append_block(c, k, v)
+    nthreads = quant_threads or min(16, len(os.sched_getaffinity(0)))
+    parts = np.array_split(np.arange(len(slices)), nthreads)
+    parts = [p for p in parts if len(p)]
+
+    def quantize(idx):
+        c = oc.SliceCache(len(idx), residual_cap=w.residual, bits=w.bits, sink=w.sink, sparse=w.sparse)
+        oc.append_block(c, k[idx], v[idx])
+        return c
+
+    t = time.perf_counter()
+    with ThreadPoolExecutor(len(parts)) as ex:
+        caches = list(ex.map(quantize, parts))
+    dq = time.perf_counter() - t
     del k, v
     dt = 0.0
     for qs in queries:
-        q = np.stack([qs[b, h * G:(h + 1) * G] for b, h in slices])       # [S, G, D]
-        t = time.perf_counter()
-        oa.decode_attention(c, q, len(slices), 1, rope_base=w.rope_base)
-        dt += time.perf_counter() - t
+        for idx, c in zip(parts, caches):
+            q = np.stack([qs[slices[i][0], slices[i][1] * G:(slices[i][1] + 1) * G] for i in idx])   # [S, G, D]
+            t = time.perf_counter()
+            oa.decode_attention(c, q, len(idx), 1, rope_base=w.rope_base)
+            dt += time.perf_counter() - t
     kv_tokens = len(slices) / w.kv_heads * context * len(queries)
-    cpu_model = None
-    try:
-        with open("/proc/cpuinfo") as f:
-            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), None)
-    except OSError:  # pragma: no cover - no procfs
-        pass
-    return {"value": kv_tokens / dt, "unit": "KV tokens/s", "cores": int(blas_threads), "kind": "oracle",
-            "blas_threads": int(blas_threads), "cpu_model": cpu_model,
-            "sample": f"{len(slices)} of {w.batch * w.kv_heads} (batch row, KV head) slices of {w.name} at "
-                      f"{context} tokens, each attended by the queries of the first {len(queries)} timed steps: "
-                      f"float64 decode attention (dequantize + softmax), {dt:.2f} s; quantization not timed",
+    blas = _blas_threads()
+    frac = len(slices) / (w.batch * w.kv_heads)
+    return {"value": kv_tokens / dt, "unit": "KV tokens/s", "cores": int(max(blas, len(parts))), "kind": "oracle",
+            "blas_threads": int(blas), "cpu_model": _cpu_model(),
+            "sample": f"{len(slices)} of {w.batch * w.kv_heads} (batch row, KV head) slices ({100 * frac:.1f}%) of "
+                      f"{w.name} at {context} tokens, each attended by the queries of the first {len(queries)} timed "
+                      f"steps: float64 decode attention (dequantize + softmax), {dt:.2f} s on {blas} BLAS threads; "
+                      f"quantization of the same slices timed separately",
+            "attention_seconds": dt,
+            "quantization": {"tokens_per_s": len(slices) * context / dq,
+                             "gb_s_fp16_read": len(slices) * context * w.head_dim * 2 * 2 / dq / 1e9,
+                             "seconds": dq, "threads": len(parts),
+                             "unit": "tokens of one KV head per second (keys per channel and values per token)",
+                             "sample": f"{len(slices)} slices x {context} tokens through the oracle's append (every "
+                                       f"flush quantized), slices spread over {len(parts)} threads"},
             "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def _probe_lib():
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "decode_attention_quant_amd", "libkvq_probe.so"))
+    lib.kvq_probe_sink_words.restype = ctypes.c_size_t
+    lib.kvq_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
+                                       ctypes.c_void_p]
+    lib.kvq_probe_clock_words.restype = ctypes.c_size_t
+    lib.kvq_probe_wall_clock_khz.restype = ctypes.c_int
+    lib.kvq_probe_clock.argtypes = [ctypes.c_uint64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    return lib
+
+
+class ClockProbe:
+    """Engine clock beside the timed calls: one sleeping wavefront per XCD on a second stream (default priority)
+    reads the shader cycle counter and the constant-rate counter over a window inside the timed region."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.lib = _probe_lib()
+        self.words = int(self.lib.kvq_probe_clock_words())
+        self.out = torch.zeros(self.words, dtype=torch.int64, device="cuda")
+        self.stream = torch.cuda.Stream()
+        self.khz = int(self.lib.kvq_probe_wall_clock_khz())
+        self.started = False
+
+    def start(self, seconds):
+        if self.khz <= 0 or seconds <= 0:
+            return
+        ticks = max(1, min(10 ** 9, int(seconds * self.khz * 1e3)))
+        rc = self.lib.kvq_probe_clock(ticks, self.out.data_ptr(), self.words, self.stream.cuda_stream)
+        self.started = rc == 0
+
+    def result(self):
+        if not self.started:
+            return None
+        self.torch.cuda.synchronize()
+        v = self.out.cpu().tolist()
+        ghz = [v[2 * i] / v[2 * i + 1] * self.khz * 1e-6 for i in range(self.words // 2) if v[2 * i + 1] > 0]
+        if not ghz:
+            return None
+        return {"ghz_mean": sum(ghz) / len(ghz), "ghz_min": min(ghz), "ghz_max": max(ghz),
+                "window_us": v[1] / self.khz * 1e3, "wavefronts": len(ghz),
+                "note": "shader cycles / constant-rate ticks of one sleeping wavefront per XCD, over a window inside "
+                        "the timed calls"}
 
 
 def hbm_read_ceiling(nbytes, reps=20):
     """The box's achievable HBM read bandwidth: a plain streaming read (`libkvq_probe.so`, every 16-byte chunk of
     the buffer loaded once) of a buffer as large as one decode call's bytes, `reps` back-to-back launches between two
     HIP events on the current stream."""
-    import ctypes
-
     import torch
-    lib = ctypes.CDLL(os.path.join(ROOT, "decode_attention_quant_amd", "libkvq_probe.so"))
-    lib.kvq_probe_sink_words.restype = ctypes.c_size_t
-    lib.kvq_probe_hbm_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_size_t,
-                                       ctypes.c_void_p]
+    lib = _probe_lib()
     nbytes = (int(nbytes) + 15) // 16 * 16
     buf = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
     nsink = lib.kvq_probe_sink_words()
@@ -389,58 +465,11 @@ def step_graph(args, kvq, kdev, kvsynth, torch):
     return 0
 
 
-def main(argv=None):
-    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=128)
-    ap.add_argument("--warmup", type=int, default=8)
-    ap.add_argument("--workload", default="llama3_8b_gqa_32k")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-slices", type=int, default=24)
-    ap.add_argument("--cpu-queries", type=int, default=12)
-    ap.add_argument("--no-fp16-comparator", action="store_true")
-    ap.add_argument("--no-hbm-ceiling", action="store_true")
-    ap.add_argument("--fp16-calls", type=int, default=20)
-    ap.add_argument("--step-graph", action="store_true",
-                    help="decode-step time: host API vs ragged step vs ragged step in a HIP graph "
-                         "(default workload llama2_7b_stream)")
-    ap.add_argument("--rotate", type=int, default=3,
-                    help="--step-graph: cache copies stepped in turn for the HBM-resident measurement")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain 1 GiB device copy (5 times), the reference for HBM byte counters")
-    args = ap.parse_args(argv)
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path (every (batch row, KV head) slice "
-              "is independent, so slices would be split across GPUs with no communication). Run with --gpus 1.",
-              file=sys.stderr)
-        return 2
-
-    import torch
-
-    if args.copy_calibration:
-        n = 1 << 30
-        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_calibration": {"bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 5}}))
-        return 0
-
-    import decode_attention_quant_amd as kvq
-    import kvsynth
-    from kvsynth import device as kdev
-
-    if args.step_graph:
-        if args.workload == "llama3_8b_gqa_32k" and "--workload" not in (argv or sys.argv):
-            args.workload = "llama2_7b_stream"
-        return step_graph(args, kvq, kdev, kvsynth, torch)
-
-    w = kvsynth.WORKLOADS[args.workload]
-    W, K, R = args.warmup, args.steps, w.residual
+def measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=True):
+    """One workload: prefill (timed as one append), W warm-up steps, then K timed steps, each one token appended to
+    every sequence and one decode-attention call, with HIP events around every append and every call on the current
+    stream. Returns the record and the device tensors the extras reuse."""
+    R = w.residual
     P = w.context - W - 1                      # first timed step attends over exactly w.context tokens
     total = P + W + K
     flags = ((kvq.FLAG_SINK if w.sink else 0) | (kvq.FLAG_PRE_ROPE if w.rope_base else 0)
@@ -489,11 +518,17 @@ def main(argv=None):
         t = P + i
         kvq.kv_append_and_flush(cache, Kd[:, :, t:t + 1], Vd[:, :, t:t + 1])
 
+    wev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     for i in range(W):
         step(i)
+        if i == W - 1:
+            wev[0].record()
         kvq.kv_decode_attention(cache, Q[i], out=out, workspace=workspace)
+    wev[1].record()
     torch.cuda.synchronize()
+    last_warm_ms = wev[0].elapsed_time(wev[1]) if W > 0 else 0.3
 
+    probe_clock = ClockProbe(torch) if clock else None
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * K + 2)]
     call_bytes, kv_tokens, contexts = [], 0, []
     ev[0].record()
@@ -504,6 +539,8 @@ def main(argv=None):
         ev[3 * j + 2].record()
         kvq.kv_decode_attention(cache, Q[i], out=out, workspace=workspace)
         ev[3 * j + 3].record()
+        if j == 0 and probe_clock is not None:   # a window inside the timed calls
+            probe_clock.start(0.7 * K * last_warm_ms * 1e-3)
         n = cache.n_tokens
         contexts.append(n)
         kv_tokens += w.batch * n
@@ -519,9 +556,10 @@ def main(argv=None):
     splits = kvq.kv_decode_attention_splits(cache)
     dsorted = sorted(decode_ms)
     pct = lambda f: 1e3 * dsorted[min(K - 1, int(f * (K - 1) + 0.5))]
-    log(f"[bench] {K} steps in {total_ms:.3f} ms; decode call avg {1e3 * sum(decode_ms) / K:.1f} us "
+    clk = probe_clock.result() if probe_clock is not None else None
+    log(f"[bench] {w.name}: {K} steps in {total_ms:.3f} ms; decode call avg {1e3 * sum(decode_ms) / K:.1f} us "
         f"({achieved:.0f} GB/s); append avg {1e3 * sum(append_ms) / K:.1f} us, max {1e3 * max(append_ms):.1f} us; "
-        f"splits={splits}")
+        f"splits={splits}" + (f"; engine clock {clk['ghz_mean']:.2f} GHz" if clk else ""))
 
     if w.bits == 2:
         detail = "2-bit codes expanded to fp16 MFMA operands (scales folded as fp16 hi+lo), fp32 accumulation"
@@ -554,6 +592,7 @@ def main(argv=None):
         "append_us_max": 1e3 * max(append_ms),
         "splits": splits,
         "decode_call_us_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
+        "engine_clock": clk,
         "prefill": {"tokens": P, "us": prefill_us, "bytes": prefill_bytes,
                     "gb_s": prefill_bytes / prefill_us / 1e3,
                     "note": "one kv_append_and_flush of the prefill: key and value quantization of the flushed "
@@ -563,6 +602,175 @@ def main(argv=None):
                      "frac": achieved / PEAK_GBS, "traffic": traffic_per_launch(w.name),
                      "kernel": kernel, "bytes_per_call": sum(call_bytes) / K},
     }
+    state = {"Kd": Kd, "Vd": Vd, "Q": Q, "cache": cache, "contexts": contexts}
+    return res, state
+
+
+def compact(rec):
+    """The sub-record of one extra workload: its shape, the call's time and its roofline."""
+    keys = ("decode_call_us", "decode_call_us_p10_p50_p90", "hbm_gb_s", "pct_of_peak", "splits", "engine_clock",
+            "append_us_avg", "steps", "warmup")
+    r = {k: rec[k] for k in keys if k in rec}
+    r["metric"] = rec["metric"]
+    r["config"] = rec["config"]
+    r["kv_tokens_per_s"] = rec["value"]
+    r["roofline"] = {k: rec["roofline"][k] for k in ("achieved", "frac", "bytes_per_call", "traffic", "kernel")}
+    r["prefill_gb_s"] = rec["prefill"]["gb_s"]
+    return r
+
+
+def step_record(kvq, kdev, kvsynth, torch, w, W, K, rot):
+    """Single-launch ragged decode steps (append with lazy flush + attention + merge + length commit in one
+    kernel) over `rot` cache copies in turn, so the steps read HBM: every step timed with HIP events when issued
+    eagerly (percentiles, flush steps apart), and the same steps captured in one HIP graph and replayed once."""
+    R = w.residual
+    P = w.prefill
+    total = P + W + K
+    cap = ((total + 31) // 32) * 32
+    Kd = kdev.kv_to_device(w, kvsynth.K_ID, 0, total)
+    Vd = kdev.kv_to_device(w, kvsynth.V_ID, 0, total)
+    Q = kdev.queries_to_device(w, range(1, W + K + 1))
+    shape = kvq.Shape(w.batch, w.kv_heads, w.q_heads, residual_cap=R, max_tokens=cap)
+
+    def fresh():
+        c = kvq.RaggedCache(shape)
+        for b in range(w.batch):
+            kvq.kv_ragged_prefill(c, b, Kd[b, :, :P], Vd[b, :, :P])
+        return c
+
+    cshape = shape.c()
+    ws = torch.empty(int(kvq.library().kv_ragged_workspace_bytes(kvq.ctypes.byref(cshape))), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((w.batch, w.q_heads, 128), dtype=torch.float32, device="cuda")
+
+    def run(copies, i, o, idx):
+        t = P + i
+        kvq.kv_ragged_decode_step(copies[idx], Kd[:, :, t], Vd[:, :, t], Q[i], out=o, workspace=ws)
+
+    # eager, every step between events (copy j % rot takes its step j // rot)
+    copies = [fresh() for _ in range(rot)]
+    for c in range(rot):
+        for i in range(W):
+            run(copies, i, out, c)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(K + 1)]
+    ev[0].record()
+    for j in range(K):
+        run(copies, W + j // rot, out, j % rot)
+        ev[j + 1].record()
+    torch.cuda.synchronize()
+    us = [1e3 * ev[j].elapsed_time(ev[j + 1]) for j in range(K)]
+    # lengths before each eager step: a step flushes when its copy's window is full
+    nq0, nr0 = lengths_after(*lengths_after(0, 0, P, R), W, R)
+    flush = []
+    for j in range(K):
+        _, nr = lengths_after(nq0, nr0, j // rot, R)
+        flush.append(nr == R)
+    steady = sorted(u for u, f in zip(us, flush) if not f)
+    pct = lambda xs, f: xs[min(len(xs) - 1, int(f * (len(xs) - 1) + 0.5))]
+    del copies
+    # the same steps in one graph over fresh copies
+    gcopies = [fresh() for _ in range(rot)]
+    for c in range(rot):
+        for i in range(W):
+            run(gcopies, i, out, c)
+    outs = torch.empty((K, w.batch, w.q_heads, 128), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for j in range(K):
+            run(gcopies, W + j // rot, outs[j], j % rot)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    us_graph = 1e3 * a.elapsed_time(b) / K
+    ln = gcopies[0].lens.cpu().tolist()
+    nq, nr = ln[0][0], ln[0][1]
+    nbytes = algorithmic_bytes(w.batch, w.kv_heads, w.q_heads, nq, nr)
+    step_bytes = nbytes + w.batch * w.kv_heads * 4 * w.head_dim * 2
+    ctx = nq + nr
+    del graph, gcopies, outs, Kd, Vd, Q
+    torch.cuda.empty_cache()
+    log(f"[bench] {w.name} decode step: graph over {rot} copies {us_graph:.1f} us per step "
+        f"({step_bytes / us_graph / 1e3:.0f} GB/s); eager steady p50 {pct(steady, 0.5):.1f} us, flush steps "
+        f"{[round(u, 1) for u, f in zip(us, flush) if f]}")
+    return {"metric": "2-bit decode step (append with lazy flush + attention), one launch per step",
+            "config": {"workload": w.name, "batch": w.batch, "q_heads": w.q_heads, "kv_heads": w.kv_heads,
+                       "prefill": P, "context_last_timed_step": ctx, "bits": 2, "residual": R},
+            "steps": K, "warmup": W, "cache_copies": rot,
+            "step_us_graph": us_graph, "kv_tokens_per_s": w.batch * ctx / (us_graph * 1e-6),
+            "step_us_eager_steady_p10_p50_p90": [pct(steady, 0.1), pct(steady, 0.5), pct(steady, 0.9)],
+            "step_us_eager_flush_steps": [u for u, f in zip(us, flush) if f],
+            "roofline": {"achieved": step_bytes / us_graph / 1e3, "frac": step_bytes / us_graph / 1e3 / PEAK_GBS,
+                         "bytes_per_step": step_bytes,
+                         "kernel": "decode_pass1_kernel<2> (kv_ragged_decode_step: flush, append, attention, merge, "
+                                   "length commit)",
+                         "note": "attention bytes at the last timed step plus the new token's K, V read and window "
+                                 "row written; the graph's mean over all timed steps, flush steps included"}}
+
+
+SUB_WORKLOADS = ("kvquant_4bit_16k", "long_1m", "llama2_7b_stream")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="llama3_8b_gqa_32k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-slices", type=int, default=64)
+    ap.add_argument("--cpu-queries", type=int, default=2)
+    ap.add_argument("--no-fp16-comparator", action="store_true")
+    ap.add_argument("--no-hbm-ceiling", action="store_true")
+    ap.add_argument("--no-clock", action="store_true", help="no engine-clock probe beside the timed calls")
+    ap.add_argument("--no-sub-records", action="store_true",
+                    help="measure only the headline workload (else also " + ", ".join(SUB_WORKLOADS) + ")")
+    ap.add_argument("--fp16-calls", type=int, default=20)
+    ap.add_argument("--step-graph", action="store_true",
+                    help="decode-step time: host API vs ragged step vs ragged step in a HIP graph "
+                         "(default workload llama2_7b_stream)")
+    ap.add_argument("--rotate", type=int, default=3,
+                    help="--step-graph: cache copies stepped in turn for the HBM-resident measurement")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (5 times), the reference for HBM byte counters")
+    args = ap.parse_args(argv)
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path (every (batch row, KV head) slice "
+              "is independent, so slices would be split across GPUs with no communication). Run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"bytes_read_per_copy": n, "bytes_written_per_copy": n, "copies": 5}}))
+        return 0
+
+    import decode_attention_quant_amd as kvq
+    import kvsynth
+    from kvsynth import device as kdev
+
+    if args.step_graph:
+        if args.workload == "llama3_8b_gqa_32k" and "--workload" not in (argv or sys.argv):
+            args.workload = "llama2_7b_stream"
+        return step_graph(args, kvq, kdev, kvsynth, torch)
+
+    w = kvsynth.WORKLOADS[args.workload]
+    W, K = args.warmup, args.steps
+    res, st = measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=not args.no_clock)
+    achieved = res["hbm_gb_s"]
     if not args.no_hbm_ceiling:
         ceil = hbm_read_ceiling(res["roofline"]["bytes_per_call"])
         ceil["decode_frac_of_ceiling"] = achieved / ceil["gb_s"]
@@ -570,12 +778,34 @@ def main(argv=None):
         log(f"[bench] streaming-read ceiling {ceil['gb_s']:.0f} GB/s ({100 * ceil['frac_of_peak']:.1f}% of "
             f"{PEAK_GBS:.0f}); the decode call reaches {100 * ceil['decode_frac_of_ceiling']:.1f}% of it")
     if not args.no_fp16_comparator and w.bits == 2:
-        res["fp16_comparator"] = fp16_comparator(kvq, w, Kd, Vd, Q[W], contexts[0], res["decode_call_us"],
-                                                 args.fp16_calls)
+        res["fp16_comparator"] = fp16_comparator(kvq, w, st["Kd"], st["Vd"], st["Q"][W], st["contexts"][0],
+                                                 res["decode_call_us"], args.fp16_calls)
+    Qcpu = [st["Q"][W + j].cpu().numpy() for j in range(min(args.cpu_queries, K))]
+    del st
+    torch.cuda.empty_cache()
+
+    if not args.no_sub_records and "--workload" not in (argv if argv is not None else sys.argv):
+        subs = {}
+        for name in SUB_WORKLOADS:
+            sw = kvsynth.WORKLOADS[name]
+            try:
+                if name == "llama2_7b_stream":
+                    subs[name + "_step"] = step_record(kvq, kdev, kvsynth, torch, sw, 8, 128, 3)
+                else:
+                    r, s2 = measure_decode(kvq, kdev, kvsynth, torch, sw, W, K, clock=not args.no_clock)
+                    del s2
+                    subs[name] = compact(r)
+            finally:
+                torch.cuda.empty_cache()
+        res["workloads"] = subs
+
     if not args.no_cpu_baseline:
-        log(f"[bench] timing the CPU oracle on {args.cpu_slices} slices x {args.cpu_queries} queries")
-        qs = [Q[W + j].cpu().numpy() for j in range(min(args.cpu_queries, K))]
-        res["cpu_baseline"] = cpu_baseline(w, qs, args.cpu_slices, contexts[0])
+        log(f"[bench] timing the CPU oracle on {args.cpu_slices} slices x {len(Qcpu)} queries")
+        res["cpu_baseline"] = cpu_baseline(w, Qcpu, args.cpu_slices, res["config"]["context_first_timed_step"])
+        log(f"[bench] oracle: attention {res['cpu_baseline']['value']:.0f} KV tokens/s "
+            f"({res['cpu_baseline']['attention_seconds']:.1f} s), quantization "
+            f"{res['cpu_baseline']['quantization']['tokens_per_s']:.0f} tokens/s "
+            f"({res['cpu_baseline']['quantization']['seconds']:.1f} s)")
     else:
         res["cpu_baseline"] = None
     print(json.dumps(res), flush=True)

@@ -1,5 +1,6 @@
-// Measurement helper for the benchmark (not part of the cache library): a plain streaming read of a device buffer,
-// the achievable HBM read bandwidth of the box to report next to the published peak. Built as libkvq_probe.so.
+// Measurement helpers for the benchmark (not part of the cache library), built as libkvq_probe.so: a plain
+// streaming read of a device buffer (the achievable HBM read bandwidth of the box, reported next to the published
+// peak) and an engine-clock probe that runs beside the timed calls.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -32,9 +33,52 @@ __global__ __launch_bounds__(64) void hbm_read_kernel(const uint4 *src, size_t n
     sink[(size_t)blockIdx.x * 64 + threadIdx.x] = acc;
 }
 
+constexpr int kClockWaves = 8;   // consecutive workgroups are dispatched to the eight XCDs in turn
+
+// Engine clock over a window of wall time: each wavefront reads the shader cycle counter and the constant-rate
+// counter, sleeps in short steps until `ticks` of the constant-rate counter have passed (every wavefront leaves the
+// loop by then), and reads both again. One wavefront per XCD, a few VGPRs and no LDS: it shares its SIMD with the
+// timed kernels' wavefronts and issues almost nothing itself.
+__global__ __launch_bounds__(64) void clock_probe_kernel(uint64_t ticks, unsigned long long *out) {
+    const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+    const uint64_t c0 = __builtin_amdgcn_s_memtime();
+    uint64_t r1 = r0;
+    while (r1 - r0 < ticks) {
+        __builtin_amdgcn_s_sleep(32);
+        r1 = __builtin_amdgcn_s_memrealtime();
+    }
+    const uint64_t c1 = __builtin_amdgcn_s_memtime();
+    r1 = __builtin_amdgcn_s_memrealtime();
+    if (threadIdx.x == 0) {
+        out[2 * blockIdx.x] = c1 - c0;
+        out[2 * blockIdx.x + 1] = r1 - r0;
+    }
+}
+
 }  // namespace
 
 extern "C" {
+
+__attribute__((visibility("default"))) size_t kvq_probe_clock_words(void) { return 2 * kClockWaves; }
+
+// Rate of the constant-rate counter in kHz (0 if the runtime does not report it).
+__attribute__((visibility("default"))) int kvq_probe_wall_clock_khz(void) {
+    int dev = 0, khz = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0;
+    return khz;
+}
+
+// Enqueues the clock probe for `ticks` constant-rate ticks on `stream`. out: device, at least
+// kvq_probe_clock_words() uint64 words: per wavefront (shader cycles, constant-rate ticks) elapsed. Returns 0, -1
+// on bad arguments (nothing launched, ticks limited to 10^9), -8 on a launch error.
+__attribute__((visibility("default"))) int kvq_probe_clock(uint64_t ticks, unsigned long long *out, size_t out_words,
+                                                            void *stream) {
+    if (!out || out_words < (size_t)(2 * kClockWaves) || ticks == 0 || ticks > 1000000000ull) return -1;
+    hipLaunchKernelGGL(clock_probe_kernel, dim3(kClockWaves), dim3(64), 0, static_cast<hipStream_t>(stream), ticks,
+                       out);
+    return hipGetLastError() == hipSuccess ? 0 : -8;
+}
 
 __attribute__((visibility("default"))) size_t kvq_probe_sink_words(void) { return (size_t)kWaves * 64; }
 
