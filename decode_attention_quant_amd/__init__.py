@@ -17,7 +17,7 @@ import torch  # loaded first so the library binds to the HIP runtime torch alrea
 _LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
 
 OK = 0
-E_NULL, E_SHAPE, E_BITS, E_ALIGN, E_CAPACITY, E_WORKSPACE, E_EMPTY, E_LAUNCH, E_STATE = range(-1, -10, -1)
+E_NULL, E_SHAPE, E_BITS, E_ALIGN, E_CAPACITY, E_WORKSPACE, E_EMPTY, E_LAUNCH, E_STATE, E_SCRATCH = range(-1, -11, -1)
 HEAD_DIM = 128
 GROUP = 32
 TILE_TOKENS = 32
@@ -25,6 +25,7 @@ RECORD_BYTES = 3072
 RECORD_BYTES_4BIT = 5120
 RECORD_BYTES_4BIT_SPARSE = 5888
 SINK_BYTES = 512
+NOALLOC_SCRATCH_BYTES = 16 << 20
 FLAG_SINK = 1
 FLAG_PRE_ROPE = 2
 FLAG_SPARSE = 4
@@ -67,6 +68,7 @@ def _load():
         "kv_decode_attention_splits": (I32, [SP, CP]),
         "kv_decode_attention_workspace_bytes": (ctypes.c_size_t, [SP, CP]),
         "kv_decode_attention": (ctypes.c_int, [SP, CP, P, F, P, P, ctypes.c_size_t, P]),
+        "kv_decode_attention_noalloc": (ctypes.c_int, [SP, CP, P, F, P, P]),
         "kvq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "kv_ragged_prefill": (ctypes.c_int, [SP, RP, I32, P, P, I64, I64, I64, P]),
         "kv_ragged_append": (ctypes.c_int, [SP, RP, P, P, I64, I64, P]),
@@ -86,6 +88,7 @@ def _load():
 _lib = _load()
 EXPORTS = ("kv_quant_keys_per_channel", "kv_quant_values_per_token", "kv_append_and_flush",
            "kv_decode_attention_splits", "kv_decode_attention_workspace_bytes", "kv_decode_attention",
+           "kv_decode_attention_noalloc",
            "kvq_status_string", "kv_ragged_prefill", "kv_ragged_append", "kv_ragged_splits",
            "kv_ragged_workspace_bytes", "kv_ragged_sync_words", "kv_ragged_decode_attention",
            "kv_ragged_decode_step")
@@ -268,6 +271,20 @@ def kv_decode_attention(cache: KVCache, q: torch.Tensor, out: torch.Tensor | Non
         ctypes.byref(cache._cshape), ctypes.byref(cache.c), ctypes.c_void_p(q.data_ptr()), float(sm_scale),
         ctypes.c_void_p(out.data_ptr()), ctypes.c_void_p(workspace.data_ptr()),
         workspace.numel() * workspace.element_size(), _stream(stream)))
+    return out
+
+
+def kv_decode_attention_noalloc(cache: KVCache, q: torch.Tensor, out: torch.Tensor, sm_scale: float = 0.0,
+                                stream=None) -> torch.Tensor:
+    """kv_decode_attention with the split partials in the library's static per-GPU scratch (no workspace, no
+    allocation by the library; ``out`` is the caller's). Calls that overlap on one GPU race (one stream, in order)."""
+    s = cache.shape
+    _check_q(q, s)
+    _check_out(out, s)
+    _same_cuda_device(cache.tiles.device, q=q, out=out)
+    _check("kv_decode_attention_noalloc", _lib.kv_decode_attention_noalloc(
+        ctypes.byref(cache._cshape), ctypes.byref(cache.c), ctypes.c_void_p(q.data_ptr()), float(sm_scale),
+        ctypes.c_void_p(out.data_ptr()), _stream(stream)))
     return out
 
 

@@ -6,10 +6,36 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kvq.h"
 #include "kvq_kernels.h"
 
+// Scratch of the allocation-free decode entry point (kv_decode_attention_noalloc): the split partials of one call
+// in a file-scope device array of KVQ_NOALLOC_SCRATCH_BYTES, one copy per GPU, held until the process ends. In
+// host code the array's name is not a device address; each device's address comes from hipGetSymbolAddress on that
+// device's first call and is the only form host code passes on.
+__device__ __align__(256) unsigned char scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Address of the current device's scratch array (looked up once per device, with that device current).
+int scratch_address(void **ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KVQ_E_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KVQ_E_LAUNCH;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return KVQ_OK;
+}
 
 // One wavefront per resident slot: the 2-bit decode kernel holds four wavefronts per SIMD (its register budget), so
 // 256 CUs x 4 SIMDs x 4 = 4096 wavefronts run as a single round with no tail of partly filled rounds. The 4-bit
@@ -218,6 +244,7 @@ const char *kvq_status_string(int status) {
         case KVQ_E_EMPTY: return "attention over an empty cache";
         case KVQ_E_LAUNCH: return "HIP launch error";
         case KVQ_E_STATE: return "inconsistent cache state";
+        case KVQ_E_SCRATCH: return "call needs more scratch than the static array holds";
         default: return "unknown status";
     }
 }
@@ -303,18 +330,27 @@ size_t kv_decode_attention_workspace_bytes(const kvq_shape *shape, const kvq_cac
     return (size_t)shape->batch * shape->q_heads * S * (KVQ_HEAD_DIM + 2) * sizeof(float);
 }
 
-int kv_decode_attention(const kvq_shape *shape, const kvq_cache *cache, const void *q, float sm_scale, float *out,
-                        void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Host checks shared by both decode entry points; on success `p` is the split plan and `need` the partials' bytes.
+int decode_checks(const kvq_shape *shape, const kvq_cache *cache, const void *q, const float *out, SplitPlan &p,
+                  size_t &need) {
     int e = check_shape(shape);
     if (e) return e;
     if ((e = check_cache(shape, cache))) return e;
     if (!q || !out) return KVQ_E_NULL;
     if (!aligned16(q) || !aligned16(out)) return KVQ_E_ALIGN;
-    const SplitPlan p = plan(shape, cache);
+    p = plan(shape, cache);
     if (p.n_vt == 0 && cache->n_sink == 0) return KVQ_E_EMPTY;
-    const size_t need = (size_t)shape->batch * shape->q_heads * p.splits * (KVQ_HEAD_DIM + 2) * sizeof(float);
-    if (!workspace || workspace_bytes < need) return KVQ_E_WORKSPACE;
-    if (!aligned16(workspace)) return KVQ_E_ALIGN;
+    need = (size_t)shape->batch * shape->q_heads * p.splits * (KVQ_HEAD_DIM + 2) * sizeof(float);
+    return KVQ_OK;
+}
+
+// Both passes of one decode call with the split partials at `workspace` (validated by the caller).
+int decode_launch(const kvq_shape *shape, const kvq_cache *cache, const SplitPlan &p, const void *q, float sm_scale,
+                  float *out, void *workspace, void *stream) {
     if (!(sm_scale > 0.0f)) sm_scale = 1.0f / sqrtf((float)KVQ_HEAD_DIM);
     float *part_o = static_cast<float *>(workspace);
     float *part_ml = part_o + (size_t)shape->batch * shape->q_heads * p.splits * KVQ_HEAD_DIM;
@@ -374,6 +410,33 @@ int kv_decode_attention(const kvq_shape *shape, const kvq_cache *cache, const vo
     a.lens_w = nullptr;
     a.sync = nullptr;
     return launched(kvq::launch_decode(a, p.splits, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+int kv_decode_attention(const kvq_shape *shape, const kvq_cache *cache, const void *q, float sm_scale, float *out,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    SplitPlan p;
+    size_t need = 0;
+    int e = decode_checks(shape, cache, q, out, p, need);
+    if (e) return e;
+    if (!workspace || workspace_bytes < need) return KVQ_E_WORKSPACE;
+    if (!aligned16(workspace)) return KVQ_E_ALIGN;
+    return decode_launch(shape, cache, p, q, sm_scale, out, workspace, stream);
+}
+
+int kv_decode_attention_noalloc(const kvq_shape *shape, const kvq_cache *cache, const void *q, float sm_scale,
+                                float *out, void *stream) {
+    SplitPlan p;
+    size_t need = 0;
+    int e = decode_checks(shape, cache, q, out, p, need);
+    if (e) return e;
+    if (need > (size_t)KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_E_SCRATCH;   // before any runtime call
+    void *ws = nullptr;
+    if ((e = scratch_address(&ws))) return e;
+    return decode_launch(shape, cache, p, q, sm_scale, out, ws, stream);
 }
 
 int kv_ragged_prefill(const kvq_shape *shape, const kvq_ragged *cache, int32_t b, const void *k, const void *v,

@@ -22,7 +22,8 @@
  * Conventions for every call:
  *  - All pointers named as device pointers refer to memory on the current HIP device; host pointers are named so.
  *    The caller owns every buffer. The library never allocates or frees memory and holds no global state; calls are
- *    re-entrant. Work is enqueued on the caller's HIP stream (`stream` is a hipStream_t; NULL = the null stream);
+ *    re-entrant. The one exception is kv_decode_attention_noalloc, which keeps its scratch in a static array per
+ *    GPU (see there). Work is enqueued on the caller's HIP stream (`stream` is a hipStream_t; NULL = the null stream);
  *    no call synchronizes. Calls that touch one cache must be issued on one stream, in order.
  *  - Return value: 0 on success (work enqueued; device faults, if any, surface at the caller's next
  *    synchronization). A negative KVQ_E_* code means the arguments were rejected on the host and NOTHING was
@@ -64,6 +65,8 @@ extern "C" {
 #define KVQ_E_STATE (-9)     /* cache host fields inconsistent: n_quant not a multiple of 32 or outside
                                 [0, max_tokens], n_resid outside [0, R], n_sink not 0/1, n_sink = 1 without
                                 KVQ_FLAG_SINK, or (with KVQ_FLAG_SINK) n_sink = 0 while the cache holds tokens */
+#define KVQ_E_SCRATCH (-10)  /* kv_decode_attention_noalloc: the call's split partials need more than
+                                KVQ_NOALLOC_SCRATCH_BYTES */
 
 /* Fixed sizes of the layouts. */
 #define KVQ_HEAD_DIM 128
@@ -73,6 +76,7 @@ extern "C" {
 #define KVQ_RECORD_BYTES_4BIT 5120  /* one 32-token tile, 4-bit codes */
 #define KVQ_RECORD_BYTES_4BIT_SPARSE 5888  /* one 32-token tile, 4-bit codes with dense-and-sparse groups */
 #define KVQ_SINK_BYTES 512          /* the sink record of one (batch row, KV head) slice */
+#define KVQ_NOALLOC_SCRATCH_BYTES (16 << 20)  /* static scratch per GPU of kv_decode_attention_noalloc */
 
 /* kvq_shape.flags (4-bit only). */
 #define KVQ_FLAG_SINK 1      /* token 0 is held apart: fp16 key, per-token 4-bit value (synthetic.wiki "KV cache
@@ -232,6 +236,24 @@ KVQ_API size_t kv_decode_attention_workspace_bytes(const kvq_shape *shape, const
  */
 KVQ_API int kv_decode_attention(const kvq_shape *shape, const kvq_cache *cache, const void *q, float sm_scale, float *out,
                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * kv_decode_attention without a workspace argument and without any allocation, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. Same
+ * definition, arguments, kernels and results as kv_decode_attention (bit for bit), except that the split partials
+ * live in a static device array of KVQ_NOALLOC_SCRATCH_BYTES (16 MiB) that the library holds on every GPU it runs
+ * on until the process ends. The call allocates and frees nothing; on the first call on a device it looks up that
+ * device's copy of the array (hipGetSymbolAddress, with that device current) and keeps the address.
+ *   Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on different streams, or from
+ *   several host threads without ordering) race and give undefined outputs. Issue them on one stream, in order.
+ *   Nothing in the array needs to start at zero: every partial a call reads was written earlier in the same call.
+ *   Limit: batch * q_heads * splits * 520 bytes <= KVQ_NOALLOC_SCRATCH_BYTES, with splits as returned by
+ *   kv_decode_attention_splits (e.g. 64 sequences x 32 query heads x 8 splits = 8.5 MB at 32K tokens).
+ * Errors: as kv_decode_attention (without KVQ_E_WORKSPACE); KVQ_E_SCRATCH when the limit is exceeded (checked on
+ *   the host before any runtime call); KVQ_E_LAUNCH also when the array's address cannot be obtained.
+ */
+KVQ_API int kv_decode_attention_noalloc(const kvq_shape *shape, const kvq_cache *cache, const void *q, float sm_scale,
+                                        float *out, void *stream);
 
 /*
  * Ragged caches: every sequence (batch row) at its own length, the lengths held in device memory, so a whole

@@ -60,7 +60,7 @@ def _cache(kvq, n_quant=0, n_resid=0, tiles=FAKE, k_res=FAKE + 4096, v_res=FAKE 
 
 
 def test_status_strings(kvq):
-    for code in range(0, -10, -1):
+    for code in range(0, -11, -1):
         assert kvq.status_string(code) and kvq.status_string(code) != "unknown status"
     assert kvq.status_string(-77) == "unknown status"
 
@@ -267,3 +267,22 @@ def test_read_probe_rejects_bad_arguments_before_launching():
     assert lib.kvq_probe_hbm_read(FAKE, 1000, FAKE, n, None) == -1          # not a multiple of 16
     assert lib.kvq_probe_hbm_read(FAKE + 8, 1 << 20, FAKE, n, None) == -1   # misaligned
     assert lib.kvq_probe_hbm_read(FAKE, 1 << 20, FAKE, n - 1, None) == -1   # sink too small
+
+
+def test_noalloc_decode_rejects_partials_beyond_its_scratch(kvq):
+    """kv_decode_attention_noalloc checks on the host, before any runtime call, that the split partials fit its
+    static scratch: 2048 sequences x 32 query heads (one split each) need 34 MB, more than 16 MiB."""
+    lib = kvq.library()
+    shape = _shape(kvq, batch=2048, kv_heads=8, q_heads=32, max_tokens=1 << 20)
+    cache = _cache(kvq, n_quant=1 << 20, n_resid=5)
+    need = lib.kv_decode_attention_workspace_bytes(ctypes.byref(shape), ctypes.byref(cache))
+    assert need > kvq.NOALLOC_SCRATCH_BYTES
+    rc = lib.kv_decode_attention_noalloc(ctypes.byref(shape), ctypes.byref(cache), ctypes.c_void_p(FAKE), 0.0,
+                                         ctypes.c_void_p(FAKE + 16), None)
+    assert rc == kvq.E_SCRATCH
+    # the usual argument checks come first
+    assert lib.kv_decode_attention_noalloc(ctypes.byref(shape), ctypes.byref(cache), None, 0.0,
+                                           ctypes.c_void_p(FAKE + 16), None) == kvq.E_NULL
+    empty = _cache(kvq)
+    assert lib.kv_decode_attention_noalloc(ctypes.byref(shape), ctypes.byref(empty), ctypes.c_void_p(FAKE), 0.0,
+                                           ctypes.c_void_p(FAKE + 16), None) == kvq.E_EMPTY
