@@ -203,6 +203,11 @@ class ClockProbe:
         self.stream = torch.cuda.Stream()
         self.khz = int(self.lib.kvq_probe_wall_clock_khz())
         self.started = False
+        # the first launch loads the probe's code object (milliseconds of host time): done here, outside any timed
+        # region
+        if self.khz > 0:
+            self.lib.kvq_probe_clock(1, self.out.data_ptr(), self.words, self.stream.cuda_stream)
+            torch.cuda.synchronize()
 
     def start(self, seconds):
         if self.khz <= 0 or seconds <= 0:
@@ -624,7 +629,8 @@ def step_record(kvq, kdev, kvsynth, torch, w, W, K, rot):
     kernel) over `rot` cache copies in turn, so the steps read HBM: every step timed with HIP events when issued
     eagerly (percentiles, flush steps apart), and the same steps captured in one HIP graph and replayed once."""
     R = w.residual
-    P = w.prefill
+    # the prefill leaves the window 20 + W tokens short of full, so every copy flushes once inside its timed steps
+    P = w.prefill + R - 20 - W - (w.prefill - 1) % R - 1
     total = P + W + K
     cap = ((total + 31) // 32) * 32
     Kd = kdev.kv_to_device(w, kvsynth.K_ID, 0, total)
