@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "kvq.h"
@@ -460,8 +461,10 @@ int kv_ragged_prefill(const kvq_shape *shape, const kvq_ragged *cache, int32_t b
     _Float16 *vres = static_cast<_Float16 *>(cache->v_res) + (int64_t)b * H * R * KVQ_HEAD_DIM;
     if (n_tokens > 0) {
         const kvq::TokSrc ks = single_src(k, 0, stride_h, stride_t), vs = single_src(v, 0, stride_h, stride_t);
-        if (flushed > 0) {
-            const int64_t nt = flushed / KVQ_TILE_TOKENS;
+        // the flushed tiles, then (written ahead, within the capacity) the complete 32-row blocks of the window:
+        // tile i holds tokens 32 i .. 32 i + 31 either way
+        const int64_t nt = std::min(n_tokens / KVQ_TILE_TOKENS, max_tiles);
+        if (nt > 0) {
             if ((e = launched(kvq::launch_quant_keys(ks, 0, nt, 1, H, tiles, max_tiles, 0, s)))) return e;
             if ((e = launched(kvq::launch_quant_values(vs, 0, nt, 1, H, tiles, max_tiles, 0, s)))) return e;
         }

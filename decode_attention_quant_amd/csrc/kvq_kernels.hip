@@ -181,15 +181,47 @@ __device__ __forceinline__ void ragged_after_append(const int32_t *ln, int res_c
     }
 }
 
+// Window blocks of a ragged cache are quantized ahead: whenever a window holds a complete 32-row block k, tile
+// n_quant / 32 + k (when it is within the capacity) already holds that block's record, written by the call that
+// completed the block (prefill, append or decode step). A flush then only moves the lengths in the single-launch
+// decode step; the records are the same bytes a quantization at flush time writes.
+__device__ __forceinline__ TokSrc window_then_new(const _Float16 *res, int kv_heads, int res_cap, int row,
+                                                   const _Float16 *nw, int64_t new_sb, int64_t new_sh) {
+    TokSrc s;   // rows below `row` from the window, row `row` from the new token
+    s.a = res; s.a_sb = (int64_t)kv_heads * res_cap * D; s.a_sh = (int64_t)res_cap * D; s.a_st = D; s.n_a = row;
+    s.b = nw; s.b_sb = new_sb; s.b_sh = new_sh; s.b_st = 0;
+    return s;
+}
+
+// Quantizes the window block that ends with the token appended at window row `row` (row % 32 == 31) into tile
+// `slot` of slice (b, h). LDS: 4 KB.
+__device__ __forceinline__ void quant_window_block(const _Float16 *k_res, const _Float16 *v_res, const _Float16 *k_new,
+                                                   const _Float16 *v_new, int64_t new_sb, int64_t new_sh,
+                                                   int kv_heads, int res_cap, int row, int b, int h, uint8_t *tiles,
+                                                   int64_t max_tiles, int64_t slot, unsigned char *lds) {
+    const TokSrc wk = window_then_new(k_res, kv_heads, res_cap, row, k_new, new_sb, new_sh);
+    const TokSrc wv = window_then_new(v_res, kv_heads, res_cap, row, v_new, new_sb, new_sh);
+    uint32_t *words = reinterpret_cast<uint32_t *>(lds);
+    _Float16 *sv = reinterpret_cast<_Float16 *>(lds + 1024), *zv = sv + 128;
+    float *gp = reinterpret_cast<float *>(lds + 2048);
+    uint8_t *rec = tiles + (((int64_t)b * kv_heads + h) * max_tiles + slot) * REC;
+    quant_keys_tile(wk, row - 31, b, h, rec, words);
+    __syncthreads();
+    quant_values_tile(wv, row - 31, b, h, rec, words, sv, zv, gp);
+    __syncthreads();
+}
+
 // One decode-step append for every sequence: workgroup (i, h, b) quantizes window tile i of slice (b, h) into tile
 // n_quant / 32 + i when the window is full (lazy flush), and workgroup (0, h, b) then copies the new token into
 // window row n_resid (row 0 after a flush, once its own tile's reads are done; the other tiles never read row 0).
+// When the token completes a window block, the last workgroup writes that block's record ahead.
 __global__ __launch_bounds__(64) void ragged_flush_append_kernel(TokSrc knew, TokSrc vnew, int kv_heads,
                                                                  uint8_t *tiles, int64_t max_tiles, _Float16 *k_res,
                                                                  _Float16 *v_res, int res_cap, int32_t *lens) {
-    __shared__ uint32_t words[256];
-    __shared__ _Float16 sv[128], zv[128];
-    __shared__ __align__(16) float gp[512];
+    __shared__ __align__(16) unsigned char lds[4096];   // words 1 KB, sv and zv 256 B each, gp 2 KB (from 2048)
+    uint32_t *words = reinterpret_cast<uint32_t *>(lds);
+    _Float16 *sv = reinterpret_cast<_Float16 *>(lds + 1024), *zv = sv + 128;
+    float *gp = reinterpret_cast<float *>(lds + 2048);
     const int l = threadIdx.x;
     const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     int32_t *ln = lens + 4 * b;
@@ -212,11 +244,18 @@ __global__ __launch_bounds__(64) void ragged_flush_append_kernel(TokSrc knew, To
         quant_values_tile(wv, 32 * i, b, h, rec, words, sv, zv, gp);
         __syncthreads();
     }
+    const int row = flush ? 0 : nr;
     if (i == 0) {
-        const int row = flush ? 0 : nr;
         const int64_t dst = ((int64_t)(b * kv_heads + h) * res_cap + row) * D;
         reinterpret_cast<uint32_t *>(k_res + dst)[l] = reinterpret_cast<const uint32_t *>(tok_row(knew, b, h, 0))[l];
         reinterpret_cast<uint32_t *>(v_res + dst)[l] = reinterpret_cast<const uint32_t *>(tok_row(vnew, b, h, 0))[l];
+    }
+    // (a flush leaves row 0, so a completed block is never one of a flush; rows below `row` are not written here)
+    if (i == (int)gridDim.x - 1 && (row & 31) == 31) {
+        const int64_t slot = nq / 32 + row / 32;
+        if (slot < max_tiles)
+            quant_window_block(k_res, v_res, knew.a, vnew.a, knew.a_sb, knew.a_sh, kv_heads, res_cap, row, b, h, tiles,
+                               max_tiles, slot, lds);
     }
 }
 
@@ -376,27 +415,36 @@ __device__ __forceinline__ void merge_splits(const float *part_o, const float *p
 // each), contracted in turn against the value codes of the 8 channel blocks of 16; for channel block j only row
 // group g = j / 2 is kept. The value zero-point term sum_t p z_V[g][t] is accumulated on the VALU.
 //
-// Per-wavefront LDS: the tile's scales/zeros (1 KB), the folded query (2 KB) and beta, all written for tile v + 1
-// at the end of iteration v after every read of tile v has been issued (a wavefront's LDS operations complete in
-// order); the probability exchange (512 B); the fp16 window value tile (8 KB, reusing the first region).
-constexpr int LDS_SZ = 0;            // 256 x uint32: s_K[128], z_K[128], s_V[4][32], z_V[4][32] (fp16)
-constexpr int LDS_QT = 1024;         // fp16 [2 (high, low)][4 heads][128 channels]
-constexpr int LDS_BETA = 3072;       // fp32 [4 heads]
-constexpr int LDS_ZERO = 3088;       // 256 zero bytes: A-operand rows 4 h + 2, 4 h + 3 of the score contraction
-constexpr int LDS_P = 8192;          // fp32 [4 heads][16][2]: p of tokens i and 16 + i
-constexpr int LDS_BYTES = 8704;      // [0, 8192) also holds the fp16 window value tile [32][128]
+// Per-wavefront LDS: the tile's scales/zeros, the folded query and beta, all written for tile v + 1 at the end of
+// iteration v after every read of tile v has been issued (a wavefront's LDS operations complete in order); the
+// probability exchange; the fp16 window value tile (8 KB, reusing the first region). Rows that lanes read together
+// are padded so that they fall in different LDS banks (64 banks of 4 bytes): unpadded, the eight 256-byte rows of
+// the folded query all start in bank 0 and every A-operand read of the score contraction is an 8-way conflict.
+constexpr int LDS_SZ = 0;            // s_K[128], z_K[128] (fp16), then s_V[4][32], z_V[4][32] with each group's 64 bytes
+                                     // followed by 16 bytes of padding (1152 bytes)
+constexpr int QT_ROW = 136;          // fp16 per (part, head) row of the folded query: 128 channels + 8 padding
+constexpr int LDS_QT = 1152;         // fp16 [2 (high, low)][4 heads][QT_ROW]
+constexpr int LDS_BETA = LDS_QT + 8 * QT_ROW * 2;   // fp32 [4 heads]
+constexpr int P_ROW = 18;            // float2 per head of the probability exchange: 16 + 2 padding
+constexpr int LDS_P = 8192;          // float2 [4 heads][P_ROW]: p of tokens i and 16 + i
+constexpr int LDS_BYTES = LDS_P + 4 * P_ROW * 8;    // [0, 8192) also holds the fp16 window value tile [32][128]
+// byte offset of metadata byte x (0..1023 of a record's scale/zero section) in the staged copy
+__device__ __forceinline__ int sz_off(int x) { return x < 512 ? x : x + 16 * ((x - 512) >> 6); }
 
 // MODE: 0 uniform lengths; 1 per-sequence lengths (ragged); 2 the single-launch ragged decode step (below).
 //
 // Decode step (MODE 2). Every workgroup derives the step of its sequence from the lengths before it (append the
 // token; a full window is flushed first; a sequence whose flush would pass the capacity refuses the token and is
-// marked full) and attends over the state after it. A workgroup whose split holds tiles of the flushed window
-// quantizes those tiles itself (the same quantizer functions as the flush kernel; workgroups of the other query-head
-// chunks of that KV head write identical bytes) and reads them back. The new token is attended straight from the
-// input (its window row is written only at the end). After its partials are stored, a workgroup counts itself in
-// sync[(b, KV head, chunk)]; the last of the splits merges them (the pass-2 code) and counts the chunk in sync[b];
-// the last chunk of the sequence writes the new window rows and the lengths, by when every workgroup of the sequence
-// has read them. Counters are reset by the workgroup that completes them. No workgroup waits for another.
+// marked full) and attends over the state after it. The tiles of a flushed window were quantized ahead (see the
+// ragged append), so a flush only moves the lengths. Grid row y = 0 holds one block workgroup per (sequence, KV
+// head, chunk): when the appended token completes a window block, the chunk-0 workgroup writes that block's record
+// ahead (from the window rows below the token and the token itself, from the input); it is dispatched first and runs
+// beside the attention. Rows y >= 1 are the splits. The new token is attended straight from the input (its window row
+// is written only at the end). After its partials are stored, a split counts itself in sync[(b, KV head, chunk)]; the
+// last of the splits merges them (the pass-2 code) and counts the chunk in sync[b], as does every block workgroup
+// once its loads are complete; the last of the sequence's 2 * KV heads * chunks counts writes the new window rows
+// (several chunks per KV head) and the lengths, by when every workgroup of the sequence has read them. Counters are
+// reset by the workgroup that completes them. No workgroup waits for another.
 // Ordering: the tickets are relaxed agent-scope atomics, so they carry no happens-before edge of the HIP memory
 // model. The merge is correct because of three hardware facts this kernel relies on instead: every value another
 // workgroup reads (the split partials) is written with agent-scope atomic stores, which write through to the
@@ -405,7 +453,12 @@ constexpr int LDS_BYTES = 8704;      // [0, 8192) also holds the fp16 window val
 // loads returned) before taking its ticket; the ticket is itself performed at the coherence point. A plain store
 // that another workgroup of the launch read would need a release/acquire pair instead (at agent scope an L2
 // write-back and invalidate per workgroup, which costs the step several times its length).
-template <int MODE>
+//
+// G1 (one query head per KV head): the four head rows of the score operand all hold that head, so every row of the
+// softmax state agrees, and PV puts the high and low parts of p~ in different A-operand rows (row 4 part + group)
+// instead of two contractions: 8 MFMAs per tile instead of 16. The parts are added across lanes (n, 0) and (n, 1) once,
+// before the partials are stored.
+template <int MODE, bool G1>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void decode_pass1_kernel(DecodeArgs a) {
     __shared__ __align__(16) unsigned char smem[LDS_BYTES];
     uint32_t *sz_lds = reinterpret_cast<uint32_t *>(smem + LDS_SZ);
@@ -421,7 +474,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     const int l = threadIdx.x;
     const int n = l & 15, kc = l >> 4, hl = n >> 2, g = n & 3;
     const int unit = blockIdx.x;
-    const int split = gridDim.y - 1 - blockIdx.y;   // the split holding the fp16 window tiles is dispatched first
+    // splits (MODE 2: grid rows 1 .. gridDim.y - 1; row 0 holds the block workgroups); the split holding the fp16
+    // window tiles is dispatched first
+    const int nsplit = MODE == 2 ? (int)gridDim.y - 1 : (int)gridDim.y;
+    const int split = (int)gridDim.y - 1 - (int)blockIdx.y;
     const int chunk = uni(unit % a.chunks);
     const int hkv = uni((unit / a.chunks) % a.kv_heads);
     const int b = uni(unit / (a.chunks * a.kv_heads));
@@ -430,7 +486,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     const int h0 = hkv * G + 4 * chunk;
 
     int n_qtiles = a.n_qtiles, n_resid = a.n_resid, tiles_per_split = a.tiles_per_split;
-    int flush_t0 = -1;   // MODE 2: first tile of the window this step flushes (or -1)
     int new_row = -1;    // MODE 2: window row of the token this step appends (or -1)
     bool refuse = false; // MODE 2: the flush does not fit: the token is refused and the sequence marked full
     if constexpr (MODE != 0) {   // this sequence's lengths; the splits share its tiles evenly
@@ -441,7 +496,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
         } else if (ln[3] == 0) {
             if (nr == a.res_cap) {
                 if ((int64_t)nq + a.res_cap <= a.max_tiles * 32) {
-                    flush_t0 = nq / 32;
                     nq += nr;
                     nr = 1;
                     new_row = 0;
@@ -455,9 +509,58 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
         }
         n_qtiles = uni(nq / 32);
         n_resid = uni(nr);
-        tiles_per_split = uni((n_qtiles + (n_resid + 31) / 32 + (int)gridDim.y - 1) / (int)gridDim.y);
-        flush_t0 = uni(flush_t0);
+        tiles_per_split = uni((n_qtiles + (n_resid + 31) / 32 + nsplit - 1) / nsplit);
         new_row = uni(new_row);
+    }
+
+    // MODE 2: the appended token's window rows of KV head h
+    auto write_rows = [&](int h) {
+        const int64_t dst = (((int64_t)b * a.kv_heads + h) * a.res_cap + new_row) * D;
+        const int64_t src = b * a.new_sb + h * a.new_sh;
+        const uint32_t kw = reinterpret_cast<const uint32_t *>(a.k_new + src)[l];
+        const uint32_t vw = reinterpret_cast<const uint32_t *>(a.v_new + src)[l];
+        reinterpret_cast<uint32_t *>(a.k_res_w + dst)[l] = kw;
+        reinterpret_cast<uint32_t *>(a.v_res_w + dst)[l] = vw;
+    };
+    // MODE 2: counts this workgroup in sync[b]; the sequence's last count writes the window rows (when a KV head has
+    // several chunks) and the lengths. Every counted workgroup has finished reading the lengths and the window rows:
+    // its loads were complete before its tickets. Nothing in this launch reads the rows or lengths written here.
+    auto sequence_ticket = [&]() {
+        uint32_t *cb = a.sync + b;
+        uint32_t prev = 0u;
+        if (l == 0) prev = __hip_atomic_fetch_add(cb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        prev = __shfl(prev, 0);
+        if (prev + 1u != (uint32_t)(2 * a.kv_heads * a.chunks)) return;
+        if (l == 0) *cb = 0u;
+        if (new_row >= 0) {
+            if (a.chunks > 1) {
+                int h = 0;
+                for (; h + 4 <= a.kv_heads; h += 4) {
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) write_rows(h + k);
+                }
+                for (; h < a.kv_heads; ++h) write_rows(h);
+            }
+            if (l == 0) {
+                a.lens_w[4 * b] = n_qtiles * 32;
+                a.lens_w[4 * b + 1] = n_resid;
+            }
+        } else if (refuse && l == 0) {
+            a.lens_w[4 * b + 3] = 1;
+        }
+    };
+    if constexpr (MODE == 2) {
+        if (blockIdx.y == 0) {   // block workgroup (no flush here: a flush leaves the token in row 0)
+            if (chunk == 0 && new_row >= 0 && (new_row & 31) == 31) {
+                const int64_t slot = n_qtiles + new_row / 32;
+                if (slot < a.max_tiles)
+                    quant_window_block(a.k_res, a.v_res, a.k_new, a.v_new, a.new_sb, a.new_sh, a.kv_heads, a.res_cap,
+                                       new_row, b, hkv, a.tiles_w, a.max_tiles, slot, smem);
+            }
+            wait_vmcnt<0>();
+            sequence_ticket();
+            return;
+        }
     }
     const int n_vt = n_qtiles + (n_resid + 31) / 32;
     const int v0 = uni(split * tiles_per_split);
@@ -465,37 +568,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     const int qend = uni(min(v1, n_qtiles));
     const uint8_t *base = a.tiles + ((int64_t)b * a.kv_heads + hkv) * a.max_tiles * (int64_t)REC;
 
-    if constexpr (MODE == 2) {   // flushed tiles in this split: quantize them from the window (LDS from offset 0)
-        const int f0 = max(v0, flush_t0), f1 = min(qend, flush_t0 + a.res_cap / 32);
-        if (flush_t0 >= 0 && f0 < f1) {
-            TokSrc wk;
-            wk.a = a.k_res; wk.a_sb = (int64_t)a.kv_heads * a.res_cap * D; wk.a_sh = (int64_t)a.res_cap * D;
-            wk.a_st = D; wk.n_a = INT64_MAX;
-            wk.b = wk.a; wk.b_sb = wk.a_sb; wk.b_sh = wk.a_sh; wk.b_st = wk.a_st;
-            TokSrc wv = wk;
-            wv.a = a.v_res; wv.b = a.v_res;
-            uint32_t *words = reinterpret_cast<uint32_t *>(smem);
-            _Float16 *sv = reinterpret_cast<_Float16 *>(smem + 1024), *zv = sv + 128;
-            float *gp = reinterpret_cast<float *>(smem + 1536);
-            for (int t = f0; t < f1; ++t) {
-                uint8_t *rec = a.tiles_w + (((int64_t)b * a.kv_heads + hkv) * a.max_tiles + t) * REC;
-                quant_keys_tile(wk, 32 * (t - flush_t0), b, hkv, rec, words);
-                __syncthreads();
-                quant_values_tile(wv, 32 * (t - flush_t0), b, hkv, rec, words, sv, zv, gp);
-                __syncthreads();
-            }
-            __threadfence_block();   // the records are read back below by this workgroup
-        }
-    }
-
     // ---- query: lane (n, kc) holds head kc of the chunk (if valid), channels 8n .. 8n+7, scaled by 2^-E with
     // 2^E > max |q| of that head (qmax is a float16 value widened, hence a normal binary32 number: its exponent
     // field gives E). C turns a raw score of head kc (in q' units) into the log2 domain.
     h8 qf = {};
     float C;
     {
-        const bool hv = kc < gc;
-        const h8 raw = *reinterpret_cast<const h8 *>(a.q + ((int64_t)b * a.q_heads + h0 + (hv ? kc : 0)) * D + 8 * n);
+        const bool hv = G1 || kc < gc;
+        const h8 raw = *reinterpret_cast<const h8 *>(a.q + ((int64_t)b * a.q_heads + h0 + (G1 || !hv ? 0 : kc)) * D + 8 * n);
         float qmax = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) qmax = fmaxf(qmax, fabsf((float)raw[e]));
@@ -511,7 +591,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     // softmax state of head kc (lanes of row kc agree): running maximum mr of the raw scores, valid once `seen`
     float mr = 0.0f, lsum = 0.0f;
     bool seen = false;
-    // PV state: o[j] rows (head kc, group r), column n = channel n + 16 j; gam: lane (n, kc) for (head hl, group g)
+    // PV state: o[j] rows (head kc, group r) (G1: part kc, group r), column n = channel n + 16 j; gam: lane (n, kc)
+    // for (head hl, group g)
     float gam = 0.0f;
     f4 o[8];
 #pragma unroll
@@ -538,24 +619,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     // p of tokens n and 16 + n to LDS; returns, for the PV A layout of lane (n, kc), p of tokens 4kc + i (p[i]) and
     // 16 + 4kc + i (p[4 + i]) of head hl
     auto exchange = [&](float p0, float p1, float p[8]) {
-        reinterpret_cast<float2 *>(p_lds)[16 * kc + n] = float2{p0, p1};
+        reinterpret_cast<float2 *>(p_lds)[P_ROW * kc + n] = float2{p0, p1};
         wave_lds_order();
-        const f4 pa = reinterpret_cast<const f4 *>(p_lds)[(16 * hl + 4 * kc) / 2];
-        const f4 pb = reinterpret_cast<const f4 *>(p_lds)[(16 * hl + 4 * kc) / 2 + 1];
+        const f4 pa = reinterpret_cast<const f4 *>(p_lds)[(P_ROW * hl + 4 * kc) / 2];
+        const f4 pb = reinterpret_cast<const f4 *>(p_lds)[(P_ROW * hl + 4 * kc) / 2 + 1];
         p[0] = pa[0]; p[4] = pa[1]; p[1] = pa[2]; p[5] = pa[3];
         p[2] = pb[0]; p[6] = pb[1]; p[3] = pb[2]; p[7] = pb[3];
     };
 
     // stage a tile's scales/zeros, its folded query (high, low) and beta into LDS
     auto stage = [&](const uint4 &sw) {
-        reinterpret_cast<uint4 *>(sz_lds)[l] = sw;
+        *reinterpret_cast<uint4 *>(smem + LDS_SZ + sz_off(16 * l)) = sw;
         wave_lds_order();
         const h8 sk = *reinterpret_cast<const h8 *>(szh + 8 * n);
         const h8 zk = *reinterpret_cast<const h8 *>(szh + 128 + 8 * n);
         const h8 hi = qf * sk;
         const h8 lo = __builtin_elementwise_fma(qf, sk, -hi);
-        *reinterpret_cast<h8 *>(qt_lds + 128 * kc + 8 * n) = hi;
-        *reinterpret_cast<h8 *>(qt_lds + 512 + 128 * kc + 8 * n) = lo;
+        *reinterpret_cast<h8 *>(qt_lds + QT_ROW * kc + 8 * n) = hi;
+        *reinterpret_cast<h8 *>(qt_lds + QT_ROW * (4 + kc) + 8 * n) = lo;
         float bp = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; e += 2)
@@ -569,10 +650,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     // Each code word is reloaded for the next tile right after its last use in this one (scales: at the top of the
     // iteration, key codes after the score contraction, value codes after PV), so no register holds two tiles. On
     // the last tile the index is clamped: the reload hits the just-read record in cache.
-    // A operand row n = 4 h + r: head h, high part (r = 0), low part (r = 1), zeros (r = 2, 3: unused outputs)
-    const _Float16 *qta = (n & 2) ? reinterpret_cast<const _Float16 *>(smem + LDS_ZERO) + 8 * kc
-                                  : qt_lds + 512 * (n & 1) + 128 * hl + 8 * kc;
-    reinterpret_cast<uint32_t *>(smem + LDS_ZERO)[l] = 0u;
+    // A operand row n = 4 h + r: head h, high part (r = 0), low part (r = 1); rows r = 2, 3 read rows 0, 1 again
+    // (their outputs are never used), so all 16 lanes of a row group read distinct or identical addresses
+    const _Float16 *qta = qt_lds + QT_ROW * (4 * (n & 1) + hl) + 8 * kc;
     uint4 kw, vw, sw;
     if (v0 < qend) {
         const uint8_t *rec = base + (int64_t)v0 * REC;
@@ -602,10 +682,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
         exchange(p0, p1, p);
 
         // p~ = p * s_V of group g, fp16 high part and the fp16 rounding of the remainder; value zero points
-        const h4 sv0 = *reinterpret_cast<const h4 *>(szh + 256 + 32 * g + 4 * kc);
-        const h4 sv1 = *reinterpret_cast<const h4 *>(szh + 256 + 32 * g + 16 + 4 * kc);
-        const h4 zv0 = *reinterpret_cast<const h4 *>(szh + 384 + 32 * g + 4 * kc);
-        const h4 zv1 = *reinterpret_cast<const h4 *>(szh + 384 + 32 * g + 16 + 4 * kc);
+        const unsigned char *szb = smem + LDS_SZ;
+        const h4 sv0 = *reinterpret_cast<const h4 *>(szb + sz_off(512 + 64 * g + 8 * kc));
+        const h4 sv1 = *reinterpret_cast<const h4 *>(szb + sz_off(512 + 64 * g + 32 + 8 * kc));
+        const h4 zv0 = *reinterpret_cast<const h4 *>(szb + sz_off(768 + 64 * g + 8 * kc));
+        const h4 zv1 = *reinterpret_cast<const h4 *>(szb + sz_off(768 + 64 * g + 32 + 8 * kc));
         const uint2 sa = __builtin_bit_cast(uint2, sv0), sb = __builtin_bit_cast(uint2, sv1);
         uint4 uh, ul;
         split_pair(p[0], p[1], sa.x, uh.x, ul.x);
@@ -618,11 +699,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
             gam = __builtin_fmaf(p[i], (float)zv0[i], gam);
             gam = __builtin_fmaf(p[4 + i], (float)zv1[i], gam);
         }
+        if constexpr (G1) {
+            const h8 pp = (hl & 1) ? plo : phi;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const h8 bv = expand8(nibbles(vw[j >> 1], j & 1));
-            o[j] = mfma(phi, bv, o[j]);
-            o[j] = mfma(plo, bv, o[j]);
+            for (int j = 0; j < 8; ++j) o[j] = mfma(pp, expand8(nibbles(vw[j >> 1], j & 1)), o[j]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const h8 bv = expand8(nibbles(vw[j >> 1], j & 1));
+                o[j] = mfma(phi, bv, o[j]);
+                o[j] = mfma(plo, bv, o[j]);
+            }
         }
         vw = reinterpret_cast<const uint4 *>(next + 1024)[l];
         // every LDS read of this tile has been issued: overwrite with the next tile (after the last tile, with
@@ -631,7 +718,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     }
 
     // ------------------------------------------------------------------ residual (fp16) tiles
-    // The same contraction with A = q' (high part; low part and rows 2, 3 zero) and B = the fp16 key rows, loaded
+    // The same contraction with A = q' (high part; the low part zero) and B = the fp16 key rows, loaded
     // straight into registers at the top of each iteration. The value rows of a tile are copied into LDS by LDS-DMA
     // loads (issued for the next tile once PV has read the current one) and reach the PV B layout through transpose
     // reads; p~ = p (no scales). Window tiles (at most four per split in the normal case) and all-fp16 caches (the
@@ -640,8 +727,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     if (w0 < v1) {
         h8 qw[4];
         __syncthreads();
-        *reinterpret_cast<h8 *>(qt_lds + 128 * kc + 8 * n) = qf;
-        *reinterpret_cast<h8 *>(qt_lds + 512 + 128 * kc + 8 * n) = h8{};
+        *reinterpret_cast<h8 *>(qt_lds + QT_ROW * kc + 8 * n) = qf;
+        *reinterpret_cast<h8 *>(qt_lds + QT_ROW * (4 + kc) + 8 * n) = h8{};
         __syncthreads();
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) qw[ks] = *reinterpret_cast<const h8 *>(qta + 32 * ks);
@@ -729,8 +816,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
                 const h4 lo4 = read_tr16(vt0 + 16 * j);
                 const h4 hi4 = read_tr16(vt1 + 16 * j);
                 const h8 bv = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
-                o[j] = mfma(phi, bv, o[j]);
-                o[j] = mfma(plo, bv, o[j]);
+                if constexpr (G1) {
+                    o[j] = mfma((hl & 1) ? plo : phi, bv, o[j]);
+                } else {
+                    o[j] = mfma(phi, bv, o[j]);
+                    o[j] = mfma(plo, bv, o[j]);
+                }
             }
             wait_lgkmcnt0();    // PV has read the value rows: the next tile may overwrite them
             if (v + 1 < v1) v_dma(v + 1);
@@ -744,7 +835,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     float gr[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) gr[r] = __shfl(gam, 4 * kc + r);
-    const int64_t S = gridDim.y;
+    if constexpr (G1) {   // lane (n, 0) adds the low parts held by lane (n, 1)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j][j >> 1] += __shfl(o[j][j >> 1], (l & 15) + 16);
+    }
+    const int64_t S = nsplit;
     if (kc < gc) {   // lane (n, kc) holds head h0 + kc, channels n + 16 j
         const int hq = h0 + kc;
         float *po = a.part_o + (((int64_t)b * a.q_heads + hq) * S + split) * D;
@@ -783,42 +878,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
             merge_splits<true>(a.part_o, a.part_ml, a.out, (int)S, (int64_t)b * a.q_heads + h0 + k, wts, true);
             __syncthreads();
         }
-        // the appended token's window rows of KV head h: with one chunk per KV head, every reader of that window
-        // is counted by now, so this workgroup writes them; otherwise the sequence's last workgroup writes all
-        auto write_rows = [&](int h) {
-            const int64_t dst = (((int64_t)b * a.kv_heads + h) * a.res_cap + new_row) * D;
-            const int64_t src = b * a.new_sb + h * a.new_sh;
-            const uint32_t kw = reinterpret_cast<const uint32_t *>(a.k_new + src)[l];
-            const uint32_t vw = reinterpret_cast<const uint32_t *>(a.v_new + src)[l];
-            reinterpret_cast<uint32_t *>(a.k_res_w + dst)[l] = kw;
-            reinterpret_cast<uint32_t *>(a.v_res_w + dst)[l] = vw;
-        };
+        // with one chunk per KV head, every reader of the window of KV head hkv is counted by now (its splits here,
+        // its block workgroup reads no window row at or past the token's), so this workgroup writes the token's rows;
+        // otherwise the sequence's last count writes all. Nothing in this launch reads the outputs or window rows
+        // stored here, so their stores need not be complete before the sequence ticket; the end of the launch makes
+        // them visible.
         if (a.chunks == 1 && new_row >= 0) write_rows(hkv);
-        // count the chunk; the last chunk of the sequence writes the lengths (every workgroup of the sequence has
-        // finished reading them: its loads were complete before its split ticket). Nothing in this launch reads the
-        // outputs or window rows stored above, so their stores need not be complete before this ticket; the end of
-        // the launch makes them visible.
-        uint32_t *cb = a.sync + b;
-        if (l == 0) prev = __hip_atomic_fetch_add(cb, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        prev = __shfl(prev, 0);
-        if (prev + 1u != (uint32_t)(a.kv_heads * a.chunks)) return;
-        if (l == 0) *cb = 0u;
-        if (new_row >= 0) {
-            if (a.chunks > 1) {
-                int h = 0;
-                for (; h + 4 <= a.kv_heads; h += 4) {
-#pragma unroll
-                    for (int k = 0; k < 4; ++k) write_rows(h + k);
-                }
-                for (; h < a.kv_heads; ++h) write_rows(h);
-            }
-            if (l == 0) {
-                a.lens_w[4 * b] = n_qtiles * 32;
-                a.lens_w[4 * b + 1] = n_resid;
-            }
-        } else if (refuse && l == 0) {
-            a.lens_w[4 * b + 3] = 1;
-        }
+        sequence_ticket();
     }
 }
 
@@ -878,7 +944,10 @@ hipError_t launch_pass2(const float *part_o, const float *part_ml, float *out, i
 
 hipError_t launch_decode(const DecodeArgs &a, int splits, hipStream_t st) {
     const int units = a.batch * a.kv_heads * a.chunks;
-    hipLaunchKernelGGL(decode_pass1_kernel<0>, dim3((unsigned)units, (unsigned)splits), dim3(64), 0, st, a);
+    if (a.q_heads == a.kv_heads)
+        hipLaunchKernelGGL((decode_pass1_kernel<0, true>), dim3((unsigned)units, (unsigned)splits), dim3(64), 0, st, a);
+    else
+        hipLaunchKernelGGL((decode_pass1_kernel<0, false>), dim3((unsigned)units, (unsigned)splits), dim3(64), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_pass2(a.part_o, a.part_ml, a.out, a.batch * a.q_heads, splits, st);
@@ -886,7 +955,10 @@ hipError_t launch_decode(const DecodeArgs &a, int splits, hipStream_t st) {
 
 hipError_t launch_decode_ragged(const DecodeArgs &a, int splits, int32_t *lens, int commit, hipStream_t st) {
     const int units = a.batch * a.kv_heads * a.chunks;
-    hipLaunchKernelGGL(decode_pass1_kernel<1>, dim3((unsigned)units, (unsigned)splits), dim3(64), 0, st, a);
+    if (a.q_heads == a.kv_heads)
+        hipLaunchKernelGGL((decode_pass1_kernel<1, true>), dim3((unsigned)units, (unsigned)splits), dim3(64), 0, st, a);
+    else
+        hipLaunchKernelGGL((decode_pass1_kernel<1, false>), dim3((unsigned)units, (unsigned)splits), dim3(64), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(decode_pass2_kernel<true>, dim3((unsigned)(a.batch * a.q_heads)), dim3(64), 0, st, a.part_o,
@@ -896,7 +968,11 @@ hipError_t launch_decode_ragged(const DecodeArgs &a, int splits, int32_t *lens, 
 
 hipError_t launch_decode_step(const DecodeArgs &a, int splits, hipStream_t st) {
     const int units = a.batch * a.kv_heads * a.chunks;
-    hipLaunchKernelGGL(decode_pass1_kernel<2>, dim3((unsigned)units, (unsigned)splits), dim3(64), 0, st, a);
+    const dim3 grid((unsigned)units, (unsigned)splits + 1u);   // row 0: the block workgroups
+    if (a.q_heads == a.kv_heads)
+        hipLaunchKernelGGL((decode_pass1_kernel<2, true>), grid, dim3(64), 0, st, a);
+    else
+        hipLaunchKernelGGL((decode_pass1_kernel<2, false>), grid, dim3(64), 0, st, a);
     return hipGetLastError();
 }
 

@@ -268,6 +268,11 @@ KVQ_API int kv_decode_attention_noalloc(const kvq_shape *shape, const kvq_cache 
  *   sync: device uint32 [kv_ragged_sync_words(shape)], 4-byte aligned, all zero when the cache is created; used by
  *     kv_ragged_decode_step only (completion counters inside its single launch), which leaves it zero again.
  *     Required by kv_ragged_decode_step (KVQ_E_NULL), ignored by the other calls.
+ * Window blocks are quantized ahead: whenever sequence b's window holds a complete 32-row block k, tile
+ * n_quant / 32 + k (if below max_tokens / 32) already holds that block's record, written by the call that completed
+ * the block (kv_ragged_prefill, kv_ragged_append or kv_ragged_decode_step). These are the bytes a flush writes, so a
+ * flush in kv_ragged_decode_step only moves the lengths. The cache state (tiles, window rows, lens) must therefore be
+ * changed through these calls only.
  * Calls on one ragged cache must be issued on one stream, in order.
  */
 typedef struct kvq_ragged {
@@ -285,8 +290,8 @@ KVQ_API size_t kv_ragged_sync_words(const kvq_shape *shape);
 /*
  * Replaces sequence b's contents with n_tokens tokens (n_tokens >= 0; 0 empties it): k, v fp16 [Hkv][n_tokens][128]
  * with element strides stride_h, stride_t (16-byte aligned rows). Same state as n_tokens single appends to an empty
- * sequence (KIVI page, paragraph on the recent-token window); writes lens[b] = {flushed, n_tokens - flushed, 0, 0}.
- * Other sequences are untouched.
+ * sequence (KIVI page, paragraph on the recent-token window); writes lens[b] = {flushed, n_tokens - flushed, 0, 0}
+ * and the records of the window's complete blocks (written ahead, as above). Other sequences are untouched.
  * Errors: KVQ_E_NULL, KVQ_E_SHAPE (b outside [0, B), n_tokens < 0), KVQ_E_BITS, KVQ_E_ALIGN, KVQ_E_CAPACITY
  *   (flushed tokens > max_tokens), KVQ_E_LAUNCH.
  */
@@ -296,7 +301,8 @@ KVQ_API int kv_ragged_prefill(const kvq_shape *shape, const kvq_ragged *cache, i
 /*
  * Appends one token to every sequence: k_new, v_new fp16 [B][Hkv][128] with element strides stride_b, stride_h.
  * Per sequence on the device: a full window is first quantized into R/32 tiles (lazy flush), then the token is
- * stored; equals kv_append_and_flush with one token applied to each sequence at its own length.
+ * stored; equals kv_append_and_flush with one token applied to each sequence at its own length. A token that
+ * completes a window block also gets that block's record written ahead.
  * Errors: KVQ_E_NULL, KVQ_E_SHAPE, KVQ_E_BITS, KVQ_E_ALIGN, KVQ_E_LAUNCH.
  */
 KVQ_API int kv_ragged_append(const kvq_shape *shape, const kvq_ragged *cache, const void *k_new, const void *v_new,
@@ -319,10 +325,11 @@ KVQ_API int kv_ragged_decode_attention(const kvq_shape *shape, const kvq_ragged 
 /*
  * One decode step: the result of kv_ragged_append(k_new, v_new) then kv_ragged_decode_attention(q), bit for bit, in a
  * single launch (KIVI page, paragraphs on the recent-token window and on decoding from the grouped and residual
- * parts). Every workgroup derives its sequence's step from the lengths before it; the workgroups whose token range
- * holds a window being flushed quantize it themselves; the new token is attended from k_new/v_new; the last split of
- * each (sequence, KV head, chunk of four query heads) merges the splits, and the last of a sequence writes the new
- * window rows and lengths (counted in cache->sync, left zero). k_new, v_new must not alias the cache.
+ * parts). Every workgroup derives its sequence's step from the lengths before it; a flushed window's tiles were
+ * written ahead, so the flush only moves the lengths; a token that completes a window block has that block's record
+ * written ahead by a workgroup running beside the attention; the new token is attended from k_new/v_new; the last
+ * split of each (sequence, KV head, chunk of four query heads) merges the splits, and the last of a sequence writes
+ * the new window rows and lengths (counted in cache->sync, left zero). k_new, v_new must not alias the cache.
  * Errors: as kv_ragged_append and kv_ragged_decode_attention; KVQ_E_NULL without cache->sync.
  */
 KVQ_API int kv_ragged_decode_step(const kvq_shape *shape, const kvq_ragged *cache, const void *k_new,
