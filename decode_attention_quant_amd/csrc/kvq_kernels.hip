@@ -436,10 +436,11 @@ __device__ __forceinline__ int sz_off(int x) { return x < 512 ? x : x + 16 * ((x
 // Decode step (MODE 2). Every workgroup derives the step of its sequence from the lengths before it (append the
 // token; a full window is flushed first; a sequence whose flush would pass the capacity refuses the token and is
 // marked full) and attends over the state after it. The tiles of a flushed window were quantized ahead (see the
-// ragged append), so a flush only moves the lengths. Grid row y = 0 holds one block workgroup per (sequence, KV
+// ragged append), so a flush only moves the lengths. The last grid row holds one block workgroup per (sequence, KV
 // head, chunk): when the appended token completes a window block, the chunk-0 workgroup writes that block's record
-// ahead (from the window rows below the token and the token itself, from the input); it is dispatched first and runs
-// beside the attention. Rows y >= 1 are the splits. The new token is attended straight from the input (its window row
+// ahead (from the window rows below the token and the token itself, from the input), beside the attention. It is
+// dispatched after the splits (first, it cost the steps ~1 us: the splits' own dispatch order matters more), and its
+// ~10 us of work ends well within a step. The other rows are the splits. The new token is attended straight from the input (its window row
 // is written only at the end). After its partials are stored, a split counts itself in sync[(b, KV head, chunk)]; the
 // last of the splits merges them (the pass-2 code) and counts the chunk in sync[b], as does every block workgroup
 // once its loads are complete; the last of the sequence's 2 * KV heads * chunks counts writes the new window rows
@@ -474,10 +475,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     const int l = threadIdx.x;
     const int n = l & 15, kc = l >> 4, hl = n >> 2, g = n & 3;
     const int unit = blockIdx.x;
-    // splits (MODE 2: grid rows 1 .. gridDim.y - 1; row 0 holds the block workgroups); the split holding the fp16
-    // window tiles is dispatched first
+    // splits (MODE 2: the last grid row holds the block workgroups); the split holding the fp16 window tiles is
+    // dispatched first
     const int nsplit = MODE == 2 ? (int)gridDim.y - 1 : (int)gridDim.y;
-    const int split = (int)gridDim.y - 1 - (int)blockIdx.y;
+    const int split = nsplit - 1 - (int)blockIdx.y;
     const int chunk = uni(unit % a.chunks);
     const int hkv = uni((unit / a.chunks) % a.kv_heads);
     const int b = uni(unit / (a.chunks * a.kv_heads));
@@ -550,7 +551,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
         }
     };
     if constexpr (MODE == 2) {
-        if (blockIdx.y == 0) {   // block workgroup (no flush here: a flush leaves the token in row 0)
+        if ((int)blockIdx.y == nsplit) {   // block workgroup (no flush here: a flush leaves the token in row 0)
             if (chunk == 0 && new_row >= 0 && (new_row & 31) == 31) {
                 const int64_t slot = n_qtiles + new_row / 32;
                 if (slot < a.max_tiles)
@@ -968,7 +969,7 @@ hipError_t launch_decode_ragged(const DecodeArgs &a, int splits, int32_t *lens, 
 
 hipError_t launch_decode_step(const DecodeArgs &a, int splits, hipStream_t st) {
     const int units = a.batch * a.kv_heads * a.chunks;
-    const dim3 grid((unsigned)units, (unsigned)splits + 1u);   // row 0: the block workgroups
+    const dim3 grid((unsigned)units, (unsigned)splits + 1u);   // last row: the block workgroups
     if (a.q_heads == a.kv_heads)
         hipLaunchKernelGGL((decode_pass1_kernel<2, true>), grid, dim3(64), 0, st, a);
     else

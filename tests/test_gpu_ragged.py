@@ -1,7 +1,8 @@
 """GPU parity of ragged caches: sequences at their own lengths, the lengths in device memory.
 
 Each sequence is checked against its own oracle cache (the oracle's state machine and attention applied to that
-sequence alone): packed tiles and window bytes bit-exact, attention outputs within max-abs 2e-3. The decode step is a
+sequence alone): packed tiles, the records of complete window blocks written ahead after them, and window bytes
+bit-exact, attention outputs within max-abs 2e-3. The decode step is a
 single launch (flush, append, attention, merge and length commit inside one kernel); it must equal
 kv_ragged_append + kv_ragged_decode_attention bit for bit, leave its completion counters at zero, and, captured once
 in a HIP graph and replayed with new inputs, equal the same step run eagerly on a twin cache, bit for bit.
@@ -74,6 +75,18 @@ def _check_state(cache, refs, what):
             want = helpers.oracle_records(ref)
             assert np.array_equal(got, want), f"{what}: seq {b}: " + helpers.first_mismatch(got, want)
         nr = ref.n_resid
+        # complete window blocks: their records are written ahead, in the tiles after the quantized part
+        for k in range(nr // 32):
+            slot = nt + k
+            if slot >= cache.tiles.shape[2]:
+                break
+            blk = oc.SliceCache(ref.slices, residual_cap=32)
+            oc.append_block(blk, ref.k_res[:, 32 * k:32 * k + 32], ref.v_res[:, 32 * k:32 * k + 32])
+            blk.flush()
+            got = cache.tiles[b, :, slot:slot + 1].cpu().numpy()
+            want = helpers.oracle_records(blk)
+            assert np.array_equal(got, want), (f"{what}: seq {b}: window block {k} (tile {slot}) not written ahead: "
+                                               + helpers.first_mismatch(got, want))
         kr = cache.k_res[b, :, :nr].cpu().numpy()
         vr = cache.v_res[b, :, :nr].cpu().numpy()
         assert np.array_equal(kr.view(np.uint16), ref.k_res.view(np.uint16)), f"{what}: seq {b} k window"
