@@ -11,6 +11,16 @@ A tile is 32 consecutive quantized tokens of one (batch row, KV head) slice. Eac
     bytes 2560..2815  value scale s_V[g][t],   g = 0..3, t = 0..31  (binary16, index 32*g + t)
     bytes 2816..3071  value zero  z_V[g][t]                        (binary16)
 
+With dense-and-sparse groups (one outlier per 32-element group, see ``oracle.sparse``) a record is 3840 bytes: the
+3072 above, then the outlier section
+
+    bytes 3072..3327  key outlier value   o_K[c],  c = 0..127          (binary16)
+    bytes 3328..3455  key outlier token   u_K[c]                       (uint8, 0..31)
+    bytes 3456..3711  value outlier value o_V[g][t]                    (binary16, index 32*g + t)
+    bytes 3712..3839  value outlier channel i_V[g][t] within group g   (uint8, 0..31)
+
+and the outlier's own code is 0. 3840 = 15 * 256 keeps records 256-byte aligned.
+
 A word holds 16 codes of 2 bits. Word w of a code region is read by lane w // 4 of a 64-lane wavefront and the
 code placement is fixed by the functions below (a layout of this library, not of the pages; it is defined so
 each lane reads 16 contiguous bytes and expands them with byte-wise fp4 conversions).
@@ -33,6 +43,8 @@ RECORD_BYTES = 3072
 K_CODES_OFF, V_CODES_OFF = 0, 1024
 K_SCALE_OFF, K_ZERO_OFF = 2048, 2304
 V_SCALE_OFF, V_ZERO_OFF = 2560, 2816
+RECORD_BYTES_SPARSE = 3840
+K_OUT_OFF, K_IDX_OFF, V_OUT_OFF, V_IDX_OFF = 3072, 3328, 3456, 3712
 
 
 def key_code_position(t: int, c: int) -> tuple[int, int]:
@@ -134,3 +146,33 @@ def unpack_tiles(rec: np.ndarray):
     v_scale = np.swapaxes(rec[..., V_SCALE_OFF:V_SCALE_OFF + 256].copy().view(np.float16).reshape(lead + (4, 32)), -1, -2)
     v_zero = np.swapaxes(rec[..., V_ZERO_OFF:V_ZERO_OFF + 256].copy().view(np.float16).reshape(lead + (4, 32)), -1, -2)
     return k_codes, k_scale, k_zero, v_codes, np.ascontiguousarray(v_scale), np.ascontiguousarray(v_zero)
+
+
+def pack_tiles_sparse(k_codes, k_scale, k_zero, v_codes, v_scale, v_zero, k_out, k_idx, v_out, v_idx) -> np.ndarray:
+    """3840-byte records: :func:`pack_tiles` plus the outlier section. Key outliers float16 / uint8 ``[..., 128]``
+    (one per channel: value and token), value outliers ``[..., 32, 4]`` (one per token and channel group: value and
+    channel within the group)."""
+    base = pack_tiles(k_codes, k_scale, k_zero, v_codes, v_scale, v_zero)
+    lead = base.shape[:-1]
+    rec = np.zeros(lead + (RECORD_BYTES_SPARSE,), dtype=np.uint8)
+    rec[..., :RECORD_BYTES] = base
+    rec[..., K_OUT_OFF:K_OUT_OFF + 256] = np.ascontiguousarray(
+        np.broadcast_to(np.asarray(k_out, np.float16), lead + (128,))).view(np.uint8).reshape(lead + (256,))
+    rec[..., K_IDX_OFF:K_IDX_OFF + 128] = np.broadcast_to(np.asarray(k_idx, np.uint8), lead + (128,))
+    vo = np.ascontiguousarray(np.swapaxes(np.asarray(v_out, np.float16), -1, -2))          # [..., 4, 32]
+    rec[..., V_OUT_OFF:V_OUT_OFF + 256] = vo.view(np.uint8).reshape(lead + (256,))
+    rec[..., V_IDX_OFF:V_IDX_OFF + 128] = np.ascontiguousarray(
+        np.swapaxes(np.asarray(v_idx, np.uint8), -1, -2)).reshape(lead + (128,))
+    return rec
+
+
+def unpack_tiles_sparse(rec: np.ndarray):
+    """Inverse of :func:`pack_tiles_sparse`: the six dense fields, then (k_out, k_idx, v_out, v_idx)."""
+    rec = np.ascontiguousarray(rec, dtype=np.uint8)
+    lead = rec.shape[:-1]
+    dense = unpack_tiles(rec[..., :RECORD_BYTES])
+    k_out = rec[..., K_OUT_OFF:K_OUT_OFF + 256].copy().view(np.float16).reshape(lead + (128,))
+    k_idx = rec[..., K_IDX_OFF:K_IDX_OFF + 128].copy()
+    v_out = np.swapaxes(rec[..., V_OUT_OFF:V_OUT_OFF + 256].copy().view(np.float16).reshape(lead + (4, 32)), -1, -2)
+    v_idx = np.swapaxes(rec[..., V_IDX_OFF:V_IDX_OFF + 128].copy().reshape(lead + (4, 32)), -1, -2)
+    return dense + (k_out, k_idx, np.ascontiguousarray(v_out), np.ascontiguousarray(v_idx))

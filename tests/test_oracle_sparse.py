@@ -210,3 +210,104 @@ def test_sparse_attention_equals_a_loop_over_packed_records(N, rope_base):
         p = np.exp(scores - scores.max())
         ref = (p[:, None] * np.array(vals)).sum(0) / p.sum()
         assert np.allclose(want[s], ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------- 2-bit records
+from oracle import layout  # noqa: E402
+
+
+def test_sparse_record_2bit_round_trip():
+    """3840-byte 2-bit records: the dense 3072 bytes are pack_tiles' own, the outlier section sits at the stated
+    offsets in [group][token] order for values, and unpacking returns every field."""
+    rng = np.random.default_rng(41)
+    kq = rng.integers(0, 4, (3, 32, 128)).astype(np.uint8)
+    vq = rng.integers(0, 4, (3, 32, 128)).astype(np.uint8)
+    ks, kz = (rng.standard_normal((3, 128)).astype(np.float16) for _ in range(2))
+    vs, vz = (rng.standard_normal((3, 32, 4)).astype(np.float16) for _ in range(2))
+    ko = rng.standard_normal((3, 128)).astype(np.float16)
+    ki = rng.integers(0, 32, (3, 128)).astype(np.uint8)
+    vo = rng.standard_normal((3, 32, 4)).astype(np.float16)
+    vi = rng.integers(0, 32, (3, 32, 4)).astype(np.uint8)
+    rec = layout.pack_tiles_sparse(kq, ks, kz, vq, vs, vz, ko, ki, vo, vi)
+    assert rec.shape == (3, layout.RECORD_BYTES_SPARSE) and layout.RECORD_BYTES_SPARSE % 256 == 0
+    assert np.array_equal(rec[:, :layout.RECORD_BYTES], layout.pack_tiles(kq, ks, kz, vq, vs, vz))
+    back = layout.unpack_tiles_sparse(rec)
+    for a, b in zip(back, (kq, ks, kz, vq, vs, vz, ko, ki, vo, vi)):
+        assert np.array_equal(np.asarray(a).view(np.uint8), np.asarray(b).view(np.uint8))
+    # key outlier of channel 77: value at 3072 + 2*77, token at 3328 + 77; value outlier of token 5, group 2 at
+    # entry 32*2 + 5 of each value array
+    assert rec[2, 3072 + 154:3072 + 156].copy().view(np.float16)[0] == ko[2, 77]
+    assert rec[2, 3328 + 77] == ki[2, 77]
+    assert rec[1, 3456 + 2 * 69:3456 + 2 * 70].copy().view(np.float16)[0] == vo[1, 5, 2]
+    assert rec[1, 3712 + 69] == vi[1, 5, 2]
+
+
+def test_sparse_2bit_prefill_equals_token_by_token():
+    rng = np.random.default_rng(42)
+    S, N = 3, 417
+    k = rng.standard_normal((S, N, 128)).astype(np.float32)
+    k[:, :, [3, 70]] *= 20
+    k = k.astype(np.float16)
+    v = rng.standard_normal((S, N, 128)).astype(np.float16)
+    a = oc.SliceCache(S, bits=2, sparse=True)
+    oc.append_block(a, k, v)
+    b = oc.SliceCache(S, bits=2, sparse=True)
+    for t in range(N):
+        b.append_token(k[:, t], v[:, t])
+    assert (a.n_quant, a.n_resid) == (b.n_quant, b.n_resid) == (384, 33)
+    for x, y in zip(a.quantized() + a.outliers(), b.quantized() + b.outliers()):
+        assert np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8))
+    kq = a.quantized()[0]
+    assert kq.max() <= 3
+
+
+def test_sparse_2bit_attention_equals_a_loop_over_packed_records():
+    """Attention of the oracle over a 2-bit dense-and-sparse cache equals a per-token loop that decodes every key and
+    value element from the packed 3840-byte records (q * s + z, the group's outlier put back at its index) and the
+    window, then runs a float64 softmax."""
+    rng = np.random.default_rng(43)
+    S, N = 2, 230
+    k = rng.standard_normal((S, N, 128)).astype(np.float32)
+    k[:, :, [9, 100]] *= 20
+    k[:, 17] *= 8                      # a spike token: the outlier of most of its channels' groups
+    k = k.astype(np.float16)
+    v = rng.standard_normal((S, N, 128)).astype(np.float32)
+    v[:, :, 45] *= 30
+    v = v.astype(np.float16)
+    q = rng.standard_normal((1, S, 128)).astype(np.float16)
+    c = oc.SliceCache(S, bits=2, sparse=True)
+    oc.append_block(c, k, v)
+    want = oa.decode_attention(c, q, 1, S)[0]
+
+    kq, ks, kz, vq, vs, vz = c.quantized()
+    ko, ki, vo, vi = c.outliers()
+    nt = c.n_quant // 32
+    rec = layout.pack_tiles_sparse(kq.reshape(S, nt, 32, 128), ks, kz, vq.reshape(S, nt, 32, 128),
+                                   vs.reshape(S, nt, 32, 4), vz.reshape(S, nt, 32, 4), ko, ki,
+                                   vo.reshape(S, nt, 32, 4), vi.reshape(S, nt, 32, 4))
+    assert rec.shape == (S, nt, 3840)
+    for s in range(S):
+        keys, vals = [], []
+        for j in range(nt):
+            tkq, tks, tkz, tvq, tvs, tvz, tko, tki, tvo, tvi = layout.unpack_tiles_sparse(rec[s, j])
+            for t in range(32):
+                key = [float(tkq[t, ch]) * float(tks[ch]) + float(tkz[ch]) for ch in range(128)]
+                for ch in range(128):
+                    if tki[ch] == t:
+                        key[ch] = float(tko[ch])
+                val = [float(tvq[t, ch]) * float(tvs[t, ch // 32]) + float(tvz[t, ch // 32]) for ch in range(128)]
+                for gg in range(4):
+                    val[32 * gg + int(tvi[t, gg])] = float(tvo[t, gg])
+                keys.append(key)
+                vals.append(val)
+        for r in range(c.n_resid):
+            keys.append(c.k_res[s, r].astype(np.float64))
+            vals.append(c.v_res[s, r].astype(np.float64))
+        scores = np.array(keys) @ q[0, s].astype(np.float64) / np.sqrt(128)
+        p = np.exp(scores - scores.max())
+        ref = (p[:, None] * np.array(vals)).sum(0) / p.sum()
+        assert np.allclose(want[s], ref, rtol=0, atol=1e-12)
+    # the outliers matter: without them the spike token's and channel 45's contributions change the output
+    dense_only = oc.SliceCache(S, bits=2)
+    oc.append_block(dense_only, k, v)
+    assert np.abs(oa.decode_attention(dense_only, q, 1, S)[0] - want).max() > 1e-2
