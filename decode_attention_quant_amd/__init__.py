@@ -22,6 +22,7 @@ HEAD_DIM = 128
 GROUP = 32
 TILE_TOKENS = 32
 RECORD_BYTES = 3072
+RECORD_BYTES_SPARSE = 3840
 RECORD_BYTES_4BIT = 5120
 RECORD_BYTES_4BIT_SPARSE = 5888
 SINK_BYTES = 512
@@ -168,13 +169,13 @@ class Shape:
     bits: int = 2
     head_dim: int = HEAD_DIM
     group: int = GROUP
-    flags: int = 0              # FLAG_SINK | FLAG_PRE_ROPE | FLAG_SPARSE (4-bit only)
+    flags: int = 0              # FLAG_SINK | FLAG_PRE_ROPE | FLAG_SPARSE (2-bit: FLAG_SPARSE only)
     rope_base: float = 0.0      # rotary base when FLAG_PRE_ROPE is set
 
     @property
     def record_bytes(self) -> int:
         if self.bits != 4:
-            return RECORD_BYTES
+            return RECORD_BYTES_SPARSE if self.flags & FLAG_SPARSE else RECORD_BYTES
         return RECORD_BYTES_4BIT_SPARSE if self.flags & FLAG_SPARSE else RECORD_BYTES_4BIT
 
     def c(self) -> KvqShape:

@@ -43,6 +43,7 @@ int scratch_address(void **ptr) {
 // kernel keeps its rotation tables in registers and holds two per SIMD.
 constexpr int64_t kTargetWaves = 4096;
 constexpr int64_t kTargetWavesB4 = 2048;
+constexpr int64_t kTargetWavesSparse = 3072;   // 2-bit dense-and-sparse: three wavefronts per SIMD (LDS and registers)
 constexpr int64_t kMinTilesPerSplit = 4;
 constexpr int64_t kMaxSplits = 1024;
 
@@ -64,7 +65,8 @@ int check_shape(const kvq_shape *s) {
         s->residual_cap % KVQ_TILE_TOKENS != 0 || s->max_tokens <= 0 || s->max_tokens % KVQ_TILE_TOKENS != 0 ||
         s->batch > 65535 || s->kv_heads > 65535 || (int64_t)s->batch * s->q_heads > 0x7fffffff)
         return KVQ_E_SHAPE;
-    if ((s->flags & ~(KVQ_FLAG_SINK | KVQ_FLAG_PRE_ROPE | KVQ_FLAG_SPARSE)) != 0 || (s->flags != 0 && s->bits != 4))
+    if ((s->flags & ~(KVQ_FLAG_SINK | KVQ_FLAG_PRE_ROPE | KVQ_FLAG_SPARSE)) != 0 ||
+        (s->bits == 2 && s->flags != 0 && s->flags != KVQ_FLAG_SPARSE))   // 2-bit: dense-and-sparse groups only
         return KVQ_E_SHAPE;
     if ((s->flags & KVQ_FLAG_PRE_ROPE) && !finite_above_one(s->rope_base)) return KVQ_E_SHAPE;
     return KVQ_OK;
@@ -113,8 +115,8 @@ hipError_t quant_launch(const kvq_shape *shape, bool keys, const kvq::TokSrc &sr
     if (shape->bits == 4)
         return keys ? kvq::launch_quant_keys_b4(src, 0, nt, B, H, tiles, max_tiles, tile0, is_sparse(shape), st)
                     : kvq::launch_quant_values_b4(src, 0, nt, B, H, tiles, max_tiles, tile0, is_sparse(shape), st);
-    return keys ? kvq::launch_quant_keys(src, 0, nt, B, H, tiles, max_tiles, tile0, st)
-                : kvq::launch_quant_values(src, 0, nt, B, H, tiles, max_tiles, tile0, st);
+    return keys ? kvq::launch_quant_keys(src, 0, nt, B, H, tiles, max_tiles, tile0, is_sparse(shape), st)
+                : kvq::launch_quant_values(src, 0, nt, B, H, tiles, max_tiles, tile0, is_sparse(shape), st);
 }
 
 int quant_common(const kvq_shape *shape, const void *x, int64_t sb, int64_t sh, int64_t st, int64_t n_tokens,
@@ -150,7 +152,7 @@ SplitPlan plan(const kvq_shape *s, const kvq_cache *c) {
     const int G = s->q_heads / s->kv_heads;
     p.chunks = (G + 3) / 4;
     const int64_t units = s->bits == 4 ? (int64_t)s->batch * s->q_heads : (int64_t)s->batch * s->kv_heads * p.chunks;
-    const int64_t target = s->bits == 4 ? kTargetWavesB4 : kTargetWaves;
+    const int64_t target = s->bits == 4 ? kTargetWavesB4 : (is_sparse(s) ? kTargetWavesSparse : kTargetWaves);
     int64_t S = (target + units - 1) / units;
     const int64_t by_len = (p.n_vt + kMinTilesPerSplit - 1) / kMinTilesPerSplit;
     if (S > by_len) S = by_len;
@@ -206,6 +208,7 @@ kvq::DecodeArgs ragged_args(const kvq_shape *shape, const kvq_ragged *cache, con
     a.chunks = p.chunks;
     a.tiles_per_split = 0;
     a.sm_log2 = (sm_scale > 0.0f ? sm_scale : 1.0f / sqrtf((float)KVQ_HEAD_DIM)) * 1.4426950408889634f;
+    a.sparse = 0;
     a.lens = cache->lens;
     a.appended = appended;
     a.k_new = nullptr;
@@ -400,6 +403,7 @@ int decode_launch(const kvq_shape *shape, const kvq_cache *cache, const SplitPla
     a.chunks = p.chunks;
     a.tiles_per_split = p.tiles_per_split;
     a.sm_log2 = sm_scale * 1.4426950408889634f;
+    a.sparse = is_sparse(shape) ? 1 : 0;
     a.lens = nullptr;
     a.appended = 0;
     a.k_new = nullptr;
@@ -465,8 +469,8 @@ int kv_ragged_prefill(const kvq_shape *shape, const kvq_ragged *cache, int32_t b
         // tile i holds tokens 32 i .. 32 i + 31 either way
         const int64_t nt = std::min(n_tokens / KVQ_TILE_TOKENS, max_tiles);
         if (nt > 0) {
-            if ((e = launched(kvq::launch_quant_keys(ks, 0, nt, 1, H, tiles, max_tiles, 0, s)))) return e;
-            if ((e = launched(kvq::launch_quant_values(vs, 0, nt, 1, H, tiles, max_tiles, 0, s)))) return e;
+            if ((e = launched(kvq::launch_quant_keys(ks, 0, nt, 1, H, tiles, max_tiles, 0, false, s)))) return e;
+            if ((e = launched(kvq::launch_quant_values(vs, 0, nt, 1, H, tiles, max_tiles, 0, false, s)))) return e;
         }
         const int64_t n_copy = n_tokens - flushed;
         if ((e = launched(kvq::launch_copy_rows(ks, vs, flushed, n_copy, 1, H, kres, vres, (int)R, 0, s)))) return e;

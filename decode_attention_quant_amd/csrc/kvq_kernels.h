@@ -34,6 +34,7 @@ struct DecodeArgs {
     int chunks;           // ceil(G / 4): query heads are processed four per wavefront
     int tiles_per_split;  // 32-token tiles (quantized, then residual) per split
     float sm_log2;        // softmax scale * log2(e)
+    int sparse;           // dense-and-sparse records (3840 bytes; uniform lengths only)
     const int32_t *lens;  // ragged caches: per-sequence {n_quant, n_resid, n_sink, status}; else null
     int appended;         // ragged: the lengths predate the append of one token per sequence (decode step)
     // single-launch decode step (ragged caches): the new token of every (batch row, KV head) at
@@ -83,10 +84,11 @@ hipError_t launch_sink_b4(const TokSrc &ksrc, const TokSrc &vsrc, int batch, int
 hipError_t launch_decode_b4(const DecodeB4Args &a, float *out, int splits, hipStream_t st);
 hipError_t launch_pass2(const float *part_o, const float *part_ml, float *out, int rows, int splits, hipStream_t st);
 
+// 2-bit tiles (sparse: dense-and-sparse records of 3840 bytes)
 hipError_t launch_quant_keys(const TokSrc &src, int64_t t_begin, int64_t n_tiles, int batch, int kv_heads,
-                             uint8_t *tiles, int64_t max_tiles, int64_t tile0, hipStream_t st);
+                             uint8_t *tiles, int64_t max_tiles, int64_t tile0, bool sparse, hipStream_t st);
 hipError_t launch_quant_values(const TokSrc &src, int64_t t_begin, int64_t n_tiles, int batch, int kv_heads,
-                               uint8_t *tiles, int64_t max_tiles, int64_t tile0, hipStream_t st);
+                               uint8_t *tiles, int64_t max_tiles, int64_t tile0, bool sparse, hipStream_t st);
 hipError_t launch_copy_rows(const TokSrc &ksrc, const TokSrc &vsrc, int64_t t_begin, int64_t n, int batch,
                             int kv_heads, _Float16 *kres, _Float16 *vres, int res_cap, int dst0, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs &a, int splits, hipStream_t st);

@@ -21,9 +21,19 @@ typedef float f4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;
 constexpr int REC = 3072;
+// dense-and-sparse records: the 3072 bytes above, then the outlier section (key outliers per channel, value outliers
+// per token and group; see kvq.h)
+constexpr int REC_SPARSE = 3840;
+constexpr int K_OUT = 3072, K_IDX = 3328, V_OUT = 3456, V_IDX = 3712;
+template <bool SPARSE>
+constexpr int rec_bytes() { return SPARSE ? REC_SPARSE : REC; }
 
 // Keys of one tile (tokens t_first .. t_first + 31 of slice (b, h)) into the record at `rec`: one workgroup of 64
 // lanes; lane l owns channels 2l and 2l+1 over the tile's 32 tokens. `words` is 1 KB of LDS.
+// SPARSE (dense-and-sparse groups; synthetic.wiki "KV cache quantization", section "What they report"): each
+// channel's token of largest magnitude (the first on ties) is kept apart as its fp16 value and token index; min and
+// max run over the other 31 tokens and the outlier's code is 0.
+template <bool SPARSE = false>
 __device__ __forceinline__ void quant_keys_tile(const TokSrc &src, int64_t t_first, int b, int h, uint8_t *rec,
                                                 uint32_t *words) {
     const int l = threadIdx.x;
@@ -31,7 +41,36 @@ __device__ __forceinline__ void quant_keys_tile(const TokSrc &src, int64_t t_fir
     uint32_t xw[32];   // token i: channels 2l (low half) and 2l + 1 (high half), binary16
     load_pairs32_packed(src, t_first, b, h, 2 * l, xw);
     h2v mn, mx;
-    minmax_pairs32(xw, mn, mx);
+    int i0 = -1, i1 = -1;   // SPARSE: the outlier tokens of channels 2l, 2l+1
+    if constexpr (SPARSE) {
+        uint32_t k0 = 0u, k1 = 0u;   // |x| bits (binary16 order) above 31 - token: the largest is the first maximum
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            k0 = max(k0, ((xw[i] & 0x7FFFu) << 5) | (31u - i));
+            k1 = max(k1, (((xw[i] >> 16) & 0x7FFFu) << 5) | (31u - i));
+        }
+        i0 = 31 - (int)(k0 & 31u);
+        i1 = 31 - (int)(k1 & 31u);
+        // min/max over the other 31: the outlier's half takes the value of a neighbouring token of its channel
+        const int r0 = i0 == 0 ? 1 : 0, r1 = i1 == 0 ? 1 : 0;
+        uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            lo = i == r0 ? xw[i] : lo;
+            hi = i == r1 ? xw[i] : hi;
+        }
+        mn = __builtin_bit_cast(h2v, (lo & 0xFFFFu) | (hi & 0xFFFF0000u));
+        mx = mn;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const uint32_t w = (i == i0 ? (xw[i] & 0xFFFF0000u) | (lo & 0xFFFFu) : xw[i]);
+            const uint32_t v = (i == i1 ? (w & 0xFFFFu) | (hi & 0xFFFF0000u) : w);
+            mn = __builtin_elementwise_min(mn, __builtin_bit_cast(h2v, v));
+            mx = __builtin_elementwise_max(mx, __builtin_bit_cast(h2v, v));
+        }
+    } else {
+        minmax_pairs32(xw, mn, mx);
+    }
     _Float16 s0, z0, s1, z1;
     group_params((float)mn[0], (float)mx[0], 3.0f, s0, z0);
     group_params((float)mn[1], (float)mx[1], 3.0f, s1, z1);
@@ -50,8 +89,13 @@ __device__ __forceinline__ void quant_keys_tile(const TokSrc &src, int64_t t_fir
     for (int i = 0; i < 32; ++i) {
         const int m = i >> 4, n = i & 15;
         const int w = 4 * (n + 16 * kc) + 2 * m + (ks >> 1);
-        const uint32_t bits = quad_or((code_from_diff(diff_half<false>(xw[i], fz0), fs0, rs0, 3u) << shift) |
-                                      (code_from_diff(diff_half<true>(xw[i], fz1), fs1, rs1, 3u) << (shift + 4)));
+        uint32_t q0 = code_from_diff(diff_half<false>(xw[i], fz0), fs0, rs0, 3u);
+        uint32_t q1 = code_from_diff(diff_half<true>(xw[i], fz1), fs1, rs1, 3u);
+        if constexpr (SPARSE) {
+            q0 = i == i0 ? 0u : q0;
+            q1 = i == i1 ? 0u : q1;
+        }
+        const uint32_t bits = quad_or((q0 << shift) | (q1 << (shift + 4)));
         uint32_t lo, hi;
         swap16(bits, lo, hi);
         if (writer) words[w] = lo | hi;
@@ -61,6 +105,16 @@ __device__ __forceinline__ void quant_keys_tile(const TokSrc &src, int64_t t_fir
     h2 sp = {s0, s1}, zp = {z0, z1};
     reinterpret_cast<h2 *>(rec + 2048)[l] = sp;
     reinterpret_cast<h2 *>(rec + 2304)[l] = zp;
+    if constexpr (SPARSE) {
+        uint32_t ow = 0u;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            ow = i == i0 ? (ow & 0xFFFF0000u) | (xw[i] & 0xFFFFu) : ow;
+            ow = i == i1 ? (ow & 0xFFFFu) | (xw[i] & 0xFFFF0000u) : ow;
+        }
+        reinterpret_cast<uint32_t *>(rec + K_OUT)[l] = ow;
+        reinterpret_cast<uint16_t *>(rec + K_IDX)[l] = (uint16_t)(i0 | (i1 << 8));
+    }
 }
 
 // Values of one tile into the record at `rec`. Parameters: lane l reduces the groups (token l / 4 and 16 + l / 4,
@@ -68,8 +122,14 @@ __device__ __forceinline__ void quant_keys_tile(const TokSrc &src, int64_t t_fir
 // zero and reciprocal scale; codes: lane l owns channels 2l and 2l+1 of every token (the row g = l / 16 of lanes
 // owns channel group g) and builds its code words over the tokens. LDS: `words` 1 KB, `sv`/`zv` 256 B each,
 // `gp` 2 KB ({s, z, 1/s, 0} as binary32 per (token, group)).
+// SPARSE: the group's outlier (largest magnitude, lowest channel on ties) is the maximum of an order key (|x| bits,
+// then the lower channel, then the sign bit, which recovers the value); min/max over the other 31 elements run with
+// the outlier's half replaced by the other half of its 32-bit word (an element of the same group, so the extremes
+// are unchanged), and the outlier's code is 0. `ov` (256 B) and `oi` (128 B) of LDS hold the outliers [g][t].
+template <bool SPARSE = false>
 __device__ __forceinline__ void quant_values_tile(const TokSrc &src, int64_t t_first, int b, int h, uint8_t *rec,
-                                                  uint32_t *words, _Float16 *sv, _Float16 *zv, float *gp) {
+                                                  uint32_t *words, _Float16 *sv, _Float16 *zv, float *gp,
+                                                  _Float16 *ov = nullptr, uint8_t *oi = nullptr) {
     const int l = threadIdx.x;
     const int c = 2 * l, j = c >> 4, cc = c & 15, g = l >> 4;
     uint32_t xw[32];
@@ -82,6 +142,23 @@ __device__ __forceinline__ void quant_values_tile(const TokSrc &src, int64_t t_f
         uint4 r4[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) r4[q] = row[q];
+        if constexpr (SPARSE) {
+            uint32_t kmax = 0u;
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const uint32_t we = r4[e >> 2][e & 3];
+                const uint32_t klo = ((we & 0x7FFFu) << 6) | ((31u - 2u * e) << 1) | ((we >> 15) & 1u);
+                const uint32_t khi = (((we >> 16) & 0x7FFFu) << 6) | ((30u - 2u * e) << 1) | (we >> 31);
+                kmax = max(kmax, max(klo, khi));
+            }
+            const uint32_t w = 31u - ((kmax >> 1) & 31u);
+            const uint32_t sel = (w & 1u) ? 0x01000100u : 0x03020302u;   // both halves = the partner half
+            ov[32 * gq + tk] = __builtin_bit_cast(_Float16, (uint16_t)(((kmax >> 6) & 0x7FFFu) | ((kmax & 1u) << 15)));
+            oi[32 * gq + tk] = (uint8_t)w;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if ((uint32_t)e == (w >> 1)) r4[e >> 2][e & 3] = __builtin_amdgcn_perm(r4[e >> 2][e & 3], r4[e >> 2][e & 3], sel);
+        }
         h2v mn = __builtin_bit_cast(h2v, r4[0].x), mx = mn;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -109,8 +186,15 @@ __device__ __forceinline__ void quant_values_tile(const TokSrc &src, int64_t t_f
         int kc, e;
         if (i < 16) { kc = i >> 2; e = i & 3; } else { kc = (i - 16) >> 2; e = 4 + ((i - 16) & 3); }
         const int shift = 4 * e + 2 * (j & 1);
-        wv[kc][0] |= code_from_diff(diff_half<false>(xw[i], prm[1]), prm[0], prm[2], 3u) << shift;
-        wv[kc][1] |= code_from_diff(diff_half<true>(xw[i], prm[1]), prm[0], prm[2], 3u) << shift;
+        uint32_t q0 = code_from_diff(diff_half<false>(xw[i], prm[1]), prm[0], prm[2], 3u);
+        uint32_t q1 = code_from_diff(diff_half<true>(xw[i], prm[1]), prm[0], prm[2], 3u);
+        if constexpr (SPARSE) {
+            const uint32_t oc = oi[32 * g + i], c0 = 2 * (l & 15);
+            q0 = oc == c0 ? 0u : q0;
+            q1 = oc == c0 + 1 ? 0u : q1;
+        }
+        wv[kc][0] |= q0 << shift;
+        wv[kc][1] |= q1 << shift;
     }
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) {
@@ -124,27 +208,36 @@ __device__ __forceinline__ void quant_values_tile(const TokSrc &src, int64_t t_f
     reinterpret_cast<uint4 *>(rec + 1024)[l] = reinterpret_cast<const uint4 *>(words)[l];
     reinterpret_cast<uint32_t *>(rec + 2560)[l] = reinterpret_cast<const uint32_t *>(sv)[l];
     reinterpret_cast<uint32_t *>(rec + 2816)[l] = reinterpret_cast<const uint32_t *>(zv)[l];
+    if constexpr (SPARSE) {
+        reinterpret_cast<uint32_t *>(rec + V_OUT)[l] = reinterpret_cast<const uint32_t *>(ov)[l];
+        reinterpret_cast<uint16_t *>(rec + V_IDX)[l] = reinterpret_cast<const uint16_t *>(oi)[l];
+    }
 }
 
+template <bool SPARSE>
 __global__ __launch_bounds__(64) void quant_keys_kernel(TokSrc src, int64_t t_begin, int kv_heads, uint8_t *tiles,
                                                         int64_t max_tiles, int64_t tile0) {
     __shared__ uint32_t words[256];
     const int64_t tile = blockIdx.x;
     const int h = blockIdx.y, b = blockIdx.z;
-    uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * REC;
-    quant_keys_tile(src, t_begin + tile * 32, b, h, rec, words);
+    uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * rec_bytes<SPARSE>();
+    quant_keys_tile<SPARSE>(src, t_begin + tile * 32, b, h, rec, words);
 }
 
-// five wavefronts per SIMD (85 registers): a memory-bound kernel whose loads want more wavefronts in flight
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(5))) void quant_values_kernel(TokSrc src, int64_t t_begin, int kv_heads,
+// five wavefronts per SIMD (85 registers): a memory-bound kernel whose loads want more wavefronts in flight (the
+// outlier search of dense-and-sparse groups needs more registers: four)
+template <bool SPARSE>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(SPARSE ? 4 : 5))) void quant_values_kernel(TokSrc src, int64_t t_begin, int kv_heads,
                                                           uint8_t *tiles, int64_t max_tiles, int64_t tile0) {
     __shared__ uint32_t words[256];
     __shared__ _Float16 sv[128], zv[128];
     __shared__ __align__(16) float gp[512];
+    __shared__ __align__(16) _Float16 ov[SPARSE ? 128 : 1];
+    __shared__ __align__(16) uint8_t oi[SPARSE ? 128 : 1];
     const int64_t tile = blockIdx.x;
     const int h = blockIdx.y, b = blockIdx.z;
-    uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * REC;
-    quant_values_tile(src, t_begin + tile * 32, b, h, rec, words, sv, zv, gp);
+    uint8_t *rec = tiles + ((int64_t)(b * kv_heads + h) * max_tiles + tile0 + tile) * rec_bytes<SPARSE>();
+    quant_values_tile<SPARSE>(src, t_begin + tile * 32, b, h, rec, words, sv, zv, gp, ov, oi);
 }
 
 // ------------------------------------------------------------------------------------------------ window append
@@ -428,6 +521,30 @@ constexpr int LDS_BETA = LDS_QT + 8 * QT_ROW * 2;   // fp32 [4 heads]
 constexpr int P_ROW = 18;            // float2 per head of the probability exchange: 16 + 2 padding
 constexpr int LDS_P = 8192;          // float2 [4 heads][P_ROW]: p of tokens i and 16 + i
 constexpr int LDS_BYTES = LDS_P + 4 * P_ROW * 8;    // [0, 8192) also holds the fp16 window value tile [32][128]
+// Dense-and-sparse records (the sparse kernel only): the tile's outlier section (768 B) and the integer correction
+// sums (H, L) of the key outliers per (head, token) inside the window-tile region, which the quantized loop leaves
+// free; the value-outlier sums per (head, channel) after the probability exchange.
+constexpr int LDS_OUT = 3456;        // the record's bytes 3072..3839
+constexpr int LDS_KACC = 4224;       // int2 [4 heads][32 tokens]
+constexpr int LDS_VACC = LDS_BYTES;  // int2 [4 heads][128 channels]
+constexpr int LDS_BYTES_SPARSE = LDS_VACC + 4 * 128 * 8;
+static_assert(LDS_OUT >= LDS_BETA + 16 && LDS_KACC + 1024 <= 8192, "sparse regions inside the free window region");
+// Exact sums of corrections through integer LDS atomics (float LDS atomics cost some thirty times an integer one on
+// this chip). Every correction is below 2^17 in magnitude (a query scaled below 1 or a probability at most 1, times
+// the difference of two binary16 values), so x = H 2^-6 + L 2^-29 + e with integers |H|, |L| < 2^23 and |e| < 2^-29;
+// up to 128 terms per target keep the sums of H and L within int32.
+__device__ __forceinline__ void fix_split(float x, int32_t &H, int32_t &L) {
+#pragma clang fp contract(off)
+    H = (int32_t)(x * 64.0f);
+    const float r = __builtin_fmaf(-(float)H, 0x1p-6f, x);   // exact: the low bits of x
+    L = (int32_t)(r * 0x1p29f);
+}
+__device__ __forceinline__ float fix_join(int2 hl) { return __builtin_fmaf((float)hl.x, 0x1p-6f, (float)hl.y * 0x1p-29f); }
+__device__ __forceinline__ void lds_add2(int32_t *p, int32_t h, int32_t lo) {
+    __hip_atomic_fetch_add(p, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __hip_atomic_fetch_add(p + 1, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 // byte offset of metadata byte x (0..1023 of a record's scale/zero section) in the staged copy
 __device__ __forceinline__ int sz_off(int x) { return x < 512 ? x : x + 16 * ((x - 512) >> 6); }
 
@@ -459,9 +576,16 @@ __device__ __forceinline__ int sz_off(int x) { return x < 512 ? x : x + 16 * ((x
 // softmax state agrees, and PV puts the high and low parts of p~ in different A-operand rows (row 4 part + group)
 // instead of two contractions: 8 MFMAs per tile instead of 16. The parts are added across lanes (n, 0) and (n, 1) once,
 // before the partials are stored.
-template <int MODE, bool G1>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void decode_pass1_kernel(DecodeArgs a) {
-    __shared__ __align__(16) unsigned char smem[LDS_BYTES];
+//
+// SPARSE (dense-and-sparse records, uniform lengths): a key outlier decodes as its zero point inside the dense
+// contraction (its code is 0), so its token's score misses q'_c (o - z_c); lane (n, kc) adds these for its eight
+// channels of head kc into the (head, token) sums while staging the tile, and the score lanes take them with the
+// zero-point term. A value outlier likewise adds p_t (o - z) to its channel: each lane adds those of its (head,
+// group, eight tokens) into the (head, channel) sums before PV and the output lanes read them back after it. Both
+// sums are exact integer sums (fix_split), so the result does not depend on the order of the adds.
+template <int MODE, bool G1, bool SPARSE>
+__device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned char *smem) {
+    constexpr int RECB = rec_bytes<SPARSE>();
     uint32_t *sz_lds = reinterpret_cast<uint32_t *>(smem + LDS_SZ);
     const _Float16 *szh = reinterpret_cast<const _Float16 *>(smem + LDS_SZ);
     _Float16 *qt_lds = reinterpret_cast<_Float16 *>(smem + LDS_QT);
@@ -567,7 +691,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     const int v0 = uni(split * tiles_per_split);
     const int v1 = uni(min(v0 + tiles_per_split, n_vt));
     const int qend = uni(min(v1, n_qtiles));
-    const uint8_t *base = a.tiles + ((int64_t)b * a.kv_heads + hkv) * a.max_tiles * (int64_t)REC;
+    const uint8_t *base = a.tiles + ((int64_t)b * a.kv_heads + hkv) * a.max_tiles * (int64_t)RECB;
 
     // ---- query: lane (n, kc) holds head kc of the chunk (if valid), channels 8n .. 8n+7, scaled by 2^-E with
     // 2^E > max |q| of that head (qmax is a float16 value widened, hence a normal binary32 number: its exponent
@@ -628,12 +752,39 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
         p[2] = pb[0]; p[6] = pb[1]; p[3] = pb[2]; p[7] = pb[3];
     };
 
-    // stage a tile's scales/zeros, its folded query (high, low) and beta into LDS
-    auto stage = [&](const uint4 &sw) {
+    int2 *kacc = reinterpret_cast<int2 *>(smem + LDS_KACC);
+    int2 *vacc = reinterpret_cast<int2 *>(smem + LDS_VACC);
+    if constexpr (SPARSE) {
+        reinterpret_cast<int4 *>(kacc)[l] = int4{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) reinterpret_cast<int4 *>(vacc)[l + 64 * i] = int4{0, 0, 0, 0};
+        wave_lds_order();
+    }
+
+    // stage a tile's scales/zeros, its folded query (high, low) and beta into LDS (SPARSE: and its outlier section,
+    // with the key-outlier corrections of the lane's eight channels added into the (head, token) sums)
+    auto stage = [&](const uint4 &sw, const uint4 &ow) {
         *reinterpret_cast<uint4 *>(smem + LDS_SZ + sz_off(16 * l)) = sw;
+        if constexpr (SPARSE) {
+            if (l < 48) reinterpret_cast<uint4 *>(smem + LDS_OUT)[l] = ow;
+        }
         wave_lds_order();
         const h8 sk = *reinterpret_cast<const h8 *>(szh + 8 * n);
         const h8 zk = *reinterpret_cast<const h8 *>(szh + 128 + 8 * n);
+        if constexpr (SPARSE) {
+            const h8 ok = *reinterpret_cast<const h8 *>(smem + LDS_OUT + 16 * n);
+            const uint2 uk = *reinterpret_cast<const uint2 *>(smem + LDS_OUT + 256 + 8 * n);
+            int32_t *ka = reinterpret_cast<int32_t *>(kacc) + 64 * kc;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float qe = (float)qf[e];
+                const float corr = __builtin_fmaf(qe, (float)ok[e], -(qe * (float)zk[e]));   // q' o and q' z exact
+                int32_t H, L;
+                fix_split(corr, H, L);
+                const uint32_t u = ((e < 4 ? uk.x : uk.y) >> (8 * (e & 3))) & 31u;
+                lds_add2(ka + 2 * u, H, L);
+            }
+        }
         const h8 hi = qf * sk;
         const h8 lo = __builtin_elementwise_fma(qf, sk, -hi);
         *reinterpret_cast<h8 *>(qt_lds + QT_ROW * kc + 8 * n) = hi;
@@ -654,20 +805,31 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     // A operand row n = 4 h + r: head h, high part (r = 0), low part (r = 1); rows r = 2, 3 read rows 0, 1 again
     // (their outputs are never used), so all 16 lanes of a row group read distinct or identical addresses
     const _Float16 *qta = qt_lds + QT_ROW * (4 * (n & 1) + hl) + 8 * kc;
-    uint4 kw, vw, sw;
+    uint4 kw, vw, sw, ow = {};
+    const int ol = l < 48 ? l : l - 48;   // SPARSE: lanes 0..47 load the outlier section (the rest reload a part)
     if (v0 < qend) {
-        const uint8_t *rec = base + (int64_t)v0 * REC;
+        const uint8_t *rec = base + (int64_t)v0 * RECB;
         kw = reinterpret_cast<const uint4 *>(rec)[l];
         vw = reinterpret_cast<const uint4 *>(rec + 1024)[l];
         sw = reinterpret_cast<const uint4 *>(rec + 2048)[l];
-        stage(sw);
+        if constexpr (SPARSE) ow = reinterpret_cast<const uint4 *>(rec + REC)[ol];
+        stage(sw, ow);
     }
     for (int v = v0; v < qend; ++v) {
-        const uint8_t *next = base + (int64_t)min(v + 1, qend - 1) * REC;
+        const uint8_t *next = base + (int64_t)min(v + 1, qend - 1) * RECB;
         sw = reinterpret_cast<const uint4 *>(next + 2048)[l];
+        if constexpr (SPARSE) ow = reinterpret_cast<const uint4 *>(next + REC)[ol];
 
-        const f4 ci = {beta_lds[kc] - mr, 0.0f, 0.0f, 0.0f};
+        f4 ci = {beta_lds[kc] - mr, 0.0f, 0.0f, 0.0f};
         f4 acc0 = ci, acc1 = ci;    // tokens n (acc0) and 16 + n (acc1); rows (head kc, part r)
+        if constexpr (SPARSE) {   // the key-outlier sums of tokens n and 16 + n of head kc, then cleared
+            int2 *kr = kacc + 32 * kc;
+            acc0[0] += fix_join(kr[n]);
+            acc1[0] += fix_join(kr[16 + n]);
+            wave_lds_order();
+            kr[n] = int2{0, 0};
+            kr[16 + n] = int2{0, 0};
+        }
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const h8 bq = *reinterpret_cast<const h8 *>(qta + 32 * ks);
@@ -700,6 +862,22 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
             gam = __builtin_fmaf(p[i], (float)zv0[i], gam);
             gam = __builtin_fmaf(p[4 + i], (float)zv1[i], gam);
         }
+        if constexpr (SPARSE) {   // value outliers of (head hl, group g) at tokens 4kc + i and 16 + 4kc + i
+            const unsigned char *os = smem + LDS_OUT;
+            const h4 ov0 = *reinterpret_cast<const h4 *>(os + 384 + 64 * g + 8 * kc);
+            const h4 ov1 = *reinterpret_cast<const h4 *>(os + 384 + 64 * g + 32 + 8 * kc);
+            const uint32_t oi0 = *reinterpret_cast<const uint32_t *>(os + 640 + 32 * g + 4 * kc);
+            const uint32_t oi1 = *reinterpret_cast<const uint32_t *>(os + 640 + 32 * g + 16 + 4 * kc);
+            int32_t *va = reinterpret_cast<int32_t *>(vacc) + 2 * (128 * hl + 32 * g);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float d = (i < 4 ? (float)ov0[i] - (float)zv0[i] : (float)ov1[i - 4] - (float)zv1[i - 4]);
+                int32_t H, L;
+                fix_split(p[i] * d, H, L);
+                const uint32_t c = ((i < 4 ? oi0 : oi1) >> (8 * (i & 3))) & 31u;
+                lds_add2(va + 2 * c, H, L);
+            }
+        }
         if constexpr (G1) {
             const h8 pp = (hl & 1) ? plo : phi;
 #pragma unroll
@@ -713,9 +891,21 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
             }
         }
         vw = reinterpret_cast<const uint4 *>(next + 1024)[l];
+        if constexpr (SPARSE) {   // head kc's value-outlier sums of channels n + 16 j, then cleared (G1: row 0 only)
+            wave_lds_order();
+            int2 *vr = vacc + 128 * kc + n;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float corr = fix_join(vr[16 * j]);
+                if (!G1 || kc == 0) o[j][j >> 1] += corr;
+            }
+            wave_lds_order();
+#pragma unroll
+            for (int j = 0; j < 8; ++j) vr[16 * j] = int2{0, 0};
+        }
         // every LDS read of this tile has been issued: overwrite with the next tile (after the last tile, with
         // that tile again; unconditional, so no load sits on only one path of the loop)
-        stage(sw);
+        stage(sw, ow);
     }
 
     // ------------------------------------------------------------------ residual (fp16) tiles
@@ -889,6 +1079,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     }
 }
 
+template <int MODE, bool G1>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void decode_pass1_kernel(DecodeArgs a) {
+    __shared__ __align__(16) unsigned char smem[LDS_BYTES];
+    decode_pass1_body<MODE, G1, false>(a, smem);
+}
+
+// dense-and-sparse records: three wavefronts per SIMD (12.6 KB of LDS, up to 168 registers)
+template <bool G1>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 3))) void decode_pass1_sparse_kernel(DecodeArgs a) {
+    __shared__ __align__(16) unsigned char smem[LDS_BYTES_SPARSE];
+    decode_pass1_body<0, G1, true>(a, smem);
+}
+
 // ------------------------------------------------------------------------------------------------ decode pass 2
 // One wavefront per (batch row, query head): out = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s. The splits'
 // (m, l) are read by all lanes at once (lane l takes splits l, l + 64, ...), M and the weighted sum of l are wave
@@ -916,16 +1119,22 @@ __global__ __launch_bounds__(64) void decode_pass2_kernel(const float *part_o, c
 
 // ------------------------------------------------------------------------------------------------ launchers
 hipError_t launch_quant_keys(const TokSrc &src, int64_t t_begin, int64_t n_tiles, int batch, int kv_heads,
-                             uint8_t *tiles, int64_t max_tiles, int64_t tile0, hipStream_t st) {
+                             uint8_t *tiles, int64_t max_tiles, int64_t tile0, bool sparse, hipStream_t st) {
     dim3 grid((unsigned)n_tiles, (unsigned)kv_heads, (unsigned)batch);
-    hipLaunchKernelGGL(quant_keys_kernel, grid, dim3(64), 0, st, src, t_begin, kv_heads, tiles, max_tiles, tile0);
+    if (sparse)
+        hipLaunchKernelGGL(quant_keys_kernel<true>, grid, dim3(64), 0, st, src, t_begin, kv_heads, tiles, max_tiles, tile0);
+    else
+        hipLaunchKernelGGL(quant_keys_kernel<false>, grid, dim3(64), 0, st, src, t_begin, kv_heads, tiles, max_tiles, tile0);
     return hipGetLastError();
 }
 
 hipError_t launch_quant_values(const TokSrc &src, int64_t t_begin, int64_t n_tiles, int batch, int kv_heads,
-                               uint8_t *tiles, int64_t max_tiles, int64_t tile0, hipStream_t st) {
+                               uint8_t *tiles, int64_t max_tiles, int64_t tile0, bool sparse, hipStream_t st) {
     dim3 grid((unsigned)n_tiles, (unsigned)kv_heads, (unsigned)batch);
-    hipLaunchKernelGGL(quant_values_kernel, grid, dim3(64), 0, st, src, t_begin, kv_heads, tiles, max_tiles, tile0);
+    if (sparse)
+        hipLaunchKernelGGL(quant_values_kernel<true>, grid, dim3(64), 0, st, src, t_begin, kv_heads, tiles, max_tiles, tile0);
+    else
+        hipLaunchKernelGGL(quant_values_kernel<false>, grid, dim3(64), 0, st, src, t_begin, kv_heads, tiles, max_tiles, tile0);
     return hipGetLastError();
 }
 
@@ -945,10 +1154,15 @@ hipError_t launch_pass2(const float *part_o, const float *part_ml, float *out, i
 
 hipError_t launch_decode(const DecodeArgs &a, int splits, hipStream_t st) {
     const int units = a.batch * a.kv_heads * a.chunks;
-    if (a.q_heads == a.kv_heads)
-        hipLaunchKernelGGL((decode_pass1_kernel<0, true>), dim3((unsigned)units, (unsigned)splits), dim3(64), 0, st, a);
+    const dim3 grid((unsigned)units, (unsigned)splits);
+    if (a.sparse && a.q_heads == a.kv_heads)
+        hipLaunchKernelGGL((decode_pass1_sparse_kernel<true>), grid, dim3(64), 0, st, a);
+    else if (a.sparse)
+        hipLaunchKernelGGL((decode_pass1_sparse_kernel<false>), grid, dim3(64), 0, st, a);
+    else if (a.q_heads == a.kv_heads)
+        hipLaunchKernelGGL((decode_pass1_kernel<0, true>), grid, dim3(64), 0, st, a);
     else
-        hipLaunchKernelGGL((decode_pass1_kernel<0, false>), dim3((unsigned)units, (unsigned)splits), dim3(64), 0, st, a);
+        hipLaunchKernelGGL((decode_pass1_kernel<0, false>), grid, dim3(64), 0, st, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_pass2(a.part_o, a.part_ml, a.out, a.batch * a.q_heads, splits, st);

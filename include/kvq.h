@@ -73,12 +73,13 @@ extern "C" {
 #define KVQ_GROUP 32
 #define KVQ_TILE_TOKENS 32
 #define KVQ_RECORD_BYTES 3072       /* one 32-token tile, 2-bit codes */
+#define KVQ_RECORD_BYTES_SPARSE 3840  /* one 32-token tile, 2-bit codes with dense-and-sparse groups */
 #define KVQ_RECORD_BYTES_4BIT 5120  /* one 32-token tile, 4-bit codes */
 #define KVQ_RECORD_BYTES_4BIT_SPARSE 5888  /* one 32-token tile, 4-bit codes with dense-and-sparse groups */
 #define KVQ_SINK_BYTES 512          /* the sink record of one (batch row, KV head) slice */
 #define KVQ_NOALLOC_SCRATCH_BYTES (16 << 20)  /* static scratch per GPU of kv_decode_attention_noalloc */
 
-/* kvq_shape.flags (4-bit only). */
+/* kvq_shape.flags (4-bit: any OR of the three; 2-bit: 0 or KVQ_FLAG_SPARSE alone). */
 #define KVQ_FLAG_SINK 1      /* token 0 is held apart: fp16 key, per-token 4-bit value (synthetic.wiki "KV cache
                                 quantization", section "What they report": KVQuant's attention sink) */
 #define KVQ_FLAG_PRE_ROPE 2  /* keys are given and cached before the rotary embedding; attention rotates every key
@@ -90,7 +91,7 @@ extern "C" {
                                 included, the element of largest magnitude (the lowest index on ties) is stored
                                 apart as its fp16 value and index; the other 31 are quantized by the rule of
                                 kv_quant_keys_per_channel over their own minimum and maximum, and the outlier's
-                                code is 0. Records are 5888 bytes. */
+                                code is 0. Records are 5888 bytes (4-bit) or 3840 bytes (2-bit). */
 
 /*
  * Shape of one cache (one attention layer).
@@ -98,7 +99,8 @@ extern "C" {
  *   consecutive query heads share a KV head — the usual grouped-query layout);
  *   head_dim: must be 128; bits: 2 or 4; group: must be 32 (tokens per key group, channels per value group);
  *   residual_cap: R, the number of newest tokens kept in fp16 (a positive multiple of 32; 128 on the pages);
- *   flags: 0, or (bits = 4 only) an OR of KVQ_FLAG_SINK, KVQ_FLAG_PRE_ROPE and KVQ_FLAG_SPARSE;
+ *   flags: 0, or (bits = 4) an OR of KVQ_FLAG_SINK, KVQ_FLAG_PRE_ROPE and KVQ_FLAG_SPARSE, or (bits = 2)
+ *     KVQ_FLAG_SPARSE alone; ragged caches take 2-bit codes with flags 0 only;
  *   max_tokens: capacity of the quantized part in tokens (a positive multiple of 32);
  *   rope_base: with KVQ_FLAG_PRE_ROPE, the rotary base (10000 in the usual models; must be > 1); ignored otherwise.
  *     Rotary form: channel pairs (2i, 2i+1), i = 0..63, turned by the angle m * theta_i with
@@ -134,6 +136,9 @@ typedef struct kvq_shape {
  *     Value code of channel c, token t: with (kc, e) = (t/4, t%4) for t < 16 and ((t-16)/4, 4 + (t-16)%4) otherwise,
  *       word 4 (c%16 + 16 kc) + (c/16)/2, bit 4 e + 2 ((c/16)%2).
  *     Decoding: x = code * s + z.
+ *     2-bit with KVQ_FLAG_SPARSE: a 3840-byte record, the 3072 bytes above followed by the outlier section laid out
+ *     as in the 4-bit one (bytes 3072..3327 o_K[c], 3328..3455 its token, 3456..3711 o_V[g][t] at 32 g + t,
+ *     3712..3839 its channel within group g); the outlier's code is 0 and it decodes as o.
  *     4-bit: a 5120-byte record (a library layout; the pages fix only the code width)
  *       bytes    0..2047  key codes,   512 little-endian uint32 words (8 four-bit codes each)
  *       bytes 2048..4095  value codes, 512 words

@@ -10,18 +10,23 @@ from oracle import layout
 
 
 def oracle_records(cache: oc.SliceCache) -> np.ndarray:
-    """Tile records [S, n_quant / 32, 3072] of the oracle's quantized part, packed by the oracle."""
+    """Tile records [S, n_quant / 32, 3072 (3840 with dense-and-sparse groups)] of the oracle's quantized part,
+    packed by the oracle."""
     kq, ks, kz, vq, vs, vz = cache.quantized()
     S, nq, D = kq.shape
     nt = nq // 32
-    return layout.pack_tiles(kq.reshape(S, nt, 32, D), ks, kz, vq.reshape(S, nt, 32, D),
-                             vs.reshape(S, nt, 32, 4), vz.reshape(S, nt, 32, 4))
+    dense = (kq.reshape(S, nt, 32, D), ks, kz, vq.reshape(S, nt, 32, D), vs.reshape(S, nt, 32, 4),
+             vz.reshape(S, nt, 32, 4))
+    if not cache.sparse:
+        return layout.pack_tiles(*dense)
+    ko, ki, vo, vi = cache.outliers()
+    return layout.pack_tiles_sparse(*dense, ko, ki, vo.reshape(S, nt, 32, 4), vi.reshape(S, nt, 32, 4))
 
 
 def records_from_device(tiles, n_tiles: int, slices=None) -> np.ndarray:
-    """GPU tile array [B, H, max_tiles, 3072] -> numpy [S, n_tiles, 3072] (optionally only slice indices)."""
+    """GPU tile array [B, H, max_tiles, record] -> numpy [S, n_tiles, record] (optionally only slice indices)."""
     B, H = tiles.shape[:2]
-    t = tiles[:, :, :n_tiles].reshape(B * H, n_tiles, 3072)
+    t = tiles[:, :, :n_tiles].reshape(B * H, n_tiles, tiles.shape[-1])
     if slices is not None:
         t = t[list(slices)]
     return t.cpu().numpy()
@@ -33,8 +38,10 @@ def first_mismatch(a: np.ndarray, b: np.ndarray) -> str:
     if len(idx) == 0:
         return "identical"
     s, t, off = idx[0][0], idx[0][1], idx[0][-1]
-    field = ["k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"][
-        0 if off < 1024 else 1 if off < 2048 else 2 + (off - 2048) // 256]
+    bounds = [(0, "k_codes"), (1024, "v_codes"), (2048, "k_scale"), (2304, "k_zero"), (2560, "v_scale"),
+              (2816, "v_zero"), (3072, "k_outlier"), (3328, "k_outlier_token"), (3456, "v_outlier"),
+              (3712, "v_outlier_channel")]
+    field = [name for start, name in bounds if off >= start][-1]
     return f"{len(idx)} bytes differ; first at slice {s} tile {t} byte {off} ({field}): gpu {a[tuple(idx[0])]} oracle {b[tuple(idx[0])]}"
 
 

@@ -71,8 +71,9 @@ def test_shape_validation(kvq):
         (dict(bits=3), kvq.E_BITS), (dict(bits=8), kvq.E_BITS), (dict(head_dim=64), kvq.E_SHAPE),
         (dict(group=16), kvq.E_SHAPE), (dict(q_heads=3), kvq.E_SHAPE), (dict(residual_cap=100), kvq.E_SHAPE),
         (dict(residual_cap=0), kvq.E_SHAPE), (dict(max_tokens=1000), kvq.E_SHAPE), (dict(batch=0), kvq.E_SHAPE),
-        # flags belong to the 4-bit variant; unknown bits and a missing rotary base are rejected
-        (dict(flags=kvq.FLAG_SINK), kvq.E_SHAPE), (dict(flags=kvq.FLAG_SPARSE), kvq.E_SHAPE),
+        # 2-bit caches take dense-and-sparse groups only; unknown bits and a missing rotary base are rejected
+        (dict(flags=kvq.FLAG_SINK), kvq.E_SHAPE), (dict(flags=kvq.FLAG_PRE_ROPE, rope_base=10000.0), kvq.E_SHAPE),
+        (dict(flags=kvq.FLAG_SPARSE | kvq.FLAG_SINK), kvq.E_SHAPE), (dict(flags=kvq.FLAG_SPARSE | 8), kvq.E_SHAPE),
         (dict(bits=4, flags=8), kvq.E_SHAPE), (dict(bits=4, flags=kvq.FLAG_SPARSE | 16), kvq.E_SHAPE),
         (dict(bits=4, flags=kvq.FLAG_PRE_ROPE, rope_base=0.0), kvq.E_SHAPE),
         (dict(bits=4, flags=kvq.FLAG_PRE_ROPE, rope_base=1.0), kvq.E_SHAPE),
@@ -286,3 +287,16 @@ def test_noalloc_decode_rejects_partials_beyond_its_scratch(kvq):
     empty = _cache(kvq)
     assert lib.kv_decode_attention_noalloc(ctypes.byref(shape), ctypes.byref(empty), ctypes.c_void_p(FAKE), 0.0,
                                            ctypes.c_void_p(FAKE + 16), None) == kvq.E_EMPTY
+
+
+def test_two_bit_sparse_shape_is_accepted_on_the_host(kvq):
+    """2-bit dense-and-sparse caches pass the host checks (split plan and workspace computed, no launch), take
+    3840-byte records, and are refused by the ragged calls."""
+    lib = kvq.library()
+    s = _shape(kvq, flags=kvq.FLAG_SPARSE)
+    c = _cache(kvq)
+    c.n_quant, c.n_resid = 512, 17
+    assert lib.kv_decode_attention_splits(ctypes.byref(s), ctypes.byref(c)) > 0
+    assert lib.kv_decode_attention_workspace_bytes(ctypes.byref(s), ctypes.byref(c)) > 0
+    assert kvq.Shape(2, 2, 8, max_tokens=1024, flags=kvq.FLAG_SPARSE).record_bytes == kvq.RECORD_BYTES_SPARSE == 3840
+    assert lib.kv_ragged_splits(ctypes.byref(s)) == 0
