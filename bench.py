@@ -34,6 +34,7 @@ import sys
 import time
 
 METRIC = "2-bit KV decode attention: KV tokens/s and achieved HBM GB/s (% of peak)"
+METRIC_SPARSE = "2-bit KV decode attention with dense-and-sparse groups: KV tokens/s and achieved HBM GB/s (% of peak)"
 METRIC_4BIT = "4-bit pre-RoPE KV decode attention with sink: KV tokens/s and achieved HBM GB/s (% of peak)"
 METRIC_4BIT_SPARSE = ("4-bit pre-RoPE KV decode attention with sink and dense-and-sparse groups: KV tokens/s and "
                       "achieved HBM GB/s (% of peak)")
@@ -47,6 +48,8 @@ TRAFFIC = {
                           [os.path.join(CSRC, "kvq_kernels.hip")] + _COMMON),
     "kvquant_4bit_16k": (os.path.join(ROOT, "profiles", "decode_b4_pass1_traffic_kvquant_4bit_16k.json"),
                          [os.path.join(CSRC, "kvq_kernels_b4.hip")] + _COMMON),
+    "llama3_8b_gqa_32k_sparse": (os.path.join(ROOT, "profiles", "decode_pass1_sparse_traffic_llama3_8b_gqa_32k_sparse.json"),
+                                 [os.path.join(CSRC, "kvq_kernels.hip")] + _COMMON),
     "kvquant_4bit_sparse_16k": (os.path.join(ROOT, "profiles",
                                              "decode_b4_pass1_traffic_kvquant_4bit_sparse_16k.json"),
                                 [os.path.join(CSRC, "kvq_kernels_b4.hip")] + _COMMON),
@@ -60,10 +63,11 @@ def log(*a):
 def algorithmic_bytes(batch, kv_heads, q_heads, n_quant, n_resid, head_dim=128, bits=2, n_sink=0, sparse=False):
     """Bytes one decode-attention call must move: per quantized token and KV head 96 B at 2 bits (32 B key codes,
     32 B value codes, 16 B key scale/zero, 16 B value scale/zero) or 160 B at 4 bits (64 + 64 + 16 + 16), plus 24 B
-    with dense-and-sparse groups (a tile's 768-byte outlier section over 32 tokens), per window token 512 B of fp16
+    with dense-and-sparse groups (a tile's 768-byte outlier section over 32 tokens: 120 B at 2 bits), per window
+    token 512 B of fp16
     K and V, per sink token 336 B (fp16 key, value codes, value scale/zero; 348 B with the value outliers), the fp16
     query and the fp32 output. Each KV slice counts once, however many query heads read it."""
-    per_q = 96 if bits == 2 else (184 if sparse else 160)
+    per_q = (120 if sparse else 96) if bits == 2 else (184 if sparse else 160)
     per_sink = 348 if sparse else 336
     return (batch * kv_heads * (n_quant * per_q + n_resid * 2 * head_dim * 2 + n_sink * per_sink)
             + batch * q_heads * head_dim * 2 + batch * q_heads * head_dim * 4)
@@ -574,7 +578,8 @@ def measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=True):
                   "P V on fp16 MFMA (probabilities as fp16 hi+lo), fp32 accumulation")
         kernel = "decode_b4_pass1_kernel + decode_pass2_kernel (one kv_decode_attention call)"
     res = {
-        "metric": METRIC if w.bits == 2 else (METRIC_4BIT_SPARSE if w.sparse else METRIC_4BIT),
+        "metric": (METRIC_SPARSE if w.sparse else METRIC) if w.bits == 2 else (METRIC_4BIT_SPARSE if w.sparse
+                                                                              else METRIC_4BIT),
         "value": value,
         "unit": "KV tokens/s",
         "n_gpus": 1,
@@ -717,7 +722,7 @@ def step_record(kvq, kdev, kvsynth, torch, w, W, K, rot):
                                  "row written; the graph's mean over all timed steps, flush steps included"}}
 
 
-SUB_WORKLOADS = ("kvquant_4bit_16k", "long_1m", "llama2_7b_stream")
+SUB_WORKLOADS = ("kvquant_4bit_16k", "llama3_8b_gqa_32k_sparse", "long_1m", "llama2_7b_stream")
 
 
 def main(argv=None):

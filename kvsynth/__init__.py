@@ -128,6 +128,11 @@ WORKLOADS = {
     # Llama-3-8B-shaped GQA decode at 32K context.
     "llama3_8b_gqa_32k": Workload("llama3_8b_gqa_32k", 64, 32, 8, 32768, 32767, 1, 1003, 6, 20.0,
                                   notes="B64 Hq32 Hkv8 D128 N32768, K outliers 6 ch x20"),
+    # The GQA 32K cache with 2-bit dense-and-sparse groups (one fp16 outlier per group of 32).
+    "llama3_8b_gqa_32k_sparse": Workload("llama3_8b_gqa_32k_sparse", 64, 32, 8, 32768, 32767, 1, 1003, 6, 20.0,
+                                         sparse=True,
+                                         notes="llama3_8b_gqa_32k with dense-and-sparse groups: per key channel and "
+                                               "value token group of 32, the largest element kept in fp16"),
     # One sequence of 1,048,576 tokens, 32 heads.
     "long_1m": Workload("long_1m", 1, 32, 32, 1048576, 1048575, 1, 1004, 4, 20.0,
                         notes="B1 H32 D128 N1048576, K outliers 4 ch x20"),
