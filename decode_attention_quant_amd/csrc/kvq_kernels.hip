@@ -525,24 +525,34 @@ constexpr int LDS_BYTES = LDS_P + 4 * P_ROW * 8;    // [0, 8192) also holds the 
 // sums (H, L) of the key outliers per (head, token) inside the window-tile region, which the quantized loop leaves
 // free; the value-outlier sums per (head, channel) after the probability exchange.
 constexpr int LDS_OUT = 3456;        // the record's bytes 3072..3839
-constexpr int LDS_KACC = 4224;       // int2 [4 heads][32 tokens]
-constexpr int LDS_VACC = LDS_BYTES;  // int2 [4 heads][128 channels]
-constexpr int LDS_BYTES_SPARSE = LDS_VACC + 4 * 128 * 8;
-static_assert(LDS_OUT >= LDS_BETA + 16 && LDS_KACC + 1024 <= 8192, "sparse regions inside the free window region");
+// Every row of 32 sums (int64) is padded to 33, so the banks of one target differ between heads and groups and a
+// wave's atomics spread over the banks.
+constexpr int KROW = 33, KSUMS = 4 * KROW;             // [4 heads][33]
+constexpr int VROW = 33, VSUMS = 16 * VROW;            // [4 heads][4 groups][33]
+constexpr int LDS_KACC = 4224;       // int64 [4 heads][KROW]: key-outlier sums per (head, token)
+constexpr int LDS_VACC = LDS_BYTES;  // int64 [4 heads][4 groups][VROW]: value-outlier sums per (head, channel)
+constexpr int LDS_BYTES_SPARSE = LDS_VACC + VSUMS * 8;
+static_assert(LDS_OUT >= LDS_BETA + 16 && LDS_KACC + KSUMS * 8 <= 8192, "sparse regions inside the free window region");
+static_assert(LDS_KACC % 8 == 0 && LDS_VACC % 8 == 0, "64-bit sums");
 // Exact sums of corrections through integer LDS atomics (float LDS atomics cost some thirty times an integer one on
 // this chip). Every correction is below 2^17 in magnitude (a query scaled below 1 or a probability at most 1, times
-// the difference of two binary16 values), so x = H 2^-6 + L 2^-29 + e with integers |H|, |L| < 2^23 and |e| < 2^-29;
-// up to 128 terms per target keep the sums of H and L within int32.
-__device__ __forceinline__ void fix_split(float x, int32_t &H, int32_t &L) {
+// the difference of two binary16 values), so x = H 2^-6 + L 2^-29 + e with integers |H|, |L| < 2^23 and |e| < 2^-29,
+// and X = H 2^23 + L is x 2^29 truncated to an integer, |X| < 2^46: up to 128 terms per target stay far inside int64,
+// added by one 64-bit atomic per term.
+__device__ __forceinline__ int64_t fix_split(float x) {
 #pragma clang fp contract(off)
-    H = (int32_t)(x * 64.0f);
+    const int32_t H = (int32_t)(x * 64.0f);
     const float r = __builtin_fmaf(-(float)H, 0x1p-6f, x);   // exact: the low bits of x
-    L = (int32_t)(r * 0x1p29f);
+    const int32_t L = (int32_t)(r * 0x1p29f);
+    return (int64_t)H * 8388608 + L;
 }
-__device__ __forceinline__ float fix_join(int2 hl) { return __builtin_fmaf((float)hl.x, 0x1p-6f, (float)hl.y * 0x1p-29f); }
-__device__ __forceinline__ void lds_add2(int32_t *p, int32_t h, int32_t lo) {
-    __hip_atomic_fetch_add(p, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-    __hip_atomic_fetch_add(p + 1, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+__device__ __forceinline__ float fix_join(int64_t X) {
+    const int32_t hi = (int32_t)(X >> 32);
+    const uint32_t lo = (uint32_t)X;
+    return __builtin_fmaf((float)hi, 0x1p3f, (float)lo * 0x1p-29f);   // 2^32 2^-29 = 2^3
+}
+__device__ __forceinline__ void lds_add64(int64_t *p, int64_t x) {
+    __hip_atomic_fetch_add(p, x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // byte offset of metadata byte x (0..1023 of a record's scale/zero section) in the staged copy
@@ -752,12 +762,11 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
         p[2] = pb[0]; p[6] = pb[1]; p[3] = pb[2]; p[7] = pb[3];
     };
 
-    int2 *kacc = reinterpret_cast<int2 *>(smem + LDS_KACC);
-    int2 *vacc = reinterpret_cast<int2 *>(smem + LDS_VACC);
+    int64_t *kacc = reinterpret_cast<int64_t *>(smem + LDS_KACC);
+    int64_t *vacc = reinterpret_cast<int64_t *>(smem + LDS_VACC);
     if constexpr (SPARSE) {
-        reinterpret_cast<int4 *>(kacc)[l] = int4{0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) reinterpret_cast<int4 *>(vacc)[l + 64 * i] = int4{0, 0, 0, 0};
+        for (int i = l; i < KSUMS; i += 64) kacc[i] = 0;
+        for (int i = l; i < VSUMS; i += 64) vacc[i] = 0;
         wave_lds_order();
     }
 
@@ -774,15 +783,13 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
         if constexpr (SPARSE) {
             const h8 ok = *reinterpret_cast<const h8 *>(smem + LDS_OUT + 16 * n);
             const uint2 uk = *reinterpret_cast<const uint2 *>(smem + LDS_OUT + 256 + 8 * n);
-            int32_t *ka = reinterpret_cast<int32_t *>(kacc) + 64 * kc;
+            const int krow = KROW * kc;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float qe = (float)qf[e];
                 const float corr = __builtin_fmaf(qe, (float)ok[e], -(qe * (float)zk[e]));   // q' o and q' z exact
-                int32_t H, L;
-                fix_split(corr, H, L);
                 const uint32_t u = ((e < 4 ? uk.x : uk.y) >> (8 * (e & 3))) & 31u;
-                lds_add2(ka + 2 * u, H, L);
+                lds_add64(kacc + krow + u, fix_split(corr));
             }
         }
         const h8 hi = qf * sk;
@@ -823,12 +830,12 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
         f4 ci = {beta_lds[kc] - mr, 0.0f, 0.0f, 0.0f};
         f4 acc0 = ci, acc1 = ci;    // tokens n (acc0) and 16 + n (acc1); rows (head kc, part r)
         if constexpr (SPARSE) {   // the key-outlier sums of tokens n and 16 + n of head kc, then cleared
-            int2 *kr = kacc + 32 * kc;
-            acc0[0] += fix_join(kr[n]);
-            acc1[0] += fix_join(kr[16 + n]);
+            int64_t *kr = kacc + KROW * kc + n;
+            acc0[0] += fix_join(kr[0]);
+            acc1[0] += fix_join(kr[16]);
             wave_lds_order();
-            kr[n] = int2{0, 0};
-            kr[16 + n] = int2{0, 0};
+            kr[0] = 0;
+            kr[16] = 0;
         }
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -868,14 +875,12 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
             const h4 ov1 = *reinterpret_cast<const h4 *>(os + 384 + 64 * g + 32 + 8 * kc);
             const uint32_t oi0 = *reinterpret_cast<const uint32_t *>(os + 640 + 32 * g + 4 * kc);
             const uint32_t oi1 = *reinterpret_cast<const uint32_t *>(os + 640 + 32 * g + 16 + 4 * kc);
-            int32_t *va = reinterpret_cast<int32_t *>(vacc) + 2 * (128 * hl + 32 * g);
+            const int vrow = VROW * (4 * hl + g);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const float d = (i < 4 ? (float)ov0[i] - (float)zv0[i] : (float)ov1[i - 4] - (float)zv1[i - 4]);
-                int32_t H, L;
-                fix_split(p[i] * d, H, L);
                 const uint32_t c = ((i < 4 ? oi0 : oi1) >> (8 * (i & 3))) & 31u;
-                lds_add2(va + 2 * c, H, L);
+                lds_add64(vacc + vrow + c, fix_split(p[i] * d));
             }
         }
         if constexpr (G1) {
@@ -893,15 +898,16 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
         vw = reinterpret_cast<const uint4 *>(next + 1024)[l];
         if constexpr (SPARSE) {   // head kc's value-outlier sums of channels n + 16 j, then cleared (G1: row 0 only)
             wave_lds_order();
-            int2 *vr = vacc + 128 * kc + n;
+            // channel n + 16 j of head kc: group j / 2, index n + 16 (j % 2) within it
+            int64_t *vr = vacc + VROW * 4 * kc + n;
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const float corr = fix_join(vr[16 * j]);
+                const float corr = fix_join(vr[VROW * (j >> 1) + 16 * (j & 1)]);
                 if (!G1 || kc == 0) o[j][j >> 1] += corr;
             }
             wave_lds_order();
 #pragma unroll
-            for (int j = 0; j < 8; ++j) vr[16 * j] = int2{0, 0};
+            for (int j = 0; j < 8; ++j) vr[VROW * (j >> 1) + 16 * (j & 1)] = 0;
         }
         // every LDS read of this tile has been issued: overwrite with the next tile (after the last tile, with
         // that tile again; unconditional, so no load sits on only one path of the loop)
@@ -1085,7 +1091,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void
     decode_pass1_body<MODE, G1, false>(a, smem);
 }
 
-// dense-and-sparse records: three wavefronts per SIMD (12.6 KB of LDS, up to 168 registers)
+// dense-and-sparse records: three wavefronts per SIMD (12.7 KB of LDS, up to 168 registers)
 template <bool G1>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 3))) void decode_pass1_sparse_kernel(DecodeArgs a) {
     __shared__ __align__(16) unsigned char smem[LDS_BYTES_SPARSE];
