@@ -1,7 +1,8 @@
 """GPU parity of decode attention on the quantizer's edge cases, 2-bit and 4-bit, through the C ABI against the fp64
 CPU oracle.
 
-The quantizer's degenerate groups reach attention here, not only the packed records:
+The quantizer's degenerate groups reach attention here, not only the packed records (2-bit with and without
+dense-and-sparse groups, 4-bit with three flag sets):
 - constant key groups and all-zero (and -0) groups: s = 0, every code 0, a score is the zero-point term alone;
 - keys offset by 1000 (fp16 steps of 0.5): the zero-point term dominates every score, and the scores of all tokens
   sit near one large common value;
@@ -111,18 +112,19 @@ def _tolerance(v: np.ndarray) -> float:
     return 2e-3 * max(1.0, vmax / 8.0)
 
 
+@pytest.mark.parametrize("sparse", [False, True], ids=["dense", "dense-and-sparse"])
 @pytest.mark.parametrize("kind", KINDS)
-def test_decode_2bit_edge_inputs(kvq, kind):
+def test_decode_2bit_edge_inputs(kvq, kind, sparse):
     B, Hq, Hkv, N = 2, 8, 2, 1187          # 1152 quantized tokens (36 tiles) and a ragged window of 35
-    say(f"[edge2] {kind} B={B} Hq={Hq} Hkv={Hkv} N={N}")
-    rng = np.random.default_rng(zlib.crc32(kind.encode()))
+    say(f"[edge2] {kind} sparse={sparse} B={B} Hq={Hq} Hkv={Hkv} N={N}")
+    rng = np.random.default_rng(zlib.crc32(kind.encode()) + (100 if sparse else 0))
     k, v = _keys_values(rng, kind, (B, Hkv, N, 128))
     q = rng.standard_normal((B, Hq, 128)).astype(np.float16)
-    cache = kvq.KVCache(kvq.Shape(B, Hkv, Hq, max_tokens=1280))
+    cache = kvq.KVCache(kvq.Shape(B, Hkv, Hq, max_tokens=1280, flags=kvq.FLAG_SPARSE if sparse else 0))
     kvq.kv_append_and_flush(cache, _dev(k), _dev(v))
     out = kvq.kv_decode_attention(cache, _dev(q))
     torch.cuda.synchronize()
-    ref = oc.SliceCache(B * Hkv)
+    ref = oc.SliceCache(B * Hkv, sparse=sparse)
     oc.append_block(ref, k.reshape(B * Hkv, N, 128), v.reshape(B * Hkv, N, 128))
     assert (cache.n_quant, cache.n_resid) == (ref.n_quant, ref.n_resid)
     want = oa.decode_attention(ref, q, B, Hkv)

@@ -106,3 +106,20 @@ def test_noalloc_rejects_partials_beyond_the_scratch(kvq):
     rc = lib.kv_decode_attention_noalloc(ctypes.byref(shape), ctypes.byref(cache), ctypes.c_void_p(fake),
                                          0.0, ctypes.c_void_p(fake + 4096), None)
     assert rc == kvq.E_SCRATCH
+
+
+def test_noalloc_2bit_dense_and_sparse(kvq):
+    """The allocation-free call on a 2-bit dense-and-sparse cache equals the workspace call bit for bit."""
+    rng = np.random.default_rng(73)
+    B, Hq, Hkv, N = 3, 12, 3, 900
+    k = rng.standard_normal((B, Hkv, N, 128)).astype(np.float32)
+    k[rng.random(k.shape) < 0.01] *= 30
+    v = rng.standard_normal((B, Hkv, N, 128)).astype(np.float16)
+    q = rng.standard_normal((B, Hq, 128)).astype(np.float16)
+    cache = kvq.KVCache(kvq.Shape(B, Hkv, Hq, max_tokens=1024, flags=kvq.FLAG_SPARSE))
+    kvq.kv_append_and_flush(cache, _dev(k.astype(np.float16)), _dev(v))
+    want = kvq.kv_decode_attention(cache, _dev(q))
+    got = torch.full_like(want, float("nan"))
+    kvq.kv_decode_attention_noalloc(cache, _dev(q), got)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
