@@ -602,6 +602,7 @@ def measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=True):
         "append_us_max": 1e3 * max(append_ms),
         "splits": splits,
         "decode_call_us_p10_p50_p90": [pct(0.1), pct(0.5), pct(0.9)],
+        "decode_call_us_series": [round(1e3 * x, 1) for x in decode_ms] if K <= 256 else None,
         "engine_clock": clk,
         "prefill": {"tokens": P, "us": prefill_us, "bytes": prefill_bytes,
                     "gb_s": prefill_bytes / prefill_us / 1e3,
