@@ -291,7 +291,7 @@ def fp16_comparator(kvq, w, Kd, Vd, q, context, call_us_2bit, calls):
     log(f"[bench] fp16 comparator: {context} fp16 tokens, {us:.1f} us per call, {nbytes / us / 1e3:.0f} GB/s")
     return {"context": context, "decode_call_us": us, "bytes_per_call": nbytes, "hbm_gb_s": nbytes / us / 1e3,
             "pct_of_peak": 100.0 * nbytes / us / 1e3 / PEAK_GBS, "kv_tokens_per_s": w.batch * context / (us * 1e-6),
-            "speedup_2bit_over_fp16": us / call_us_2bit,
+            "speedup_2bit_over_fp16": us / call_us_2bit if call_us_2bit else None,
             "note": "same library and kernel over a window as large as the context (no quantized tiles)"}
 
 
@@ -474,10 +474,12 @@ def step_graph(args, kvq, kdev, kvsynth, torch):
     return 0
 
 
-def measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=True):
+def measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=True, before_timed=None):
     """One workload: prefill (timed as one append), W warm-up steps, then K timed steps, each one token appended to
     every sequence and one decode-attention call, with HIP events around every append and every call on the current
-    stream. Returns the record and the device tensors the extras reuse."""
+    stream. `before_timed(state)`, if given, runs after the prefill and before the warm-up steps (other measurements
+    of the same run) and returns entries for the record. Returns the record and the device tensors the extras
+    reuse."""
     R = w.residual
     P = w.context - W - 1                      # first timed step attends over exactly w.context tokens
     total = P + W + K
@@ -522,6 +524,8 @@ def measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=True):
             kvq.ctypes.byref(cache._cshape), kvq.ctypes.byref(probe))))
     workspace = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     out = torch.empty((w.batch, w.q_heads, 128), dtype=torch.float32, device="cuda")
+    before = before_timed({"cache": cache, "Kd": Kd, "Vd": Vd, "Q": Q, "out": out, "workspace": workspace}) \
+        if before_timed is not None else {}
 
     def step(i):
         t = P + i
@@ -613,6 +617,7 @@ def measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=True):
                      "frac": achieved / PEAK_GBS, "traffic": traffic_per_launch(w.name),
                      "kernel": kernel, "bytes_per_call": sum(call_bytes) / K},
     }
+    res.update(before)
     state = {"Kd": Kd, "Vd": Vd, "Q": Q, "cache": cache, "contexts": contexts}
     return res, state
 
@@ -741,6 +746,8 @@ def main(argv=None):
     ap.add_argument("--no-sub-records", action="store_true",
                     help="measure only the headline workload (else also " + ", ".join(SUB_WORKLOADS) + ")")
     ap.add_argument("--fp16-calls", type=int, default=20)
+    ap.add_argument("--cold-calls", type=int, default=20,
+                    help="decode calls timed right after the prefill, before the warm-up steps (0: none)")
     ap.add_argument("--step-graph", action="store_true",
                     help="decode-step time: host API vs ragged step vs ragged step in a HIP graph "
                          "(default workload llama2_7b_stream)")
@@ -781,17 +788,54 @@ def main(argv=None):
 
     w = kvsynth.WORKLOADS[args.workload]
     W, K = args.warmup, args.steps
-    res, st = measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=not args.no_clock)
+
+    def before_timed(s):
+        """The run's other measurements, between the prefill and the warm-up steps: the decode calls right after
+        the prefill (no appends), the streaming-read ceiling and the fp16 comparator."""
+        extra = {}
+        cache = s["cache"]
+        nbytes = algorithmic_bytes(w.batch, w.kv_heads, w.q_heads, cache.n_quant, cache.n_resid, bits=w.bits,
+                                   n_sink=cache.n_sink, sparse=w.sparse)
+        n = args.cold_calls
+        if n > 0:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+            ev[0].record()
+            for i in range(n):
+                kvq.kv_decode_attention(cache, s["Q"][0], out=s["out"], workspace=s["workspace"])
+                ev[i + 1].record()
+            torch.cuda.synchronize()
+            us = [1e3 * ev[i].elapsed_time(ev[i + 1]) for i in range(n)]
+            srt = sorted(us)
+            pick = lambda f: srt[min(n - 1, int(f * (n - 1) + 0.5))]
+            extra["cold_start"] = {
+                "calls": n, "context": cache.n_tokens, "decode_call_us": sum(us) / n,
+                "decode_call_us_p10_p50_p90": [pick(0.1), pick(0.5), pick(0.9)],
+                "hbm_gb_s": nbytes / (sum(us) / n) / 1e3, "pct_of_peak": 100.0 * nbytes / (sum(us) / n) / 1e3
+                / PEAK_GBS, "decode_call_us_series": [round(u, 1) for u in us],
+                "note": "the first decode calls after the prefill and the host-side input generation, the same call "
+                        "on the prefilled cache with no appends in between; the engine clock drops a few calls in "
+                        "and recovers over tens of calls"}
+            log(f"[bench] {n} calls right after the prefill: avg {sum(us) / n:.1f} us "
+                f"({nbytes / (sum(us) / n) / 1e3:.0f} GB/s)")
+        if not args.no_hbm_ceiling:
+            extra["hbm_read_ceiling"] = hbm_read_ceiling(nbytes)
+        if not args.no_fp16_comparator and w.bits == 2:
+            extra["fp16_comparator"] = fp16_comparator(kvq, w, s["Kd"], s["Vd"], s["Q"][W], w.context, None,
+                                                       args.fp16_calls)
+        return extra
+
+    res, st = measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=not args.no_clock, before_timed=before_timed)
     achieved = res["hbm_gb_s"]
-    if not args.no_hbm_ceiling:
-        ceil = hbm_read_ceiling(res["roofline"]["bytes_per_call"])
+    if "hbm_read_ceiling" in res:
+        ceil = res["hbm_read_ceiling"]
         ceil["decode_frac_of_ceiling"] = achieved / ceil["gb_s"]
-        res["hbm_read_ceiling"] = ceil
         log(f"[bench] streaming-read ceiling {ceil['gb_s']:.0f} GB/s ({100 * ceil['frac_of_peak']:.1f}% of "
             f"{PEAK_GBS:.0f}); the decode call reaches {100 * ceil['decode_frac_of_ceiling']:.1f}% of it")
-    if not args.no_fp16_comparator and w.bits == 2:
-        res["fp16_comparator"] = fp16_comparator(kvq, w, st["Kd"], st["Vd"], st["Q"][W], st["contexts"][0],
-                                                 res["decode_call_us"], args.fp16_calls)
+    if "fp16_comparator" in res:
+        res["fp16_comparator"]["speedup_2bit_over_fp16"] = res["fp16_comparator"]["decode_call_us"] / \
+            res["decode_call_us"]
+    res["measurement_order"] = ("input generation and upload; prefill; cold_start calls; hbm_read_ceiling; "
+                                "fp16_comparator; warm-up steps; timed steps; sub-record workloads; cpu_baseline")
     Qcpu = [st["Q"][W + j].cpu().numpy() for j in range(min(args.cpu_queries, K))]
     del st
     torch.cuda.empty_cache()

@@ -22,10 +22,10 @@ def _filled(bits=2, sparse=False, sink=False, tokens=160):
     return c
 
 
-@pytest.mark.parametrize("bits,sparse", [(2, False), (4, False), (4, True)])
+@pytest.mark.parametrize("bits,sparse", [(2, False), (2, True), (4, False), (4, True)])
 def test_quantized_bytes_per_token_are_the_packed_record_size(bits, sparse):
     """Per quantized token and KV head the call reads one 32-token tile record: the oracle's packed record bytes
-    over 32 (2-bit 3072 B, 4-bit 5120 B, with the outlier section 5888 B)."""
+    over 32 (2-bit 3072 B, 4-bit 5120 B; with the outlier section 3840 B and 5888 B)."""
     c = _filled(bits, sparse)
     rec = helpers.oracle_records(c) if bits == 2 else helpers.oracle_records4(c)
     assert rec.shape[:2] == (1, c.n_quant // 32)
