@@ -474,12 +474,14 @@ def step_graph(args, kvq, kdev, kvsynth, torch):
     return 0
 
 
-def measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=True, before_timed=None):
+def measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=True, before_timed=None, settle_calls=0):
     """One workload: prefill (timed as one append), W warm-up steps, then K timed steps, each one token appended to
     every sequence and one decode-attention call, with HIP events around every append and every call on the current
     stream. `before_timed(state)`, if given, runs after the prefill and before the warm-up steps (other measurements
-    of the same run) and returns entries for the record. Returns the record and the device tensors the extras
-    reuse."""
+    of the same run) and returns entries for the record. With settle_calls > 0, that many further decode calls on the
+    final cache (no appends) follow the timed steps, each timed, and are reported apart (`settled`): the rate once the
+    engine clock has left the slow stretch that follows the prefill. Returns the record and the device tensors the
+    extras reuse."""
     R = w.residual
     P = w.context - W - 1                      # first timed step attends over exactly w.context tokens
     total = P + W + K
@@ -570,6 +572,28 @@ def measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=True, before_timed=
     dsorted = sorted(decode_ms)
     pct = lambda f: 1e3 * dsorted[min(K - 1, int(f * (K - 1) + 0.5))]
     clk = probe_clock.result() if probe_clock is not None else None
+
+    settled = None
+    if settle_calls > 0:   # after the timed region: does not enter value, ms_per_step or the roofline
+        sev = [torch.cuda.Event(enable_timing=True) for _ in range(settle_calls + 1)]
+        sev[0].record()
+        for i in range(settle_calls):
+            kvq.kv_decode_attention(cache, Q[W + K - 1], out=out, workspace=workspace)
+            sev[i + 1].record()
+        torch.cuda.synchronize()
+        sus = [1e3 * sev[i].elapsed_time(sev[i + 1]) for i in range(settle_calls)]
+        tail = sus[settle_calls // 2:]
+        sb = call_bytes[-1]
+        settled = {"calls": settle_calls, "context": cache.n_tokens,
+                   "decode_call_us_all": sum(sus) / settle_calls,
+                   "decode_call_us_second_half": sum(tail) / len(tail),
+                   "hbm_gb_s_second_half": sb / (sum(tail) / len(tail)) / 1e3,
+                   "pct_of_peak_second_half": 100.0 * sb / (sum(tail) / len(tail)) / 1e3 / PEAK_GBS,
+                   "decode_call_us_series": [round(u, 1) for u in sus],
+                   "note": "decode calls on the cache of the last timed step, no appends, after the timed region "
+                           "(not part of value); the second half is the rate once the clock has recovered"}
+        log(f"[bench] {settle_calls} further calls after the timed steps: second half avg "
+            f"{settled['decode_call_us_second_half']:.1f} us ({settled['hbm_gb_s_second_half']:.0f} GB/s)")
     log(f"[bench] {w.name}: {K} steps in {total_ms:.3f} ms; decode call avg {1e3 * sum(decode_ms) / K:.1f} us "
         f"({achieved:.0f} GB/s); append avg {1e3 * sum(append_ms) / K:.1f} us, max {1e3 * max(append_ms):.1f} us; "
         f"splits={splits}" + (f"; engine clock {clk['ghz_mean']:.2f} GHz" if clk else ""))
@@ -618,6 +642,8 @@ def measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=True, before_timed=
                      "kernel": kernel, "bytes_per_call": sum(call_bytes) / K},
     }
     res.update(before)
+    if settled is not None:
+        res["settled"] = settled
     state = {"Kd": Kd, "Vd": Vd, "Q": Q, "cache": cache, "contexts": contexts}
     return res, state
 
@@ -746,6 +772,8 @@ def main(argv=None):
     ap.add_argument("--no-sub-records", action="store_true",
                     help="measure only the headline workload (else also " + ", ".join(SUB_WORKLOADS) + ")")
     ap.add_argument("--fp16-calls", type=int, default=20)
+    ap.add_argument("--settle-calls", type=int, default=160,
+                    help="decode calls timed after the timed steps, reported apart as `settled` (0: none)")
     ap.add_argument("--cold-calls", type=int, default=20,
                     help="decode calls timed right after the prefill, before the warm-up steps (0: none)")
     ap.add_argument("--step-graph", action="store_true",
@@ -824,7 +852,8 @@ def main(argv=None):
                                                        args.fp16_calls)
         return extra
 
-    res, st = measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=not args.no_clock, before_timed=before_timed)
+    res, st = measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=not args.no_clock, before_timed=before_timed,
+                             settle_calls=args.settle_calls)
     achieved = res["hbm_gb_s"]
     if "hbm_read_ceiling" in res:
         ceil = res["hbm_read_ceiling"]
@@ -835,7 +864,8 @@ def main(argv=None):
         res["fp16_comparator"]["speedup_2bit_over_fp16"] = res["fp16_comparator"]["decode_call_us"] / \
             res["decode_call_us"]
     res["measurement_order"] = ("input generation and upload; prefill; cold_start calls; hbm_read_ceiling; "
-                                "fp16_comparator; warm-up steps; timed steps; sub-record workloads; cpu_baseline")
+                                "fp16_comparator; warm-up steps; timed steps; settled calls; sub-record workloads; "
+                                "cpu_baseline")
     Qcpu = [st["Q"][W + j].cpu().numpy() for j in range(min(args.cpu_queries, K))]
     del st
     torch.cuda.empty_cache()
