@@ -532,6 +532,12 @@ constexpr int VROW = 33, VSUMS = 16 * VROW;            // [4 heads][4 groups][33
 constexpr int LDS_KACC = 4224;       // int64 [4 heads][KROW]: key-outlier sums per (head, token)
 constexpr int LDS_VACC = LDS_BYTES;  // int64 [4 heads][4 groups][VROW]: value-outlier sums per (head, channel)
 constexpr int LDS_BYTES_SPARSE = LDS_VACC + VSUMS * 8;
+// 256 zero bytes after each kernel's LDS, read by the score operand's unused rows; placed in banks the folded-query
+// rows of the same reads do not use
+template <bool SPARSE>
+constexpr int lds_zero() { return SPARSE ? LDS_BYTES_SPARSE + 64 : LDS_BYTES; }
+template <bool SPARSE>
+constexpr int lds_total() { return lds_zero<SPARSE>() + 256; }
 static_assert(LDS_OUT >= LDS_BETA + 16 && LDS_KACC + KSUMS * 8 <= 8192, "sparse regions inside the free window region");
 static_assert(LDS_KACC % 8 == 0 && LDS_VACC % 8 == 0, "64-bit sums");
 // Exact sums of corrections through integer LDS atomics (float LDS atomics cost some thirty times an integer one on
@@ -809,9 +815,11 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
     // Each code word is reloaded for the next tile right after its last use in this one (scales: at the top of the
     // iteration, key codes after the score contraction, value codes after PV), so no register holds two tiles. On
     // the last tile the index is clamped: the reload hits the just-read record in cache.
-    // A operand row n = 4 h + r: head h, high part (r = 0), low part (r = 1); rows r = 2, 3 read rows 0, 1 again
-    // (their outputs are never used), so all 16 lanes of a row group read distinct or identical addresses
-    const _Float16 *qta = qt_lds + QT_ROW * (4 * (n & 1) + hl) + 8 * kc;
+    // A operand row n = 4 h + r: head h, high part (r = 0), low part (r = 1); rows r = 2, 3 (outputs never used) read
+    // a zero row: zero operands draw less power than repeated ones, and the clock this kernel runs at is power-limited
+    const _Float16 *qta = (n & 2) ? reinterpret_cast<const _Float16 *>(smem + lds_zero<SPARSE>()) + 8 * kc
+                                  : qt_lds + QT_ROW * (4 * (n & 1) + hl) + 8 * kc;
+    reinterpret_cast<uint32_t *>(smem + lds_zero<SPARSE>())[l] = 0u;
     uint4 kw, vw, sw, ow = {};
     const int ol = l < 48 ? l : l - 48;   // SPARSE: lanes 0..47 load the outlier section (the rest reload a part)
     if (v0 < qend) {
@@ -1087,14 +1095,14 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
 
 template <int MODE, bool G1>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(4, 4))) void decode_pass1_kernel(DecodeArgs a) {
-    __shared__ __align__(16) unsigned char smem[LDS_BYTES];
+    __shared__ __align__(16) unsigned char smem[lds_total<false>()];
     decode_pass1_body<MODE, G1, false>(a, smem);
 }
 
 // dense-and-sparse records: three wavefronts per SIMD (12.7 KB of LDS, up to 168 registers)
 template <bool G1>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 3))) void decode_pass1_sparse_kernel(DecodeArgs a) {
-    __shared__ __align__(16) unsigned char smem[LDS_BYTES_SPARSE];
+    __shared__ __align__(16) unsigned char smem[lds_total<true>()];
     decode_pass1_body<0, G1, true>(a, smem);
 }
 
