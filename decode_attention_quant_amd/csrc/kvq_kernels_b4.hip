@@ -410,7 +410,7 @@ __device__ __forceinline__ void split_hi(float pa, float pb, uint32_t sa, uint32
 //
 // PV (MFMA). 16x16x32 fp16: B = the value codes of 16 channels (column n = channel 16j + n) and the tile's 32
 // tokens, one code word per lane (expanded exactly by the fp8 converter); A row g = p~[t] = p[t] s_V[g][t] for value
-// group g, split into fp16 high and low parts contracted in turn (rows 4..15 repeat rows 0..3). For channel block j
+// group g, split into fp16 high and low parts contracted in turn (rows 4..15 are zero). For channel block j
 // only row g = j/2 is kept. The zero-point term sum_t p z_V[g][t] is accumulated on the VALU; window tiles and the
 // sink add their values on the VALU.
 //
@@ -443,7 +443,9 @@ struct B4Lds {
     // key-outlier sums, int32 (H, L) [32 tokens], filled with the coefficients and read by the next softmax step
     static constexpr int VACC = RED;
     static constexpr int KACC = PBUF + 128;
-    static constexpr int BYTES = SPARSE ? KACC + 256 : COEF2 + 512;
+    // f32 [32] zeros: the P V operand's unused rows (4..15) read their probabilities here
+    static constexpr int ZERO = SPARSE ? KACC + 256 : COEF2 + 512;
+    static constexpr int BYTES = ZERO + 128;
     static constexpr int ND = SPARSE ? 6 : 5;       // LDS-DMA loads per tile
     static constexpr int NC = SPARSE ? 2 : 1;       // the first NC of them hold what the coefficients need
 };
@@ -487,6 +489,7 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
     __shared__ __align__(16) unsigned char smem[L::BYTES];
     float *red = reinterpret_cast<float *>(smem + L::RED);
     float *pbuf = reinterpret_cast<float *>(smem + L::PBUF);
+    if (threadIdx.x < 32) reinterpret_cast<float *>(smem + L::ZERO)[threadIdx.x] = 0.0f;
     float4 *coef4 = reinterpret_cast<float4 *>(smem + L::COEF4);
     float2 *coef2 = reinterpret_cast<float2 *>(smem + L::COEF2);
     const uint32_t ring_base = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char *)smem + L::RING;
@@ -777,12 +780,14 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
             lds_add(cg + 2 * ((vi >> 8) & 31u) + 1, l1);
         }
 
-        // PV: A rows g = n & 3 over tokens 8kg .. 8kg+7 in the expand8_b4 order (t0 t2 t4 t6 t1 t3 t5 t7)
+        // PV: A rows g = n & 3 over tokens 8kg .. 8kg+7 in the expand8_b4 order (t0 t2 t4 t6 t1 t3 t5 t7); rows 4..15
+        // (outputs never used) are zero: zero operands draw less power than repeated ones
         const int gA = n & 3;
+        const float *pz = n < 4 ? pbuf : reinterpret_cast<const float *>(smem + L::ZERO);
         const uint4 svr = *reinterpret_cast<const uint4 *>(tl + V4_SCALE + 2 * (32 * gA + 8 * kg));
         const h8 zvh = __builtin_bit_cast(h8, *reinterpret_cast<const uint4 *>(tl + V4_ZERO + 2 * (32 * gA + 8 * kg)));
-        const float4 pa = *reinterpret_cast<const float4 *>(pbuf + 8 * kg);
-        const float4 pb = *reinterpret_cast<const float4 *>(pbuf + 8 * kg + 4);
+        const float4 pa = *reinterpret_cast<const float4 *>(pz + 8 * kg);
+        const float4 pb = *reinterpret_cast<const float4 *>(pz + 8 * kg + 4);
         uint32_t ah[4], alo[4];
         split_lo(pa.x, pa.z, svr.x, svr.y, ah[0], alo[0]);
         split_lo(pb.x, pb.z, svr.z, svr.w, ah[1], alo[1]);
