@@ -602,6 +602,9 @@ __device__ __forceinline__ int sz_off(int x) { return x < 512 ? x : x + 16 * ((x
 template <int MODE, bool G1, bool SPARSE>
 __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned char *smem) {
     constexpr int RECB = rec_bytes<SPARSE>();
+    // G1, dense records: only head part 0 of the score operand and P V parts 0, 1 are read back, so the repeated
+    // rows are zero (lower matrix-unit power); the softmax of head part 0 drives every row
+    constexpr bool G1Z = G1 && !SPARSE;
     uint32_t *sz_lds = reinterpret_cast<uint32_t *>(smem + LDS_SZ);
     const _Float16 *szh = reinterpret_cast<const _Float16 *>(smem + LDS_SZ);
     _Float16 *qt_lds = reinterpret_cast<_Float16 *>(smem + LDS_QT);
@@ -750,11 +753,12 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
         s0 -= d;
         s1 -= d;
         lsum *= alpha;
+        const float ao = G1Z ? __shfl(alpha, 0) : alpha;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[j][r] *= alpha;
-        gam *= __shfl(alpha, 16 * hl);
+            for (int r = 0; r < 4; ++r) o[j][r] *= ao;
+        gam *= G1Z ? ao : __shfl(alpha, 16 * hl);
         seen = true;
     };
     // p of tokens n and 16 + n to LDS; returns, for the PV A layout of lane (n, kc), p of tokens 4kc + i (p[i]) and
@@ -762,8 +766,11 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
     auto exchange = [&](float p0, float p1, float p[8]) {
         reinterpret_cast<float2 *>(p_lds)[P_ROW * kc + n] = float2{p0, p1};
         wave_lds_order();
-        const f4 pa = reinterpret_cast<const f4 *>(p_lds)[(P_ROW * hl + 4 * kc) / 2];
-        const f4 pb = reinterpret_cast<const f4 *>(p_lds)[(P_ROW * hl + 4 * kc) / 2 + 1];
+        const f4 *pr = G1Z ? (hl < 2 ? reinterpret_cast<const f4 *>(p_lds) + 2 * kc
+                                     : reinterpret_cast<const f4 *>(smem + lds_zero<SPARSE>()))
+                           : reinterpret_cast<const f4 *>(p_lds) + (P_ROW * hl + 4 * kc) / 2;
+        const f4 pa = pr[0];
+        const f4 pb = pr[1];
         p[0] = pa[0]; p[4] = pa[1]; p[1] = pa[2]; p[5] = pa[3];
         p[2] = pb[0]; p[6] = pb[1]; p[3] = pb[2]; p[7] = pb[3];
     };
@@ -817,7 +824,7 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
     // the last tile the index is clamped: the reload hits the just-read record in cache.
     // A operand row n = 4 h + r: head h, high part (r = 0), low part (r = 1); rows r = 2, 3 (outputs never used) read
     // a zero row: zero operands draw less power than repeated ones, and the clock this kernel runs at is power-limited
-    const _Float16 *qta = (n & 2) ? reinterpret_cast<const _Float16 *>(smem + lds_zero<SPARSE>()) + 8 * kc
+    const _Float16 *qta = ((n & 2) || (G1Z && hl > 0)) ? reinterpret_cast<const _Float16 *>(smem + lds_zero<SPARSE>()) + 8 * kc
                                   : qt_lds + QT_ROW * (4 * (n & 1) + hl) + 8 * kc;
     reinterpret_cast<uint32_t *>(smem + lds_zero<SPARSE>())[l] = 0u;
     uint4 kw, vw, sw, ow = {};
