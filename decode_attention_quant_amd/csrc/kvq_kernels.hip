@@ -588,10 +588,11 @@ __device__ __forceinline__ int sz_off(int x) { return x < 512 ? x : x + 16 * ((x
 // that another workgroup of the launch read would need a release/acquire pair instead (at agent scope an L2
 // write-back and invalidate per workgroup, which costs the step several times its length).
 //
-// G1 (one query head per KV head): the four head rows of the score operand all hold that head, so every row of the
-// softmax state agrees, and PV puts the high and low parts of p~ in different A-operand rows (row 4 part + group)
-// instead of two contractions: 8 MFMAs per tile instead of 16. The parts are added across lanes (n, 0) and (n, 1) once,
-// before the partials are stored.
+// G1 (one query head per KV head): head row 0 of the score operand holds the head; with dense records rows 1..3
+// are zero (with dense-and-sparse records they repeat it), and the softmax state of row 0 drives every accumulator
+// row. PV puts the high and low parts of p~ in different A-operand rows (row 4 part + group) instead of two
+// contractions: 8 MFMAs per tile instead of 16 (rows 8..15 zero with dense records). The parts are added across lanes
+// (n, 0) and (n, 1) once, before the partials are stored.
 //
 // SPARSE (dense-and-sparse records, uniform lengths): a key outlier decodes as its zero point inside the dense
 // contraction (its code is 0), so its token's score misses q'_c (o - z_c); lane (n, kc) adds these for its eight
@@ -762,7 +763,8 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
         seen = true;
     };
     // p of tokens n and 16 + n to LDS; returns, for the PV A layout of lane (n, kc), p of tokens 4kc + i (p[i]) and
-    // 16 + 4kc + i (p[4 + i]) of head hl
+    // 16 + 4kc + i (p[4 + i]) of head hl (G1 with dense records: of head row 0 for parts hl = 0, 1 and zeros for the
+    // repeated parts 2, 3)
     auto exchange = [&](float p0, float p1, float p[8]) {
         reinterpret_cast<float2 *>(p_lds)[P_ROW * kc + n] = float2{p0, p1};
         wave_lds_order();
@@ -822,8 +824,9 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
     // Each code word is reloaded for the next tile right after its last use in this one (scales: at the top of the
     // iteration, key codes after the score contraction, value codes after PV), so no register holds two tiles. On
     // the last tile the index is clamped: the reload hits the just-read record in cache.
-    // A operand row n = 4 h + r: head h, high part (r = 0), low part (r = 1); rows r = 2, 3 (outputs never used) read
-    // a zero row: zero operands draw less power than repeated ones, and the clock this kernel runs at is power-limited
+    // A operand row n = 4 h + r: head h, high part (r = 0), low part (r = 1); rows r = 2, 3 (outputs never used), and
+    // with G1 and dense records head rows 1..3, read a zero row: zero operands draw less power than repeated ones, and
+    // the clock this kernel runs at is power-limited
     const _Float16 *qta = ((n & 2) || (G1Z && hl > 0)) ? reinterpret_cast<const _Float16 *>(smem + lds_zero<SPARSE>()) + 8 * kc
                                   : qt_lds + QT_ROW * (4 * (n & 1) + hl) + 8 * kc;
     reinterpret_cast<uint32_t *>(smem + lds_zero<SPARSE>())[l] = 0u;
