@@ -18,6 +18,7 @@ typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 128;
 constexpr int REC = 3072;
@@ -503,14 +504,17 @@ __device__ __forceinline__ void merge_splits(const float *part_o, const float *p
 // Softmax. Lagged maximum: p = 2^(C_h (score - mr)) is taken directly unless some score exceeds mr (or on the
 // first tile); only then the tile maximum is reduced over the row, mr raised and the accumulators rescaled.
 //
-// PV. The probabilities go through 512 B of LDS to the A layout of the PV contraction: row n = (head n / 4,
-// value group g = n % 4) carries p~ = p s_V[g][t] as fp16 high and low parts (mixed-precision fmas, one rounding
-// each), contracted in turn against the value codes of the 8 channel blocks of 16; for channel block j only row
-// group g = j / 2 is kept. The value zero-point term sum_t p z_V[g][t] is accumulated on the VALU.
+// PV. The probabilities go through 512 B of LDS to lane (n, kc), which forms p~ = p s_V[g][t] of head n / 4 and
+// value group g = n % 4 for its eight tokens as fp16 high and low parts (mixed-precision fmas, one rounding each).
+// A second LDS pass (2 KB) regroups them into two A operands, one per value-group pair (groups 0, 1 and 2, 3):
+// row 4 h + 2 m + r carries part r of head h for group m of the pair. Channel block j (16 channels, group j / 2)
+// takes one MFMA with the operand of its pair, 8 per tile; its output lane (channel, kc) holds head kc's four rows,
+// and the two rows of group j / 2 (high and low part) are added once, before the partials are stored. The value
+// zero-point term sum_t p z_V[g][t] is accumulated on the VALU.
 //
 // Per-wavefront LDS: the tile's scales/zeros, the folded query and beta, all written for tile v + 1 at the end of
 // iteration v after every read of tile v has been issued (a wavefront's LDS operations complete in order); the
-// probability exchange; the fp16 window value tile (8 KB, reusing the first region). Rows that lanes read together
+// probability exchange and the P V operands; the fp16 window value tile (8 KB, reusing the first region). Rows that lanes read together
 // are padded so that they fall in different LDS banks (64 banks of 4 bytes): unpadded, the eight 256-byte rows of
 // the folded query all start in bank 0 and every A-operand read of the score contraction is an 8-way conflict.
 constexpr int LDS_SZ = 0;            // s_K[128], z_K[128] (fp16), then s_V[4][32], z_V[4][32] with each group's 64 bytes
@@ -532,6 +536,10 @@ constexpr int VROW = 33, VSUMS = 16 * VROW;            // [4 heads][4 groups][33
 constexpr int LDS_KACC = 4224;       // int64 [4 heads][KROW]: key-outlier sums per (head, token)
 constexpr int LDS_VACC = LDS_BYTES;  // int64 [4 heads][4 groups][VROW]: value-outlier sums per (head, channel)
 constexpr int LDS_BYTES_SPARSE = LDS_VACC + VSUMS * 8;
+// The P V A operands of the quantized loop (two value-group pairs x 64 lanes x 16 bytes), inside the region the
+// quantized loop leaves free (after the outlier section and the key-outlier sums of the sparse kernel)
+constexpr int LDS_PV = 5376;
+static_assert(LDS_PV >= LDS_KACC + KSUMS * 8 && LDS_PV + 2048 <= LDS_P, "P V operands inside the free region");
 // 256 zero bytes after each kernel's LDS, read by the score operand's unused rows; placed in banks the folded-query
 // rows of the same reads do not use
 template <bool SPARSE>
@@ -590,8 +598,8 @@ __device__ __forceinline__ int sz_off(int x) { return x < 512 ? x : x + 16 * ((x
 //
 // G1 (one query head per KV head): head row 0 of the score operand holds the head; with dense records rows 1..3
 // are zero (with dense-and-sparse records they repeat it), and the softmax state of row 0 drives every accumulator
-// row. PV puts the high and low parts of p~ in different A-operand rows (row 4 part + group) instead of two
-// contractions: 8 MFMAs per tile instead of 16 (rows 8..15 zero with dense records). The parts are added across lanes
+// row. PV puts the high and low parts of p~ in different A-operand rows (row 4 part + group) straight from the
+// probability exchange, with no regrouping pass: 8 MFMAs per tile (rows 8..15 zero with dense records). The parts are added across lanes
 // (n, 0) and (n, 1) once, before the partials are stored.
 //
 // SPARSE (dense-and-sparse records, uniform lengths): a key outlier decodes as its zero point inside the dense
@@ -613,9 +621,11 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
     float *p_lds = reinterpret_cast<float *>(smem + LDS_P);
     _Float16 *vres_lds = reinterpret_cast<_Float16 *>(smem);
 
-    // MODE 2 keeps the workgroup's uniform indices and lengths in scalar registers (integer division runs on the
-    // vector unit; without this they stay in vector registers and spill around the in-kernel flush)
-    auto uni = [](int x) { return MODE == 2 ? __builtin_amdgcn_readfirstlane(x) : x; };
+    // The workgroup's indices, lengths and tile range are uniform; they are kept in scalar registers (integer
+    // division runs on the vector unit, and its results would otherwise stay in vector registers: the loop counter
+    // and every record address would then cost vector instructions per tile, and in MODE 2 they spill around the
+    // in-kernel flush)
+    auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
     const int l = threadIdx.x;
     const int n = l & 15, kc = l >> 4, hl = n >> 2, g = n & 3;
     const int unit = blockIdx.x;
@@ -841,8 +851,18 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
         stage(sw, ow);
     }
     for (int v = v0; v < qend; ++v) {
+        // the next record's address is uniform: kept in scalar registers (opaque to the compiler, which would
+        // otherwise hoist a per-lane 64-bit base out of the loop and rebuild every address with vector arithmetic),
+        // each load a scalar base plus the lane's offset
         const uint8_t *next = base + (int64_t)min(v + 1, qend - 1) * RECB;
-        sw = reinterpret_cast<const uint4 *>(next + 2048)[l];
+        uint64_t next_s = reinterpret_cast<uint64_t>(next);
+        asm volatile("" : "+s"(next_s));
+        auto load_rec = [&](int off) {
+            typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
+            return __builtin_bit_cast(uint4, reinterpret_cast<g_u32x4 *>(next_s + off)[l]);
+        };
+        sw = load_rec(2048);
+        const uint4 vw_next = load_rec(1024);
         if constexpr (SPARSE) ow = reinterpret_cast<const uint4 *>(next + REC)[ol];
 
         f4 ci = {beta_lds[kc] - mr, 0.0f, 0.0f, 0.0f};
@@ -861,7 +881,7 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
             acc0 = mfma(bq, expand8(nibbles(kw[ks >> 1], ks & 1)), acc0);
             acc1 = mfma(bq, expand8(nibbles(kw[2 + (ks >> 1)], ks & 1)), acc1);
         }
-        kw = reinterpret_cast<const uint4 *>(next)[l];
+        kw = load_rec(0);
         float s0 = acc0[0] + acc0[1], s1 = acc1[0] + acc1[1];
         if (!seen || __any(fmaxf(s0, s1) > 0.0f)) rescale(s0, s1);
         const float p0 = __builtin_amdgcn_exp2f(s0 * C), p1 = __builtin_amdgcn_exp2f(s1 * C);
@@ -905,15 +925,18 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
             const h8 pp = (hl & 1) ? plo : phi;
 #pragma unroll
             for (int j = 0; j < 8; ++j) o[j] = mfma(pp, expand8(nibbles(vw[j >> 1], j & 1)), o[j]);
-        } else {
+        } else {   // the two A operands of the value-group pairs, rows (head, group in pair, part), through LDS
+            uint4 *pvw = reinterpret_cast<uint4 *>(smem + LDS_PV) + 64 * (g >> 1) + 16 * kc + 4 * hl + 2 * (g & 1);
+            pvw[0] = uh;
+            pvw[1] = ul;
+            wave_lds_order();
+            const uint4 *pvr = reinterpret_cast<const uint4 *>(smem + LDS_PV) + l;
+            const h8 pa0 = __builtin_bit_cast(h8, pvr[0]);
+            const h8 pa1 = __builtin_bit_cast(h8, pvr[64]);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const h8 bv = expand8(nibbles(vw[j >> 1], j & 1));
-                o[j] = mfma(phi, bv, o[j]);
-                o[j] = mfma(plo, bv, o[j]);
-            }
+            for (int j = 0; j < 8; ++j) o[j] = mfma(j < 4 ? pa0 : pa1, expand8(nibbles(vw[j >> 1], j & 1)), o[j]);
         }
-        vw = reinterpret_cast<const uint4 *>(next + 1024)[l];
+        vw = vw_next;
         if constexpr (SPARSE) {   // head kc's value-outlier sums of channels n + 16 j, then cleared (G1: row 0 only)
             wave_lds_order();
             // channel n + 16 j of head kc: group j / 2, index n + 16 (j % 2) within it
@@ -921,7 +944,7 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const float corr = fix_join(vr[VROW * (j >> 1) + 16 * (j & 1)]);
-                if (!G1 || kc == 0) o[j][j >> 1] += corr;
+                if (!G1 || kc == 0) o[j][G1 ? (j >> 1) : 2 * ((j >> 1) & 1)] += corr;
             }
             wave_lds_order();
 #pragma unroll
@@ -1033,9 +1056,8 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
                 const h8 bv = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
                 if constexpr (G1) {
                     o[j] = mfma((hl & 1) ? plo : phi, bv, o[j]);
-                } else {
-                    o[j] = mfma(phi, bv, o[j]);
-                    o[j] = mfma(plo, bv, o[j]);
+                } else {   // row n: part n % 2 of head n / 4 (p~ = p, the same for both groups of a pair)
+                    o[j] = mfma((n & 1) ? plo : phi, bv, o[j]);
                 }
             }
             wait_lgkmcnt0();    // PV has read the value rows: the next tile may overwrite them
@@ -1053,6 +1075,9 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
     if constexpr (G1) {   // lane (n, 0) adds the low parts held by lane (n, 1)
 #pragma unroll
         for (int j = 0; j < 8; ++j) o[j][j >> 1] += __shfl(o[j][j >> 1], (l & 15) + 16);
+    } else {              // high and low part of channel block j's group (row 2 (group % 2) + part of head kc)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j][j >> 1] = o[j][2 * ((j >> 1) & 1)] + o[j][2 * ((j >> 1) & 1) + 1];
     }
     const int64_t S = nsplit;
     if (kc < gc) {   // lane (n, kc) holds head h0 + kc, channels n + 16 j
