@@ -498,8 +498,8 @@ __device__ __forceinline__ void merge_splits(const float *part_o, const float *p
 // kc's high-part and low-part sums for token t in its first two accumulator registers: one add gives the score,
 // and each lane owns the scores of exactly one (head, token) pair per block, two per tile. The accumulator starts
 // at beta[h] - mr[h] in the high-part row, where beta[h] = sum_c q'[h][c] z_K[c] is the tile's zero-point term
-// (computed once per tile on the VALU: packed fp16 dot products, fp32 sums) and mr[h] the running maximum, so the
-// sum is already relative to the maximum.
+// (computed once per tile on the VALU: packed fp16 dot products, fp32 sums, kept in a register of every lane of
+// row h) and mr[h] the running maximum, so the sum is already relative to the maximum.
 //
 // Softmax. Lagged maximum: p = 2^(C_h (score - mr)) is taken directly unless some score exceeds mr (or on the
 // first tile); only then the tile maximum is reduced over the row, mr raised and the accumulators rescaled.
@@ -512,7 +512,7 @@ __device__ __forceinline__ void merge_splits(const float *part_o, const float *p
 // and the two rows of group j / 2 (high and low part) are added once, before the partials are stored. The value
 // zero-point term sum_t p z_V[g][t] is accumulated on the VALU.
 //
-// Per-wavefront LDS: the tile's scales/zeros, the folded query and beta, all written for tile v + 1 at the end of
+// Per-wavefront LDS: the tile's scales/zeros and the folded query, both written for tile v + 1 at the end of
 // iteration v after every read of tile v has been issued (a wavefront's LDS operations complete in order); the
 // probability exchange and the P V operands; the fp16 window value tile (8 KB, reusing the first region). Rows that lanes read together
 // are padded so that they fall in different LDS banks (64 banks of 4 bytes): unpadded, the eight 256-byte rows of
@@ -521,7 +521,6 @@ constexpr int LDS_SZ = 0;            // s_K[128], z_K[128] (fp16), then s_V[4][3
                                      // followed by 16 bytes of padding (1152 bytes)
 constexpr int QT_ROW = 136;          // fp16 per (part, head) row of the folded query: 128 channels + 8 padding
 constexpr int LDS_QT = 1152;         // fp16 [2 (high, low)][4 heads][QT_ROW]
-constexpr int LDS_BETA = LDS_QT + 8 * QT_ROW * 2;   // fp32 [4 heads]
 constexpr int P_ROW = 18;            // float2 per head of the probability exchange: 16 + 2 padding
 constexpr int LDS_P = 8192;          // float2 [4 heads][P_ROW]: p of tokens i and 16 + i
 constexpr int LDS_BYTES = LDS_P + 4 * P_ROW * 8;    // [0, 8192) also holds the fp16 window value tile [32][128]
@@ -546,7 +545,7 @@ template <bool SPARSE>
 constexpr int lds_zero() { return SPARSE ? LDS_BYTES_SPARSE + 64 : LDS_BYTES; }
 template <bool SPARSE>
 constexpr int lds_total() { return lds_zero<SPARSE>() + 256; }
-static_assert(LDS_OUT >= LDS_BETA + 16 && LDS_KACC + KSUMS * 8 <= 8192, "sparse regions inside the free window region");
+static_assert(LDS_OUT >= LDS_QT + 8 * QT_ROW * 2 && LDS_KACC + KSUMS * 8 <= 8192, "sparse regions inside the free window region");
 static_assert(LDS_KACC % 8 == 0 && LDS_VACC % 8 == 0, "64-bit sums");
 // Exact sums of corrections through integer LDS atomics (float LDS atomics cost some thirty times an integer one on
 // this chip). Every correction is below 2^17 in magnitude (a query scaled below 1 or a probability at most 1, times
@@ -617,7 +616,6 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
     uint32_t *sz_lds = reinterpret_cast<uint32_t *>(smem + LDS_SZ);
     const _Float16 *szh = reinterpret_cast<const _Float16 *>(smem + LDS_SZ);
     _Float16 *qt_lds = reinterpret_cast<_Float16 *>(smem + LDS_QT);
-    float *beta_lds = reinterpret_cast<float *>(smem + LDS_BETA);
     float *p_lds = reinterpret_cast<float *>(smem + LDS_P);
     _Float16 *vres_lds = reinterpret_cast<_Float16 *>(smem);
 
@@ -795,9 +793,11 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
         wave_lds_order();
     }
 
-    // stage a tile's scales/zeros, its folded query (high, low) and beta into LDS (SPARSE: and its outlier section,
-    // with the key-outlier corrections of the lane's eight channels added into the (head, token) sums)
-    auto stage = [&](const uint4 &sw, const uint4 &ow) {
+    // stage a tile's scales/zeros and its folded query (high, low) into LDS (SPARSE: and its outlier section, with
+    // the key-outlier corrections of the lane's eight channels added into the (head, token) sums); returns the
+    // tile's beta of head kc minus the running maximum, the same in every lane of row kc (each of the row's 16
+    // partial sums starts at -mr / 16; mr only changes after the next tile's scores)
+    auto stage = [&](const uint4 &sw, const uint4 &ow) -> float {
         *reinterpret_cast<uint4 *>(smem + LDS_SZ + sz_off(16 * l)) = sw;
         if constexpr (SPARSE) {
             if (l < 48) reinterpret_cast<uint4 *>(smem + LDS_OUT)[l] = ow;
@@ -821,13 +821,12 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
         const h8 lo = __builtin_elementwise_fma(qf, sk, -hi);
         *reinterpret_cast<h8 *>(qt_lds + QT_ROW * kc + 8 * n) = hi;
         *reinterpret_cast<h8 *>(qt_lds + QT_ROW * (4 + kc) + 8 * n) = lo;
-        float bp = 0.0f;
+        float bp = -0.0625f * mr;
 #pragma unroll
         for (int e = 0; e < 8; e += 2)
             bp = __builtin_amdgcn_fdot2(h2{zk[e], zk[e + 1]}, h2{qf[e], qf[e + 1]}, bp, false);
-        bp = row16_sum(bp);    // beta of head kc, in every lane of row kc
-        if (n == 0) beta_lds[kc] = bp;
         wave_lds_order();
+        return row16_sum(bp);
     };
 
     // ------------------------------------------------------------------ quantized tiles
@@ -841,6 +840,8 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
                                   : qt_lds + QT_ROW * (4 * (n & 1) + hl) + 8 * kc;
     reinterpret_cast<uint32_t *>(smem + lds_zero<SPARSE>())[l] = 0u;
     uint4 kw, vw, sw, ow = {};
+    // start of the score accumulators: row 0 (high part) beta - mr of the current tile, rows 1..3 zero
+    f4 ci = {0.0f, 0.0f, 0.0f, 0.0f};
     const int ol = l < 48 ? l : l - 48;   // SPARSE: lanes 0..47 load the outlier section (the rest reload a part)
     if (v0 < qend) {
         const uint8_t *rec = base + (int64_t)v0 * RECB;
@@ -848,7 +849,7 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
         vw = reinterpret_cast<const uint4 *>(rec + 1024)[l];
         sw = reinterpret_cast<const uint4 *>(rec + 2048)[l];
         if constexpr (SPARSE) ow = reinterpret_cast<const uint4 *>(rec + REC)[ol];
-        stage(sw, ow);
+        ci[0] = stage(sw, ow);
     }
     for (int v = v0; v < qend; ++v) {
         // the next record's address is uniform: kept in scalar registers (opaque to the compiler, which would
@@ -857,16 +858,13 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
         const uint8_t *next = base + (int64_t)min(v + 1, qend - 1) * RECB;
         uint64_t next_s = reinterpret_cast<uint64_t>(next);
         asm volatile("" : "+s"(next_s));
-        auto load_rec = [&](int off) {
-            typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
-            return __builtin_bit_cast(uint4, reinterpret_cast<g_u32x4 *>(next_s + off)[l]);
-        };
+        typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
+        g_u32x4 *next_g = reinterpret_cast<g_u32x4 *>(next_s);
+        auto load_rec = [&](int off) { return __builtin_bit_cast(uint4, next_g[off / 16 + l]); };
         sw = load_rec(2048);
-        const uint4 vw_next = load_rec(1024);
         if constexpr (SPARSE) ow = reinterpret_cast<const uint4 *>(next + REC)[ol];
 
-        f4 ci = {beta_lds[kc] - mr, 0.0f, 0.0f, 0.0f};
-        f4 acc0 = ci, acc1 = ci;    // tokens n (acc0) and 16 + n (acc1); rows (head kc, part r)
+        f4 acc0 = ci, acc1 = ci;   // tokens n (acc0) and 16 + n (acc1); rows (head kc, part r)
         if constexpr (SPARSE) {   // the key-outlier sums of tokens n and 16 + n of head kc, then cleared
             int64_t *kr = kacc + KROW * kc + n;
             acc0[0] += fix_join(kr[0]);
@@ -936,7 +934,8 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
 #pragma unroll
             for (int j = 0; j < 8; ++j) o[j] = mfma(j < 4 ? pa0 : pa1, expand8(nibbles(vw[j >> 1], j & 1)), o[j]);
         }
-        vw = vw_next;
+        asm volatile("" : "+s"(next_s));   // the base again from scalar registers (this is a later block)
+        vw = __builtin_bit_cast(uint4, reinterpret_cast<g_u32x4 *>(next_s)[64 + l]);
         if constexpr (SPARSE) {   // head kc's value-outlier sums of channels n + 16 j, then cleared (G1: row 0 only)
             wave_lds_order();
             // channel n + 16 j of head kc: group j / 2, index n + 16 (j % 2) within it
@@ -952,7 +951,7 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
         }
         // every LDS read of this tile has been issued: overwrite with the next tile (after the last tile, with
         // that tile again; unconditional, so no load sits on only one path of the loop)
-        stage(sw, ow);
+        ci[0] = stage(sw, ow);
     }
 
     // ------------------------------------------------------------------ residual (fp16) tiles
