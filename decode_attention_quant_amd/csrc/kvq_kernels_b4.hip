@@ -501,12 +501,15 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
     const int bh = blockIdx.x;
     const int split = blockIdx.y;
     const int S = gridDim.y;
-    const int b = bh / a.q_heads, hq = bh - b * a.q_heads;
+    // the workgroup's indices and tile range are uniform: kept in scalar registers (integer division runs on the
+    // vector unit, and its results would otherwise make the tile loop's counter, branches and addresses vector work)
+    auto uni = [](int x) { return __builtin_amdgcn_readfirstlane(x); };
+    const int b = uni(bh / a.q_heads), hq = uni(bh - b * a.q_heads);
     const int G = a.q_heads / a.kv_heads;
-    const int64_t slice = (int64_t)b * a.kv_heads + hq / G;
+    const int64_t slice = (int64_t)b * a.kv_heads + uni(hq / G);
     const int n_vt = a.n_qtiles + (a.n_resid + 31) / 32;
-    const int v0 = split * a.tiles_per_split;
-    const int v1 = min(n_vt, v0 + a.tiles_per_split);
+    const int v0 = uni(split * a.tiles_per_split);
+    const int v1 = uni(min(n_vt, v0 + a.tiles_per_split));
     const float C = a.sm_log2;
     const float NEG_INF = -__builtin_inff();
 
@@ -666,17 +669,17 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
     // bytes [32 l, 32 l + 16) go to slot + 16 l and [32 l + 16, 32 l + 32) to slot + 1024 + 16 l; value codes,
     // scales and zeros at their record offsets
     // SPARSE: the outlier section (768 bytes, lanes 0..47) right after the scales
-    auto dma_tile = [&](int v, int slot) {
-        const uint8_t *rec = recs + (int64_t)v * REC;
+    auto dma_tile = [&](int v, int slot) {   // v and slot are uniform: the record base stays in scalar registers
+        const uint64_t rec = reinterpret_cast<uint64_t>(recs + (int64_t)v * REC);
         const uint32_t base = ring_base + slot * REC;
-        lds_dma16(rec + K4_SCALE + 16 * l, base + K4_SCALE);
+        lds_dma16_s(rec + K4_SCALE, 16 * l, base + K4_SCALE);
         if constexpr (SPARSE) {
-            if (l < 48) lds_dma16(rec + K4_OUT + 16 * l, base + K4_OUT);
+            if (l < 48) lds_dma16_s(rec + K4_OUT, 16 * l, base + K4_OUT);
         }
-        lds_dma16(rec + 32 * l, base);
-        lds_dma16(rec + 32 * l + 16, base + 1024);
-        lds_dma16(rec + V4_CODES + 16 * l, base + V4_CODES);
-        lds_dma16(rec + V4_CODES + 1024 + 16 * l, base + V4_CODES + 1024);
+        lds_dma16_s(rec, 32 * l, base);
+        lds_dma16_s(rec + 16, 32 * l, base + 1024);
+        lds_dma16_s(rec + V4_CODES, 16 * l, base + V4_CODES);
+        lds_dma16_s(rec + V4_CODES + 1024, 16 * l, base + V4_CODES + 1024);
     };
     auto tile_coefficients = [&](int slot) {
         const unsigned char *tl = smem + L::RING + slot * REC;

@@ -97,6 +97,15 @@ __device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds_base) {
                  : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                  : "memory");
 }
+// The same with a uniform base address in scalar registers and a 32-bit per-lane byte offset (the global
+// scalar-base form: no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void lds_dma16_s(uint64_t base, uint32_t lane_off, uint32_t lds_base) {
+    uint32_t saved;
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+                 : "=&s"(saved)
+                 : "v"(lane_off), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "memory");
+}
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
