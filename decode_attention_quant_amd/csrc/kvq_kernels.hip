@@ -535,10 +535,13 @@ constexpr int VROW = 33, VSUMS = 16 * VROW;            // [4 heads][4 groups][33
 constexpr int LDS_KACC = 4224;       // int64 [4 heads][KROW]: key-outlier sums per (head, token)
 constexpr int LDS_VACC = LDS_BYTES;  // int64 [4 heads][4 groups][VROW]: value-outlier sums per (head, channel)
 constexpr int LDS_BYTES_SPARSE = LDS_VACC + VSUMS * 8;
-// The P V A operands of the quantized loop (two value-group pairs x 64 lanes x 16 bytes), inside the region the
+// The P V A operands of the quantized loop (two value-group pairs x 64 lanes x 16 bytes; the second starts 16
+// bytes past the first's end, so the 16 lanes of a write pass hit distinct banks), inside the region the
 // quantized loop leaves free (after the outlier section and the key-outlier sums of the sparse kernel)
 constexpr int LDS_PV = 5376;
-static_assert(LDS_PV >= LDS_KACC + KSUMS * 8 && LDS_PV + 2048 <= LDS_P, "P V operands inside the free region");
+constexpr int PV_PAIR = 65;   // 16-byte units from one pair's operand to the next
+static_assert(LDS_PV >= LDS_KACC + KSUMS * 8 && LDS_PV + 16 * (PV_PAIR + 64) <= LDS_P,
+              "P V operands inside the free region");
 // 256 zero bytes after each kernel's LDS, read by the score operand's unused rows; placed in banks the folded-query
 // rows of the same reads do not use
 template <bool SPARSE>
@@ -924,13 +927,13 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
 #pragma unroll
             for (int j = 0; j < 8; ++j) o[j] = mfma(pp, expand8(nibbles(vw[j >> 1], j & 1)), o[j]);
         } else {   // the two A operands of the value-group pairs, rows (head, group in pair, part), through LDS
-            uint4 *pvw = reinterpret_cast<uint4 *>(smem + LDS_PV) + 64 * (g >> 1) + 16 * kc + 4 * hl + 2 * (g & 1);
+            uint4 *pvw = reinterpret_cast<uint4 *>(smem + LDS_PV) + PV_PAIR * (g >> 1) + 16 * kc + 4 * hl + 2 * (g & 1);
             pvw[0] = uh;
             pvw[1] = ul;
             wave_lds_order();
             const uint4 *pvr = reinterpret_cast<const uint4 *>(smem + LDS_PV) + l;
             const h8 pa0 = __builtin_bit_cast(h8, pvr[0]);
-            const h8 pa1 = __builtin_bit_cast(h8, pvr[64]);
+            const h8 pa1 = __builtin_bit_cast(h8, pvr[PV_PAIR]);
 #pragma unroll
             for (int j = 0; j < 8; ++j) o[j] = mfma(j < 4 ? pa0 : pa1, expand8(nibbles(vw[j >> 1], j & 1)), o[j]);
         }
