@@ -395,13 +395,19 @@ __device__ __forceinline__ float pow2(int k) { return __builtin_bit_cast(float, 
 __device__ __forceinline__ f4 mfma(h8 a, h8 b, f4 c) { return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0); }
 
 // x = (pa * s.lo, pb * s.hi) for an fp32 pair (pa, pb) and a packed fp16 pair s: hi = RN16(x), lo = RN16(x - hi),
-// each element one mixed-precision fma with a single rounding, written straight into the packed halves
+// packed. x is formed in binary32 (one mixed-precision fma each, one rounding), its high parts by one packed
+// conversion, the exact remainders x - hi by mixed fmas that read hi's halves, the low parts by a second packed
+// conversion: six instructions at the full vector rate (fp16-destination mixed fmas, which would write the halves
+// directly, issue at about half that rate). hi + lo is x to within 2^-22 |x|.
 __device__ __forceinline__ void split_pair(float pa, float pb, uint32_t s, uint32_t &hi, uint32_t &lo) {
-    asm("v_fma_mixlo_f16 %0, %2, %4, 0 op_sel_hi:[0,1,0]\n\t"
-        "v_fma_mixhi_f16 %0, %3, %4, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]\n\t"
-        "v_fma_mixlo_f16 %1, %2, %4, -%0 op_sel_hi:[0,1,1]\n\t"
-        "v_fma_mixhi_f16 %1, %3, %4, -%0 op_sel:[0,1,1] op_sel_hi:[0,1,1]"
-        : "=&v"(hi), "=&v"(lo)
+    float x0, x1;
+    asm("v_fma_mix_f32 %2, %4, %6, 0 op_sel_hi:[0,1,0]\n\t"
+        "v_fma_mix_f32 %3, %5, %6, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]\n\t"
+        "v_cvt_pk_f16_f32 %0, %2, %3\n\t"
+        "v_fma_mix_f32 %2, -%0, 1.0, %2 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mix_f32 %3, -%0, 1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+        "v_cvt_pk_f16_f32 %1, %2, %3"
+        : "=&v"(hi), "=&v"(lo), "=&v"(x0), "=&v"(x1)
         : "v"(pa), "v"(pb), "v"(s));
 }
 

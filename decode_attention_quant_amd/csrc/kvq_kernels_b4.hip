@@ -362,22 +362,29 @@ __device__ __forceinline__ h8 expand8_b4(uint32_t w) {
     return r;
 }
 
-// x = (pa * sa.lo, pb * sb.lo) (or the high halves), hi = RN16(x), lo = RN16(x - hi); every element is one
-// mixed-precision fma with a single rounding, written into the packed halves.
+// x = (pa * sa.lo, pb * sb.lo) (or the high halves), hi = RN16(x), lo = RN16(x - hi), packed: x in binary32 (one
+// mixed-precision fma each), the high parts by one packed conversion, the exact remainders by mixed fmas that read
+// hi's halves, the low parts by a second packed conversion (six instructions at the full vector rate).
 __device__ __forceinline__ void split_lo(float pa, float pb, uint32_t sa, uint32_t sb, uint32_t &hi, uint32_t &lo) {
-    asm("v_fma_mixlo_f16 %0, %2, %4, 0 op_sel_hi:[0,1,0]\n\t"
-        "v_fma_mixhi_f16 %0, %3, %5, 0 op_sel_hi:[0,1,0]\n\t"
-        "v_fma_mixlo_f16 %1, %2, %4, -%0 op_sel_hi:[0,1,1]\n\t"
-        "v_fma_mixhi_f16 %1, %3, %5, -%0 op_sel:[0,0,1] op_sel_hi:[0,1,1]"
-        : "=&v"(hi), "=&v"(lo)
+    float x0, x1;
+    asm("v_fma_mix_f32 %2, %4, %6, 0 op_sel_hi:[0,1,0]\n\t"
+        "v_fma_mix_f32 %3, %5, %7, 0 op_sel_hi:[0,1,0]\n\t"
+        "v_cvt_pk_f16_f32 %0, %2, %3\n\t"
+        "v_fma_mix_f32 %2, -%0, 1.0, %2 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mix_f32 %3, -%0, 1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+        "v_cvt_pk_f16_f32 %1, %2, %3"
+        : "=&v"(hi), "=&v"(lo), "=&v"(x0), "=&v"(x1)
         : "v"(pa), "v"(pb), "v"(sa), "v"(sb));
 }
 __device__ __forceinline__ void split_hi(float pa, float pb, uint32_t sa, uint32_t sb, uint32_t &hi, uint32_t &lo) {
-    asm("v_fma_mixlo_f16 %0, %2, %4, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]\n\t"
-        "v_fma_mixhi_f16 %0, %3, %5, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]\n\t"
-        "v_fma_mixlo_f16 %1, %2, %4, -%0 op_sel:[0,1,0] op_sel_hi:[0,1,1]\n\t"
-        "v_fma_mixhi_f16 %1, %3, %5, -%0 op_sel:[0,1,1] op_sel_hi:[0,1,1]"
-        : "=&v"(hi), "=&v"(lo)
+    float x0, x1;
+    asm("v_fma_mix_f32 %2, %4, %6, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]\n\t"
+        "v_fma_mix_f32 %3, %5, %7, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]\n\t"
+        "v_cvt_pk_f16_f32 %0, %2, %3\n\t"
+        "v_fma_mix_f32 %2, -%0, 1.0, %2 op_sel_hi:[1,0,0]\n\t"
+        "v_fma_mix_f32 %3, -%0, 1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+        "v_cvt_pk_f16_f32 %1, %2, %3"
+        : "=&v"(hi), "=&v"(lo), "=&v"(x0), "=&v"(x1)
         : "v"(pa), "v"(pb), "v"(sa), "v"(sb));
 }
 
