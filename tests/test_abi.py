@@ -148,7 +148,7 @@ def test_decode_validation(kvq):
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,n_q,n_r,min_splits", [
-    (64, 32, 8, 32640, 128, 8), (1, 32, 32, 1048448, 128, 64), (8, 32, 32, 3968, 128, 8), (1, 1, 1, 896, 128, 1)])
+    (64, 32, 8, 32640, 128, 6), (1, 32, 32, 1048448, 128, 64), (8, 32, 32, 3968, 128, 8), (1, 1, 1, 896, 128, 1)])
 def test_split_plan_covers_every_tile(kvq, B, Hq, Hkv, n_q, n_r, min_splits):
     lib = kvq.library()
     s = _shape(kvq, batch=B, q_heads=Hq, kv_heads=Hkv, max_tokens=n_q + 1024)
