@@ -213,10 +213,14 @@ class ClockProbe:
             self.lib.kvq_probe_clock(1, self.out.data_ptr(), self.words, self.stream.cuda_stream)
             torch.cuda.synchronize()
 
-    def start(self, seconds):
+    def start(self, seconds, after=None):
+        """Probe `seconds` of wall time; with `after` (an event recorded on the timed stream) the probe's stream
+        waits for it, so the window starts with the work that follows the event."""
         if self.khz <= 0 or seconds <= 0:
             return
         ticks = max(1, min(10 ** 9, int(seconds * self.khz * 1e3)))
+        if after is not None:
+            self.stream.wait_event(after)
         rc = self.lib.kvq_probe_clock(ticks, self.out.data_ptr(), self.words, self.stream.cuda_stream)
         self.started = rc == 0
 
@@ -477,11 +481,12 @@ def step_graph(args, kvq, kdev, kvsynth, torch):
 def measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=True, before_timed=None, settle_calls=0):
     """One workload: prefill (timed as one append), W warm-up steps, then K timed steps, each one token appended to
     every sequence and one decode-attention call, with HIP events around every append and every call on the current
-    stream. `before_timed(state)`, if given, runs after the prefill and before the warm-up steps (other measurements
-    of the same run) and returns entries for the record. With settle_calls > 0, that many further decode calls on the
-    final cache (no appends) follow the timed steps, each timed, and are reported apart (`settled`): the rate once the
-    engine clock has left the slow stretch that follows the prefill. Returns the record and the device tensors the
-    extras reuse."""
+    stream. `before_timed(state)`, if given, runs after the prefill (other measurements of the same run) and returns
+    entries for the record. With settle_calls > 0, that many decode calls on the prefilled cache (no appends) lead
+    in to the warm-up steps: they, the warm-up steps and the timed steps are enqueued back to back with no host
+    synchronization in between, as in a serving loop, so the timed steps run at the steady rate and not in the
+    engine-clock dip that follows any pause of the GPU (each lead-in call is timed and reported as `settled`).
+    Returns the record and the device tensors the extras reuse."""
     R = w.residual
     P = w.context - W - 1                      # first timed step attends over exactly w.context tokens
     total = P + W + K
@@ -513,6 +518,8 @@ def measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=True, before_timed=
     # prefill traffic: every token's fp16 K and V read once; tiles, window rows (and the sink record) written
     prefill_bytes = (w.batch * w.kv_heads * (P * 512 + cache.n_quant // 32 * rec_bytes + cache.n_resid * 512
                                              + cache.n_sink * 512))
+    prefill_quant, prefill_resid, prefill_sink, prefill_tokens = cache.n_quant, cache.n_resid, cache.n_sink, \
+        cache.n_tokens
     log(f"[bench] prefill {P} tokens: n_sink={cache.n_sink} n_quant={cache.n_quant} n_resid={cache.n_resid} "
         f"in {prefill_us:.0f} us ({prefill_bytes / prefill_us / 1e3:.0f} GB/s)")
 
@@ -533,17 +540,27 @@ def measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=True, before_timed=
         t = P + i
         kvq.kv_append_and_flush(cache, Kd[:, :, t:t + 1], Vd[:, :, t:t + 1])
 
-    wev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    probe_clock = ClockProbe(torch) if clock else None   # (its set-up synchronizes: before the lead-in)
+    # one call on its own: the length of the clock probe's window inside the timed calls
+    e1 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e1[0].record()
+    kvq.kv_decode_attention(cache, Q[0], out=out, workspace=workspace)
+    e1[1].record()
+    torch.cuda.synchronize()
+    est_call_ms = e1[0].elapsed_time(e1[1])
+
+    # from here to the end of the timed steps, no host synchronization
+    sev = None
+    if settle_calls > 0:
+        sev = [torch.cuda.Event(enable_timing=True) for _ in range(settle_calls + 1)]
+        sev[0].record()
+        for i in range(settle_calls):
+            kvq.kv_decode_attention(cache, Q[0], out=out, workspace=workspace)
+            sev[i + 1].record()
     for i in range(W):
         step(i)
-        if i == W - 1:
-            wev[0].record()
         kvq.kv_decode_attention(cache, Q[i], out=out, workspace=workspace)
-    wev[1].record()
-    torch.cuda.synchronize()
-    last_warm_ms = wev[0].elapsed_time(wev[1]) if W > 0 else 0.3
 
-    probe_clock = ClockProbe(torch) if clock else None
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * K + 2)]
     call_bytes, kv_tokens, contexts = [], 0, []
     ev[0].record()
@@ -555,7 +572,7 @@ def measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=True, before_timed=
         kvq.kv_decode_attention(cache, Q[i], out=out, workspace=workspace)
         ev[3 * j + 3].record()
         if j == 0 and probe_clock is not None:   # a window inside the timed calls
-            probe_clock.start(0.7 * K * last_warm_ms * 1e-3)
+            probe_clock.start(0.7 * K * est_call_ms * 1e-3, after=ev[1])
         n = cache.n_tokens
         contexts.append(n)
         kv_tokens += w.batch * n
@@ -574,25 +591,21 @@ def measure_decode(kvq, kdev, kvsynth, torch, w, W, K, clock=True, before_timed=
     clk = probe_clock.result() if probe_clock is not None else None
 
     settled = None
-    if settle_calls > 0:   # after the timed region: does not enter value, ms_per_step or the roofline
-        sev = [torch.cuda.Event(enable_timing=True) for _ in range(settle_calls + 1)]
-        sev[0].record()
-        for i in range(settle_calls):
-            kvq.kv_decode_attention(cache, Q[W + K - 1], out=out, workspace=workspace)
-            sev[i + 1].record()
-        torch.cuda.synchronize()
+    if sev is not None:   # the lead-in calls: before the warm-up steps, not part of value, ms_per_step or the roofline
         sus = [1e3 * sev[i].elapsed_time(sev[i + 1]) for i in range(settle_calls)]
         tail = sus[settle_calls // 2:]
-        sb = call_bytes[-1]
-        settled = {"calls": settle_calls, "context": cache.n_tokens,
+        sb = algorithmic_bytes(w.batch, w.kv_heads, w.q_heads, prefill_quant, prefill_resid, bits=w.bits,
+                               n_sink=prefill_sink, sparse=w.sparse)
+        settled = {"calls": settle_calls, "context": prefill_tokens,
                    "decode_call_us_all": sum(sus) / settle_calls,
                    "decode_call_us_second_half": sum(tail) / len(tail),
                    "hbm_gb_s_second_half": sb / (sum(tail) / len(tail)) / 1e3,
                    "pct_of_peak_second_half": 100.0 * sb / (sum(tail) / len(tail)) / 1e3 / PEAK_GBS,
                    "decode_call_us_series": [round(u, 1) for u in sus],
-                   "note": "decode calls on the cache of the last timed step, no appends, after the timed region "
-                           "(not part of value); the second half is the rate once the clock has recovered"}
-        log(f"[bench] {settle_calls} further calls after the timed steps: second half avg "
+                   "note": "decode calls on the prefilled cache (no appends) that lead in to the warm-up steps, "
+                           "enqueued back to back with them and the timed steps (no host synchronization): not part "
+                           "of value; the second half is the steady rate"}
+        log(f"[bench] {settle_calls} lead-in calls before the warm-up steps: second half avg "
             f"{settled['decode_call_us_second_half']:.1f} us ({settled['hbm_gb_s_second_half']:.0f} GB/s)")
     log(f"[bench] {w.name}: {K} steps in {total_ms:.3f} ms; decode call avg {1e3 * sum(decode_ms) / K:.1f} us "
         f"({achieved:.0f} GB/s); append avg {1e3 * sum(append_ms) / K:.1f} us, max {1e3 * max(append_ms):.1f} us; "
@@ -658,6 +671,9 @@ def compact(rec):
     r["kv_tokens_per_s"] = rec["value"]
     r["roofline"] = {k: rec["roofline"][k] for k in ("achieved", "frac", "bytes_per_call", "traffic", "kernel")}
     r["prefill_gb_s"] = rec["prefill"]["gb_s"]
+    if "settled" in rec:
+        r["settled_decode_call_us"] = rec["settled"]["decode_call_us_second_half"]
+        r["settled_pct_of_peak"] = rec["settled"]["pct_of_peak_second_half"]
     return r
 
 
@@ -773,7 +789,9 @@ def main(argv=None):
                     help="measure only the headline workload (else also " + ", ".join(SUB_WORKLOADS) + ")")
     ap.add_argument("--fp16-calls", type=int, default=20)
     ap.add_argument("--settle-calls", type=int, default=160,
-                    help="decode calls timed after the timed steps, reported apart as `settled` (0: none)")
+                    help="decode calls that lead in to the warm-up steps with no host synchronization in between, "
+                         "each timed and reported apart as `settled` (0: none; the timed steps then start after a "
+                         "pause of the GPU)")
     ap.add_argument("--cold-calls", type=int, default=20,
                     help="decode calls timed right after the prefill, before the warm-up steps (0: none)")
     ap.add_argument("--step-graph", action="store_true",
@@ -864,8 +882,9 @@ def main(argv=None):
         res["fp16_comparator"]["speedup_2bit_over_fp16"] = res["fp16_comparator"]["decode_call_us"] / \
             res["decode_call_us"]
     res["measurement_order"] = ("input generation and upload; prefill; cold_start calls; hbm_read_ceiling; "
-                                "fp16_comparator; warm-up steps; timed steps; settled calls; sub-record workloads; "
-                                "cpu_baseline")
+                                "fp16_comparator; one call (the clock probe's window); then with no host "
+                                "synchronization: settled (lead-in) calls, warm-up steps, timed steps; sub-record "
+                                "workloads; cpu_baseline")
     Qcpu = [st["Q"][W + j].cpu().numpy() for j in range(min(args.cpu_queries, K))]
     del st
     torch.cuda.empty_cache()
@@ -878,7 +897,8 @@ def main(argv=None):
                 if name == "llama2_7b_stream":
                     subs[name + "_step"] = step_record(kvq, kdev, kvsynth, torch, sw, 8, 128, 3)
                 else:
-                    r, s2 = measure_decode(kvq, kdev, kvsynth, torch, sw, W, K, clock=not args.no_clock)
+                    r, s2 = measure_decode(kvq, kdev, kvsynth, torch, sw, W, K, clock=not args.no_clock,
+                                           settle_calls=args.settle_calls)
                     del s2
                     subs[name] = compact(r)
             finally:
