@@ -20,6 +20,13 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+// Packed tile records are read once per decode call: their loads carry the non-temporal hint. On MI355X a plain
+// streaming read of a 1.6 GB buffer runs at 6.0-6.2 TB/s and the same read with non-temporal loads at 6.9-7.1 TB/s.
+// (The fp16 window rows, rewritten and reread every step, keep ordinary loads.) 16 bytes at p + 16 * i.
+__device__ __forceinline__ uint4 load_stream(const void *p, int i) {
+    return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p) + i));
+}
+
 constexpr int D = 128;
 constexpr int REC = 3072;
 // dense-and-sparse records: the 3072 bytes above, then the outlier section (key outliers per channel, value outliers
@@ -854,10 +861,10 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
     const int ol = l < 48 ? l : l - 48;   // SPARSE: lanes 0..47 load the outlier section (the rest reload a part)
     if (v0 < qend) {
         const uint8_t *rec = base + (int64_t)v0 * RECB;
-        kw = reinterpret_cast<const uint4 *>(rec)[l];
-        vw = reinterpret_cast<const uint4 *>(rec + 1024)[l];
-        sw = reinterpret_cast<const uint4 *>(rec + 2048)[l];
-        if constexpr (SPARSE) ow = reinterpret_cast<const uint4 *>(rec + REC)[ol];
+        kw = load_stream(rec, l);
+        vw = load_stream(rec + 1024, l);
+        sw = load_stream(rec + 2048, l);
+        if constexpr (SPARSE) ow = load_stream(rec + REC, ol);
         ci[0] = stage(sw, ow);
     }
     for (int v = v0; v < qend; ++v) {
@@ -869,9 +876,9 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
         asm volatile("" : "+s"(next_s));
         typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
         g_u32x4 *next_g = reinterpret_cast<g_u32x4 *>(next_s);
-        auto load_rec = [&](int off) { return __builtin_bit_cast(uint4, next_g[off / 16 + l]); };
+        auto load_rec = [&](int off) { return __builtin_bit_cast(uint4, __builtin_nontemporal_load(next_g + off / 16 + l)); };
         sw = load_rec(2048);
-        if constexpr (SPARSE) ow = reinterpret_cast<const uint4 *>(next + REC)[ol];
+        if constexpr (SPARSE) ow = load_stream(next + REC, ol);
 
         f4 acc0 = ci, acc1 = ci;   // tokens n (acc0) and 16 + n (acc1); rows (head kc, part r)
         if constexpr (SPARSE) {   // the key-outlier sums of tokens n and 16 + n of head kc, then cleared
@@ -944,7 +951,7 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
             for (int j = 0; j < 8; ++j) o[j] = mfma(j < 4 ? pa0 : pa1, expand8(nibbles(vw[j >> 1], j & 1)), o[j]);
         }
         asm volatile("" : "+s"(next_s));   // the base again from scalar registers (this is a later block)
-        vw = __builtin_bit_cast(uint4, reinterpret_cast<g_u32x4 *>(next_s)[64 + l]);
+        vw = __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<g_u32x4 *>(next_s) + 64 + l));
         if constexpr (SPARSE) {   // head kc's value-outlier sums of channels n + 16 j, then cleared (G1: row 0 only)
             wave_lds_order();
             // channel n + 16 j of head kc: group j / 2, index n + 16 (j % 2) within it

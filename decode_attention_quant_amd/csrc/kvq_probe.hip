@@ -8,21 +8,26 @@
 namespace {
 
 constexpr int kWaves = 2048;   // one 64-lane workgroup per wavefront, 8 per CU; one contiguous segment each
-constexpr int kVec = 8;        // 1 KB loads in flight per wavefront
+constexpr int kVec = 3;        // 1 KB loads in flight per wavefront
 
-// Wavefront w reads its contiguous segment of src (a multiple of 1 KB, the last one shorter) with 16-byte loads,
-// kVec consecutive kilobytes per iteration, folded by XOR into one word per lane, which is written so the loads are
-// kept. (A shape sweep on MI355X, 2048..65536 wavefronts with 4..16 loads in flight, gave 5.7-6.1 TB/s, best with
-// the fewest wavefronts; a grid-stride order with 8 MB between a wavefront's loads gave 5.5.)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Wavefront w reads its contiguous segment of src (a multiple of 1 KB, the last one shorter) with 16-byte
+// non-temporal loads, kVec consecutive kilobytes per iteration, folded by XOR into one word per lane, which is
+// written so the loads are kept. (A shape sweep on MI355X over 1.6 GB, 2048..4096 wavefronts with 3, 4 or 8 loads in
+// flight: 6.7-7.1 TB/s with non-temporal loads, best at 2048 wavefronts and 3 loads; 6.0-6.2 TB/s with plain loads.
+// An earlier plain-load sweep up to 65536 wavefronts and 16 loads gave 5.7-6.1 TB/s, and a grid-stride order with
+// 8 MB between a wavefront's loads 5.5.)
 __global__ __launch_bounds__(64) void hbm_read_kernel(const uint4 *src, size_t n16, size_t per, uint32_t *sink) {
     const size_t beg = (size_t)blockIdx.x * per;
     const size_t end = beg + per < n16 ? beg + per : n16;
     uint32_t acc = 0;
     size_t i = beg + threadIdx.x;
+    const u32x4 *s4 = reinterpret_cast<const u32x4 *>(src);
     for (; i + (kVec - 1) * 64 < end; i += kVec * 64) {
         uint4 b[kVec];
 #pragma unroll
-        for (int k = 0; k < kVec; ++k) b[k] = src[i + k * 64];
+        for (int k = 0; k < kVec; ++k) b[k] = __builtin_bit_cast(uint4, __builtin_nontemporal_load(s4 + i + k * 64));
 #pragma unroll
         for (int k = 0; k < kVec; ++k) acc ^= b[k].x ^ b[k].y ^ b[k].z ^ b[k].w;
     }
