@@ -362,30 +362,33 @@ __device__ __forceinline__ h8 expand8_b4(uint32_t w) {
     return r;
 }
 
-// x = (pa * sa.lo, pb * sb.lo) (or the high halves), hi = RN16(x), lo = RN16(x - hi), packed: x in binary32 (one
-// mixed-precision fma each), the high parts by one packed conversion, the exact remainders by mixed fmas that read
-// hi's halves, the low parts by a second packed conversion (six instructions at the full vector rate).
-__device__ __forceinline__ void split_lo(float pa, float pb, uint32_t sa, uint32_t sb, uint32_t &hi, uint32_t &lo) {
+// x = (pa * sa.lo, pb * sb.lo) (HI: the high halves of sa, sb), hi = RN16(x), then RN16(x - w hi) packed: the high
+// parts for w = 0, the low parts (x - hi is exact) for w = 1. x in binary32 (one mixed-precision fma each), hi by one
+// packed conversion, x - w hi by mixed fmas that read hi's halves, the result by a second packed conversion (six
+// instructions at the full vector rate).
+template <bool HI>
+__device__ __forceinline__ uint32_t split_part(float pa, float pb, uint32_t sa, uint32_t sb, float w) {
+    uint32_t part, hi;
     float x0, x1;
-    asm("v_fma_mix_f32 %2, %4, %6, 0 op_sel_hi:[0,1,0]\n\t"
-        "v_fma_mix_f32 %3, %5, %7, 0 op_sel_hi:[0,1,0]\n\t"
-        "v_cvt_pk_f16_f32 %0, %2, %3\n\t"
-        "v_fma_mix_f32 %2, -%0, 1.0, %2 op_sel_hi:[1,0,0]\n\t"
-        "v_fma_mix_f32 %3, -%0, 1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
-        "v_cvt_pk_f16_f32 %1, %2, %3"
-        : "=&v"(hi), "=&v"(lo), "=&v"(x0), "=&v"(x1)
-        : "v"(pa), "v"(pb), "v"(sa), "v"(sb));
-}
-__device__ __forceinline__ void split_hi(float pa, float pb, uint32_t sa, uint32_t sb, uint32_t &hi, uint32_t &lo) {
-    float x0, x1;
-    asm("v_fma_mix_f32 %2, %4, %6, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]\n\t"
-        "v_fma_mix_f32 %3, %5, %7, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]\n\t"
-        "v_cvt_pk_f16_f32 %0, %2, %3\n\t"
-        "v_fma_mix_f32 %2, -%0, 1.0, %2 op_sel_hi:[1,0,0]\n\t"
-        "v_fma_mix_f32 %3, -%0, 1.0, %3 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
-        "v_cvt_pk_f16_f32 %1, %2, %3"
-        : "=&v"(hi), "=&v"(lo), "=&v"(x0), "=&v"(x1)
-        : "v"(pa), "v"(pb), "v"(sa), "v"(sb));
+    if constexpr (HI)
+        asm("v_fma_mix_f32 %1, %4, %6, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]\n\t"
+            "v_fma_mix_f32 %2, %5, %7, 0 op_sel:[0,1,0] op_sel_hi:[0,1,0]\n\t"
+            "v_cvt_pk_f16_f32 %3, %1, %2\n\t"
+            "v_fma_mix_f32 %1, -%3, %8, %1 op_sel_hi:[1,0,0]\n\t"
+            "v_fma_mix_f32 %2, -%3, %8, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+            "v_cvt_pk_f16_f32 %0, %1, %2"
+            : "=&v"(part), "=&v"(x0), "=&v"(x1), "=&v"(hi)
+            : "v"(pa), "v"(pb), "v"(sa), "v"(sb), "v"(w));
+    else
+        asm("v_fma_mix_f32 %1, %4, %6, 0 op_sel_hi:[0,1,0]\n\t"
+            "v_fma_mix_f32 %2, %5, %7, 0 op_sel_hi:[0,1,0]\n\t"
+            "v_cvt_pk_f16_f32 %3, %1, %2\n\t"
+            "v_fma_mix_f32 %1, -%3, %8, %1 op_sel_hi:[1,0,0]\n\t"
+            "v_fma_mix_f32 %2, -%3, %8, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+            "v_cvt_pk_f16_f32 %0, %1, %2"
+            : "=&v"(part), "=&v"(x0), "=&v"(x1), "=&v"(hi)
+            : "v"(pa), "v"(pb), "v"(sa), "v"(sb), "v"(w));
+    return part;
 }
 
 }  // namespace
@@ -416,9 +419,9 @@ __device__ __forceinline__ void split_hi(float pa, float pb, uint32_t sa, uint32
 // the tile exceeds it.
 //
 // PV (MFMA). 16x16x32 fp16: B = the value codes of 16 channels (column n = channel 16j + n) and the tile's 32
-// tokens, one code word per lane (expanded exactly by the fp8 converter); A row g = p~[t] = p[t] s_V[g][t] for value
-// group g, split into fp16 high and low parts contracted in turn (rows 4..15 are zero). For channel block j
-// only row g = j/2 is kept. The zero-point term sum_t p z_V[g][t] is accumulated on the VALU; window tiles and the
+// tokens, one code word per lane (expanded exactly by the fp8 converter); A row g = the fp16 high part of
+// p~[t] = p[t] s_V[g][t] for value group g and row 4 + g its low part (rows 8..15 are zero), one MFMA per channel
+// block. For channel block j only rows g = j/2 and 4 + g are kept, and they are added once per split. The zero-point term sum_t p z_V[g][t] is accumulated on the VALU; window tiles and the
 // sink add their values on the VALU.
 //
 // Dense-and-sparse records (SPARSE). The outlier of a key channel's group decodes as its zero point z (code 0), so
@@ -790,35 +793,26 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
             lds_add(cg + 2 * ((vi >> 8) & 31u) + 1, l1);
         }
 
-        // PV: A rows g = n & 3 over tokens 8kg .. 8kg+7 in the expand8_b4 order (t0 t2 t4 t6 t1 t3 t5 t7); rows 4..15
-        // (outputs never used) are zero: zero operands draw less power than repeated ones
+        // PV: A row g = the high part of p~ of value group g, row 4 + g its low part, over tokens 8kg .. 8kg+7 in the
+        // expand8_b4 order (t0 t2 t4 t6 t1 t3 t5 t7); rows 8..15 (outputs never used) are zero: zero operands draw
+        // less power than repeated ones
         const int gA = n & 3;
-        const float *pz = n < 4 ? pbuf : reinterpret_cast<const float *>(smem + L::ZERO);
+        const float *pz = n < 8 ? pbuf : reinterpret_cast<const float *>(smem + L::ZERO);
+        const float wpart = n < 4 ? 0.0f : 1.0f;
         const uint4 svr = *reinterpret_cast<const uint4 *>(tl + V4_SCALE + 2 * (32 * gA + 8 * kg));
         const h8 zvh = __builtin_bit_cast(h8, *reinterpret_cast<const uint4 *>(tl + V4_ZERO + 2 * (32 * gA + 8 * kg)));
         const float4 pa = *reinterpret_cast<const float4 *>(pz + 8 * kg);
         const float4 pb = *reinterpret_cast<const float4 *>(pz + 8 * kg + 4);
-        uint32_t ah[4], alo[4];
-        split_lo(pa.x, pa.z, svr.x, svr.y, ah[0], alo[0]);
-        split_lo(pb.x, pb.z, svr.z, svr.w, ah[1], alo[1]);
-        split_hi(pa.y, pa.w, svr.x, svr.y, ah[2], alo[2]);
-        split_hi(pb.y, pb.w, svr.z, svr.w, ah[3], alo[3]);
-        const h8 Ahi = __builtin_bit_cast(h8, uint4{ah[0], ah[1], ah[2], ah[3]});
-        const h8 Alo = __builtin_bit_cast(h8, uint4{alo[0], alo[1], alo[2], alo[3]});
+        const h8 A = __builtin_bit_cast(h8, uint4{split_part<false>(pa.x, pa.z, svr.x, svr.y, wpart),
+                                                  split_part<false>(pb.x, pb.z, svr.z, svr.w, wpart),
+                                                  split_part<true>(pa.y, pa.w, svr.x, svr.y, wpart),
+                                                  split_part<true>(pb.y, pb.w, svr.z, svr.w, wpart)});
+        // (lanes 4..7 repeat the sums of lanes 0..3; only rows 0..3 of the sums are read at the end)
         gam += ((pa.x * (float)zvh[0] + pa.y * (float)zvh[1]) + (pa.z * (float)zvh[2] + pa.w * (float)zvh[3])) +
                ((pb.x * (float)zvh[4] + pb.y * (float)zvh[5]) + (pb.z * (float)zvh[6] + pb.w * (float)zvh[7]));
         const uint32_t *vwl = reinterpret_cast<const uint32_t *>(tl + V4_CODES);
 #pragma unroll
-        for (int j0 = 0; j0 < 8; j0 += 4) {   // high parts of four blocks, then their low parts (no back-to-back
-            h8 B[4];                          // dependence on one accumulator)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                B[j] = expand8_b4(vwl[4 * (16 * (j0 + j) + n) + kg]);
-                acc[j0 + j] = mfma(Ahi, B[j], acc[j0 + j]);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j0 + j] = mfma(Alo, B[j], acc[j0 + j]);
-        }
+        for (int j = 0; j < 8; ++j) acc[j] = mfma(A, expand8_b4(vwl[4 * (16 * j + n) + kg]), acc[j]);
         if constexpr (SPARSE) {   // the value-outlier sums of channels 2l, 2l+1
             wave_lds_order();
             const int4 cv = reinterpret_cast<const int4 *>(vacc)[l];
@@ -868,19 +862,22 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
         }
     }
 
-    // ---- partials of this split: lanes 0..15 hold channel 16j + n of the MFMA sums in acc[j][j / 2]
+    // ---- partials of this split: channel 16j + n of the MFMA sums is the high-part row j / 2 in acc[j][j / 2] of
+    // lane n plus the low-part row 4 + j / 2 in the same register of lane 16 + n
     float *obuf = red;
     float *gbuf = pbuf;
     lsum = rows_sum(row16_sum(lsum));
     gam = rows_sum(gam);   // lane n (any row): value group n & 3
     wave_lds_order();
-    if (l < 16) {
+    if (l < 32) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) obuf[16 * j + l] = acc[j][j >> 1];
+        for (int j = 0; j < 8; ++j) obuf[128 * (l >> 4) + 16 * j + (l & 15)] = acc[j][j >> 1];
     }
     if (l < 4) gbuf[l] = gam;
     wave_lds_order();
-    const float2 ov = reinterpret_cast<const float2 *>(obuf)[l];
+    const float2 oh = reinterpret_cast<const float2 *>(obuf)[l];
+    const float2 olo = reinterpret_cast<const float2 *>(obuf)[64 + l];
+    const float2 ov = {oh.x + olo.x, oh.y + olo.y};
     const float gz = gbuf[l >> 4];
     const int64_t row = (int64_t)bh * S + split;
     float2 res;
