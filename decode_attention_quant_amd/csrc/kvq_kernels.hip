@@ -20,9 +20,9 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// Packed tile records are read once per decode call: their loads carry the non-temporal hint. On MI355X a plain
-// streaming read of a 1.6 GB buffer runs at 6.0-6.2 TB/s and the same read with non-temporal loads at 6.9-7.1 TB/s.
-// (The fp16 window rows, rewritten and reread every step, keep ordinary loads.) 16 bytes at p + 16 * i.
+// Every byte of the cache is read once per decode call: the loads of tile records and fp16 window rows carry the
+// non-temporal hint. On MI355X a plain streaming read of a 1.6 GB buffer runs at 6.0-6.2 TB/s and the same read
+// with non-temporal loads at 6.9-7.1 TB/s. 16 bytes at p + 16 * i.
 __device__ __forceinline__ uint4 load_stream(const void *p, int i) {
     return __builtin_bit_cast(uint4, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p) + i));
 }
@@ -1013,8 +1013,8 @@ __device__ __forceinline__ void decode_pass1_body(const DecodeArgs &a, unsigned 
             const _Float16 *k1 = krow(r0 + min(16 + n, nv - 1)) + 8 * kc;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                kr[ks] = *reinterpret_cast<const h8 *>(k0 + 32 * ks);
-                kr[4 + ks] = *reinterpret_cast<const h8 *>(k1 + 32 * ks);
+                kr[ks] = __builtin_bit_cast(h8, load_stream(k0 + 32 * ks, 0));
+                kr[4 + ks] = __builtin_bit_cast(h8, load_stream(k1 + 32 * ks, 0));
             }
         };
         // transpose-read addressing: lane (n, kc) reads token 4 TQ + n / 4, channels 16 j + 4 (n % 4) .. + 3 and

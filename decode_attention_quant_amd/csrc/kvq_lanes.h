@@ -89,18 +89,19 @@ __device__ __forceinline__ void wave_lds_order() { asm volatile("" : : : "memory
 // the statement saves and restores). Issued from inline asm so that the compiler's wait insertion, which cannot tell
 // the destination from the other LDS buffers, does not drain the vector-memory counter before every LDS access; the
 // destination's readers wait explicitly (wait_vmcnt), and loads complete in order, so these extra loads can only
-// make the compiler's own counted waits stricter.
+// make the compiler's own counted waits stricter. Every caller streams data that a decode call reads once, so the
+// load carries the non-temporal hint (a plain streaming read of HBM runs at 6.0-6.2 TB/s on MI355X, with
+// non-temporal loads at 6.9-7.1 TB/s).
 __device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds_base) {
     uint32_t saved;
-    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+    asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off nt\n\ts_mov_b32 m0, %0"
                  : "=&s"(saved)
                  : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                  : "memory");
 }
 // The same with a uniform base address in scalar registers and a 32-bit per-lane byte offset (the global
-// scalar-base form: no per-lane 64-bit address arithmetic), for packed tile records: read once per decode call, so
-// the load carries the non-temporal hint (a plain streaming read of HBM runs at 6.0-6.2 TB/s on MI355X, with
-// non-temporal loads at 6.9-7.1 TB/s).
+// scalar-base form: no per-lane 64-bit address arithmetic), for packed tile records, also with the non-temporal
+// hint.
 __device__ __forceinline__ void lds_dma16_s(uint64_t base, uint32_t lane_off, uint32_t lds_base) {
     uint32_t saved;
     asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\tglobal_load_lds_dwordx4 %1, %2 nt\n\ts_mov_b32 m0, %0"
