@@ -240,8 +240,8 @@ class ClockProbe:
 
 def hbm_read_ceiling(nbytes, reps=20):
     """The box's achievable HBM read bandwidth: a plain streaming read (`libkvq_probe.so`, every 16-byte chunk of
-    the buffer loaded once) of a buffer as large as one decode call's bytes, `reps` back-to-back launches between two
-    HIP events on the current stream."""
+    the buffer loaded once, with the non-temporal hint the decode kernels' loads also carry) of a buffer as large as
+    one decode call's bytes, `reps` back-to-back launches between two HIP events on the current stream."""
     import torch
     lib = _probe_lib()
     nbytes = (int(nbytes) + 15) // 16 * 16
