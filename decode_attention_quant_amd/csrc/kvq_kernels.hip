@@ -525,11 +525,11 @@ __device__ __forceinline__ void merge_splits(const float *part_o, const float *p
 // and the two rows of group j / 2 (high and low part) are added once, before the partials are stored. The value
 // zero-point term sum_t p z_V[g][t] is accumulated on the VALU.
 //
-// Per-wavefront LDS: the tile's scales/zeros and the folded query, both written for tile v + 1 at the end of
-// iteration v after every read of tile v has been issued (a wavefront's LDS operations complete in order); the
-// probability exchange and the P V operands; the fp16 window value tile (8 KB, reusing the first region). Rows that lanes read together
-// are padded so that they fall in different LDS banks (64 banks of 4 bytes): unpadded, the eight 256-byte rows of
-// the folded query all start in bank 0 and every A-operand read of the score contraction is an 8-way conflict.
+// Per-wavefront LDS: the tile's scales/zeros and the folded query, both written for tile v + 1 at the end of iteration
+// v after every read of tile v has been issued (a wavefront's LDS operations complete in order); the probability
+// exchange and the P V operands; the fp16 window value tile (8 KB, reusing the first region). Rows that lanes read
+// together are padded so that they fall in different LDS banks (64 banks of 4 bytes): unpadded, the eight 256-byte rows
+// of the folded query all start in bank 0 and every A-operand read of the score contraction is an 8-way conflict.
 constexpr int LDS_SZ = 0;            // s_K[128], z_K[128] (fp16), then s_V[4][32], z_V[4][32] with each group's 64 bytes
                                      // followed by 16 bytes of padding (1152 bytes)
 constexpr int QT_ROW = 136;          // fp16 per (part, head) row of the folded query: 128 channels + 8 padding
@@ -596,26 +596,26 @@ __device__ __forceinline__ int sz_off(int x) { return x < 512 ? x : x + 16 * ((x
 // head, chunk): when the appended token completes a window block, the chunk-0 workgroup writes that block's record
 // ahead (from the window rows below the token and the token itself, from the input), beside the attention. It is
 // dispatched after the splits (first, it cost the steps ~1 us: the splits' own dispatch order matters more), and its
-// ~10 us of work ends well within a step. The other rows are the splits. The new token is attended straight from the input (its window row
-// is written only at the end). After its partials are stored, a split counts itself in sync[(b, KV head, chunk)]; the
-// last of the splits merges them (the pass-2 code) and counts the chunk in sync[b], as does every block workgroup
-// once its loads are complete; the last of the sequence's 2 * KV heads * chunks counts writes the new window rows
-// (several chunks per KV head) and the lengths, by when every workgroup of the sequence has read them. Counters are
-// reset by the workgroup that completes them. No workgroup waits for another.
-// Ordering: the tickets are relaxed agent-scope atomics, so they carry no happens-before edge of the HIP memory
-// model. The merge is correct because of three hardware facts this kernel relies on instead: every value another
-// workgroup reads (the split partials) is written with agent-scope atomic stores, which write through to the
-// device's coherence point, and read with agent-scope atomic loads, which read from it (never from a non-coherent
-// per-XCD L2 line); a workgroup waits for all its memory operations (s_waitcnt vmcnt(0): stores acknowledged,
-// loads returned) before taking its ticket; the ticket is itself performed at the coherence point. A plain store
-// that another workgroup of the launch read would need a release/acquire pair instead (at agent scope an L2
-// write-back and invalidate per workgroup, which costs the step several times its length).
+// ~10 us of work ends well within a step. The other rows are the splits. The new token is attended straight from the
+// input (its window row is written only at the end). After its partials are stored, a split counts itself in
+// sync[(b, KV head, chunk)]; the last of the splits merges them (the pass-2 code) and counts the chunk in sync[b], as
+// does every block workgroup once its loads are complete; the last of the sequence's 2 * KV heads * chunks counts
+// writes the new window rows (several chunks per KV head) and the lengths, by when every workgroup of the sequence has
+// read them. Counters are reset by the workgroup that completes them. No workgroup waits for another. Ordering: the
+// tickets are relaxed agent-scope atomics, so they carry no happens-before edge of the HIP memory model. The merge is
+// correct because of three hardware facts this kernel relies on instead: every value another workgroup reads (the split
+// partials) is written with agent-scope atomic stores, which write through to the device's coherence point, and read
+// with agent-scope atomic loads, which read from it (never from a non-coherent per-XCD L2 line); a workgroup waits for
+// all its memory operations (s_waitcnt vmcnt(0): stores acknowledged, loads returned) before taking its ticket; the
+// ticket is itself performed at the coherence point. A plain store that another workgroup of the launch read would need
+// a release/acquire pair instead (at agent scope an L2 write-back and invalidate per workgroup, which costs the step
+// several times its length).
 //
-// G1 (one query head per KV head): head row 0 of the score operand holds the head; with dense records rows 1..3
-// are zero (with dense-and-sparse records they repeat it), and the softmax state of row 0 drives every accumulator
-// row. PV puts the high and low parts of p~ in different A-operand rows (row 4 part + group) straight from the
-// probability exchange, with no regrouping pass: 8 MFMAs per tile (rows 8..15 zero with dense records). The parts are added across lanes
-// (n, 0) and (n, 1) once, before the partials are stored.
+// G1 (one query head per KV head): head row 0 of the score operand holds the head; with dense records rows 1..3 are
+// zero (with dense-and-sparse records they repeat it), and the softmax state of row 0 drives every accumulator row. PV
+// puts the high and low parts of p~ in different A-operand rows (row 4 part + group) straight from the probability
+// exchange, with no regrouping pass: 8 MFMAs per tile (rows 8..15 zero with dense records). The parts are added across
+// lanes (n, 0) and (n, 1) once, before the partials are stored.
 //
 // SPARSE (dense-and-sparse records, uniform lengths): a key outlier decodes as its zero point inside the dense
 // contraction (its code is 0), so its token's score misses q'_c (o - z_c); lane (n, kc) adds these for its eight

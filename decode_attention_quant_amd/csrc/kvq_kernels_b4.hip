@@ -408,12 +408,12 @@ __device__ __forceinline__ uint32_t split_part(float pa, float pb, uint32_t sa, 
 // pair's share of the score of token u is
 //     cos(u theta) (a0 x0 + a1 x1 + alpha) + sin(u theta) (b0 x0 + b1 x1 + beta)
 // with a0 = qr0 s0, a1 = qr1 s1, alpha = qr0 z0 + qr1 z1, b0 = qr1 s0, b1 = -qr0 s1, beta = qr1 z0 - qr0 z1: the
-// dot product of the query with the dequantized key rotated by m0 + u, expanded by angle addition. Lane l computes
-// the six coefficients of pair l once per tile and shares them through LDS. The cos/sin of u theta for a lane's 32
-// (token, pair) combinations are the same for every tile and stay in registers; the rotation by the tile start
-// advances by 32 theta per tile (recomputed from the position every 16 tiles). Window tiles use the same expansion with the
-// fp16 keys (s = 1, z = 0). Partial sums of the 16 lanes of a token are added through LDS. The query carries the
-// softmax scale times log2(e), so scores are in the log2 domain.
+// dot product of the query with the dequantized key rotated by m0 + u, expanded by angle addition. Lane l computes the
+// six coefficients of pair l once per tile and shares them through LDS. The cos/sin of u theta for a lane's 32 (token,
+// pair) combinations are the same for every tile and stay in registers; the rotation by the tile start advances by 32
+// theta per tile (recomputed from the position every 16 tiles). Window tiles use the same expansion with the fp16 keys
+// (s = 1, z = 0). Partial sums of the 16 lanes of a token are added through LDS. The query carries the softmax scale
+// times log2(e), so scores are in the log2 domain.
 //
 // Softmax. Lagged maximum: the running maximum is raised (and every accumulator rescaled) only when some score of
 // the tile exceeds it.
@@ -421,8 +421,9 @@ __device__ __forceinline__ uint32_t split_part(float pa, float pb, uint32_t sa, 
 // PV (MFMA). 16x16x32 fp16: B = the value codes of 16 channels (column n = channel 16j + n) and the tile's 32
 // tokens, one code word per lane (expanded exactly by the fp8 converter); A row g = the fp16 high part of
 // p~[t] = p[t] s_V[g][t] for value group g and row 4 + g its low part (rows 8..15 are zero), one MFMA per channel
-// block. For channel block j only rows g = j/2 and 4 + g are kept, and they are added once per split. The zero-point term sum_t p z_V[g][t] is accumulated on the VALU; window tiles and the
-// sink add their values on the VALU.
+// block. For channel block j only rows g = j/2 and 4 + g are kept, and they are added once per split. The
+// zero-point term sum_t p z_V[g][t] is accumulated on the VALU; window tiles and the sink add their values on the
+// VALU.
 //
 // Dense-and-sparse records (SPARSE). The outlier of a key channel's group decodes as its zero point z (code 0), so
 // the score of its token u misses d (dq/dk_c) with d = o - z: for pair l this is d (cos(u theta) qr0 + sin(u theta)
@@ -807,7 +808,7 @@ __global__ __launch_bounds__(64) void decode_b4_pass1_kernel(DecodeB4Args a) {
                                                   split_part<false>(pb.x, pb.z, svr.z, svr.w, wpart),
                                                   split_part<true>(pa.y, pa.w, svr.x, svr.y, wpart),
                                                   split_part<true>(pb.y, pb.w, svr.z, svr.w, wpart)});
-        // (lanes 4..7 repeat the sums of lanes 0..3; only rows 0..3 of the sums are read at the end)
+        // (lanes 4..7 repeat the zero-point sums of lanes 0..3; only those of lanes 0..3 are stored at the end)
         gam += ((pa.x * (float)zvh[0] + pa.y * (float)zvh[1]) + (pa.z * (float)zvh[2] + pa.w * (float)zvh[3])) +
                ((pb.x * (float)zvh[4] + pb.y * (float)zvh[5]) + (pb.z * (float)zvh[6] + pb.w * (float)zvh[7]));
         const uint32_t *vwl = reinterpret_cast<const uint32_t *>(tl + V4_CODES);
